@@ -320,17 +320,17 @@ def build_coarse(st: UnitState, *, coarse_tokens_per_centroid: int = 128, iters:
     st.coffsets = np.zeros(cap + 1, np.int32)
     st.cmembers = np.zeros(st.capacity_clusters, np.int32)
     st.cJ = []
-    g0, pos = 0, 0
+    g0 = 0
     for b in st.blocks:
         D = clusters_for(b.L, coarse_tokens_per_centroid)
         J = np.zeros(max(iters, 1))
         s0 = block_stream(seed, unit, b.index, 1)
+        # the block's member list starts at its first fine cluster id
         n = _lib.orc_coarse_block(_d(st.kbar), _d(st.vbar), _i(st.sizes), d, b.c0, b.C, g0, D, iters,
-                                  st.storage, s0, pos, _d(st.cmu), _d(st.ckbar), _d(st.cvbar),
+                                  st.storage, s0, b.c0, _d(st.cmu), _d(st.ckbar), _d(st.cvbar),
                                   _i(st.csizes), _i(st.parent), _i(st.coffsets), _i(st.cmembers), _d(J))
         if n < 0:
             raise RuntimeError("orc_coarse_block failed (fewer non-empty fine clusters than coarse ones?)")
-        pos += n
         g0 += D
         st.cJ.append(J[:iters])
     st.n_coarse = g0
@@ -378,6 +378,32 @@ def decode_unit_hier(q, K, V, n_total: int, st: UnitState, budget: int, cand_bud
                                  _d(np.ascontiguousarray(st.ckbar[:D])), _d(np.ascontiguousarray(st.cvbar[:D])),
                                  _i(st.csizes), D, cand_budget, budget, _d(out), _i(csel), _i(sel), _d(s), _d(cs))
     return DecodeResult(out, sel, s, np.zeros(C), int(taken), csel, cs)
+
+
+def decode_with_selection(q, K, V, n_total: int, st: UnitState, selected, mode: int = 0) -> np.ndarray:
+    """The combine of one decode step for a given selection (1 = exact) of
+    the flat clusters; used to compare outputs when two correct selections
+    differ only among near-equal scores."""
+    q, K, V = f64(q), f64(K), f64(V)
+    G, d = q.shape
+    C = st.n_clusters
+    sel = np.ascontiguousarray(selected, dtype=np.int32)
+    s = np.zeros((G, C))
+    r = np.zeros(C)
+    kbar = np.ascontiguousarray(st.kbar[:C])
+    vbar = np.ascontiguousarray(st.vbar[:C])
+    _lib.orc_scores(_d(q), G, d, _d(kbar), C, _d(s), _d(r))
+    exact = np.array([1 if i >= st.n_clustered else sel[st.assign[i]] for i in range(n_total)], np.int32)
+    sizes = np.ascontiguousarray(st.sizes[:C])
+    pseudo = ((mode == 0) & (sizes > 0) & (sel == 0)).astype(np.int32)
+    out = np.zeros((G, d))
+    for g in range(G):
+        og = np.zeros(d)
+        sg = np.ascontiguousarray(s[g])
+        _lib.orc_combine(_d(np.ascontiguousarray(q[g])), d, _d(K), _d(V), n_total, _i(exact), _d(sg), _d(vbar),
+                         _i(sizes), _i(pseudo), C, _d(og))
+        out[g] = og
+    return out
 
 
 def parallel_map(fn, items, threads: Optional[int] = None):

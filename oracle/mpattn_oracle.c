@@ -285,7 +285,23 @@ int orc_coarse_block(const double* kbar, const double* vbar, const int32_t* size
                      double* J) {
     int32_t m = 0;
     for (int32_t c = 0; c < C; ++c) m += sizes[c0 + c] > 0;
-    if (D > m) return -1; /* caller guarantees at least D non-empty fine clusters */
+    /* Reading: with fewer non-empty fine clusters than coarse ones, only m
+     * coarse clusters are seeded; the others stay empty (zero centroids). */
+    const int32_t Dfull = D;
+    if (D > m) D = m;
+    for (int32_t g = D; g < Dfull; ++g) {
+        for (int32_t j = 0; j < d; ++j) {
+            cmu[(int64_t)(g0 + g) * d + j] = 0.0;
+            ckbar[(int64_t)(g0 + g) * d + j] = 0.0;
+            cvbar[(int64_t)(g0 + g) * d + j] = 0.0;
+        }
+        csizes[g0 + g] = 0;
+    }
+    if (m == 0) {
+        for (int32_t c = 0; c < C; ++c) parent[c0 + c] = -1;
+        for (int32_t g = 0; g <= Dfull; ++g) coffsets[g0 + g] = cpos0;
+        return 0;
+    }
     double* pts = (double*)malloc(sizeof(double) * (size_t)m * d);
     double* w = (double*)malloc(sizeof(double) * (size_t)m);
     int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)m);
@@ -327,7 +343,7 @@ int orc_coarse_block(const double* kbar, const double* vbar, const int32_t* size
         csizes[g0 + g] = (int32_t)tot;
         for (int32_t j = 0; j < d; ++j) cv[j] = tot > 0 ? orc_round_storage(cv[j] / tot, storage) : 0.0;
     }
-    coffsets[g0 + D] = pos;
+    for (int32_t g = D; g <= Dfull; ++g) coffsets[g0 + g] = pos;
     free(pts); free(w); free(ids); free(init_idx); free(local); free(counts);
     return pos - cpos0;
 }

@@ -1,0 +1,389 @@
+// api.hip -- the C ABI of include/mpattn.h: argument validation, workspace
+// layout and the launch sequence of each entry point.  Everything is enqueued
+// on the caller's stream; nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mpattn.h"
+#include "kernels.hpp"
+
+using namespace mpa;
+
+namespace {
+
+constexpr int kD = 128;
+constexpr size_t kAlign = 256;
+constexpr int kMaxFinePerBlockHier = 2048;
+constexpr int kMaxCoarsePerBlock = 64;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_hier(const mpattn_params* p) { return p->coarse_tokens_per_centroid > 0; }
+
+mpattn_status check_params(const mpattn_params* p) {
+    if (!p) return MPATTN_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 || p->capacity_tokens < 1 ||
+        p->tokens_per_centroid < 1 || p->cluster_block < 1 || p->build_iters < 1 || p->update_iters < 1 ||
+        p->splits < 0 || p->coarse_tokens_per_centroid < 0 || p->head_dim < 1)
+        return MPATTN_ERR_INVALID_ARG;
+    if (p->n_q_heads % p->n_kv_heads != 0) return MPATTN_ERR_INVALID_ARG;
+    if (p->dtype != MPATTN_F32 && p->dtype != MPATTN_BF16) return MPATTN_ERR_INVALID_ARG;
+    if (p->head_dim != kD) return MPATTN_ERR_UNSUPPORTED;
+    const int G = p->n_q_heads / p->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return MPATTN_ERR_UNSUPPORTED;
+    if (p->cluster_block > kMaxBlock) return MPATTN_ERR_UNSUPPORTED;
+    if (p->tokens_per_centroid > p->cluster_block) return MPATTN_ERR_INVALID_ARG;
+    if ((int64_t)p->batch * p->n_kv_heads > 65535) return MPATTN_ERR_UNSUPPORTED;  // grid y
+    if (is_hier(p)) {
+        if (p->coarse_iters < 1 || p->coarse_candidate_tokens < 0) return MPATTN_ERR_INVALID_ARG;
+        if (ceil_div(p->cluster_block, p->tokens_per_centroid) > kMaxFinePerBlockHier ||
+            ceil_div(p->cluster_block, p->coarse_tokens_per_centroid) > kMaxCoarsePerBlock)
+            return MPATTN_ERR_UNSUPPORTED;
+    }
+    return MPATTN_OK;
+}
+
+int default_splits(int units) {
+    int s = 1024 / (units > 0 ? units : 1);
+    if (s < 1) s = 1;
+    if (s > 64) s = 64;
+    return s;
+}
+
+int splits_of(const mpattn_params* p) {
+    return p->splits > 0 ? p->splits : default_splits(p->batch * p->n_kv_heads);
+}
+
+// Decode workspace regions.
+struct DecodeWs {
+    float* s;        // [U][Cmax][G]
+    float* r;        // [U][Cmax]
+    int32_t* rows;   // [U][Nmax]
+    int32_t* plist;  // [U][Cmax]
+    int32_t* counts; // [U][4]
+    float* part_ml;  // [U][G][S][2]
+    float* part_acc; // [U][G][S][d]
+    // hierarchy
+    float* cs;        // [U][Dmax][G]
+    float* cr;        // [U][Dmax]
+    int32_t* crows;   // [U][Cmax]
+    int32_t* cplist;  // [U][Dmax]
+    int32_t* ccounts; // [U][4]
+    float* fr;        // [U][Cmax]
+    int32_t* fids;    // [U][Cmax]
+    size_t bytes;
+};
+
+DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char* base) {
+    const size_t U = (size_t)p->batch * p->n_kv_heads;
+    const size_t G = (size_t)(p->n_q_heads / p->n_kv_heads);
+    const size_t N = (size_t)p->capacity_tokens;
+    const size_t S = (size_t)splits_of(p);
+    DecodeWs w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* ptr = base ? base + off : nullptr;
+        off += align_up(bytes);
+        return ptr;
+    };
+    w.s = (float*)take(U * Cmax * G * 4);
+    w.r = (float*)take(U * Cmax * 4);
+    w.rows = (int32_t*)take(U * N * 4);
+    w.plist = (int32_t*)take(U * Cmax * 4);
+    w.counts = (int32_t*)take(U * 4 * 4);
+    w.part_ml = (float*)take(U * G * S * 2 * 4);
+    w.part_acc = (float*)take(U * G * S * kD * 4);
+    if (is_hier(p)) {
+        w.cs = (float*)take(U * Dmax * G * 4);
+        w.cr = (float*)take(U * Dmax * 4);
+        w.crows = (int32_t*)take(U * Cmax * 4);
+        w.cplist = (int32_t*)take(U * Dmax * 4);
+        w.ccounts = (int32_t*)take(U * 4 * 4);
+        w.fr = (float*)take(U * Cmax * 4);
+        w.fids = (int32_t*)take(U * Cmax * 4);
+    }
+    w.bytes = off;
+    return w;
+}
+
+mpattn_status hip_status(hipError_t e) { return e == hipSuccess ? MPATTN_OK : MPATTN_ERR_HIP; }
+
+#define MPA_TRY(expr)                                  \
+    do {                                               \
+        hipError_t e_ = (expr);                        \
+        if (e_ != hipSuccess) return MPATTN_ERR_HIP;   \
+    } while (0)
+
+mpattn_status check_state(const mpattn_params* p, const mpattn_state* st) {
+    if (!st || !st->key_centroids || !st->value_centroids || !st->key_centroids_f32 || !st->sizes || !st->offsets ||
+        !st->token_ids || !st->assign)
+        return MPATTN_ERR_INVALID_ARG;
+    if ((st->sorted_keys == nullptr) != (st->sorted_values == nullptr)) return MPATTN_ERR_INVALID_ARG;
+    if (st->capacity_clusters < 1) return MPATTN_ERR_INVALID_ARG;
+    if (st->n_clustered < 0 || st->n_clusters < 0 || st->n_coarse < 0 || st->n_blocks < 0)
+        return MPATTN_ERR_INVALID_ARG;
+    if (is_hier(p)) {
+        if (!st->coarse_key_centroids || !st->coarse_value_centroids || !st->coarse_key_centroids_f32 ||
+            !st->coarse_sizes || !st->coarse_offsets || !st->coarse_members || !st->parent ||
+            st->capacity_coarse < 1)
+            return MPATTN_ERR_INVALID_ARG;
+    }
+    return MPATTN_OK;
+}
+
+// Clusters the blocks of `br` for every unit: init, `iters` Lloyd rounds,
+// value centroids, optional sorted copy, optional coarse level.
+mpattn_status run_blocks(const mpattn_params* p, const void* k, const void* v, mpattn_state* st, BlockRange br,
+                         int iters, int32_t n_new_clusters, int32_t d_base, hipStream_t s) {
+    const UnitGeom g{p->batch * p->n_kv_heads, p->capacity_tokens, st->capacity_clusters};
+    MPA_TRY(launch_kmeans_init(p->dtype, k, g, br, p->seed, st->key_centroids_f32, st->key_centroids, s));
+    for (int it = 0; it < iters; ++it) {
+        MPA_TRY(launch_kmeans_assign(p->dtype, k, g, br, st->key_centroids, st->assign, s));
+        MPA_TRY(launch_kmeans_csr(st->assign, g, br, st->sizes, st->offsets, st->token_ids, s));
+        MPA_TRY(launch_segmented_mean(p->dtype, k, g, br.c_base, n_new_clusters, st->sizes, st->offsets,
+                                      st->token_ids, st->key_centroids_f32, st->key_centroids, false, s));
+    }
+    MPA_TRY(launch_segmented_mean(p->dtype, v, g, br.c_base, n_new_clusters, st->sizes, st->offsets, st->token_ids,
+                                  nullptr, st->value_centroids, true, s));
+    if (st->sorted_keys)
+        MPA_TRY(launch_sorted_copy(p->dtype, k, v, g, br.p_base, br.n_end - br.p_base, st->token_ids,
+                                   st->sorted_keys, st->sorted_values, s));
+    if (is_hier(p)) {
+        CoarseRange cr{br, d_base, p->coarse_tokens_per_centroid,
+                       (int32_t)ceil_div(p->cluster_block, p->coarse_tokens_per_centroid), st->capacity_coarse};
+        MPA_TRY(launch_coarse_build(p->dtype, g, cr, p->seed, p->coarse_iters, st->key_centroids,
+                                    st->value_centroids, st->sizes, st->coarse_key_centroids_f32,
+                                    st->coarse_key_centroids, st->coarse_value_centroids, st->coarse_sizes,
+                                    st->parent, st->coarse_offsets, st->coarse_members, s));
+    }
+    return MPATTN_OK;
+}
+
+const char* kFlatStages[] = {"score", "select", "attend", "merge"};
+const char* kHierStages[] = {"score_coarse", "select_coarse", "score_fine", "select_fine", "attend", "merge"};
+
+}  // namespace
+
+extern "C" {
+
+const char* mpattn_status_string(mpattn_status status) {
+    switch (status) {
+        case MPATTN_OK: return "ok";
+        case MPATTN_ERR_INVALID_ARG: return "invalid argument";
+        case MPATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MPATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case MPATTN_ERR_CAPACITY: return "state capacity exceeded";
+        case MPATTN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t mpattn_max_clusters(const mpattn_params* p) {
+    if (check_params(p) != MPATTN_OK) return 0;
+    const int64_t N = p->capacity_tokens;
+    const int64_t c = ceil_div(N, p->tokens_per_centroid) + ceil_div(N, p->cluster_block) + 1;
+    return c > INT32_MAX ? 0 : (int32_t)c;
+}
+
+int32_t mpattn_max_coarse(const mpattn_params* p) {
+    if (check_params(p) != MPATTN_OK || !is_hier(p)) return 0;
+    const int64_t N = p->capacity_tokens;
+    const int64_t c = ceil_div(N, p->coarse_tokens_per_centroid) + ceil_div(N, p->cluster_block) + 1;
+    return c > INT32_MAX ? 0 : (int32_t)c;
+}
+
+size_t mpattn_workspace_bytes(const mpattn_params* p, int32_t capacity_clusters, int32_t capacity_coarse,
+                              int32_t op) {
+    if (check_params(p) != MPATTN_OK || capacity_clusters < 1 || capacity_coarse < 0) return (size_t)-1;
+    if (op == MPATTN_OP_BUILD || op == MPATTN_OP_UPDATE) return 0;
+    if (op != MPATTN_OP_DECODE) return (size_t)-1;
+    return layout_decode(p, capacity_clusters, capacity_coarse, nullptr).bytes;
+}
+
+mpattn_status mpattn_build_clusters(const mpattn_params* p, const void* k, const void* v, int32_t n_tokens,
+                                    mpattn_state* st, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    mpattn_status rc = check_params(p);
+    if (rc != MPATTN_OK) return rc;
+    if (!k || !v) return MPATTN_ERR_INVALID_ARG;
+    if ((rc = check_state(p, st)) != MPATTN_OK) return rc;
+    if (n_tokens < 1) return MPATTN_ERR_INVALID_ARG;
+    if (n_tokens > p->capacity_tokens) return MPATTN_ERR_CAPACITY;
+    const int32_t Bc = p->cluster_block, r = p->tokens_per_centroid;
+    const int32_t nb = (int32_t)ceil_div(n_tokens, Bc);
+    const int32_t cfull = (int32_t)ceil_div(Bc, r);
+    const int32_t last = n_tokens - (nb - 1) * Bc;
+    const int64_t C = (int64_t)(nb - 1) * cfull + ceil_div(last, r);
+    if (C > st->capacity_clusters) return MPATTN_ERR_CAPACITY;
+    int64_t D = 0;
+    if (is_hier(p)) {
+        const int32_t dfull = (int32_t)ceil_div(Bc, p->coarse_tokens_per_centroid);
+        D = (int64_t)(nb - 1) * dfull + ceil_div(last, p->coarse_tokens_per_centroid);
+        if (D > st->capacity_coarse) return MPATTN_ERR_CAPACITY;
+    }
+    const BlockRange br{0, n_tokens, 0, Bc, r, cfull, 0, nb};
+    rc = run_blocks(p, k, v, st, br, p->build_iters, (int32_t)C, 0, (hipStream_t)stream);
+    if (rc != MPATTN_OK) return rc;
+    st->n_clustered = n_tokens;
+    st->n_clusters = (int32_t)C;
+    st->n_coarse = (int32_t)D;
+    st->n_blocks = nb;
+    return MPATTN_OK;
+}
+
+mpattn_status mpattn_update_window(const mpattn_params* p, const void* k, const void* v, int32_t n_tokens_total,
+                                   mpattn_state* st, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    mpattn_status rc = check_params(p);
+    if (rc != MPATTN_OK) return rc;
+    if (!k || !v) return MPATTN_ERR_INVALID_ARG;
+    if ((rc = check_state(p, st)) != MPATTN_OK) return rc;
+    if (n_tokens_total < st->n_clustered) return MPATTN_ERR_INVALID_ARG;
+    if (n_tokens_total > p->capacity_tokens) return MPATTN_ERR_CAPACITY;
+    const int32_t Bc = p->cluster_block, r = p->tokens_per_centroid;
+    const int32_t nb = (n_tokens_total - st->n_clustered) / Bc;
+    if (nb == 0) return MPATTN_OK;
+    const int32_t cfull = (int32_t)ceil_div(Bc, r);
+    const int64_t C = (int64_t)st->n_clusters + (int64_t)nb * cfull;
+    if (C > st->capacity_clusters) return MPATTN_ERR_CAPACITY;
+    int64_t D = st->n_coarse;
+    if (is_hier(p)) {
+        D += (int64_t)nb * ceil_div(Bc, p->coarse_tokens_per_centroid);
+        if (D > st->capacity_coarse) return MPATTN_ERR_CAPACITY;
+    }
+    const BlockRange br{st->n_clustered, st->n_clustered + nb * Bc, st->n_clusters, Bc, r, cfull, st->n_blocks, nb};
+    rc = run_blocks(p, k, v, st, br, p->update_iters, nb * cfull, st->n_coarse, (hipStream_t)stream);
+    if (rc != MPATTN_OK) return rc;
+    st->n_clustered += nb * Bc;
+    st->n_clusters = (int32_t)C;
+    st->n_coarse = (int32_t)D;
+    st->n_blocks += nb;
+    return MPATTN_OK;
+}
+
+int32_t mpattn_decode_stage_count(const mpattn_params* p) {
+    if (check_params(p) != MPATTN_OK) return 0;
+    return is_hier(p) ? 6 : 4;
+}
+
+const char* mpattn_decode_stage_name(const mpattn_params* p, int32_t stage) {
+    const int32_t n = mpattn_decode_stage_count(p);
+    if (stage < 0 || stage >= n) return nullptr;
+    return is_hier(p) ? kHierStages[stage] : kFlatStages[stage];
+}
+
+mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void* k, const void* v,
+                               int32_t n_tokens_total, const mpattn_state* st, int32_t token_budget, int32_t mode,
+                               float* out, void* workspace, size_t workspace_bytes, void* stream,
+                               const mpattn_decode_debug* debug, int32_t first_stage, int32_t last_stage) {
+    mpattn_status rc = check_params(p);
+    if (rc != MPATTN_OK) return rc;
+    if (!q || !k || !v || !out) return MPATTN_ERR_INVALID_ARG;
+    if ((rc = check_state(p, st)) != MPATTN_OK) return rc;
+    if (st->n_clusters < 1 || st->n_clusters > st->capacity_clusters) return MPATTN_ERR_INVALID_ARG;
+    if (n_tokens_total < st->n_clustered || n_tokens_total > p->capacity_tokens) return MPATTN_ERR_INVALID_ARG;
+    if (token_budget < 0) return MPATTN_ERR_INVALID_ARG;
+    if (mode != MPATTN_MODE_MULTIPOLE && mode != MPATTN_MODE_OMIT) return MPATTN_ERR_INVALID_ARG;
+    const bool hier = is_hier(p);
+    if (hier && mode != MPATTN_MODE_MULTIPOLE) return MPATTN_ERR_UNSUPPORTED;
+    if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
+    const int32_t n_stages = hier ? 6 : 4;
+    if (first_stage < 0 || last_stage >= n_stages || first_stage > last_stage) return MPATTN_ERR_INVALID_ARG;
+    const DecodeWs need = layout_decode(p, st->capacity_clusters, st->capacity_coarse, nullptr);
+    if (!workspace || workspace_bytes < need.bytes) return MPATTN_ERR_WORKSPACE;
+    const DecodeWs w = layout_decode(p, st->capacity_clusters, st->capacity_coarse, (char*)workspace);
+
+    const hipStream_t s = (hipStream_t)stream;
+    const int U = p->batch * p->n_kv_heads;
+    const int G = p->n_q_heads / p->n_kv_heads;
+    const int S = splits_of(p);
+    const int32_t Cmax = st->capacity_clusters, Dmax = st->capacity_coarse, N = p->capacity_tokens;
+    const int32_t C = st->n_clusters;
+    const bool sorted = st->sorted_keys != nullptr;
+    const int32_t want_pseudo = mode == MPATTN_MODE_MULTIPOLE ? 1 : 0;
+
+    for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
+        const char* name = hier ? kHierStages[stage] : kFlatStages[stage];
+        const bool attend = name[0] == 'a', merge = name[0] == 'm';
+        if (!hier && stage == 0) {
+            ScoreArgs a{q, st->key_centroids, Cmax, C, nullptr, nullptr, nullptr, 0, w.s, w.r, Cmax, nullptr,
+                        p->n_q_heads, p->n_kv_heads};
+            MPA_TRY(launch_score(p->dtype, G, a, U, s));
+        } else if (!hier && stage == 1) {
+            SelectArgs a{w.r, Cmax, nullptr, st->sizes, Cmax, st->offsets, C, nullptr, token_budget, want_pseudo,
+                         w.rows, N, w.plist, Cmax, w.counts,
+                         debug ? debug->selected : nullptr, C};
+            MPA_TRY(launch_select(a, U, s));
+        } else if (hier && stage == 0) {
+            ScoreArgs a{q, st->coarse_key_centroids, Dmax, st->n_coarse, nullptr, nullptr, nullptr, 0, w.cs, w.cr,
+                        Dmax, nullptr, p->n_q_heads, p->n_kv_heads};
+            MPA_TRY(launch_score(p->dtype, G, a, U, s));
+        } else if (hier && stage == 1) {
+            SelectArgs a{w.cr, Dmax, nullptr, st->coarse_sizes, Dmax, st->coarse_offsets, st->n_coarse, nullptr,
+                         p->coarse_candidate_tokens, want_pseudo, w.crows, Cmax, w.cplist, Dmax, w.ccounts,
+                         debug ? debug->candidates : nullptr, st->n_coarse};
+            MPA_TRY(launch_select(a, U, s));
+        } else if (hier && stage == 2) {
+            const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
+            ScoreArgs a{q, st->key_centroids, Cmax, bound, w.ccounts, w.crows, st->coarse_members, Cmax, w.s, w.fr,
+                        Cmax, w.fids, p->n_q_heads, p->n_kv_heads};
+            MPA_TRY(launch_score(p->dtype, G, a, U, s));
+        } else if (hier && stage == 3) {
+            if (debug && debug->selected)
+                MPA_TRY(hipMemsetAsync(debug->selected, 0, (size_t)U * C * sizeof(int32_t), s));
+            SelectArgs a{w.fr, Cmax, w.fids, st->sizes, Cmax, st->offsets, C, w.ccounts, token_budget, want_pseudo,
+                         w.rows, N, w.plist, Cmax, w.counts, debug ? debug->selected : nullptr, C};
+            MPA_TRY(launch_select(a, U, s));
+        } else if (attend) {
+            AttendArgs a{};
+            a.q = q;
+            a.Kx = sorted ? st->sorted_keys : k;
+            a.Vx = sorted ? st->sorted_values : v;
+            a.token_ids = sorted ? nullptr : st->token_ids;
+            a.K = k;
+            a.V = v;
+            a.rows = w.rows;
+            a.row_stride = N;
+            a.row_counts = w.counts;
+            a.Nmax = N;
+            a.n_clustered = st->n_clustered;
+            a.n_total = n_tokens_total;
+            a.pa = PseudoList{want_pseudo ? w.plist : nullptr, Cmax, w.counts, w.s, st->sizes, st->value_centroids,
+                              Cmax};
+            a.pb = PseudoList{(want_pseudo && hier) ? w.cplist : nullptr, Dmax, w.ccounts, w.cs, st->coarse_sizes,
+                              st->coarse_value_centroids, Dmax};
+            a.Hq = p->n_q_heads;
+            a.Hkv = p->n_kv_heads;
+            a.S = S;
+            a.part_ml = w.part_ml;
+            a.part_acc = w.part_acc;
+            MPA_TRY(launch_attend(p->dtype, G, a, U, s));
+        } else if (merge) {
+            MPA_TRY(launch_merge(w.part_ml, w.part_acc, U, G, S, p->n_kv_heads, out, s));
+        }
+    }
+    // optional inspection copies once the selection exists
+    if (debug && last_stage >= (hier ? 3 : 1)) {
+        if (debug->scores)
+            MPA_TRY(hipMemcpy2DAsync(debug->scores, (size_t)C * G * 4, w.s, (size_t)Cmax * G * 4, (size_t)C * G * 4,
+                                     U, hipMemcpyDeviceToDevice, s));
+        if (debug->exact_tokens)
+            MPA_TRY(hipMemcpy2DAsync(debug->exact_tokens, 4, w.counts, 16, 4, U, hipMemcpyDeviceToDevice, s));
+    }
+    return MPATTN_OK;
+}
+
+mpattn_status mpattn_decode(const mpattn_params* p, const void* q, const void* k, const void* v,
+                            int32_t n_tokens_total, const mpattn_state* st, int32_t token_budget, int32_t mode,
+                            float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    const int32_t n = mpattn_decode_stage_count(p);
+    if (n == 0) return check_params(p) == MPATTN_OK ? MPATTN_ERR_INVALID_ARG : check_params(p);
+    return mpattn_decode_ex(p, q, k, v, n_tokens_total, st, token_budget, mode, out, workspace, workspace_bytes,
+                            stream, nullptr, 0, n - 1);
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal API of
+// the library; the public C ABI lives in include/mpattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpa {
+
+constexpr int kMaxBlock = 16384;  // largest clustering block (LDS-resident sort)
+
+// Clustering blocks handled by one launch.  Block j (0 <= j < nb) covers
+// tokens [p_base + j * block_len, min(p_base + (j + 1) * block_len, n_end))
+// and owns clusters starting at c_base + j * cfull; it is seeded as block
+// index j_base + j.  Only the last block of a launch may be short.
+struct BlockRange {
+    int32_t p_base, n_end, c_base, block_len, tpc, cfull, j_base, nb;
+};
+
+// Strides shared by all per-unit arrays.
+struct UnitGeom {
+    int32_t units;  // B * Hkv
+    int32_t Nmax;   // token capacity per unit
+    int32_t Cmax;   // cluster capacity per unit (rows of the centroid arrays)
+};
+
+// ---- clustering (kmeans.hip) --------------------------------------------
+hipError_t launch_kmeans_init(int dtype, const void* K, UnitGeom g, BlockRange br, uint64_t seed, float* mu,
+                              void* kbar, hipStream_t st);
+hipError_t launch_kmeans_assign(int dtype, const void* K, UnitGeom g, BlockRange br, const void* kbar,
+                                int32_t* assign, hipStream_t st);
+hipError_t launch_kmeans_csr(const int32_t* assign, UnitGeom g, BlockRange br, int32_t* sizes,
+                             int32_t* offsets, int32_t* token_ids, hipStream_t st);
+// Mean of each cluster's member rows of X for clusters [c_begin, c_begin +
+// c_count).  `master` (fp32, may be null) and `store` (storage dtype) receive
+// it; an empty cluster is skipped, or zeroed in `store` when empty_zero.
+hipError_t launch_segmented_mean(int dtype, const void* X, UnitGeom g, int c_begin, int c_count,
+                                 const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
+                                 float* master, void* store, bool empty_zero, hipStream_t st);
+hipError_t launch_sorted_copy(int dtype, const void* K, const void* V, UnitGeom g, int p_begin, int count,
+                              const int32_t* token_ids, void* SK, void* SV, hipStream_t st);
+
+// Coarse level: size-weighted k-means over each block's non-empty fine key
+// centroids.  `fine` describes the fine blocks (token ranges and cluster
+// ranges); coarse block j owns coarse clusters from d_base + j * dfull and has
+// ceil(L_j / coarse_tpc) of them.
+struct CoarseRange {
+    BlockRange fine;
+    int32_t d_base, coarse_tpc, dfull, Dmax;
+};
+hipError_t launch_coarse_build(int dtype, UnitGeom g, CoarseRange cr, uint64_t seed, int iters,
+                               const void* kbar, const void* vbar, const int32_t* sizes, float* cmu,
+                               void* ckbar, void* cvbar, int32_t* csizes, int32_t* parent, int32_t* coffsets,
+                               int32_t* cmembers, hipStream_t st);
+
+// ---- decode (decode.hip) --------------------------------------------------
+struct ScoreArgs {
+    const void* q;          // [B][Hq][d]
+    const void* cent;       // [U][cent_rows][d] key centroids
+    int32_t cent_rows;
+    int32_t n_items;        // items per unit (host bound)
+    const int32_t* n_items_dev;  // optional per-unit count: n_items_dev[unit * 4]
+    const int32_t* pos_list;     // optional [U][list_stride]: item -> position in members
+    const int32_t* members;      // [U][cent_rows] position -> cluster id (with pos_list)
+    int32_t list_stride;
+    float* s_out;           // [U][cent_rows][G] scores by cluster id
+    float* r_out;           // [U][r_stride] group-mean score by item
+    int32_t r_stride;
+    int32_t* ids_out;       // optional [U][r_stride]: cluster id of each item
+    int32_t Hq, Hkv;
+};
+hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st);
+
+struct SelectArgs {
+    const float* key;        // [U][key_stride] ranking key per item
+    int32_t key_stride;
+    const int32_t* ids;      // optional [U][key_stride]: cluster id per item (else id = item)
+    const int32_t* sizes;    // [U][size_stride] by cluster id
+    int32_t size_stride;
+    const int32_t* offsets;  // [U][size_stride + 1] by cluster id
+    int32_t n_items;         // host count (used when n_items_dev is null)
+    const int32_t* n_items_dev;  // optional per-unit count at n_items_dev[unit * 4]
+    int32_t budget;
+    int32_t want_pseudo;
+    int32_t* rows;           // [U][row_stride] positions offsets[id] + j of selected items
+    int32_t row_stride;
+    int32_t* plist;          // [U][plist_stride] unselected non-empty cluster ids
+    int32_t plist_stride;
+    int32_t* counts;         // [U][4]: rows, pseudo items, selected items, 0
+    int32_t* dbg_selected;   // optional [U][dbg_stride] by cluster id
+    int32_t dbg_stride;
+};
+hipError_t launch_select(const SelectArgs& a, int units, hipStream_t st);
+
+struct PseudoList {
+    const int32_t* list;     // [U][stride] cluster ids
+    int32_t stride;
+    const int32_t* counts;   // count at counts[unit * 4 + 1]
+    const float* s;          // [U][rows][G]
+    const int32_t* sizes;    // [U][rows]
+    const void* vbar;        // [U][rows][d]
+    int32_t rows;
+};
+struct AttendArgs {
+    const void* q;
+    const void* Kx;          // exact-row source: sorted copy or K
+    const void* Vx;
+    const int32_t* token_ids;  // non-null: exact positions go through token ids
+    const void* K;           // tail rows
+    const void* V;
+    const int32_t* rows;     // [U][row_stride] exact positions
+    int32_t row_stride;
+    const int32_t* row_counts;  // count at row_counts[unit * 4]
+    int32_t Nmax;
+    int32_t n_clustered, n_total;
+    PseudoList pa, pb;       // approximate items (pb.list may be null)
+    int32_t Hq, Hkv, S;
+    float* part_ml;          // [U][G][S][2]
+    float* part_acc;         // [U][G][S][d]
+};
+hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipStream_t st);
+hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int S, int Hkv,
+                        float* out, hipStream_t st);
+
+}  // namespace mpa

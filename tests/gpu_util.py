@@ -1,0 +1,146 @@
+"""Helpers of the GPU parity tests: moving cluster state between the oracle's
+per-unit numpy form and the library's device arrays, and the acceptance rules
+for integer decisions taken from floating-point scores.
+
+Tie windows.  The GPU takes nearest-centroid and ranking decisions from fp32
+sums; the oracle from fp64.  A differing decision is accepted only when the
+two candidates' fp64 scores are closer than the rigorous bound on the fp32
+rounding of the GPU's sum (Higham: |fl(sum) - sum| <= gamma_n * sum |terms|,
+gamma_n = n u / (1 - n u), u = 2^-24), or than 1e-6 relative.
+"""
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+
+U32 = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U32 / (1 - n * U32)
+
+
+def storage_of(dtype):
+    return O.BF16 if dtype == torch.bfloat16 else O.F32
+
+
+# ---------------------------------------------------------------------------
+# state transfer
+# ---------------------------------------------------------------------------
+
+def oracle_state_from_gpu(state, b, h, params) -> O.UnitState:
+    """Copies unit (b, h) of a device ClusterState into an oracle UnitState."""
+    C, n = state.n_clusters, state.n_clustered
+    st = O.empty_state(params.head_dim, params.capacity_tokens, state.capacity_clusters, storage_of(params.dtype))
+    st.kbar[:C] = state.key_centroids[b, h, :C].double().cpu().numpy()
+    st.vbar[:C] = state.value_centroids[b, h, :C].double().cpu().numpy()
+    st.mu[:C] = state.key_centroids_f32[b, h, :C].double().cpu().numpy()
+    st.sizes[:C] = state.sizes[b, h, :C].cpu().numpy()
+    st.offsets[:C + 1] = state.offsets[b, h, :C + 1].cpu().numpy()
+    st.token_ids[:n] = state.token_ids[b, h, :n].cpu().numpy()
+    st.assign[:n] = state.assign[b, h, :n].cpu().numpy()
+    st.n_clusters, st.n_clustered = C, n
+    # block table implied by the build/update history (regular blocks)
+    Bc, r = params.cluster_block, params.tokens_per_centroid
+    p, c0, j = 0, 0, 0
+    while p < n:
+        L = min(Bc, n - p)
+        Cj = -(-L // r)
+        st.blocks.append(O.Block(p, L, c0, Cj, j))
+        p, c0, j = p + L, c0 + Cj, j + 1
+    if params.hierarchical:
+        D = state.n_coarse
+        st.ckbar = state.coarse_key_centroids[b, h, :D].double().cpu().numpy()
+        st.cvbar = state.coarse_value_centroids[b, h, :D].double().cpu().numpy()
+        st.cmu = state.coarse_key_centroids_f32[b, h, :D].double().cpu().numpy()
+        st.csizes = state.coarse_sizes[b, h, :D].cpu().numpy().astype(np.int32)
+        st.coffsets = state.coarse_offsets[b, h, :D + 1].cpu().numpy().astype(np.int32)
+        st.cmembers = state.coarse_members[b, h].cpu().numpy().astype(np.int32)
+        st.parent = state.parent[b, h].cpu().numpy().astype(np.int32)
+        st.n_coarse = D
+    return st
+
+
+def load_oracle_states(state, params, units, K=None, V=None):
+    """Writes oracle UnitStates (list indexed by unit = b * Hkv + h) into a
+    device ClusterState; fills the sorted copy from K/V when it exists."""
+    dev = state.key_centroids.device
+    Hkv = params.n_kv_heads
+    dt = params.dtype
+    for u, st in enumerate(units):
+        b, h = divmod(u, Hkv)
+        C, n = st.n_clusters, st.n_clustered
+        state.key_centroids[b, h, :C] = torch.from_numpy(st.kbar[:C]).to(dt).to(dev)
+        state.value_centroids[b, h, :C] = torch.from_numpy(st.vbar[:C]).to(dt).to(dev)
+        state.key_centroids_f32[b, h, :C] = torch.from_numpy(st.mu[:C]).float().to(dev)
+        state.sizes[b, h, :C] = torch.from_numpy(st.sizes[:C]).to(dev)
+        state.offsets[b, h, :C + 1] = torch.from_numpy(st.offsets[:C + 1]).to(dev)
+        state.token_ids[b, h, :n] = torch.from_numpy(st.token_ids[:n]).to(dev)
+        state.assign[b, h, :n] = torch.from_numpy(st.assign[:n]).to(dev)
+        if state.sorted_keys is not None:
+            ids = torch.from_numpy(st.token_ids[:n]).long()
+            state.sorted_keys[b, h, :n] = K[b, h, ids].to(dev)
+            state.sorted_values[b, h, :n] = V[b, h, ids].to(dev)
+    state.n_clusters = units[0].n_clusters
+    state.n_clustered = units[0].n_clustered
+    state.n_blocks = len(units[0].blocks)
+
+
+# ---------------------------------------------------------------------------
+# acceptance rules
+# ---------------------------------------------------------------------------
+
+def assign_tie_violations(x, mu_s, a_gpu, a_ref):
+    """Indices where the GPU's nearest centroid differs from the oracle's by
+    more than the fp32 rounding window.  Returns (n_differing, violations)."""
+    diff = np.nonzero(a_gpu != a_ref)[0]
+    bad = []
+    for i in diff:
+        c1, c0 = int(a_gpu[i]), int(a_ref[i])
+        D = lambda c: float(x[i] @ mu_s[c] - 0.5 * mu_s[c] @ mu_s[c])
+        E = lambda c: gamma(130) * float(np.abs(x[i] * mu_s[c]).sum() + 0.5 * (mu_s[c] ** 2).sum())
+        gap = D(c0) - D(c1)
+        if gap > max(1e-6 * max(1.0, abs(D(c0))), E(c0) + E(c1)):
+            bad.append(int(i))
+    return len(diff), bad
+
+
+def rank_tolerance(q, kbar):
+    """Per-cluster bound on the fp32 rounding of the group-mean score."""
+    d = q.shape[1]
+    terms = np.abs(q)[:, None, :] * np.abs(kbar)[None, :, :]  # [G][C][d]
+    s_abs = terms.sum(-1) / math.sqrt(d)
+    r = (q @ kbar.T).mean(0) / math.sqrt(d)
+    return gamma(d + 8) * s_abs.mean(0) + 8 * U32 * np.abs(r) + 1e-12
+
+
+def selection_is_valid(r64, tol, sizes, budget, sel):
+    """True when `sel` is the budget cut of some order that agrees with r64
+    outside the tolerance windows."""
+    sel = sel.astype(bool)
+    live = sizes > 0
+    if sizes[sel].sum() > budget or np.any(sel & ~live):
+        return False
+    inc, exc = np.nonzero(sel)[0], np.nonzero(~sel & live)[0]
+    if len(inc) and len(exc):
+        # no excluded cluster ranks clearly above an included one
+        worst_in = inc[np.argmin(r64[inc] + tol[inc])]
+        if np.any(r64[exc] - tol[exc] > r64[worst_in] + tol[worst_in]):
+            return False
+    if len(exc):
+        # the selection stopped because a near-top excluded cluster did not fit
+        top = r64[exc].max()
+        near = exc[r64[exc] + tol[exc] >= top - tol[exc].max()]
+        if not np.any(sizes[near] + sizes[sel].sum() > budget):
+            return False
+    return True
+
+
+def close(gpu, ref, atol=2e-3, rtol=1e-2):
+    """Elementwise |gpu - ref| <= atol + rtol * |ref|; returns (ok, max_abs, max_rel)."""
+    err = np.abs(gpu - ref)
+    ok = bool(np.all(err <= atol + rtol * np.abs(ref)))
+    rel = float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0
+    return ok, float(err.max()) if err.size else 0.0, rel

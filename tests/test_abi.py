@@ -1,0 +1,188 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, its struct layouts match the header as a C compiler sees it, and
+every validation error is returned before anything touches a GPU (all pointers
+below are fake and never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from sparse_long_context_means_amd import mpattn as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpattn.h")
+
+
+def test_exports_every_declared_function():
+    text = open(HEADER).read()
+    names = set(re.findall(r"\b(mpattn_[a-z_0-9]+)\s*\(", text))
+    assert {"mpattn_build_clusters", "mpattn_update_window", "mpattn_decode"} <= names
+    for n in sorted(names):
+        assert hasattr(M.lib, n), n
+
+
+def test_struct_layout_matches_header():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "mpattn.h"
+#define P(T, f) printf("%s.%s %zu\n", #T, #f, offsetof(T, f));
+int main(void) {
+  printf("params %zu state %zu debug %zu\n", sizeof(mpattn_params), sizeof(mpattn_state), sizeof(mpattn_decode_debug));
+  P(mpattn_params, seed) P(mpattn_params, splits) P(mpattn_state, parent) P(mpattn_state, capacity_clusters)
+  P(mpattn_state, n_blocks) P(mpattn_decode_debug, exact_tokens)
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    sizes = dict(zip(out[0].split()[0::2], map(int, out[0].split()[1::2])))
+    assert sizes["params"] == ctypes.sizeof(M.CParams)
+    assert sizes["state"] == ctypes.sizeof(M.CState)
+    assert sizes["debug"] == ctypes.sizeof(M.CDebug)
+    offs = dict(line.split() for line in out[1:] if line)
+    assert int(offs["mpattn_params.seed"]) == M.CParams.seed.offset
+    assert int(offs["mpattn_params.splits"]) == M.CParams.splits.offset
+    assert int(offs["mpattn_state.parent"]) == M.CState.parent.offset
+    assert int(offs["mpattn_state.capacity_clusters"]) == M.CState.capacity_clusters.offset
+    assert int(offs["mpattn_state.n_blocks"]) == M.CState.n_blocks.offset
+    assert int(offs["mpattn_decode_debug.exact_tokens"]) == M.CDebug.exact_tokens.offset
+
+
+def test_status_strings():
+    for s in (M.OK, M.ERR_INVALID_ARG, M.ERR_UNSUPPORTED, M.ERR_WORKSPACE, M.ERR_CAPACITY, M.ERR_HIP):
+        assert M.status_string(s) and M.status_string(s) != "unknown status"
+    assert M.status_string(42) == "unknown status"
+
+
+def _params(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, capacity_tokens=32768)
+    base.update(kw)
+    return M.Params(**base)
+
+
+def test_capacity_bounds():
+    p = _params()
+    assert p.max_clusters() == 2048 + 4 + 1
+    assert p.max_coarse() == 0
+    ph = _params(capacity_tokens=131072, coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
+    assert ph.max_coarse() == 1024 + 16 + 1
+    assert _params(head_dim=64).max_clusters() == 0
+
+
+def _fake_state(p, C=None, **over):
+    C = C or p.max_clusters()
+    fake = ctypes.c_void_p(0x10000)
+    s = M.CState(*([fake] * 7 + [None, None] + [None] * 7), C, 0, 0, 0, 0, 0)
+    if p.hierarchical:
+        for f in ("coarse_key_centroids", "coarse_value_centroids", "coarse_key_centroids_f32", "coarse_sizes",
+                  "coarse_offsets", "coarse_members", "parent"):
+            setattr(s, f, fake)
+        s.capacity_coarse = p.max_coarse()
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = ctypes.c_void_p(0x20000)
+
+
+def _build(p, n, st):
+    cp = p.c()
+    return M.lib.mpattn_build_clusters(ctypes.byref(cp), FAKE, FAKE, n, ctypes.byref(st), None, 0, None)
+
+
+def _decode(p, st, n_total, budget=128, mode=0, ws=1 << 40, first=0, last=None, q=FAKE):
+    cp = p.c()
+    last = M.lib.mpattn_decode_stage_count(ctypes.byref(cp)) - 1 if last is None else last
+    return M.lib.mpattn_decode_ex(ctypes.byref(cp), q, FAKE, FAKE, n_total, ctypes.byref(st), budget, mode, FAKE,
+                                  FAKE, ws, None, None, first, last)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), M.ERR_UNSUPPORTED),
+    (dict(n_q_heads=6, n_kv_heads=2), M.ERR_UNSUPPORTED),    # G = 3
+    (dict(n_q_heads=32, n_kv_heads=2), M.ERR_UNSUPPORTED),   # G = 16
+    (dict(n_q_heads=7, n_kv_heads=2), M.ERR_INVALID_ARG),
+    (dict(batch=0), M.ERR_INVALID_ARG),
+    (dict(cluster_block=32768), M.ERR_UNSUPPORTED),
+    (dict(tokens_per_centroid=0), M.ERR_INVALID_ARG),
+    (dict(build_iters=0), M.ERR_INVALID_ARG),
+    (dict(splits=-1), M.ERR_INVALID_ARG),
+    (dict(coarse_tokens_per_centroid=64, cluster_block=8192), M.ERR_UNSUPPORTED),  # 128 coarse per block
+])
+def test_parameter_validation(kw, status):
+    p = _params(**kw)
+    st = _fake_state(_params())
+    assert _build(p, 100, st) == status
+    assert _decode(p, st, 100) == status or status == M.ERR_INVALID_ARG
+
+
+def test_build_validation():
+    p = _params()
+    st = _fake_state(p)
+    cp = p.c()
+    assert M.lib.mpattn_build_clusters(None, FAKE, FAKE, 10, ctypes.byref(st), None, 0, None) == M.ERR_INVALID_ARG
+    assert M.lib.mpattn_build_clusters(ctypes.byref(cp), None, FAKE, 10, ctypes.byref(st), None, 0, None) == \
+        M.ERR_INVALID_ARG
+    assert M.lib.mpattn_build_clusters(ctypes.byref(cp), FAKE, FAKE, 10, None, None, 0, None) == M.ERR_INVALID_ARG
+    assert _build(p, 0, st) == M.ERR_INVALID_ARG
+    assert _build(p, 32769, st) == M.ERR_CAPACITY
+    assert _build(p, 32768, _fake_state(p, C=2047)) == M.ERR_CAPACITY
+    assert _build(p, 100, _fake_state(p, sorted_keys=FAKE)) == M.ERR_INVALID_ARG  # sorted K without sorted V
+    assert _build(p, 100, _fake_state(p, sizes=None)) == M.ERR_INVALID_ARG
+    ph = _params(coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
+    assert _build(ph, 100, _fake_state(p)) == M.ERR_INVALID_ARG  # coarse arrays missing
+
+
+def test_update_validation():
+    p = _params()
+    st = _fake_state(p, n_clustered=16384, n_clusters=1024, n_blocks=2)
+    cp = p.c()
+    upd = lambda n, s: M.lib.mpattn_update_window(ctypes.byref(cp), FAKE, FAKE, n, ctypes.byref(s), None, 0, None)
+    assert upd(16000, st) == M.ERR_INVALID_ARG     # behind the clustered prefix
+    assert upd(40000, st) == M.ERR_CAPACITY
+    assert upd(16384 + 8191, st) == M.OK            # tail shorter than a block: nothing to do
+    assert st.n_clustered == 16384 and st.n_clusters == 1024
+    full = _fake_state(p, n_clustered=16384, n_clusters=2040, n_blocks=2)
+    assert upd(16384 + 8192, full) == M.ERR_CAPACITY
+
+
+def test_decode_validation():
+    p = _params()
+    st = _fake_state(p, n_clustered=4096, n_clusters=256, n_blocks=1)
+    need = M.lib.mpattn_workspace_bytes(ctypes.byref(p.c()), st.capacity_clusters, 0, M.OP_DECODE)
+    assert 0 < need < (1 << 32)
+    assert _decode(p, st, 4096, ws=need - 1) == M.ERR_WORKSPACE
+    assert _decode(p, st, 4096, budget=-1) == M.ERR_INVALID_ARG
+    assert _decode(p, st, 4000) == M.ERR_INVALID_ARG              # fewer tokens than clustered
+    assert _decode(p, st, 40000) == M.ERR_INVALID_ARG             # beyond capacity
+    assert _decode(p, st, 4096, mode=7) == M.ERR_INVALID_ARG
+    assert _decode(p, st, 4096, q=None) == M.ERR_INVALID_ARG
+    assert _decode(p, st, 4096, first=2, last=1) == M.ERR_INVALID_ARG
+    assert _decode(p, st, 4096, first=0, last=4) == M.ERR_INVALID_ARG
+    assert _decode(p, _fake_state(p), 0) == M.ERR_INVALID_ARG     # nothing clustered
+    ph = _params(capacity_tokens=131072, coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
+    sh = _fake_state(ph, n_clustered=8192, n_clusters=512, n_coarse=64, n_blocks=1)
+    assert _decode(ph, sh, 8192, mode=M.MODE_OMIT) == M.ERR_UNSUPPORTED
+    assert _decode(ph, sh, 8192, ws=10) == M.ERR_WORKSPACE
+
+
+def test_workspace_and_stages():
+    p = _params()
+    cp = p.c()
+    assert M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 100, 0, M.OP_BUILD) == 0
+    assert M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 100, 0, 9) == ctypes.c_size_t(-1).value
+    assert p.decode_stages() == ["score", "select", "attend", "merge"]
+    ph = _params(coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
+    assert ph.decode_stages() == ["score_coarse", "select_coarse", "score_fine", "select_fine", "attend", "merge"]
+    small = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=1).c()), 2053, 0, M.OP_DECODE)
+    big = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=64).c()), 2053, 0, M.OP_DECODE)
+    assert big > small

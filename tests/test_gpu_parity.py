@@ -1,0 +1,328 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Teacher forcing: every step the oracle checks starts from the GPU's own
+previous state (assignment from the GPU's stored centroids, update from the
+GPU's assignment, decode from the GPU's cluster state), so each kernel is
+compared on identical inputs.  Integer decisions must match exactly outside
+the fp32 rounding windows of tests/gpu_util.py; floating-point results within
+the stated tolerances.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from gpu_util import (assign_tie_violations, close, gamma, load_oracle_states, oracle_state_from_gpu,
+                      rank_tolerance, selection_is_valid, storage_of, U32)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def M():
+    from sparse_long_context_means_amd import mpattn
+
+    return mpattn
+
+
+def small_workload(B, Hq, Hkv, n, components, dtype=torch.bfloat16, outliers=0, index=90):
+    base = workloads.WORKLOADS["qwen3-8b-layer-b1-32k"]
+    return dataclasses.replace(base, name="test", index=index, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_tokens=n,
+                               components=components, dtype=dtype, outlier_channels=outliers)
+
+
+def queries(w, means, step):
+    return workloads.make_queries(w, means, step)
+
+
+# ---------------------------------------------------------------------------
+# decode from an oracle-built state (teacher-forced state)
+# ---------------------------------------------------------------------------
+DECODE_CASES = [
+    # dtype, B, Hq, Hkv, n_clustered, n_total, block, tpc, budgets, sorted copy, splits
+    ("bf16", 2, 8, 2, 5000, 5000, 2048, 16, [0, 1, 100, 517, 5000], True, 0),
+    ("bf16", 1, 8, 2, 3000, 3333, 1024, 16, [64, 3000], False, 3),
+    ("fp32", 1, 1, 1, 4096, 4096, 8192, 16, [128], True, 0),
+    ("bf16", 1, 8, 1, 2000, 2000, 512, 8, [200], True, 0),
+    ("bf16", 1, 2, 1, 777, 777, 256, 4, [50, 0], False, 0),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{c[0]}-B{c[1]}-G{c[2] // c[3]}-N{c[5]}")
+def test_decode_matches_oracle_on_oracle_state(case):
+    mp = M()
+    dt_name, B, Hq, Hkv, n_cl, n_tot, Bc, r, budgets, sorted_copy, splits = case
+    dt = torch.bfloat16 if dt_name == "bf16" else torch.float32
+    w = small_workload(B, Hq, Hkv, n_tot, max(8, n_tot // 16), dt, outliers=4 if dt_name == "bf16" else 0)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=n_tot, dtype=dt, tokens_per_centroid=r,
+                  cluster_block=Bc, build_iters=3, splits=splits, seed=5)
+    storage = storage_of(dt)
+    units = O.parallel_map(lambda u: O.build_unit(K[u // Hkv, u % Hkv], V[u // Hkv, u % Hkv], n_cl,
+                                                  tokens_per_centroid=r, cluster_block_size=Bc, iters=3,
+                                                  storage=storage, seed=5, unit=u,
+                                                  capacity_clusters=p.max_clusters()),
+                           range(B * Hkv))
+    state = mp.ClusterState(p, DEV, sorted_copy=sorted_copy)
+    load_oracle_states(state, p, units, K, V)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    G = Hq // Hkv
+    for step, T in enumerate(budgets):
+        q = queries(w, means, step)
+        dbg = mp.DecodeDebug.allocate(p, state, DEV)
+        out = mp.decode(p, q.to(DEV), Kd, Vd, n_tot, state, T, debug=dbg).cpu().numpy()
+        sel_g = dbg.selected.cpu().numpy()
+        s_g = dbg.scores.cpu().numpy()
+        exact_g = dbg.exact_tokens.cpu().numpy()
+        for u, st in enumerate(units):
+            b, h = divmod(u, Hkv)
+            qu = q[b, h * G:(h + 1) * G]
+            ref = O.decode_unit(qu, K[b, h], V[b, h], n_tot, st, T)
+            C = st.n_clusters
+            # scores within the fp32 bound of a 128-term dot product
+            s64 = ref.s.T  # [C][G]
+            q64 = O.f64(qu)
+            bound = gamma(136) * (np.abs(q64)[:, None, :] * np.abs(st.kbar[:C])[None]).sum(-1).T / math.sqrt(128)
+            assert np.all(np.abs(s_g[b, h] - s64) <= bound + 4 * U32 * np.abs(s64) + 1e-30), "scores"
+            live = st.sizes[:C] > 0
+            assert np.array_equal(sel_g[b, h][~live], np.zeros((~live).sum(), np.int32))
+            if np.array_equal(sel_g[b, h], ref.selected):
+                ok, ea, er = close(out[b, h * G:(h + 1) * G], ref.out)
+                assert ok, f"unit {u} T={T}: max abs {ea:.3g} max rel {er:.3g}"
+            else:
+                tol = rank_tolerance(q64, st.kbar[:C])
+                assert selection_is_valid(ref.r, tol, st.sizes[:C], T, sel_g[b, h]), f"unit {u}: invalid selection"
+                want = O.decode_with_selection(qu, K[b, h], V[b, h], n_tot, st, sel_g[b, h])
+                ok, ea, er = close(out[b, h * G:(h + 1) * G], want)
+                assert ok, f"unit {u} T={T} (tie-broken selection): max abs {ea:.3g}"
+            assert exact_g[b, h] == st.sizes[:C][sel_g[b, h].astype(bool)].sum()
+
+
+def test_hand_derived_example_on_gpu(golden_dir):
+    """The hand-worked decode of tests/golden/tiny_decode.json, padded to d = 128."""
+    import json
+    import os
+
+    mp = M()
+    g = json.load(open(os.path.join(golden_dir, "tiny_decode.json")))
+    d = 128
+
+    def pad(rows):
+        a = np.zeros((len(rows), d))
+        a[:, :2] = rows
+        return a
+
+    K = torch.from_numpy(pad(g["keys"])).float()[None, None]
+    V = torch.from_numpy(pad(g["values"])).float()[None, None]
+    q = torch.zeros(1, 1, d)
+    q[0, 0, :2] = torch.tensor([math.log(2), math.log(3)], dtype=torch.float64) * math.sqrt(d)
+    p = mp.Params(batch=1, n_q_heads=1, n_kv_heads=1, capacity_tokens=4, dtype=torch.float32, tokens_per_centroid=2,
+                  cluster_block=4)
+    st = O.empty_state(d, 4, p.max_clusters(), O.F32)
+    st.kbar[:2] = pad(g["key_centroids"])
+    st.mu[:2] = pad(g["key_centroids"])
+    st.vbar[:2] = pad(g["value_centroids"])
+    st.sizes[:2] = g["sizes"]
+    st.offsets[:3] = [0, 2, 4]
+    st.token_ids[:4] = [0, 1, 2, 3]
+    st.assign[:4] = g["assign"]
+    st.n_clusters, st.n_clustered = 2, 4
+    st.blocks.append(O.Block(0, 4, 0, 2, 0))
+    state = mp.ClusterState(p, DEV, sorted_copy=True)
+    load_oracle_states(state, p, [st], K, V)
+    for case in g["cases"]:
+        dbg = mp.DecodeDebug.allocate(p, state, DEV)
+        out = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 4, state, case["budget"], debug=dbg).cpu().numpy()
+        assert dbg.selected.cpu().numpy()[0, 0].tolist() == case["selected"]
+        np.testing.assert_allclose(out[0, 0, :2], case["out"], rtol=1e-5, atol=1e-6)
+        assert np.all(out[0, 0, 2:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# clustering, teacher-forced round by round
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt_name", ["bf16", "fp32"])
+def test_build_rounds_match_oracle(dt_name):
+    mp = M()
+    dt = torch.bfloat16 if dt_name == "bf16" else torch.float32
+    B, Hq, Hkv, N, Bc, r, seed = 1, 8, 2, 5000, 2048, 16, 3
+    w = small_workload(B, Hq, Hkv, N, 300, dt, outliers=4 if dt_name == "bf16" else 0)
+    K, V, _ = workloads.make_cache(w)
+    storage = storage_of(dt)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    snaps = []
+    for t in (1, 2, 3):
+        p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=dt, tokens_per_centroid=r,
+                      cluster_block=Bc, build_iters=t, seed=seed)
+        state = mp.ClusterState(p, DEV, sorted_copy=True)
+        mp.build_clusters(p, Kd, Vd, N, state)
+        torch.cuda.synchronize()
+        snaps.append([oracle_state_from_gpu(state, u // Hkv, u % Hkv, p) for u in range(B * Hkv)] +
+                     [state.sorted_keys.cpu(), state.sorted_values.cpu()])
+    n_diff_total = 0
+    for u in range(B * Hkv):
+        Ku, Vu = O.f64(K[0, u]), O.f64(V[0, u])
+        for t in range(3):
+            cur = snaps[t][u]
+            for blk in cur.blocks:
+                x = Ku[blk.p:blk.p + blk.L]
+                if t == 0:
+                    init = O.init_indices(O.block_stream(seed, u, blk.index), blk.L, blk.C)
+                    mu_prev, mus_prev = x[init].copy(), O.round_storage(x[init], storage)
+                else:
+                    prev = snaps[t - 1][u]
+                    mu_prev = prev.mu[blk.c0:blk.c0 + blk.C].copy()
+                    mus_prev = prev.kbar[blk.c0:blk.c0 + blk.C].copy()
+                a_ref, _, _ = O.assign_step(x, mus_prev)
+                a_gpu = cur.assign[blk.p:blk.p + blk.L] - blk.c0
+                nd, bad = assign_tie_violations(x, mus_prev, a_gpu, a_ref)
+                n_diff_total += nd
+                assert not bad, f"unit {u} round {t + 1} block {blk.index}: {len(bad)} assignments outside ties"
+                # update from the GPU's assignment
+                mu, mus, counts = O.update_step(x, a_gpu, mu_prev, mus_prev, storage)
+                np.testing.assert_array_equal(cur.sizes[blk.c0:blk.c0 + blk.C], counts)
+                live = counts > 0
+                gm = cur.mu[blk.c0:blk.c0 + blk.C]
+                # fp32 mean of n terms: |err| <= gamma(n + 1) * mean|x| + u |mean|
+                absmean = np.stack([np.abs(x[a_gpu == c]).mean(0) if counts[c] else np.zeros(x.shape[1])
+                                    for c in range(blk.C)])
+                bound = gamma(counts[:, None] + 1) * absmean + U32 * np.abs(mu)
+                assert np.all(np.abs(gm - mu)[live] <= bound[live] + 1e-30), "centroid means"
+                np.testing.assert_array_equal(gm[~live], mu_prev[~live])  # empty clusters keep their centroid
+                np.testing.assert_array_equal(cur.kbar[blk.c0:blk.c0 + blk.C], O.round_storage(gm, storage))
+                # membership lists in (cluster, token) order
+                order = np.lexsort((np.arange(blk.L), a_gpu))
+                np.testing.assert_array_equal(cur.token_ids[blk.p:blk.p + blk.L], blk.p + order)
+                starts = blk.p + np.concatenate([[0], np.cumsum(counts)[:-1]])
+                np.testing.assert_array_equal(cur.offsets[blk.c0:blk.c0 + blk.C], starts)
+                if t == 2:  # value centroids of the final round and the sorted copy
+                    vx = Vu[blk.p:blk.p + blk.L]
+                    for c in np.nonzero(live)[0][:64]:
+                        m = vx[a_gpu == c].mean(0)
+                        vb = gamma(counts[c] + 1) * np.abs(vx[a_gpu == c]).mean(0) + U32 * np.abs(m)
+                        gv = cur.vbar[blk.c0 + c]
+                        lo = O.round_storage(m - vb, storage)
+                        hi = O.round_storage(m + vb, storage)
+                        assert np.all((gv >= lo) & (gv <= hi)), "value centroid"
+                    sk = snaps[t][-2][0, u].double().numpy()
+                    np.testing.assert_array_equal(sk[blk.p:blk.p + blk.L], Ku[blk.p + order])
+    print(f"assignments differing inside tie windows: {n_diff_total}")
+
+
+def test_tiny_config_free_running():
+    """The tiny fp32 workload end to end: well-separated components, so the
+    GPU and the oracle follow the same Lloyd trajectory."""
+    mp = M()
+    w = workloads.WORKLOADS["tiny-fp32"]
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=1, n_q_heads=1, n_kv_heads=1, capacity_tokens=w.n_tokens, dtype=torch.float32,
+                  build_iters=w.build_iters, seed=0)
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, w.n_tokens, state)
+    q = workloads.make_queries(w, means, 0)
+    out = mp.decode(p, q.to(DEV), Kd, Vd, w.n_tokens, state, w.budgets[0]).cpu().numpy()
+    ref = O.build_unit(K[0, 0], V[0, 0], w.n_tokens, iters=w.build_iters, storage=O.F32, seed=0)
+    gst = oracle_state_from_gpu(state, 0, 0, p)
+    assert state.n_clusters == ref.n_clusters == 256
+    mism = int((gst.assign[:w.n_tokens] != ref.assign[:w.n_tokens]).sum())
+    assert mism == 0, f"{mism} tokens assigned differently"
+    np.testing.assert_allclose(gst.kbar[:256], ref.kbar[:256], rtol=1e-5, atol=1e-6)
+    res = O.decode_unit(q[0], K[0, 0], V[0, 0], w.n_tokens, ref, w.budgets[0])
+    ok, ea, er = close(out[0], res.out)
+    assert ok, (ea, er)
+    assert np.all(np.diff(ref.J[0]) <= 1e-9 * ref.J[0][:-1])
+
+
+# ---------------------------------------------------------------------------
+# reductions, determinism, split invariance
+# ---------------------------------------------------------------------------
+
+def _built(B=2, Hq=8, Hkv=2, N=4500, Bc=2048, splits=0, dt=torch.bfloat16, sorted_copy=True, iters=4):
+    mp = M()
+    w = small_workload(B, Hq, Hkv, N, 200, dt, outliers=4)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=dt, cluster_block=Bc,
+                  build_iters=iters, splits=splits, seed=1)
+    state = mp.ClusterState(p, DEV, sorted_copy=sorted_copy)
+    mp.build_clusters(p, K.to(DEV), V.to(DEV), N, state)
+    return mp, w, K, V, means, p, state
+
+
+def test_full_budget_is_dense_attention():
+    mp, w, K, V, means, p, state = _built()
+    q = queries(w, means, 3)
+    out = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), p.capacity_tokens, state, p.capacity_tokens).cpu().numpy()
+    G = p.group
+    for b in range(p.batch):
+        for h in range(p.n_kv_heads):
+            ref = O.dense(q[b, h * G:(h + 1) * G], K[b, h], V[b, h])
+            ok, ea, er = close(out[b, h * G:(h + 1) * G], ref)
+            assert ok, (b, h, ea, er)
+
+
+def test_gpu_state_decode_matches_oracle():
+    """Decode on the GPU-built state, checked by the oracle on that state."""
+    mp, w, K, V, means, p, state = _built(sorted_copy=False)
+    G = p.group
+    for step, T in enumerate([0, 128, 700]):
+        q = queries(w, means, step)
+        dbg = mp.DecodeDebug.allocate(p, state, DEV)
+        out = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), p.capacity_tokens, state, T, debug=dbg).cpu().numpy()
+        for u in range(p.units):
+            b, h = divmod(u, p.n_kv_heads)
+            st = oracle_state_from_gpu(state, b, h, p)
+            sel = dbg.selected[b, h].cpu().numpy()
+            ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], p.capacity_tokens, st, T)
+            if not np.array_equal(sel, ref.selected):
+                tol = rank_tolerance(O.f64(q[b, h * G:(h + 1) * G]), st.kbar[:st.n_clusters])
+                assert selection_is_valid(ref.r, tol, st.sizes[:st.n_clusters], T, sel)
+                ref_out = O.decode_with_selection(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], p.capacity_tokens,
+                                                  st, sel)
+            else:
+                ref_out = ref.out
+            ok, ea, er = close(out[b, h * G:(h + 1) * G], ref_out)
+            assert ok, (u, T, ea, er)
+
+
+def test_repeatable_bitwise():
+    mp, w, K, V, means, p, s1 = _built()
+    s2 = mp.ClusterState(p, DEV)
+    mp.build_clusters(p, K.to(DEV), V.to(DEV), p.capacity_tokens, s2)
+    for name in ("key_centroids", "value_centroids", "key_centroids_f32", "sizes", "offsets", "token_ids", "assign",
+                 "sorted_keys", "sorted_values"):
+        assert torch.equal(getattr(s1, name), getattr(s2, name)), name
+    q = queries(w, means, 1).to(DEV)
+    o1 = mp.decode(p, q, K.to(DEV), V.to(DEV), p.capacity_tokens, s1, 300)
+    o2 = mp.decode(p, q, K.to(DEV), V.to(DEV), p.capacity_tokens, s1, 300)
+    assert torch.equal(o1, o2)
+
+
+def test_split_count_does_not_change_the_result():
+    mp, w, K, V, means, p, state = _built()
+    q = queries(w, means, 2).to(DEV)
+    outs = []
+    for S in (1, 3, 16, 64):
+        ps = dataclasses.replace(p, splits=S)
+        outs.append(mp.decode(ps, q, K.to(DEV), V.to(DEV), p.capacity_tokens, state, 400).cpu().numpy())
+    for o in outs[1:]:
+        np.testing.assert_allclose(o, outs[0], rtol=1e-5, atol=1e-6)
+
+
+def test_omit_mode_matches_oracle():
+    mp, w, K, V, means, p, state = _built(B=1)
+    q = queries(w, means, 4)
+    G = p.group
+    for T in (0, 256):
+        out = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), p.capacity_tokens, state, T,
+                        mode=mp.MODE_OMIT).cpu().numpy()
+        for h in range(p.n_kv_heads):
+            st = oracle_state_from_gpu(state, 0, h, p)
+            ref = O.decode_unit(q[0, h * G:(h + 1) * G], K[0, h], V[0, h], p.capacity_tokens, st, T, mode=1)
+            ok, ea, er = close(out[0, h * G:(h + 1) * G], ref.out)
+            assert ok, (h, T, ea)
