@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the Multipole Attention hot path on one MI355X.
+
+Workload: a Qwen3-8B-shaped attention layer (32 query heads, 8 KV heads, head
+dim 128, bf16), batch 16, 32768-token clustered-Gaussian KV cache per sequence
+(synthetic: no dataset or weights are available), 1 centroid per 16 tokens in
+8192-token blocks, 95% sparsity (1638 exactly attended tokens per KV head),
+a fresh query per step.
+
+One step = one decode of the whole batch through the C ABI: score and budget
+cut (one launch), then split-K attention with the merge (one launch).  The clustering is built once before timing (prefill time)
+and reported separately.  Headline timing is cold: before every step a 1 GiB
+read evicts the 256 MB Infinity Cache (and the L2s) with clean lines, outside
+the timed events, so the centroids and rows come from HBM.  Warm (back-to-back) timing is reported as
+well.  Per-stage HIP events on the launch stream give the dominant kernel's
+average duration for the roofline object.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3-8b-layer-b16-32k-s95")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=8, help="oracle decode steps timed for the CPU baseline")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--gather", action="store_true", help="decode by token-id gather instead of the sorted copy")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (sequence, KV head) unit is independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from sparse_long_context_means_amd import mpattn as M
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 copies of {args.copy_probe_mb} MiB")
+        return
+
+    w = workloads.WORKLOADS[args.workload]
+    B, Hq, Hkv, N, d = w.batch, w.n_q_heads, w.n_kv_heads, w.n_tokens, w.head_dim
+    G = Hq // Hkv
+    T = w.budgets[0]
+    t0 = time.time()
+    K, V, means = workloads.make_cache(w)
+    log(f"[bench] synthetic cache {tuple(K.shape)} {K.dtype} in {time.time() - t0:.1f}s")
+    Kd, Vd = K.to(dev), V.to(dev)
+    p = M.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=w.dtype,
+                 tokens_per_centroid=w.tokens_per_centroid, cluster_block=w.cluster_block,
+                 build_iters=w.build_iters, update_iters=w.update_iters, splits=args.splits, seed=0)
+    state = M.ClusterState(p, dev, sorted_copy=not args.gather)
+
+    # ---- build (prefill time), reported separately -------------------------
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    M.build_clusters(p, Kd, Vd, N, state)  # warm-up build (also JIT/code-object load)
+    torch.cuda.synchronize()
+    e0.record()
+    M.build_clusters(p, Kd, Vd, N, state)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    U = B * Hkv
+    C = state.n_clusters
+    nb = math.ceil(N / w.cluster_block)
+    assign_flop = 2.0 * U * N * (w.cluster_block // w.tokens_per_centroid) * d * w.build_iters
+    log(f"[bench] build {build_ms:.2f} ms ({C} clusters per unit, {nb} blocks)")
+
+    # ---- queries and per-step selection sizes (untimed) ----------------------
+    n_q = args.warmup + args.steps
+    qs = [workloads.make_queries(w, means, s).to(dev) for s in range(n_q)]
+    ws = M.Workspace().get(p, state, dev)  # zero-filled
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    dbg = M.DecodeDebug.allocate(p, state, dev)
+    sizes = state.sizes[:, :, :C].cpu().numpy()
+    live = sizes > 0
+    exact_rows, pseudo_items = [], []
+    for s in range(n_q):
+        M.decode(p, qs[s], Kd, Vd, N, state, T, out=out, workspace=ws, debug=dbg)
+        sel = dbg.selected.cpu().numpy().astype(bool)
+        exact_rows.append(int(dbg.exact_tokens.sum()))
+        pseudo_items.append(int((live & ~sel).sum()))
+    torch.cuda.synchronize()
+
+    def bytes_of(step):
+        e, pc = exact_rows[step], pseudo_items[step]
+        score = B * Hq * d * 2 + U * C * d * 2            # queries + key centroids
+        attend = e * d * 2 * 2 + e * 4 + pc * d * 2        # exact K/V rows + their ids + value centroids
+        other = U * C * 4 + B * Hq * d * 4                 # sizes + output
+        return score, attend, other
+
+    # ---- timed decode --------------------------------------------------------
+    cp, cs = p.c(), state.c()
+    n_stages = M.lib.mpattn_decode_stage_count(ctypes.byref(cp))
+    stage_names = p.decode_stages()
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict caches
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def evict():
+        torch.sum(flush, dim=0, out=sink)
+
+    def enqueue(s, first=0, last=n_stages - 1):
+        st = M.lib.mpattn_decode_ex(ctypes.byref(cp), ctypes.c_void_p(qs[s].data_ptr()),
+                                    ctypes.c_void_p(Kd.data_ptr()), ctypes.c_void_p(Vd.data_ptr()), N,
+                                    ctypes.byref(cs), T, 0, ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(ws.data_ptr()), ws.numel(), sptr, None, first, last)
+        if st != 0:
+            raise RuntimeError(M.status_string(st))
+
+    for s in range(args.warmup):
+        evict()
+        enqueue(s)
+    torch.cuda.synchronize()
+
+    # cold, headline: one event pair per step, cache flushed before each step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        evict()
+        ev[i][0].record(stream)
+        enqueue(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # cold, per stage: events between the stage launches (same stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_stages + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        s = args.warmup + i
+        evict()
+        evs[i][0].record(stream)
+        for k in range(n_stages):
+            enqueue(s, k, k)
+            evs[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(n_stages)]
+                         for i in range(args.steps)])
+
+    # warm: back-to-back full steps, one event pair around all of them
+    wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wa.record(stream)
+    for i in range(args.steps):
+        enqueue(args.warmup + i)
+    wb.record(stream)
+    torch.cuda.synchronize()
+    warm_us = wa.elapsed_time(wb) * 1e3 / args.steps
+
+    steps_idx = range(args.warmup, args.warmup + args.steps)
+    byts = np.array([sum(bytes_of(s)) for s in steps_idx], dtype=np.float64)
+    att_bytes = np.array([bytes_of(s)[1] for s in steps_idx], dtype=np.float64)
+    cold_us = float(step_ms.mean() * 1e3)
+    eff_gbps = float((byts / (step_ms * 1e-3)).mean() / 1e9)
+    att_k = stage_names.index("attend")
+    att_ms = stage_ms[:, att_k]
+    att_gbps = float(att_bytes.mean() / (att_ms.mean() * 1e-3) / 1e9)
+    log(f"[bench] cold {cold_us:.1f} us/step  warm {warm_us:.1f} us/step  "
+        f"stages(us) " + " ".join(f"{n}={stage_ms[:, k].mean() * 1e3:.1f}" for k, n in enumerate(stage_names)))
+
+    # ---- CPU baseline: the oracle on the machine's host cores --------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        from concurrent.futures import ThreadPoolExecutor
+
+        threads = min(16, os.cpu_count() or 1)
+        ust = []
+        for u in range(U):
+            b, h = divmod(u, Hkv)
+            st = O.empty_state(d, N, state.capacity_clusters, O.BF16)
+            st.kbar[:C] = state.key_centroids[b, h, :C].double().cpu().numpy()
+            st.vbar[:C] = state.value_centroids[b, h, :C].double().cpu().numpy()
+            st.sizes[:C] = state.sizes[b, h, :C].cpu().numpy()
+            st.assign[:N] = state.assign[b, h, :N].cpu().numpy()
+            st.n_clusters, st.n_clustered = C, N
+            ust.append((st, O.f64(K[b, h]), O.f64(V[b, h])))
+        qcpu = [qs[args.warmup + i].cpu() for i in range(args.cpu_steps)]
+
+        def one(args_):
+            i, u = args_
+            b, h = divmod(u, Hkv)
+            st, Ku, Vu = ust[u]
+            O.decode_unit(qcpu[i][b, h * G:(h + 1) * G], Ku, Vu, N, st, T)
+
+        jobs = [(i, u) for i in range(args.cpu_steps) for u in range(U)]
+        c0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, jobs))
+        cpu_s = time.perf_counter() - c0
+        cpu = {"value": cpu_s / args.cpu_steps * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+               "sample": f"{args.cpu_steps} full decode steps ({U} units each) of the same workload, fp64 oracle, "
+                         f"one host thread per unit",
+               "cpu_model": _cpu_model()}
+        log(f"[bench] oracle {cpu['value'] / 1e3:.1f} ms/step on {threads} threads")
+
+    res = {
+        "metric": "decode attn µs/step + effective HBM GB/s, 32K ctx, bs16, 95% sparsity",
+        "value": round(cold_us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cold_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic clustered-Gaussian KV cache (no dataset/weights)",
+        "config": {"workload": w.name, "batch": B, "seq_len": N, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
+                   "token_budget": T, "tokens_per_centroid": w.tokens_per_centroid,
+                   "cluster_block": w.cluster_block, "exact_rows": "sorted copy" if not args.gather else "gather",
+                   "splits": args.splits or "auto"},
+        "effective_GBps": round(eff_gbps, 1),
+        "effective_frac_of_hbm_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_MB_per_step": round(float(byts.mean()) / 1e6, 2),
+        "warm_us_per_step": round(warm_us, 2),
+        "cold_us_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "stage_sum_us": round(float(stage_ms.sum(1).mean()) * 1e3, 2),
+        "stage_us": {n: round(float(stage_ms[:, k].mean()) * 1e3, 2) for k, n in enumerate(stage_names)},
+        "timed_wall_ms_incl_cache_flush": round(wall_ms, 2),
+        "build_ms": round(build_ms, 2),
+        "build_assign_TFLOPs_lower_bound": round(assign_flop / (build_ms * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "hbm", "kernel": "attend", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
+                     "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+if __name__ == "__main__":
+    main()

@@ -143,7 +143,8 @@ int32_t mpattn_max_coarse(const mpattn_params* params);
 
 /* Workspace bytes an operation needs for a state of `capacity_clusters`
  * clusters (and `capacity_coarse` coarse clusters).  0 means no workspace.
- * Returns (size_t)-1 when the parameters are invalid. */
+ * Returns (size_t)-1 when the parameters are invalid.  Decodes that share a
+ * workspace must not overlap in time. */
 size_t mpattn_workspace_bytes(const mpattn_params* params, int32_t capacity_clusters, int32_t capacity_coarse,
                               int32_t op);
 
@@ -206,7 +207,10 @@ mpattn_status mpattn_decode(const mpattn_params* params, const void* q, const vo
                             int32_t n_tokens_total, const mpattn_state* state, int32_t token_budget,
                             int32_t mode, float* out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of kernel stages one decode enqueues (for timing stage by stage). */
+/* Number of kernel stages one decode enqueues (for timing stage by stage):
+ * 4 for the flat method (score, select, attend, merge), 6 for the
+ * hierarchical one (coarse_score, coarse_select, fine_score, fine_select,
+ * attend, merge). */
 int32_t mpattn_decode_stage_count(const mpattn_params* params);
 
 /* Name of decode stage i (static storage), NULL if out of range. */

@@ -62,7 +62,7 @@ def _load():
         "orc_decode": (_i64, [_D, _i32, _i32, _D, _D, _i32, _i32, _D, _D, _I, _I, _i32, _i64,
                               ctypes.c_int, _D, _I, _D, _D]),
         "orc_decode_hier": (_i64, [_D, _i32, _i32, _D, _D, _i32, _i32, _D, _D, _I, _I, _I, _i32,
-                                   _D, _D, _I, _i32, _i64, _i64, _D, _I, _I, _D, _D]),
+                                   _D, _D, _I, _i32, _i64, _i64, _I, _I, _D, _I, _I, _D, _D, _D]),
         "orc_dense": (None, [_D, _i32, _D, _D, _i32, _D]),
     }
     for name, (res, args) in sig.items():
@@ -363,7 +363,10 @@ def decode_unit(q, K, V, n_total: int, st: UnitState, budget: int, mode: int = 0
     return DecodeResult(out, sel[:C], s[:, :C], r[:C], int(taken))
 
 
-def decode_unit_hier(q, K, V, n_total: int, st: UnitState, budget: int, cand_budget: int) -> DecodeResult:
+def decode_unit_hier(q, K, V, n_total: int, st: UnitState, budget: int, cand_budget: int,
+                     candidates=None, selected=None) -> DecodeResult:
+    """Two-level decode step; `candidates` / `selected` (0/1 arrays) force the
+    coarse candidate set and the fine selection instead of computing them."""
     q, K, V = f64(q), f64(K), f64(V)
     G, d = q.shape
     C, D = st.n_clusters, st.n_coarse
@@ -372,12 +375,16 @@ def decode_unit_hier(q, K, V, n_total: int, st: UnitState, budget: int, cand_bud
     csel = np.zeros(D, np.int32)
     s = np.zeros((G, C))
     cs = np.zeros((G, D))
+    r = np.zeros(C)
+    fc = _i(np.ascontiguousarray(candidates, dtype=np.int32)) if candidates is not None else None
+    fs = _i(np.ascontiguousarray(selected, dtype=np.int32)) if selected is not None else None
     taken = _lib.orc_decode_hier(_d(q), G, d, _d(K), _d(V), n_total, st.n_clustered,
                                  _d(np.ascontiguousarray(st.kbar[:C])), _d(np.ascontiguousarray(st.vbar[:C])),
                                  _i(st.sizes), _i(st.assign), _i(st.parent), C,
                                  _d(np.ascontiguousarray(st.ckbar[:D])), _d(np.ascontiguousarray(st.cvbar[:D])),
-                                 _i(st.csizes), D, cand_budget, budget, _d(out), _i(csel), _i(sel), _d(s), _d(cs))
-    return DecodeResult(out, sel, s, np.zeros(C), int(taken), csel, cs)
+                                 _i(st.csizes), D, cand_budget, budget, fc, fs, _d(out), _i(csel), _i(sel), _d(s),
+                                 _d(cs), _d(r))
+    return DecodeResult(out, sel, s, r, int(taken), csel, cs)
 
 
 def decode_with_selection(q, K, V, n_total: int, st: UnitState, selected, mode: int = 0) -> np.ndarray:

@@ -492,20 +492,26 @@ int64_t orc_decode(const double* q, int32_t G, int32_t d, const double* K, const
  *   `budget`; the exact set is the selected fine clusters' tokens plus the
  *   tail; the approximate set is every unselected non-empty fine cluster
  *   inside a candidate plus every non-candidate non-empty coarse cluster.
+ * forced_csel / forced_sel (may be NULL) replace the candidate and fine
+ * selections (to evaluate the combine for a given selection).
  * Outputs: out[G][d], csel[D] (candidates), sel[C] (selected fine), s[G][C]
  *   (fine scores; only candidates' entries are computed, others zero),
- *   cs[G][D]; returns tokens selected.
+ *   cs[G][D], r_out[C] (may be NULL); returns tokens selected.
  */
 int64_t orc_decode_hier(const double* q, int32_t G, int32_t d, const double* K, const double* V,
                         int32_t n_total, int32_t n_clustered, const double* kbar,
                         const double* vbar, const int32_t* sizes, const int32_t* assign,
                         const int32_t* parent, int32_t C, const double* ckbar,
                         const double* cvbar, const int32_t* csizes, int32_t D,
-                        int64_t cand_budget, int64_t budget, double* out, int32_t* csel,
-                        int32_t* sel, double* s, double* cs) {
+                        int64_t cand_budget, int64_t budget, const int32_t* forced_csel,
+                        const int32_t* forced_sel, double* out, int32_t* csel, int32_t* sel, double* s,
+                        double* cs, double* r_out) {
     double* cr = (double*)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
     orc_scores(q, G, d, ckbar, D, cs, cr);
-    orc_select(cr, csizes, D, cand_budget, csel);
+    if (forced_csel)
+        for (int32_t k = 0; k < D; ++k) csel[k] = forced_csel[k];
+    else
+        orc_select(cr, csizes, D, cand_budget, csel);
     /* fine scores for candidate members only */
     double* r = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
     int32_t* csize_f = (int32_t*)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
@@ -526,7 +532,17 @@ int64_t orc_decode_hier(const double* q, int32_t G, int32_t d, const double* K, 
         }
         r[c] /= G;
     }
-    int64_t taken = orc_select(r, csize_f, C, budget, sel);
+    int64_t taken = 0;
+    if (forced_sel) {
+        for (int32_t c = 0; c < C; ++c) {
+            sel[c] = forced_sel[c];
+            if (sel[c]) taken += sizes[c];
+        }
+    } else {
+        taken = orc_select(r, csize_f, C, budget, sel);
+    }
+    if (r_out)
+        for (int32_t c = 0; c < C; ++c) r_out[c] = r[c];
     int32_t* exact = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_total > 0 ? n_total : 1));
     for (int32_t i = 0; i < n_total; ++i) exact[i] = i >= n_clustered ? 1 : sel[assign[i]];
     /* Approximate items: fine (inside candidates, unselected) then coarse

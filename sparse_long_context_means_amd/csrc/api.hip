@@ -162,7 +162,7 @@ mpattn_status run_blocks(const mpattn_params* p, const void* k, const void* v, m
 }
 
 const char* kFlatStages[] = {"score", "select", "attend", "merge"};
-const char* kHierStages[] = {"score_coarse", "select_coarse", "score_fine", "select_fine", "attend", "merge"};
+const char* kHierStages[] = {"coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"};
 
 }  // namespace
 
@@ -305,6 +305,7 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const int32_t C = st->n_clusters;
     const bool sorted = st->sorted_keys != nullptr;
     const int32_t want_pseudo = mode == MPATTN_MODE_MULTIPOLE ? 1 : 0;
+    const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
 
     for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
         const char* name = hier ? kHierStages[stage] : kFlatStages[stage];
@@ -314,30 +315,28 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
                         p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (!hier && stage == 1) {
-            SelectArgs a{w.r, Cmax, nullptr, st->sizes, Cmax, st->offsets, C, nullptr, token_budget, want_pseudo,
-                         w.rows, N, w.plist, Cmax, w.counts,
-                         debug ? debug->selected : nullptr, C};
-            MPA_TRY(launch_select(a, U, s));
+            SelectArgs se{w.r, Cmax, nullptr, st->sizes, Cmax, st->offsets, C, nullptr, token_budget, want_pseudo,
+                          w.rows, N, w.plist, Cmax, w.counts, debug ? debug->selected : nullptr, C};
+            MPA_TRY(launch_select(se, U, s));
         } else if (hier && stage == 0) {
             ScoreArgs a{q, st->coarse_key_centroids, Dmax, st->n_coarse, nullptr, nullptr, nullptr, 0, w.cs, w.cr,
                         Dmax, nullptr, p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (hier && stage == 1) {
-            SelectArgs a{w.cr, Dmax, nullptr, st->coarse_sizes, Dmax, st->coarse_offsets, st->n_coarse, nullptr,
-                         p->coarse_candidate_tokens, want_pseudo, w.crows, Cmax, w.cplist, Dmax, w.ccounts,
-                         debug ? debug->candidates : nullptr, st->n_coarse};
-            MPA_TRY(launch_select(a, U, s));
+            SelectArgs se{w.cr, Dmax, nullptr, st->coarse_sizes, Dmax, st->coarse_offsets, st->n_coarse, nullptr,
+                          p->coarse_candidate_tokens, want_pseudo, w.crows, Cmax, w.cplist, Dmax, w.ccounts,
+                          debug ? debug->candidates : nullptr, st->n_coarse};
+            MPA_TRY(launch_select(se, U, s));
         } else if (hier && stage == 2) {
-            const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
             ScoreArgs a{q, st->key_centroids, Cmax, bound, w.ccounts, w.crows, st->coarse_members, Cmax, w.s, w.fr,
                         Cmax, w.fids, p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (hier && stage == 3) {
             if (debug && debug->selected)
                 MPA_TRY(hipMemsetAsync(debug->selected, 0, (size_t)U * C * sizeof(int32_t), s));
-            SelectArgs a{w.fr, Cmax, w.fids, st->sizes, Cmax, st->offsets, C, w.ccounts, token_budget, want_pseudo,
-                         w.rows, N, w.plist, Cmax, w.counts, debug ? debug->selected : nullptr, C};
-            MPA_TRY(launch_select(a, U, s));
+            SelectArgs se{w.fr, Cmax, w.fids, st->sizes, Cmax, st->offsets, bound, w.ccounts, token_budget,
+                          want_pseudo, w.rows, N, w.plist, Cmax, w.counts, debug ? debug->selected : nullptr, C};
+            MPA_TRY(launch_select(se, U, s));
         } else if (attend) {
             AttendArgs a{};
             a.q = q;

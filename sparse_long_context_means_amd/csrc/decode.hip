@@ -7,16 +7,19 @@
 // value centroids).  The approximate term of an unselected cluster c is
 // n_c * exp(q . Kbar_c / sqrt(d)) on Vbar_c, in numerator and denominator.
 //
-// Stages (one launch each):
+// Launches:
 //   score  -- s[c][g] = q_g . Kbar_c / sqrt(d) and the group-mean ranking key;
-//   select -- per unit, radix select of the budget cut over the ranking keys
-//             (longest prefix of the (key desc, id asc) order whose sizes fit
-//             the budget), then lists of exact row positions and of
+//   select -- one wave per unit takes the budget cut (longest prefix of the
+//             (key desc, id asc) order whose sizes fit the budget) with a radix
+//             select and writes the exact row positions and the list of
 //             approximated clusters;
 //   attend -- split-K online softmax over exact rows (gathered K/V), the
 //             unclustered tail and the approximated clusters (logit s + ln n,
 //             value Vbar), in base-2 exponent units, fp32 partials;
 //   merge  -- log-sum-exp merge of the splits.
+// Kernel boundaries carry the cross-workgroup dependencies: a device-scope
+// fence per workgroup (write back + invalidate of an XCD's L2) serialises and
+// costs far more than a launch on this chip.
 #include <math.h>
 
 #include "device.hpp"
@@ -25,88 +28,19 @@
 namespace mpa {
 
 // ---------------------------------------------------------------------------
-// score: 16 lanes per centroid row, 4 rows per wave instruction, 16 rows per
-// wave per step.  Each lane keeps its 8-element slice of the G queries.
+// score: workgroup (chunk, unit) scores 256 items, 16 lanes per centroid row,
+// 8 rows per lane group in flight, two passes.
+// select: one wave per unit (separate launch: the kernel boundary makes every
+// score visible to it across XCDs).
 // ---------------------------------------------------------------------------
-constexpr int kScoreChunk = 256;  // items per workgroup
+constexpr int kScoreChunk = 256;  // items per workgroup (64 per wave)
+constexpr int kSelCap = 2048;     // items staged in LDS for the cut
+constexpr int kSelPad = kSelCap + kSelCap / 32;  // one pad word per 32 items
 
-template <typename T, int G>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-    const int unit = blockIdx.y;
-    int n = a.n_items;
-    if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
-    const int i_begin = blockIdx.x * kScoreChunk;
-    if (i_begin >= n) return;
-    const int i_end = min(n, i_begin + kScoreChunk);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int rg = lane >> 4, li = lane & 15;
-    const int b = unit / a.Hkv, h = unit % a.Hkv;
-
-    float qv[G][8];
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        Slice8<T> s;
-        s.load(qb + (size_t)g * kHeadDim);
-        s.unpack(qv[g]);
-    }
-    const T* cu = reinterpret_cast<const T*>(a.cent) + (size_t)unit * a.cent_rows * kHeadDim + li * 8;
-    const int32_t* pl = a.pos_list ? a.pos_list + (size_t)unit * a.list_stride : nullptr;
-    const int32_t* mem = a.members ? a.members + (size_t)unit * a.cent_rows : nullptr;
-
-    for (int base = i_begin + wave * 16; base < i_end; base += 64) {
-        int cid[4];
-        bool valid[4];
-        Slice8<T> row[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = base + u * 4 + rg;
-            valid[u] = i < i_end;
-            const int ii = valid[u] ? i : i_begin;
-            cid[u] = pl ? mem[pl[ii]] : ii;
-            row[u].load(cu + (size_t)cid[u] * kHeadDim);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float x[8];
-            row[u].unpack(x);
-            float sg[G];
-            float r = 0.f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = qv[g][0] * x[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) d = fmaf(qv[g][e], x[e], d);
-                sg[g] = row16_sum(d) * kInvSqrtD;
-                r += sg[g];
-            }
-            r *= 1.0f / G;
-            if (valid[u]) {
-                const int i = base + u * 4 + rg;
-                float* so = a.s_out + ((size_t)unit * a.cent_rows + cid[u]) * G;
-                float mine = sg[0];
-#pragma unroll
-                for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
-                if (li < G) so[li] = mine;
-                if (li == G) a.r_out[(size_t)unit * a.r_stride + i] = r;
-                if (a.ids_out && li == 15) a.ids_out[(size_t)unit * a.r_stride + i] = cid[u];
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// select: one 256-thread workgroup per unit.
-//   1. items (key, size, start offset) staged in LDS (up to kSelCap items;
-//      larger counts read global memory through the same generic pointers);
-//   2. four 8-bit radix passes over the order-preserving key bits, each a
-//      size-weighted LDS histogram and a descending scan, locate the cut:
-//      every item with key above the cut value fits, items equal to it are
-//      taken in item order while they fit;
-//   3. chunks of 256 items: flags, scans, exact-row positions and the list
-//      of approximated clusters.
-// ---------------------------------------------------------------------------
-constexpr int kSelCap = 3072;  // 4 LDS arrays of this many items stay under 64 KB
+// LDS slot of item t: lane l reads items 32 l .. 32 l + 31, so one pad word
+// per 32 items puts the 64 lanes of a wave on distinct banks.
+__device__ __forceinline__ int sel_slot(int t) { return t + (t >> 5); }
+constexpr int kSelTile = 2048;    // items per lane-tile pass (32 consecutive items per lane)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -114,118 +48,254 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-    __shared__ float s_key[kSelCap];
-    __shared__ int32_t s_size[kSelCap];
-    __shared__ int32_t s_off[kSelCap];
-    __shared__ int32_t s_id[kSelCap];
-    __shared__ int hist[256];
-    __shared__ int scan_lds[16];
-    __shared__ int bcast[2];
-    const int unit = blockIdx.x;
-    const int tid = threadIdx.x;
-    int n = a.n_items;
-    if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
+// Orders LDS and memory accesses of this wave before the following ones.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
 
+__device__ __forceinline__ int wave_exclusive_sum(int v, int& total) {
+    const int inc = wave_inclusive_sum(v);
+    total = __shfl(inc, kWave - 1, kWave);
+    return inc - v;
+}
+
+// Budget cut of one unit by a single wave (lane = threadIdx.x < 64).
+// Items t in [0, n): key, size and start offset (through ids when present).
+// Four 8-bit radix passes over the order-preserving key bits find the cut
+// value: the size-weighted histogram of the items still matching the prefix
+// is scanned from the top digit down until the budget left is crossed.
+// Items above the cut value are selected; items equal to it are taken in
+// item order while they fit.  Then, in item order: positions of the exact
+// rows, the list of approximated clusters and the counts.
+template <bool kLds>
+__device__ __forceinline__ void select_wave(const SelectArgs& a, int unit, int n, float* s_key, int32_t* s_size, int32_t* s_off,
+                            int32_t* s_end, int32_t* s_id, int* hist) {
+    const int lane = threadIdx.x & (kWave - 1);
     const float* gkey = a.key + (size_t)unit * a.key_stride;
     const int32_t* gids = a.ids ? a.ids + (size_t)unit * a.key_stride : nullptr;
     const int32_t* gsz = a.sizes + (size_t)unit * a.size_stride;
     const int32_t* goff = a.offsets + (size_t)unit * (a.size_stride + 1);
-    const bool in_lds = n <= kSelCap;
-    for (int t = tid; t < (in_lds ? n : 0); t += 256) {
-        const int id = gids ? gids[t] : t;
-        s_key[t] = gkey[t];
-        s_id[t] = id;
-        s_size[t] = gsz[id];
-        s_off[t] = goff[id];
+    if (kLds) {
+        for (int t = lane; t < n; t += kWave) {
+            const int id = gids ? gids[t] : t;
+            const int sl = sel_slot(t);
+            s_key[sl] = gkey[t];
+            s_id[sl] = id;
+            s_size[sl] = gsz[id];
+            s_off[sl] = goff[id];
+            s_end[sl] = goff[id + 1];
+        }
+        wave_sync();
     }
-    __syncthreads();
-#define ITEM_KEY(t) (in_lds ? s_key[t] : gkey[t])
-#define ITEM_ID(t) (in_lds ? s_id[t] : (gids ? gids[t] : (t)))
-#define ITEM_SIZE(t) (in_lds ? s_size[t] : gsz[ITEM_ID(t)])
-#define ITEM_OFF(t) (in_lds ? s_off[t] : goff[ITEM_ID(t)])
+    auto KEY = [&](int t) { return kLds ? s_key[sel_slot(t)] : gkey[t]; };
+    auto ID = [&](int t) { return kLds ? s_id[sel_slot(t)] : (gids ? gids[t] : t); };
+    auto SIZE = [&](int t) { return kLds ? s_size[sel_slot(t)] : gsz[gids ? gids[t] : t]; };
+    auto OFF = [&](int t) { return kLds ? s_off[sel_slot(t)] : goff[gids ? gids[t] : t]; };
+    auto END = [&](int t) { return kLds ? s_end[sel_slot(t)] : goff[(gids ? gids[t] : t) + 1]; };
 
     uint32_t prefix = 0, mask = 0;
     int R = a.budget;
     bool done = false;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
-        __syncthreads();
-        for (int t = tid; t < n; t += 256) {
-            const int sz = ITEM_SIZE(t);
-            if (sz > 0) {
-                const uint32_t u = order_key(ITEM_KEY(t));
-                if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], sz);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+        wave_sync();
+        for (int base = 0; base < n; base += kSelTile) {
+            for (int k = 0; k < 32; ++k) {
+                const int t = base + lane * 32 + k;
+                if (t < n) {
+                    const int sz = SIZE(t);
+                    if (sz > 0) {
+                        const uint32_t u = order_key(KEY(t));
+                        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], sz);
+                    }
+                }
             }
         }
-        __syncthreads();
-        const int v = hist[255 - tid];
-        int4 tot;
-        const int4 ex = block256_exclusive_sum4(make_int4(v, 0, 0, 0), tot, scan_lds);
-        if (tot.x <= R) {
-            done = true;  // every item matching the prefix fits
+        wave_sync();
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = hist[255 - (4 * lane + j)];
+        int total;
+        int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
+        if (total <= R) {  // uniform across the wave
+            done = true;
             break;
         }
-        if (ex.x <= R && R < ex.x + v) {
-            bcast[0] = 255 - tid;
-            bcast[1] = ex.x;
+        int found = -1, cum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (found < 0 && run <= R && R < run + v[j]) {
+                found = 255 - (4 * lane + j);
+                cum = run;
+            }
+            run += v[j];
         }
-        __syncthreads();
-        R -= bcast[1];
-        prefix |= (uint32_t)bcast[0] << shift;
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = __ffsll((long long)bal) - 1;
+        const int digit = __shfl(found, src, kWave);
+        R -= __shfl(cum, src, kWave);
+        prefix |= (uint32_t)digit << shift;
         mask |= 0xFFu << shift;
-        __syncthreads();
+        wave_sync();
     }
     const uint32_t tau = prefix;
 
-    int carry_tie = 0;
-    int4 carry = make_int4(0, 0, 0, 0);  // rows, pseudo items, selected items
     int32_t* rows = a.rows + (size_t)unit * a.row_stride;
     int32_t* plist = a.plist + (size_t)unit * a.plist_stride;
     int32_t* dbg = a.dbg_selected ? a.dbg_selected + (size_t)unit * a.dbg_stride : nullptr;
-    for (int base = 0; base < n; base += 256) {
-        const int t = base + tid;
-        const bool valid = t < n;
-        const int sz = valid ? ITEM_SIZE(t) : 0;
-        const uint32_t u = valid ? order_key(ITEM_KEY(t)) : 0u;
-        bool sel;
-        if (done) {
-            sel = sz > 0 && u >= prefix;
-        } else {
-            const int tie_w = (sz > 0 && u == tau) ? sz : 0;
-            int4 tt;
-            const int4 ex = block256_exclusive_sum4(make_int4(tie_w, 0, 0, 0), tt, scan_lds);
-            sel = sz > 0 && (u > tau || (tie_w > 0 && carry_tie + ex.x + sz <= R));
-            carry_tie += tt.x;
-        }
-        const bool pse = !sel && sz > 0 && a.want_pseudo;
-        int4 tot;
-        const int4 ex = block256_exclusive_sum4(make_int4(sel ? sz : 0, pse ? 1 : 0, sel ? 1 : 0, 0), tot, scan_lds);
-        if (valid) {
-            const int id = ITEM_ID(t);
-            if (sel) {
-                const int off = ITEM_OFF(t);
-                const int r0 = carry.x + ex.x;
-                for (int jx = 0; jx < sz; ++jx) rows[r0 + jx] = off + jx;
+    int carry_tie = 0, carry_rows = 0, carry_p = 0, carry_sel = 0;
+    for (int base = 0; base < n; base += kSelTile) {
+        int tie_local = 0;
+        if (!done) {
+            for (int k = 0; k < 32; ++k) {
+                const int t = base + lane * 32 + k;
+                if (t < n) {
+                    const int sz = SIZE(t);
+                    if (sz > 0 && order_key(KEY(t)) == tau) tie_local += sz;
+                }
             }
-            if (pse) plist[carry.y + ex.y] = id;
+        }
+        int tie_total;
+        int run_tie = carry_tie + wave_exclusive_sum(tie_local, tie_total);
+        uint32_t selbits = 0;
+        int rows_local = 0, p_local = 0, s_local = 0;
+        for (int k = 0; k < 32; ++k) {
+            const int t = base + lane * 32 + k;
+            if (t >= n) break;
+            const int sz = SIZE(t);
+            if (sz <= 0) continue;
+            const uint32_t u = order_key(KEY(t));
+            bool sel;
+            if (done) {
+                sel = u >= prefix;
+            } else {
+                const bool tie = u == tau;
+                sel = u > tau || (tie && run_tie + sz <= R);
+                if (tie) run_tie += sz;
+            }
+            if (sel) {
+                selbits |= 1u << k;
+                rows_local += END(t) - OFF(t);
+                ++s_local;
+            } else if (a.want_pseudo) {
+                ++p_local;
+            }
+        }
+        int rt, pt, st;
+        int ro = carry_rows + wave_exclusive_sum(rows_local, rt);
+        int po = carry_p + wave_exclusive_sum(p_local, pt);
+        wave_exclusive_sum(s_local, st);
+        for (int k = 0; k < 32; ++k) {
+            const int t = base + lane * 32 + k;
+            if (t >= n) break;
+            const int sz = SIZE(t);
+            const int id = ID(t);
+            const bool sel = (selbits >> k) & 1u;
+            if (sel) {
+                const int off = OFF(t), nr = END(t) - off;
+                for (int jx = 0; jx < nr; ++jx) rows[ro + jx] = off + jx;
+                ro += nr;
+            } else if (sz > 0 && a.want_pseudo) {
+                plist[po++] = id;
+            }
             if (dbg) dbg[id] = sel ? 1 : 0;
         }
-        carry.x += tot.x;
-        carry.y += tot.y;
-        carry.z += tot.z;
+        carry_tie += tie_total;
+        carry_rows += rt;
+        carry_p += pt;
+        carry_sel += st;
     }
-    if (tid == 0) {
+    if (lane == 0) {
         int32_t* cnt = a.counts + unit * 4;
-        cnt[0] = carry.x;
-        cnt[1] = carry.y;
-        cnt[2] = carry.z;
+        cnt[0] = carry_rows;
+        cnt[1] = carry_p;
+        cnt[2] = carry_sel;
         cnt[3] = 0;
     }
-#undef ITEM_KEY
-#undef ITEM_ID
-#undef ITEM_SIZE
-#undef ITEM_OFF
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+    const int unit = blockIdx.y;
+    int n = a.n_items;
+    if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rg = lane >> 4, li = lane & 15;
+    const int i0 = blockIdx.x * kScoreChunk + wave * 64;
+
+    if (i0 < n) {
+        const int b = unit / a.Hkv, h = unit % a.Hkv;
+        float qv[G][8];
+        const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            Slice8<T> s;
+            s.load(qb + (size_t)g * kHeadDim);
+            s.unpack(qv[g]);
+        }
+        const T* cu = reinterpret_cast<const T*>(a.cent) + (size_t)unit * a.cent_rows * kHeadDim + li * 8;
+        const int32_t* pl = a.pos_list ? a.pos_list + (size_t)unit * a.list_stride : nullptr;
+        const int32_t* mem = a.members ? a.members + (size_t)unit * a.cent_rows : nullptr;
+#pragma unroll 1
+        for (int half = 0; half < 2; ++half) {  // 2 x 8 rows per lane group in flight
+            const int ib = i0 + half * 32;
+            int cid[8];
+            Slice8<T> row[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = ib + u * 4 + rg;
+                const int ii = i < n ? i : i0;
+                cid[u] = pl ? mem[pl[ii]] : ii;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) row[u].load(cu + (size_t)cid[u] * kHeadDim);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = ib + u * 4 + rg;
+                float x[8];
+                row[u].unpack(x);
+                float sg[G];
+                float r = 0.f;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    float d = qv[g][0] * x[0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) d = fmaf(qv[g][e], x[e], d);
+                    sg[g] = row16_sum(d) * kInvSqrtD;
+                    r += sg[g];
+                }
+                r *= 1.0f / G;
+                if (i < n) {
+                    float* so = a.s_out + ((size_t)unit * a.cent_rows + cid[u]) * G;
+                    float mine = sg[0];
+#pragma unroll
+                    for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
+                    if (li < G) so[li] = mine;
+                    if (li == G) a.r_out[(size_t)unit * a.r_stride + i] = r;
+                    if (a.ids_out && li == 15) a.ids_out[(size_t)unit * a.r_stride + i] = cid[u];
+                }
+            }
+        }
+    }
+}
+
+// One wave per unit takes the budget cut.
+__global__ __launch_bounds__(64) void select_kernel(SelectArgs se) {
+    __shared__ float s_key[kSelPad];
+    __shared__ int32_t s_size[kSelPad];
+    __shared__ int32_t s_off[kSelPad];
+    __shared__ int32_t s_end[kSelPad];
+    __shared__ int32_t s_id[kSelPad];
+    __shared__ int hist[256];
+    const int unit = blockIdx.x;
+    int n = se.n_items;
+    if (se.n_items_dev) n = min(n, se.n_items_dev[unit * 4]);
+    if (n <= kSelCap)
+        select_wave<true>(se, unit, n, s_key, s_size, s_off, s_end, s_id, hist);
+    else
+        select_wave<false>(se, unit, n, s_key, s_size, s_off, s_end, s_id, hist);
 }
 
 // ---------------------------------------------------------------------------
@@ -551,8 +621,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
         }
     }
     const int b = unit / Hkv, h = unit % Hkv;
-    const int Hq = Hkv * G;
-    out[((size_t)b * Hq + (size_t)h * G + g) * kHeadDim + dd] = l > 0.f ? acc / l : 0.f;
+    out[((size_t)b * Hkv * G + (size_t)h * G + g) * kHeadDim + dd] = l > 0.f ? acc / l : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -577,7 +646,7 @@ hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStre
 }
 
 hipError_t launch_select(const SelectArgs& a, int units, hipStream_t st) {
-    hipLaunchKernelGGL(select_kernel, dim3(units), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(select_kernel, dim3(units), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

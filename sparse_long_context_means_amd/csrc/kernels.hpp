@@ -69,7 +69,6 @@ struct ScoreArgs {
     int32_t* ids_out;       // optional [U][r_stride]: cluster id of each item
     int32_t Hq, Hkv;
 };
-hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st);
 
 struct SelectArgs {
     const float* key;        // [U][key_stride] ranking key per item
@@ -82,7 +81,7 @@ struct SelectArgs {
     const int32_t* n_items_dev;  // optional per-unit count at n_items_dev[unit * 4]
     int32_t budget;
     int32_t want_pseudo;
-    int32_t* rows;           // [U][row_stride] positions offsets[id] + j of selected items
+    int32_t* rows;           // [U][row_stride] member positions of selected items
     int32_t row_stride;
     int32_t* plist;          // [U][plist_stride] unselected non-empty cluster ids
     int32_t plist_stride;
@@ -90,6 +89,9 @@ struct SelectArgs {
     int32_t* dbg_selected;   // optional [U][dbg_stride] by cluster id
     int32_t dbg_stride;
 };
+hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st);
+// Budget cut of every unit (one wave each).  Rows of a selected item are its
+// member positions offsets[id] .. offsets[id + 1]; its budget weight is sizes[id].
 hipError_t launch_select(const SelectArgs& a, int units, hipStream_t st);
 
 struct PseudoList {

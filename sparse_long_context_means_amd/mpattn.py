@@ -250,7 +250,7 @@ class Workspace:
         key = str(device)
         buf = self._buf.get(key)
         if buf is None or buf.numel() < max(n, 1):
-            buf = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+            buf = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # counters start at zero
             self._buf[key] = buf
         return buf
 

@@ -182,7 +182,7 @@ def test_workspace_and_stages():
     assert M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 100, 0, 9) == ctypes.c_size_t(-1).value
     assert p.decode_stages() == ["score", "select", "attend", "merge"]
     ph = _params(coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
-    assert ph.decode_stages() == ["score_coarse", "select_coarse", "score_fine", "select_fine", "attend", "merge"]
+    assert ph.decode_stages() == ["coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"]
     small = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=1).c()), 2053, 0, M.OP_DECODE)
     big = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=64).c()), 2053, 0, M.OP_DECODE)
     assert big > small
