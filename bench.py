@@ -10,8 +10,9 @@ a fresh query per step.
 One step = one decode of the whole batch through the C ABI: score and budget
 cut (one launch), then split-K attention with the merge (one launch).  The clustering is built once before timing (prefill time)
 and reported separately.  Headline timing is cold: before every step a 1 GiB
-read evicts the 256 MB Infinity Cache (and the L2s) with clean lines, outside
-the timed events, so the centroids and rows come from HBM.  Warm (back-to-back) timing is reported as
+streaming read (the library's read probe) evicts the 256 MB Infinity Cache and
+the L2s with clean lines, outside the timed events, so the centroids and rows
+come from HBM.  The same probe, timed alone, gives the achievable read rate.  Warm (back-to-back) timing is reported as
 well.  Per-stage HIP events on the launch stream give the dominant kernel's
 average duration for the roofline object.
 
@@ -137,10 +138,23 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict caches
-    sink = torch.empty((), dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def evict():
-        torch.sum(flush, dim=0, out=sink)
+        M.read_probe(flush, sink)
+
+    # achievable streaming-read rate of this GPU (the same 1 GiB read)
+    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evict()
+    probe_ms = []
+    for _ in range(5):
+        pa.record(stream)
+        evict()
+        pb.record(stream)
+        torch.cuda.synchronize()
+        probe_ms.append(pa.elapsed_time(pb))
+    probe_gbps = flush.numel() * 4 / (min(probe_ms) * 1e-3) / 1e9
+    log(f"[bench] streaming-read probe {probe_gbps:.0f} GB/s")
 
     def enqueue(s, first=0, last=n_stages - 1):
         st = M.lib.mpattn_decode_ex(ctypes.byref(cp), ctypes.c_void_p(qs[s].data_ptr()),
@@ -258,6 +272,8 @@ def main():
                    "splits": args.splits or "auto"},
         "effective_GBps": round(eff_gbps, 1),
         "effective_frac_of_hbm_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
+        "hbm_read_probe_GBps": round(probe_gbps, 1),
+        "effective_frac_of_read_probe": round(eff_gbps / probe_gbps, 4),
         "algorithmic_MB_per_step": round(float(byts.mean()) / 1e6, 2),
         "warm_us_per_step": round(warm_us, 2),
         "cold_us_p10_p50_p90": [round(float(np.percentile(step_ms, q)) * 1e3, 2) for q in (10, 50, 90)],

@@ -228,6 +228,15 @@ mpattn_status mpattn_decode_ex(const mpattn_params* params, const void* q, const
                                void* stream, const mpattn_decode_debug* debug, int32_t first_stage,
                                int32_t last_stage);
 
+/*
+ * Measurement utility: streams `bytes` (a multiple of 16) from the device
+ * buffer `buf` with 16-byte loads and no reuse, so that the achievable HBM
+ * read rate can be timed next to the decode.  `sink` (device, one uint32) is
+ * written only if the XOR of all data equals an arbitrary constant.
+ * Errors: INVALID_ARG (null pointer, bad size), HIP.
+ */
+mpattn_status mpattn_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

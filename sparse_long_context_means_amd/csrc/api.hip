@@ -385,4 +385,9 @@ mpattn_status mpattn_decode(const mpattn_params* p, const void* q, const void* k
                             stream, nullptr, 0, n - 1);
 }
 
+mpattn_status mpattn_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return MPATTN_ERR_INVALID_ARG;
+    return hip_status(launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

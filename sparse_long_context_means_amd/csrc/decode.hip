@@ -30,17 +30,10 @@ namespace mpa {
 // ---------------------------------------------------------------------------
 // score: workgroup (chunk, unit) scores 256 items, 16 lanes per centroid row,
 // 8 rows per lane group in flight, two passes.
-// select: one wave per unit (separate launch: the kernel boundary makes every
-// score visible to it across XCDs).
+// select: one workgroup per unit takes the budget cut (separate launch: the
+// kernel boundary makes every score visible to it).
 // ---------------------------------------------------------------------------
 constexpr int kScoreChunk = 256;  // items per workgroup (64 per wave)
-constexpr int kSelCap = 2048;     // items staged in LDS for the cut
-constexpr int kSelPad = kSelCap + kSelCap / 32;  // one pad word per 32 items
-
-// LDS slot of item t: lane l reads items 32 l .. 32 l + 31, so one pad word
-// per 32 items puts the 64 lanes of a wave on distinct banks.
-__device__ __forceinline__ int sel_slot(int t) { return t + (t >> 5); }
-constexpr int kSelTile = 2048;    // items per lane-tile pass (32 consecutive items per lane)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -56,70 +49,95 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ int wave_exclusive_sum(int v, int& total) {
     const int inc = wave_inclusive_sum(v);
-    total = __shfl(inc, kWave - 1, kWave);
+    total = lane_value(inc, kWave - 1);
     return inc - v;
 }
 
-// Budget cut of one unit by a single wave (lane = threadIdx.x < 64).
-// Items t in [0, n): key, size and start offset (through ids when present).
+// Budget cut of one unit by one 256-thread workgroup.  Thread t owns items
+// 8 t .. 8 t + 7 of each tile of 2048 (key, size, member range in registers).
 // Four 8-bit radix passes over the order-preserving key bits find the cut
-// value: the size-weighted histogram of the items still matching the prefix
-// is scanned from the top digit down until the budget left is crossed.
-// Items above the cut value are selected; items equal to it are taken in
-// item order while they fit.  Then, in item order: positions of the exact
-// rows, the list of approximated clusters and the counts.
-template <bool kLds>
-__device__ __forceinline__ void select_wave(const SelectArgs& a, int unit, int n, float* s_key, int32_t* s_size, int32_t* s_off,
-                            int32_t* s_end, int32_t* s_id, int* hist) {
-    const int lane = threadIdx.x & (kWave - 1);
+// value: pass p adds the sizes of the items still matching the prefix into
+// its own LDS histogram (all four are cleared up front, so a pass needs one
+// barrier), then every wave scans that histogram from the top digit down to
+// the budget left, and all reach the same digit.  Items above the cut value
+// are selected; items equal to it are taken in item order while they fit.
+// Two workgroup scans then place, in item order, the exact row positions and
+// the approximated clusters.
+constexpr int kSelItems = 8;                 // items per thread per tile
+constexpr int kSelTileN = 256 * kSelItems;   // items per tile
+
+struct SelItems {
+    uint32_t key[kSelItems];
+    int32_t sz[kSelItems], off[kSelItems], nr[kSelItems], id[kSelItems];
+};
+
+__device__ __forceinline__ void load_items(const SelectArgs& a, int unit, int n, int base, SelItems& it) {
     const float* gkey = a.key + (size_t)unit * a.key_stride;
     const int32_t* gids = a.ids ? a.ids + (size_t)unit * a.key_stride : nullptr;
     const int32_t* gsz = a.sizes + (size_t)unit * a.size_stride;
     const int32_t* goff = a.offsets + (size_t)unit * (a.size_stride + 1);
-    if (kLds) {
-        for (int t = lane; t < n; t += kWave) {
-            const int id = gids ? gids[t] : t;
-            const int sl = sel_slot(t);
-            s_key[sl] = gkey[t];
-            s_id[sl] = id;
-            s_size[sl] = gsz[id];
-            s_off[sl] = goff[id];
-            s_end[sl] = goff[id + 1];
-        }
-        wave_sync();
+    const int t0 = base + threadIdx.x * kSelItems;
+    float kk[kSelItems];
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        const bool v = t0 + j < n;
+        it.id[j] = v ? (gids ? gids[t0 + j] : t0 + j) : 0;
+        kk[j] = v ? gkey[t0 + j] : 0.f;
     }
-    auto KEY = [&](int t) { return kLds ? s_key[sel_slot(t)] : gkey[t]; };
-    auto ID = [&](int t) { return kLds ? s_id[sel_slot(t)] : (gids ? gids[t] : t); };
-    auto SIZE = [&](int t) { return kLds ? s_size[sel_slot(t)] : gsz[gids ? gids[t] : t]; };
-    auto OFF = [&](int t) { return kLds ? s_off[sel_slot(t)] : goff[gids ? gids[t] : t]; };
-    auto END = [&](int t) { return kLds ? s_end[sel_slot(t)] : goff[(gids ? gids[t] : t) + 1]; };
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+        const bool v = t0 + j < n;
+        const int sz = gsz[it.id[j]];
+        const int of = goff[it.id[j]];
+        const int en = goff[it.id[j] + 1];
+        it.sz[j] = v ? sz : 0;
+        it.off[j] = of;
+        it.nr[j] = v ? en - of : 0;
+        it.key[j] = order_key(kk[j]);
+    }
+}
+
+// Exclusive prefix of v over the workgroup in thread order (4 waves); also
+// returns the total.  `lds` holds 4 ints per value slot.
+__device__ __forceinline__ int4 block_excl4(int4 v, int4& total, int* lds) {
+    return block256_exclusive_sum4(v, total, lds);
+}
+
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+    __shared__ int hist[4][256];
+    __shared__ int scan_lds[16];
+    const int unit = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    int n = a.n_items;
+    if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
+
+    SelItems it;
+    const bool resident = n <= kSelTileN;
+    if (resident) load_items(a, unit, n, 0, it);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) hist[p][tid] = 0;
+    __syncthreads();
 
     uint32_t prefix = 0, mask = 0;
     int R = a.budget;
     bool done = false;
-    for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
-        wave_sync();
-        for (int base = 0; base < n; base += kSelTile) {
-            for (int k = 0; k < 32; ++k) {
-                const int t = base + lane * 32 + k;
-                if (t < n) {
-                    const int sz = SIZE(t);
-                    if (sz > 0) {
-                        const uint32_t u = order_key(KEY(t));
-                        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], sz);
-                    }
-                }
-            }
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+        for (int base = 0; base < n; base += kSelTileN) {
+            if (!resident) load_items(a, unit, n, base, it);
+#pragma unroll
+            for (int j = 0; j < kSelItems; ++j)
+                if (it.sz[j] > 0 && (it.key[j] & mask) == prefix)
+                    atomicAdd(&hist[p][(it.key[j] >> shift) & 255u], it.sz[j]);
         }
-        wave_sync();
+        __syncthreads();
         int v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = hist[255 - (4 * lane + j)];
+        for (int j = 0; j < 4; ++j) v[j] = hist[p][255 - (4 * lane + j)];
         int total;
         int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
-        if (total <= R) {  // uniform across the wave
+        if (total <= R) {  // the same in every wave
             done = true;
             break;
         }
@@ -134,39 +152,42 @@ __device__ __forceinline__ void select_wave(const SelectArgs& a, int unit, int n
         }
         const uint64_t bal = __ballot(found >= 0);
         const int src = __ffsll((long long)bal) - 1;
-        const int digit = __shfl(found, src, kWave);
-        R -= __shfl(cum, src, kWave);
+        const int digit = lane_value(found, src);
+        R -= lane_value(cum, src);
         prefix |= (uint32_t)digit << shift;
         mask |= 0xFFu << shift;
-        wave_sync();
     }
     const uint32_t tau = prefix;
 
     int32_t* rows = a.rows + (size_t)unit * a.row_stride;
     int32_t* plist = a.plist + (size_t)unit * a.plist_stride;
     int32_t* dbg = a.dbg_selected ? a.dbg_selected + (size_t)unit * a.dbg_stride : nullptr;
-    int carry_tie = 0, carry_rows = 0, carry_p = 0, carry_sel = 0;
-    for (int base = 0; base < n; base += kSelTile) {
+    int4 carry = make_int4(0, 0, 0, 0);  // rows, pseudo items, selected items
+    int carry_tie = 0;
+    for (int base = 0; base < n; base += kSelTileN) {
+        if (!resident) load_items(a, unit, n, base, it);
         int tie_local = 0;
         if (!done) {
-            for (int k = 0; k < 32; ++k) {
-                const int t = base + lane * 32 + k;
-                if (t < n) {
-                    const int sz = SIZE(t);
-                    if (sz > 0 && order_key(KEY(t)) == tau) tie_local += sz;
-                }
+#pragma unroll
+            for (int j = 0; j < kSelItems; ++j)
+                if (it.sz[j] > 0 && it.key[j] == tau) tie_local += it.sz[j];
+        }
+        int run_tie = carry_tie;
+        if (!done) {
+            // usually a single item carries the cut value: then no scan is needed
+            const int holders = __syncthreads_count(tie_local > 0);
+            if (holders > 1 || !resident) {
+                int4 tt;
+                run_tie += block_excl4(make_int4(tie_local, 0, 0, 0), tt, scan_lds).x;
+                carry_tie += tt.x;
             }
         }
-        int tie_total;
-        int run_tie = carry_tie + wave_exclusive_sum(tie_local, tie_total);
         uint32_t selbits = 0;
         int rows_local = 0, p_local = 0, s_local = 0;
-        for (int k = 0; k < 32; ++k) {
-            const int t = base + lane * 32 + k;
-            if (t >= n) break;
-            const int sz = SIZE(t);
-            if (sz <= 0) continue;
-            const uint32_t u = order_key(KEY(t));
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j) {
+            const int sz = it.sz[j];
+            const uint32_t u = it.key[j];
             bool sel;
             if (done) {
                 sel = u >= prefix;
@@ -175,43 +196,34 @@ __device__ __forceinline__ void select_wave(const SelectArgs& a, int unit, int n
                 sel = u > tau || (tie && run_tie + sz <= R);
                 if (tie) run_tie += sz;
             }
-            if (sel) {
-                selbits |= 1u << k;
-                rows_local += END(t) - OFF(t);
-                ++s_local;
-            } else if (a.want_pseudo) {
-                ++p_local;
-            }
+            sel = sel && sz > 0;
+            selbits |= (uint32_t)sel << j;
+            rows_local += sel ? it.nr[j] : 0;
+            s_local += sel;
+            p_local += (!sel && sz > 0 && a.want_pseudo) ? 1 : 0;
         }
-        int rt, pt, st;
-        int ro = carry_rows + wave_exclusive_sum(rows_local, rt);
-        int po = carry_p + wave_exclusive_sum(p_local, pt);
-        wave_exclusive_sum(s_local, st);
-        for (int k = 0; k < 32; ++k) {
-            const int t = base + lane * 32 + k;
-            if (t >= n) break;
-            const int sz = SIZE(t);
-            const int id = ID(t);
-            const bool sel = (selbits >> k) & 1u;
-            if (sel) {
-                const int off = OFF(t), nr = END(t) - off;
-                for (int jx = 0; jx < nr; ++jx) rows[ro + jx] = off + jx;
-                ro += nr;
-            } else if (sz > 0 && a.want_pseudo) {
-                plist[po++] = id;
+        int4 tot;
+        const int4 ex = block_excl4(make_int4(rows_local, p_local, s_local, 0), tot, scan_lds);
+        int ro = carry.x + ex.x, po = carry.y + ex.y;
+#pragma unroll
+        for (int j = 0; j < kSelItems; ++j) {
+            if ((selbits >> j) & 1u) {
+                for (int jx = 0; jx < it.nr[j]; ++jx) rows[ro + jx] = it.off[j] + jx;
+                ro += it.nr[j];
+            } else if (it.sz[j] > 0 && a.want_pseudo) {
+                plist[po++] = it.id[j];
             }
-            if (dbg) dbg[id] = sel ? 1 : 0;
+            if (dbg && base + tid * kSelItems + j < n) dbg[it.id[j]] = (selbits >> j) & 1u;
         }
-        carry_tie += tie_total;
-        carry_rows += rt;
-        carry_p += pt;
-        carry_sel += st;
+        carry.x += tot.x;
+        carry.y += tot.y;
+        carry.z += tot.z;
     }
-    if (lane == 0) {
+    if (tid == 0) {
         int32_t* cnt = a.counts + unit * 4;
-        cnt[0] = carry_rows;
-        cnt[1] = carry_p;
-        cnt[2] = carry_sel;
+        cnt[0] = carry.x;
+        cnt[1] = carry.y;
+        cnt[2] = carry.z;
         cnt[3] = 0;
     }
 }
@@ -227,14 +239,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
     if (i0 < n) {
         const int b = unit / a.Hkv, h = unit % a.Hkv;
-        float qv[G][8];
+        QSlice<T> qv[G];
         const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            Slice8<T> s;
-            s.load(qb + (size_t)g * kHeadDim);
-            s.unpack(qv[g]);
-        }
+        for (int g = 0; g < G; ++g) qv[g].load(qb + (size_t)g * kHeadDim);
         const T* cu = reinterpret_cast<const T*>(a.cent) + (size_t)unit * a.cent_rows * kHeadDim + li * 8;
         const int32_t* pl = a.pos_list ? a.pos_list + (size_t)unit * a.list_stride : nullptr;
         const int32_t* mem = a.members ? a.members + (size_t)unit * a.cent_rows : nullptr;
@@ -254,16 +262,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int i = ib + u * 4 + rg;
-                float x[8];
-                row[u].unpack(x);
                 float sg[G];
                 float r = 0.f;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    float d = qv[g][0] * x[0];
-#pragma unroll
-                    for (int e = 1; e < 8; ++e) d = fmaf(qv[g][e], x[e], d);
-                    sg[g] = row16_sum(d) * kInvSqrtD;
+                    sg[g] = row16_sum(dot8(qv[g], row[u])) * kInvSqrtD;
                     r += sg[g];
                 }
                 r *= 1.0f / G;
@@ -281,62 +284,45 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     }
 }
 
-// One wave per unit takes the budget cut.
-__global__ __launch_bounds__(64) void select_kernel(SelectArgs se) {
-    __shared__ float s_key[kSelPad];
-    __shared__ int32_t s_size[kSelPad];
-    __shared__ int32_t s_off[kSelPad];
-    __shared__ int32_t s_end[kSelPad];
-    __shared__ int32_t s_id[kSelPad];
-    __shared__ int hist[256];
-    const int unit = blockIdx.x;
-    int n = se.n_items;
-    if (se.n_items_dev) n = min(n, se.n_items_dev[unit * 4]);
-    if (n <= kSelCap)
-        select_wave<true>(se, unit, n, s_key, s_size, s_off, s_end, s_id, hist);
-    else
-        select_wave<false>(se, unit, n, s_key, s_size, s_off, s_end, s_id, hist);
-}
-
 // ---------------------------------------------------------------------------
-// attend: workgroup (split, unit), 4 waves, 16 lanes per row.  Each row group
-// (16 lanes) keeps its own online-softmax state (m, l, acc[8] per head) over
-// the rows it visits, 4 rows per step; the 4 row groups of a wave and the 4
-// waves are merged at the end.  Index lists of the split are staged in LDS;
-// row loads of the next step are issued before the current step's math.
+// attend: workgroup (split, unit), 4 waves, 16 lanes per row, 8 dims a lane.
+// A row group (16 lanes) keeps its own online-softmax state (m, l, acc[8] per
+// head) over the rows it visits, 2 rows per step with the next step's rows
+// already in flight.  The running maximum is only raised when a logit exceeds
+// it by more than 2^8 (every weight stays <= 256 in fp32), so rescaling is
+// rare.  The split's exact positions and approximated items are staged in LDS
+// up front, together.  Row groups and waves are merged at the end.
 // ---------------------------------------------------------------------------
-constexpr int kAttCap = 512;  // staged indices per list and pass
+constexpr int kAttCap = 512;       // staged items per list and pass
+constexpr float kLazyMax = 8.0f;   // base-2 headroom before the running max moves
 
 template <int G>
 struct SoftState {
     float m[G], l[G], acc[G][8];
 };
 
+// Adds 2 rows with base-2 logits lg[u][g] (-inf for an absent row).
 template <typename T, int G>
-__device__ __forceinline__ void absorb4(SoftState<G>& st, const float (&lg)[4][G], const Slice8<T> (&v)[4]) {
-    float x[4][8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u].unpack(x[u]);
+__device__ __forceinline__ void absorb2(SoftState<G>& st, const float (&lg)[2][G], const Slice8<T> (&v)[2]) {
+    float x0[8], x1[8];
+    v[0].unpack(x0);
+    v[1].unpack(x1);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const float mx = fmaxf(fmaxf(lg[0][g], lg[1][g]), fmaxf(lg[2][g], lg[3][g]));
-        const float mnew = fmaxf(st.m[g], mx);
-        if (mnew == -INFINITY) continue;
-        const float sc = __builtin_amdgcn_exp2f(st.m[g] - mnew);
-        float p[4];
+        const float mx = fmaxf(lg[0][g], lg[1][g]);
+        if (mx == -INFINITY) continue;
+        if (mx > st.m[g] + kLazyMax) {  // rare: raise the reference maximum
+            const float sc = __builtin_amdgcn_exp2f(st.m[g] - mx);
+            st.l[g] *= sc;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) p[u] = __builtin_amdgcn_exp2f(lg[u][g] - mnew);
-        st.l[g] = fmaf(st.l[g], sc, (p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float t = st.acc[g][e] * sc;
-            t = fmaf(p[0], x[0][e], t);
-            t = fmaf(p[1], x[1][e], t);
-            t = fmaf(p[2], x[2][e], t);
-            t = fmaf(p[3], x[3][e], t);
-            st.acc[g][e] = t;
+            for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
+            st.m[g] = mx;
         }
-        st.m[g] = mnew;
+        const float p0 = __builtin_amdgcn_exp2f(lg[0][g] - st.m[g]);
+        const float p1 = __builtin_amdgcn_exp2f(lg[1][g] - st.m[g]);
+        st.l[g] += p0 + p1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(p1, x1[e], fmaf(p0, x0[e], st.acc[g][e]));
     }
 }
 
@@ -356,45 +342,19 @@ __device__ __forceinline__ void merge_state(SoftState<G>& st, const float* om, c
     }
 }
 
-// Dot products of 4 rows with the G scaled queries (logits in base-2 units).
-template <typename T, int G>
-__device__ __forceinline__ void logits4(const float (&qs)[G][8], const Slice8<T> (&k)[4], const bool (&valid)[4],
-                                        float (&lg)[4][G]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        float x[8];
-        k[u].unpack(x);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float d = qs[g][0] * x[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) d = fmaf(qs[g][e], x[e], d);
-            d = row16_sum(d);
-            lg[u][g] = valid[u] ? d : -INFINITY;
-        }
-    }
-}
-
-// Row buffers of one step: 4 rows per row group (row i = step*64 + wave*16 +
-// u*4 + rg of the staged list).
 template <typename T>
 struct RowBuf {
-    Slice8<T> k[4], v[4];
-    bool ok[4];
-};
-template <typename T>
-struct PseudoBuf {
-    Slice8<T> v[4];
-    bool ok[4];
-    int i[4];
+    Slice8<T> k[2], v[2];
+    bool ok[2];
 };
 
+// Loads rows it * 32 + wave * 8 + u * 4 + rg (u = 0, 1) of a staged list.
 template <typename T>
 __device__ __forceinline__ void load_rows(RowBuf<T>& bf, const int32_t* s_row, int cnt, int it, int wave, int rg,
                                           const T* Kx, const T* Vx) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = it * 64 + wave * 16 + u * 4 + rg;
+    for (int u = 0; u < 2; ++u) {
+        const int i = it * 32 + wave * 8 + u * 4 + rg;
         bf.ok[u] = i < cnt;
         const int r = s_row[bf.ok[u] ? i : 0];
         bf.k[u].load(Kx + (size_t)r * kHeadDim);
@@ -403,32 +363,114 @@ __device__ __forceinline__ void load_rows(RowBuf<T>& bf, const int32_t* s_row, i
 }
 
 template <typename T, int G>
-__device__ __forceinline__ void exact_step(SoftState<G>& st, const float (&qs)[G][8], const RowBuf<T>& bf) {
-    float lg[4][G];
-    logits4<T, G>(qs, bf.k, bf.ok, lg);
-    absorb4<T, G>(st, lg, bf.v);
+__device__ __forceinline__ void exact_step(SoftState<G>& st, const QSlice<T> (&qs)[G], float qscale,
+                                           const RowBuf<T>& bf) {
+    float lg[2][G];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float d = row16_sum(dot8(qs[g], bf.k[u])) * qscale;
+            lg[u][g] = bf.ok[u] ? d : -INFINITY;
+        }
+    absorb2<T, G>(st, lg, bf.v);
 }
+
+template <typename T>
+struct PseudoBuf {
+    Slice8<T> v[2];
+    bool ok[2];
+    int i[2];
+};
 
 template <typename T>
 __device__ __forceinline__ void load_pseudo(PseudoBuf<T>& bf, const int32_t* s_pid, int cnt, int it, int wave, int rg,
                                             const T* vbar) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = it * 64 + wave * 16 + u * 4 + rg;
+    for (int u = 0; u < 2; ++u) {
+        const int i = it * 32 + wave * 8 + u * 4 + rg;
         bf.ok[u] = i < cnt;
         bf.i[u] = bf.ok[u] ? i : 0;
         bf.v[u].load(vbar + (size_t)s_pid[bf.i[u]] * kHeadDim);
     }
 }
 
+// Adds 2 approximated items: precomputed weights w (relative to the chunk
+// reference) times the row group's factor f.
 template <typename T, int G>
-__device__ __forceinline__ void pseudo_step(SoftState<G>& st, const float (*s_plg)[G], const PseudoBuf<T>& bf) {
-    float lg[4][G];
+__device__ __forceinline__ void pseudo_step(SoftState<G>& st, const float (*s_w)[G], const float (&f)[G],
+                                            const PseudoBuf<T>& bf) {
+    float x0[8], x1[8];
+    bf.v[0].unpack(x0);
+    bf.v[1].unpack(x1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int g = 0; g < G; ++g) {
+        const float p0 = bf.ok[0] ? s_w[bf.i[0]][g] * f[g] : 0.f;
+        const float p1 = bf.ok[1] ? s_w[bf.i[1]][g] * f[g] : 0.f;
+        st.l[g] += p0 + p1;
 #pragma unroll
-        for (int g = 0; g < G; ++g) lg[u][g] = bf.ok[u] ? s_plg[bf.i[u]][g] : -INFINITY;
-    absorb4<T, G>(st, lg, bf.v);
+        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(p1, x1[e], fmaf(p0, x0[e], st.acc[g][e]));
+    }
+}
+
+// Stages exact positions [c0, c0 + cnt) of the unit (through token ids when
+// rows are gathered from K/V).
+__device__ __forceinline__ void stage_exact(int32_t* s_row, const int32_t* rws, const int32_t* tids, int c0,
+                                            int cnt) {
+    for (int i = threadIdx.x; i < cnt; i += 256) {
+        const int pos = rws[c0 + i];
+        s_row[i] = tids ? tids[pos] : pos;
+    }
+}
+
+// Stages approximated items [c0, c0 + cnt) (cnt <= 512): cluster id, and per
+// head the weight n * 2^(lambda - M) with lambda = s * log2(e) (base-2 logit)
+// and M the chunk's largest log2(n) + lambda, left in s_pm[g].  Ends with a
+// barrier.
+template <int G>
+__device__ __forceinline__ void stage_pseudo(int32_t* s_pid, float (*s_plg)[G], float* s_pm, float (*s_wmax)[G],
+                                             const int32_t* lst, const float* su, const int32_t* szu, int c0,
+                                             int cnt) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float lg[2][G];
+    float mx[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = tid + 256 * k;
+        if (i < cnt) {
+            const int c = lst[c0 + i];
+            s_pid[i] = c;
+            const float ln2n = __builtin_amdgcn_logf((float)szu[c]);  // log2(n)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                lg[k][g] = fmaf(su[(size_t)c * G + g], kLog2e, ln2n);
+                mx[g] = fmaxf(mx[g], lg[k][g]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float m = mx[g];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
+        if (lane == 0) s_wmax[wave][g] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        mx[g] = fmaxf(fmaxf(s_wmax[0][g], s_wmax[1][g]), fmaxf(s_wmax[2][g], s_wmax[3][g]));
+    if (tid < G) s_pm[tid] = mx[tid];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = tid + 256 * k;
+        if (i < cnt) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) s_plg[i][g] = __builtin_amdgcn_exp2f(lg[k][g] - mx[g]);
+        }
+    }
+    __syncthreads();
 }
 
 template <typename T, int G>
@@ -436,6 +478,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     __shared__ int32_t s_row[kAttCap];
     __shared__ int32_t s_pid[kAttCap];
     __shared__ float s_plg[kAttCap][G];
+    __shared__ float s_pm[G];
+    __shared__ float s_wmax[4][G];
     __shared__ float s_red[4][G][kHeadDim + 2];
 
     const int split = blockIdx.x, unit = blockIdx.y;
@@ -444,18 +488,27 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int wave = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, li = lane & 15;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
-
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
-    float qs[G][8];
     const float qscale = kInvSqrtD * kLog2e;
+
+    const int E = a.row_counts[unit * 4];
+    const int e0 = (int)((int64_t)E * split / S), e1 = (int)((int64_t)E * (split + 1) / S);
+    const int32_t* rws = a.rows + (size_t)unit * a.row_stride;
+    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
+
+    const PseudoList& pa = a.pa;
+    const int Pa = pa.list ? pa.counts[unit * 4 + 1] : 0;
+    const int pa0 = (int)((int64_t)Pa * split / S), pa1 = (int)((int64_t)Pa * (split + 1) / S);
+    const int32_t* lsta = pa.list ? pa.list + (size_t)unit * pa.stride : nullptr;
+    const float* sua = pa.s + (size_t)unit * pa.rows * G;
+    const int32_t* szua = pa.sizes + (size_t)unit * pa.rows;
+
+    // stage the first chunk of both lists together, load the queries meanwhile
+    stage_exact(s_row, rws, tids, e0, min(kAttCap, e1 - e0));
+    if (lsta) stage_pseudo<G>(s_pid, s_plg, s_pm, s_wmax, lsta, sua, szua, pa0, min(kAttCap, pa1 - pa0));
+    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
+    QSlice<T> qs[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        Slice8<T> s;
-        s.load(qb + (size_t)g * kHeadDim);
-        s.unpack(qs[g]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qs[g][e] *= qscale;
-    }
+    for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
     SoftState<G> st;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -467,31 +520,25 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const size_t ubase = (size_t)unit * a.Nmax * kHeadDim + li * 8;
     const T* Kx = reinterpret_cast<const T*>(a.Kx) + ubase;
     const T* Vx = reinterpret_cast<const T*>(a.Vx) + ubase;
+    __syncthreads();
 
     // ---- exact rows of selected clusters -------------------------------
-    {
-        const int E = a.row_counts[unit * 4];
-        const int e0 = (int)((int64_t)E * split / S), e1 = (int)((int64_t)E * (split + 1) / S);
-        const int32_t* rws = a.rows + (size_t)unit * a.row_stride;
-        const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
-        for (int c0 = e0; c0 < e1; c0 += kAttCap) {
-            const int cnt = min(kAttCap, e1 - c0);
+    for (int c0 = e0; c0 < e1; c0 += kAttCap) {
+        const int cnt = min(kAttCap, e1 - c0);
+        if (c0 != e0) {
             __syncthreads();
-            for (int i = tid; i < cnt; i += 256) {
-                const int pos = rws[c0 + i];
-                s_row[i] = tids ? tids[pos] : pos;
-            }
+            stage_exact(s_row, rws, tids, c0, cnt);
             __syncthreads();
-            const int steps = (cnt + 63) / 64;
-            RowBuf<T> A, B;
-            if (steps > 0) load_rows<T>(A, s_row, cnt, 0, wave, rg, Kx, Vx);
-            for (int it = 0; it < steps; it += 2) {
-                if (it + 1 < steps) load_rows<T>(B, s_row, cnt, it + 1, wave, rg, Kx, Vx);
-                exact_step<T, G>(st, qs, A);
-                if (it + 1 < steps) {
-                    if (it + 2 < steps) load_rows<T>(A, s_row, cnt, it + 2, wave, rg, Kx, Vx);
-                    exact_step<T, G>(st, qs, B);
-                }
+        }
+        const int steps = (cnt + 31) / 32;
+        RowBuf<T> A, B;
+        if (steps > 0) load_rows<T>(A, s_row, cnt, 0, wave, rg, Kx, Vx);
+        for (int it = 0; it < steps; it += 2) {
+            if (it + 1 < steps) load_rows<T>(B, s_row, cnt, it + 1, wave, rg, Kx, Vx);
+            exact_step<T, G>(st, qs, qscale, A);
+            if (it + 1 < steps) {
+                if (it + 2 < steps) load_rows<T>(A, s_row, cnt, it + 2, wave, rg, Kx, Vx);
+                exact_step<T, G>(st, qs, qscale, B);
             }
         }
     }
@@ -501,20 +548,17 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         const int t0 = (int)((int64_t)Tn * split / S), t1 = (int)((int64_t)Tn * (split + 1) / S);
         const T* Kt = reinterpret_cast<const T*>(a.K) + ubase;
         const T* Vt = reinterpret_cast<const T*>(a.V) + ubase;
-        for (int base = t0 + wave * 16; base < t1; base += 64) {
-            Slice8<T> kb[4], vb[4];
-            bool ok[4];
+        for (int base = t0 + wave * 8; base < t1; base += 32) {
+            RowBuf<T> bf;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 2; ++u) {
                 const int i = base + u * 4 + rg;
-                ok[u] = i < t1;
-                const int r = a.n_clustered + (ok[u] ? i : t0);
-                kb[u].load(Kt + (size_t)r * kHeadDim);
-                vb[u].load(Vt + (size_t)r * kHeadDim);
+                bf.ok[u] = i < t1;
+                const int r = a.n_clustered + (bf.ok[u] ? i : t0);
+                bf.k[u].load(Kt + (size_t)r * kHeadDim);
+                bf.v[u].load(Vt + (size_t)r * kHeadDim);
             }
-            float lg[4][G];
-            logits4<T, G>(qs, kb, ok, lg);
-            absorb4<T, G>(st, lg, vb);
+            exact_step<T, G>(st, qs, qscale, bf);
         }
     }
     // ---- approximated clusters: logit s + ln n, value Vbar ----------------
@@ -530,24 +574,34 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         const T* vbar = reinterpret_cast<const T*>(pl.vbar) + (size_t)unit * pl.rows * kHeadDim + li * 8;
         for (int c0 = p0; c0 < p1; c0 += kAttCap) {
             const int cnt = min(kAttCap, p1 - c0);
-            __syncthreads();
-            for (int i = tid; i < cnt; i += 256) {
-                const int c = lst[c0 + i];
-                s_pid[i] = c;
-                const float ln2n = __builtin_amdgcn_logf((float)szu[c]);  // log2(n)
-#pragma unroll
-                for (int g = 0; g < G; ++g) s_plg[i][g] = fmaf(su[(size_t)c * G + g], kLog2e, ln2n);
+            if (which == 1 || c0 != p0) {  // the first chunk of the first list is staged already
+                __syncthreads();
+                stage_pseudo<G>(s_pid, s_plg, s_pm, s_wmax, lst, su, szu, c0, cnt);
             }
-            __syncthreads();
-            const int steps = (cnt + 63) / 64;
+            // move this row group's state to reference max(m, M) once; the
+            // staged weights are relative to M
+            float f[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float M = s_pm[g];
+                if (M > st.m[g]) {
+                    const float sc = __builtin_amdgcn_exp2f(st.m[g] - M);
+                    st.l[g] *= sc;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
+                    st.m[g] = M;
+                }
+                f[g] = __builtin_amdgcn_exp2f(M - st.m[g]);
+            }
+            const int steps = (cnt + 31) / 32;
             PseudoBuf<T> A, B;
             if (steps > 0) load_pseudo<T>(A, s_pid, cnt, 0, wave, rg, vbar);
             for (int it = 0; it < steps; it += 2) {
                 if (it + 1 < steps) load_pseudo<T>(B, s_pid, cnt, it + 1, wave, rg, vbar);
-                pseudo_step<T, G>(st, s_plg, A);
+                pseudo_step<T, G>(st, s_plg, f, A);
                 if (it + 1 < steps) {
                     if (it + 2 < steps) load_pseudo<T>(A, s_pid, cnt, it + 2, wave, rg, vbar);
-                    pseudo_step<T, G>(st, s_plg, B);
+                    pseudo_step<T, G>(st, s_plg, f, B);
                 }
             }
         }
@@ -646,7 +700,7 @@ hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStre
 }
 
 hipError_t launch_select(const SelectArgs& a, int units, hipStream_t st) {
-    hipLaunchKernelGGL(select_kernel, dim3(units), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(select_kernel, dim3(units), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

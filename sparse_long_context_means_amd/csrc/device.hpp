@@ -107,16 +107,21 @@ __device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
 }
 constexpr uint64_t kSm64Gamma = 0x9E3779B97F4A7C15ull;
 
-// Inclusive sum over the 64 lanes of a wave (Hillis-Steele with shuffles).
+// Inclusive sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2,
+// 4 and 8 lanes inside each row of 16, then the last lane of row 0 (and 2) is
+// broadcast into rows 1 and 3, and the last lane of row 1 into rows 2 and 3.
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
     return v;
 }
+
+// Value of lane `src` (uniform) in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 // Exclusive prefix sums of four ints over a 256-thread workgroup, in thread
 // order; `totals` receives the four sums.  Uses 4 * 4 ints of LDS.
@@ -147,6 +152,47 @@ __device__ __forceinline__ int4 block256_exclusive_sum4(int4 v, int4& totals, in
     }
     __syncthreads();  // lds16 may be reused right after
     return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
+}
+
+// The query slice of one head: bf16 pairs for the packed dot product, or fp32.
+template <typename T>
+struct QSlice;
+template <>
+struct QSlice<bf16_t> {
+    uint4 raw;
+    __device__ __forceinline__ void load(const bf16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+};
+template <>
+struct QSlice<float> {
+    float v[8];
+    __device__ __forceinline__ void load(const float* p) {
+        Slice8<float> s;
+        s.load(p);
+        s.unpack(v);
+    }
+};
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Partial dot product of a lane's 8 elements (fp32 accumulation).
+__device__ __forceinline__ float dot8(const QSlice<bf16_t>& q, const Slice8<bf16_t>& k) {
+    float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.raw.x),
+                                              __builtin_bit_cast(bf16x2_t, k.raw.x), 0.f, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.raw.y), __builtin_bit_cast(bf16x2_t, k.raw.y),
+                                        d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.raw.z), __builtin_bit_cast(bf16x2_t, k.raw.z),
+                                        d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.raw.w), __builtin_bit_cast(bf16x2_t, k.raw.w),
+                                        d, false);
+    return d;
+}
+__device__ __forceinline__ float dot8(const QSlice<float>& q, const Slice8<float>& k) {
+    float x[8];
+    k.unpack(x);
+    float d = q.v[0] * x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) d = fmaf(q.v[e], x[e], d);
+    return d;
 }
 
 }  // namespace mpa

@@ -124,4 +124,7 @@ hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipSt
 hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int S, int Hkv,
                         float* out, hipStream_t st);
 
+// ---- measurement (probe.hip) ----------------------------------------------
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+
 }  // namespace mpa

@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.mpattn_decode_stage_count.argtypes = [P]
     lib.mpattn_decode_stage_name.restype = ctypes.c_char_p
     lib.mpattn_decode_stage_name.argtypes = [P, i32]
+    lib.mpattn_read_probe.restype = ctypes.c_int
+    lib.mpattn_read_probe.argtypes = [_VP, sz, _VP, _VP]
     return lib
 
 
@@ -306,6 +308,12 @@ def decode(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_token
                               _stream(q.device), ctypes.byref(dbg) if dbg is not None else None, first, last)
     _raise(st, "mpattn_decode")
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Enqueues one streaming read of `buf` (see mpattn_read_probe)."""
+    _raise(lib.mpattn_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(buf.device)), "mpattn_read_probe")
 
 
 def workspace_bytes(p: Params, state: ClusterState) -> int:
