@@ -16,6 +16,7 @@ constexpr int kD = 128;
 constexpr size_t kAlign = 256;
 constexpr int kMaxFinePerBlockHier = 2048;
 constexpr int kMaxCoarsePerBlock = 64;
+constexpr int kMaxDecodeClusters = 32768;  // selection bitmask held in LDS
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -58,30 +59,35 @@ int splits_of(const mpattn_params* p) {
 
 // Decode workspace regions.
 struct DecodeWs {
-    float* s;        // [U][Cmax][G]
-    float* r;        // [U][Cmax]
-    int32_t* rows;   // [U][Nmax]
-    int32_t* plist;  // [U][Cmax]
-    int32_t* counts; // [U][4]
-    float* part_ml;  // [U][G][S][2]
-    float* part_acc; // [U][G][S][d]
-    // hierarchy
-    float* cs;        // [U][Dmax][G]
-    float* cr;        // [U][Dmax]
-    int32_t* crows;   // [U][Cmax]
-    int32_t* cplist;  // [U][Dmax]
-    int32_t* ccounts; // [U][4]
-    float* fr;        // [U][Cmax]
-    int32_t* fids;    // [U][Cmax]
+    float* s;             // [U][Cmax][G] scores by cluster id
+    int2* rs;             // [U][Cmax] (key, size) by item
+    uint32_t* selmask;    // [U][Cw] selected clusters
+    int32_t* sel_ids;     // [U][Cmax]
+    int32_t* sel_off;     // [U][Cmax]
+    int32_t* sel_pre;     // [U][Cmax + 1]
+    int32_t* counts;      // [U][4]
+    float* part_ml;       // [U][G][S][2]
+    float* part_acc;      // [U][G][S][d]
+    // hierarchy: coarse level and the fine items inside the candidates
+    float* cs;            // [U][Dmax][G]
+    int2* crs;            // [U][Dmax]
+    uint32_t* cmask;      // [U][Dw]
+    int32_t* csel_ids;    // [U][Dmax]
+    int32_t* csel_off;    // [U][Dmax]
+    int32_t* csel_pre;    // [U][Dmax + 1]
+    int32_t* ccounts;     // [U][4]
+    int32_t* fids;        // [U][Cmax]
+    int32_t Cw, Dw;       // mask words
     size_t bytes;
 };
 
 DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char* base) {
     const size_t U = (size_t)p->batch * p->n_kv_heads;
     const size_t G = (size_t)(p->n_q_heads / p->n_kv_heads);
-    const size_t N = (size_t)p->capacity_tokens;
     const size_t S = (size_t)splits_of(p);
     DecodeWs w{};
+    w.Cw = (Cmax + 31) / 32;
+    w.Dw = (Dmax + 31) / 32;
     size_t off = 0;
     auto take = [&](size_t bytes) -> char* {
         char* ptr = base ? base + off : nullptr;
@@ -89,19 +95,22 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
         return ptr;
     };
     w.s = (float*)take(U * Cmax * G * 4);
-    w.r = (float*)take(U * Cmax * 4);
-    w.rows = (int32_t*)take(U * N * 4);
-    w.plist = (int32_t*)take(U * Cmax * 4);
+    w.rs = (int2*)take(U * Cmax * 8);
+    w.selmask = (uint32_t*)take(U * w.Cw * 4);
+    w.sel_ids = (int32_t*)take(U * Cmax * 4);
+    w.sel_off = (int32_t*)take(U * Cmax * 4);
+    w.sel_pre = (int32_t*)take(U * (Cmax + 1) * 4);
     w.counts = (int32_t*)take(U * 4 * 4);
     w.part_ml = (float*)take(U * G * S * 2 * 4);
     w.part_acc = (float*)take(U * G * S * kD * 4);
     if (is_hier(p)) {
         w.cs = (float*)take(U * Dmax * G * 4);
-        w.cr = (float*)take(U * Dmax * 4);
-        w.crows = (int32_t*)take(U * Cmax * 4);
-        w.cplist = (int32_t*)take(U * Dmax * 4);
+        w.crs = (int2*)take(U * Dmax * 8);
+        w.cmask = (uint32_t*)take(U * w.Dw * 4);
+        w.csel_ids = (int32_t*)take(U * Dmax * 4);
+        w.csel_off = (int32_t*)take(U * Dmax * 4);
+        w.csel_pre = (int32_t*)take(U * (Dmax + 1) * 4);
         w.ccounts = (int32_t*)take(U * 4 * 4);
-        w.fr = (float*)take(U * Cmax * 4);
         w.fids = (int32_t*)take(U * Cmax * 4);
     }
     w.bytes = off;
@@ -290,6 +299,8 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     if (mode != MPATTN_MODE_MULTIPOLE && mode != MPATTN_MODE_OMIT) return MPATTN_ERR_INVALID_ARG;
     const bool hier = is_hier(p);
     if (hier && mode != MPATTN_MODE_MULTIPOLE) return MPATTN_ERR_UNSUPPORTED;
+    if (st->capacity_clusters > kMaxDecodeClusters || st->capacity_coarse > kMaxDecodeClusters)
+        return MPATTN_ERR_UNSUPPORTED;
     if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
     const int32_t n_stages = hier ? 6 : 4;
     if (first_stage < 0 || last_stage >= n_stages || first_stage > last_stage) return MPATTN_ERR_INVALID_ARG;
@@ -311,31 +322,32 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         const char* name = hier ? kHierStages[stage] : kFlatStages[stage];
         const bool attend = name[0] == 'a', merge = name[0] == 'm';
         if (!hier && stage == 0) {
-            ScoreArgs a{q, st->key_centroids, Cmax, C, nullptr, nullptr, nullptr, 0, w.s, w.r, Cmax, nullptr,
-                        p->n_q_heads, p->n_kv_heads};
+            ScoreArgs a{q, st->key_centroids, Cmax, C, nullptr, nullptr, nullptr, nullptr, 0, nullptr, st->sizes,
+                        w.s, w.rs, Cmax, nullptr, p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (!hier && stage == 1) {
-            SelectArgs se{w.r, Cmax, nullptr, st->sizes, Cmax, st->offsets, C, nullptr, token_budget, want_pseudo,
-                          w.rows, N, w.plist, Cmax, w.counts, debug ? debug->selected : nullptr, C};
+            SelectArgs se{w.rs, Cmax, nullptr, st->offsets, Cmax + 1, C, nullptr, token_budget, C, w.selmask, w.Cw,
+                          w.sel_ids, w.sel_off, w.sel_pre, Cmax, w.counts, debug ? debug->selected : nullptr, C};
             MPA_TRY(launch_select(se, U, s));
         } else if (hier && stage == 0) {
-            ScoreArgs a{q, st->coarse_key_centroids, Dmax, st->n_coarse, nullptr, nullptr, nullptr, 0, w.cs, w.cr,
-                        Dmax, nullptr, p->n_q_heads, p->n_kv_heads};
+            ScoreArgs a{q, st->coarse_key_centroids, Dmax, st->n_coarse, nullptr, nullptr, nullptr, nullptr, 0,
+                        nullptr, st->coarse_sizes, w.cs, w.crs, Dmax, nullptr, p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (hier && stage == 1) {
-            SelectArgs se{w.cr, Dmax, nullptr, st->coarse_sizes, Dmax, st->coarse_offsets, st->n_coarse, nullptr,
-                          p->coarse_candidate_tokens, want_pseudo, w.crows, Cmax, w.cplist, Dmax, w.ccounts,
-                          debug ? debug->candidates : nullptr, st->n_coarse};
+            SelectArgs se{w.crs, Dmax, nullptr, st->coarse_offsets, Dmax + 1, st->n_coarse, nullptr,
+                          p->coarse_candidate_tokens, st->n_coarse, w.cmask, w.Dw, w.csel_ids, w.csel_off, w.csel_pre,
+                          Dmax, w.ccounts, debug ? debug->candidates : nullptr, st->n_coarse};
             MPA_TRY(launch_select(se, U, s));
         } else if (hier && stage == 2) {
-            ScoreArgs a{q, st->key_centroids, Cmax, bound, w.ccounts, w.crows, st->coarse_members, Cmax, w.s, w.fr,
-                        Cmax, w.fids, p->n_q_heads, p->n_kv_heads};
+            ScoreArgs a{q, st->key_centroids, Cmax, bound, w.ccounts, w.csel_pre, w.csel_off, w.ccounts, Dmax,
+                        st->coarse_members, st->sizes, w.s, w.rs, Cmax, w.fids, p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (hier && stage == 3) {
             if (debug && debug->selected)
                 MPA_TRY(hipMemsetAsync(debug->selected, 0, (size_t)U * C * sizeof(int32_t), s));
-            SelectArgs se{w.fr, Cmax, w.fids, st->sizes, Cmax, st->offsets, bound, w.ccounts, token_budget,
-                          want_pseudo, w.rows, N, w.plist, Cmax, w.counts, debug ? debug->selected : nullptr, C};
+            SelectArgs se{w.rs, Cmax, w.fids, st->offsets, Cmax + 1, bound, w.ccounts, token_budget, C, w.selmask,
+                          w.Cw, w.sel_ids, w.sel_off, w.sel_pre, Cmax, w.counts,
+                          debug ? debug->selected : nullptr, C};
             MPA_TRY(launch_select(se, U, s));
         } else if (attend) {
             AttendArgs a{};
@@ -345,16 +357,23 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
             a.token_ids = sorted ? nullptr : st->token_ids;
             a.K = k;
             a.V = v;
-            a.rows = w.rows;
-            a.row_stride = N;
-            a.row_counts = w.counts;
+            a.sel_off = w.sel_off;
+            a.sel_rowpre = w.sel_pre;
+            a.sel_stride = Cmax;
+            a.counts = w.counts;
             a.Nmax = N;
             a.n_clustered = st->n_clustered;
             a.n_total = n_tokens_total;
-            a.pa = PseudoList{want_pseudo ? w.plist : nullptr, Cmax, w.counts, w.s, st->sizes, st->value_centroids,
-                              Cmax};
-            a.pb = PseudoList{(want_pseudo && hier) ? w.cplist : nullptr, Dmax, w.ccounts, w.cs, st->coarse_sizes,
-                              st->coarse_value_centroids, Dmax};
+            if (hier) {
+                a.pa = PseudoSrc{w.fids, Cmax, bound, w.ccounts, w.selmask, w.Cw, w.s, st->sizes, st->value_centroids,
+                                 Cmax};
+                a.pb = PseudoSrc{nullptr, 0, st->n_coarse, nullptr, w.cmask, w.Dw, w.cs, st->coarse_sizes,
+                                 st->coarse_value_centroids, Dmax};
+                a.n_pseudo = want_pseudo ? 2 : 0;
+            } else {
+                a.pa = PseudoSrc{nullptr, 0, C, nullptr, w.selmask, w.Cw, w.s, st->sizes, st->value_centroids, Cmax};
+                a.n_pseudo = want_pseudo ? 1 : 0;
+            }
             a.Hq = p->n_q_heads;
             a.Hkv = p->n_kv_heads;
             a.S = S;

@@ -55,70 +55,85 @@ hipError_t launch_coarse_build(int dtype, UnitGeom g, CoarseRange cr, uint64_t s
 
 // ---- decode (decode.hip) --------------------------------------------------
 struct ScoreArgs {
-    const void* q;          // [B][Hq][d]
-    const void* cent;       // [U][cent_rows][d] key centroids
+    const void* q;               // [B][Hq][d]
+    const void* cent;            // [U][cent_rows][d] key centroids
     int32_t cent_rows;
-    int32_t n_items;        // items per unit (host bound)
+    int32_t n_items;             // items per unit (host bound)
     const int32_t* n_items_dev;  // optional per-unit count: n_items_dev[unit * 4]
-    const int32_t* pos_list;     // optional [U][list_stride]: item -> position in members
-    const int32_t* members;      // [U][cent_rows] position -> cluster id (with pos_list)
+    // optional item source: the member rows of a selection (list_pre/list_off
+    // of a previous select, count list_counts[unit * 4 + 1]), mapped through
+    // members[] to cluster ids
+    const int32_t* list_pre;     // [U][list_stride + 1]
+    const int32_t* list_off;     // [U][list_stride]
+    const int32_t* list_counts;  // [U][4]
     int32_t list_stride;
-    float* s_out;           // [U][cent_rows][G] scores by cluster id
-    float* r_out;           // [U][r_stride] group-mean score by item
-    int32_t r_stride;
-    int32_t* ids_out;       // optional [U][r_stride]: cluster id of each item
+    const int32_t* members;      // [U][cent_rows] position -> cluster id
+    const int32_t* sizes;        // [U][cent_rows] cluster sizes
+    float* s_out;                // [U][cent_rows][G] scores by cluster id
+    int2* rs_out;                // [U][rs_stride] (group-mean key bits, size) by item
+    int32_t rs_stride;
+    int32_t* ids_out;            // optional [U][rs_stride]: cluster id of each item
     int32_t Hq, Hkv;
 };
+hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st);
 
 struct SelectArgs {
-    const float* key;        // [U][key_stride] ranking key per item
-    int32_t key_stride;
-    const int32_t* ids;      // optional [U][key_stride]: cluster id per item (else id = item)
-    const int32_t* sizes;    // [U][size_stride] by cluster id
-    int32_t size_stride;
-    const int32_t* offsets;  // [U][size_stride + 1] by cluster id
-    int32_t n_items;         // host count (used when n_items_dev is null)
+    const int2* rs;              // [U][rs_stride] (key bits, size) per item
+    int32_t rs_stride;
+    const int32_t* ids;          // optional [U][rs_stride]: cluster id per item (else id = item)
+    const int32_t* offsets;      // [U][off_stride] member start by cluster id (CSR)
+    int32_t off_stride;
+    int32_t n_items;             // host count (bound when n_items_dev is set)
     const int32_t* n_items_dev;  // optional per-unit count at n_items_dev[unit * 4]
     int32_t budget;
-    int32_t want_pseudo;
-    int32_t* rows;           // [U][row_stride] member positions of selected items
-    int32_t row_stride;
-    int32_t* plist;          // [U][plist_stride] unselected non-empty cluster ids
-    int32_t plist_stride;
-    int32_t* counts;         // [U][4]: rows, pseudo items, selected items, 0
-    int32_t* dbg_selected;   // optional [U][dbg_stride] by cluster id
+    int32_t mask_bits;           // cluster ids < mask_bits
+    uint32_t* selmask;           // [U][mask_stride] 1 bit per cluster id: selected
+    int32_t mask_stride;
+    int32_t* sel_ids;            // [U][sel_stride] selected cluster ids, item order
+    int32_t* sel_off;            // [U][sel_stride] their first member position
+    int32_t* sel_rowpre;         // [U][sel_stride + 1] exclusive prefix of member rows
+    int32_t sel_stride;
+    int32_t* counts;             // [U][4]: member rows, selected items, 0, 0
+    int32_t* dbg_selected;       // optional [U][dbg_stride] by cluster id
     int32_t dbg_stride;
 };
-hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st);
-// Budget cut of every unit (one wave each).  Rows of a selected item are its
-// member positions offsets[id] .. offsets[id + 1]; its budget weight is sizes[id].
+// Budget cut of every unit (one workgroup each).  Rows of a selected item are
+// its member positions offsets[id] .. offsets[id + 1]; its budget weight is
+// its size.
 hipError_t launch_select(const SelectArgs& a, int units, hipStream_t st);
 
-struct PseudoList {
-    const int32_t* list;     // [U][stride] cluster ids
-    int32_t stride;
-    const int32_t* counts;   // count at counts[unit * 4 + 1]
-    const float* s;          // [U][rows][G]
-    const int32_t* sizes;    // [U][rows]
-    const void* vbar;        // [U][rows][d]
+// Approximated clusters: the non-empty, unselected clusters among a set of
+// items (ids [0, n) or an id list).
+struct PseudoSrc {
+    const int32_t* ids;          // optional [U][ids_stride]
+    int32_t ids_stride;
+    int32_t n_host;              // item count (bound when n_dev is set)
+    const int32_t* n_dev;        // optional count at n_dev[unit * 4]
+    const uint32_t* selmask;     // [U][mask_stride] selected bits by id
+    int32_t mask_stride;
+    const float* s;              // [U][rows][G] scores
+    const int32_t* sizes;        // [U][rows]
+    const void* vbar;            // [U][rows][d]
     int32_t rows;
 };
 struct AttendArgs {
     const void* q;
-    const void* Kx;          // exact-row source: sorted copy or K
+    const void* Kx;              // exact-row source: sorted copy or K
     const void* Vx;
-    const int32_t* token_ids;  // non-null: exact positions go through token ids
-    const void* K;           // tail rows
+    const int32_t* token_ids;    // non-null: member positions go through token ids
+    const void* K;               // tail rows
     const void* V;
-    const int32_t* rows;     // [U][row_stride] exact positions
-    int32_t row_stride;
-    const int32_t* row_counts;  // count at row_counts[unit * 4]
+    const int32_t* sel_off;      // [U][sel_stride]
+    const int32_t* sel_rowpre;   // [U][sel_stride + 1]
+    int32_t sel_stride;
+    const int32_t* counts;       // [U][4] of the (fine) select
     int32_t Nmax;
     int32_t n_clustered, n_total;
-    PseudoList pa, pb;       // approximate items (pb.list may be null)
+    int32_t n_pseudo;            // sources used (0, 1 or 2)
+    PseudoSrc pa, pb;
     int32_t Hq, Hkv, S;
-    float* part_ml;          // [U][G][S][2]
-    float* part_acc;         // [U][G][S][d]
+    float* part_ml;              // [U][G][S][2]
+    float* part_acc;             // [U][G][S][d]
 };
 hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipStream_t st);
 hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int S, int Hkv,
