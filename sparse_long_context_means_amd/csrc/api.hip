@@ -60,17 +60,18 @@ int splits_of(const mpattn_params* p) {
 // Decode workspace regions.
 struct DecodeWs {
     float* s;             // [U][Cmax][G] scores by cluster id
-    int2* rs;             // [U][Cmax] (key, size) by item
+    int4* rs;             // [U][Cmax] cut records by item
     uint32_t* selmask;    // [U][Cw] selected clusters
     int32_t* sel_ids;     // [U][Cmax]
     int32_t* sel_off;     // [U][Cmax]
     int32_t* sel_pre;     // [U][Cmax + 1]
     int32_t* counts;      // [U][4]
-    float* part_ml;       // [U][G][S][2]
-    float* part_acc;      // [U][G][S][d]
+    float* part_ml;       // [U][G][P][2]: attend splits, then score chunks
+    float* part_acc;      // [U][G][P][d]
+    int32_t P;            // partial slots available
     // hierarchy: coarse level and the fine items inside the candidates
     float* cs;            // [U][Dmax][G]
-    int2* crs;            // [U][Dmax]
+    int4* crs;            // [U][Dmax]
     uint32_t* cmask;      // [U][Dw]
     int32_t* csel_ids;    // [U][Dmax]
     int32_t* csel_off;    // [U][Dmax]
@@ -95,17 +96,18 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
         return ptr;
     };
     w.s = (float*)take(U * Cmax * G * 4);
-    w.rs = (int2*)take(U * Cmax * 8);
+    w.rs = (int4*)take(U * Cmax * 16);
     w.selmask = (uint32_t*)take(U * w.Cw * 4);
     w.sel_ids = (int32_t*)take(U * Cmax * 4);
     w.sel_off = (int32_t*)take(U * Cmax * 4);
     w.sel_pre = (int32_t*)take(U * (Cmax + 1) * 4);
     w.counts = (int32_t*)take(U * 4 * 4);
-    w.part_ml = (float*)take(U * G * S * 2 * 4);
-    w.part_acc = (float*)take(U * G * S * kD * 4);
+    w.P = (int32_t)S + score_chunks(Cmax) + (is_hier(p) ? score_chunks(Dmax) : 0);
+    w.part_ml = (float*)take(U * G * w.P * 2 * 4);
+    w.part_acc = (float*)take(U * G * w.P * kD * 4);
     if (is_hier(p)) {
         w.cs = (float*)take(U * Dmax * G * 4);
-        w.crs = (int2*)take(U * Dmax * 8);
+        w.crs = (int4*)take(U * Dmax * 16);
         w.cmask = (uint32_t*)take(U * w.Dw * 4);
         w.csel_ids = (int32_t*)take(U * Dmax * 4);
         w.csel_off = (int32_t*)take(U * Dmax * 4);
@@ -317,37 +319,41 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const bool sorted = st->sorted_keys != nullptr;
     const int32_t want_pseudo = mode == MPATTN_MODE_MULTIPOLE ? 1 : 0;
     const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
+    // partial slots: attend splits, then the score chunks (coarse, then fine)
+    const int32_t P = S + (want_pseudo ? (hier ? score_chunks(st->n_coarse) + score_chunks(bound) : score_chunks(C)) : 0);
+    if (P > w.P) return MPATTN_ERR_WORKSPACE;
 
     for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
         const char* name = hier ? kHierStages[stage] : kFlatStages[stage];
         const bool attend = name[0] == 'a', merge = name[0] == 'm';
         if (!hier && stage == 0) {
             ScoreArgs a{q, st->key_centroids, Cmax, C, nullptr, nullptr, nullptr, nullptr, 0, nullptr, st->sizes,
-                        w.s, w.rs, Cmax, nullptr, p->n_q_heads, p->n_kv_heads};
+                        st->offsets, Cmax + 1, w.s, w.rs, Cmax, nullptr, p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (!hier && stage == 1) {
-            SelectArgs se{w.rs, Cmax, nullptr, st->offsets, Cmax + 1, C, nullptr, token_budget, C, w.selmask, w.Cw,
-                          w.sel_ids, w.sel_off, w.sel_pre, Cmax, w.counts, debug ? debug->selected : nullptr, C};
+            SelectArgs se{w.rs, Cmax, nullptr, C, nullptr, token_budget, C, w.selmask, w.Cw, w.sel_ids, w.sel_off,
+                          w.sel_pre, Cmax, w.counts, debug ? debug->selected : nullptr, C};
             MPA_TRY(launch_select(se, U, s));
         } else if (hier && stage == 0) {
             ScoreArgs a{q, st->coarse_key_centroids, Dmax, st->n_coarse, nullptr, nullptr, nullptr, nullptr, 0,
-                        nullptr, st->coarse_sizes, w.cs, w.crs, Dmax, nullptr, p->n_q_heads, p->n_kv_heads};
+                        nullptr, st->coarse_sizes, st->coarse_offsets, Dmax + 1, w.cs, w.crs, Dmax, nullptr,
+                        p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (hier && stage == 1) {
-            SelectArgs se{w.crs, Dmax, nullptr, st->coarse_offsets, Dmax + 1, st->n_coarse, nullptr,
-                          p->coarse_candidate_tokens, st->n_coarse, w.cmask, w.Dw, w.csel_ids, w.csel_off, w.csel_pre,
-                          Dmax, w.ccounts, debug ? debug->candidates : nullptr, st->n_coarse};
+            SelectArgs se{w.crs, Dmax, nullptr, st->n_coarse, nullptr, p->coarse_candidate_tokens, st->n_coarse,
+                          w.cmask, w.Dw, w.csel_ids, w.csel_off, w.csel_pre, Dmax, w.ccounts,
+                          debug ? debug->candidates : nullptr, st->n_coarse};
             MPA_TRY(launch_select(se, U, s));
         } else if (hier && stage == 2) {
             ScoreArgs a{q, st->key_centroids, Cmax, bound, w.ccounts, w.csel_pre, w.csel_off, w.ccounts, Dmax,
-                        st->coarse_members, st->sizes, w.s, w.rs, Cmax, w.fids, p->n_q_heads, p->n_kv_heads};
+                        st->coarse_members, st->sizes, st->offsets, Cmax + 1, w.s, w.rs, Cmax, w.fids,
+                        p->n_q_heads, p->n_kv_heads};
             MPA_TRY(launch_score(p->dtype, G, a, U, s));
         } else if (hier && stage == 3) {
             if (debug && debug->selected)
                 MPA_TRY(hipMemsetAsync(debug->selected, 0, (size_t)U * C * sizeof(int32_t), s));
-            SelectArgs se{w.rs, Cmax, w.fids, st->offsets, Cmax + 1, bound, w.ccounts, token_budget, C, w.selmask,
-                          w.Cw, w.sel_ids, w.sel_off, w.sel_pre, Cmax, w.counts,
-                          debug ? debug->selected : nullptr, C};
+            SelectArgs se{w.rs, Cmax, w.fids, bound, w.ccounts, token_budget, C, w.selmask, w.Cw, w.sel_ids,
+                          w.sel_off, w.sel_pre, Cmax, w.counts, debug ? debug->selected : nullptr, C};
             MPA_TRY(launch_select(se, U, s));
         } else if (attend) {
             AttendArgs a{};
@@ -364,14 +370,21 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
             a.Nmax = N;
             a.n_clustered = st->n_clustered;
             a.n_total = n_tokens_total;
+            a.sa = SubSrc{w.sel_ids, Cmax, w.counts, w.s, st->sizes, st->value_centroids, Cmax};
             if (hier) {
-                a.pa = PseudoSrc{w.fids, Cmax, bound, w.ccounts, w.selmask, w.Cw, w.s, st->sizes, st->value_centroids,
-                                 Cmax};
-                a.pb = PseudoSrc{nullptr, 0, st->n_coarse, nullptr, w.cmask, w.Dw, w.cs, st->coarse_sizes,
-                                 st->coarse_value_centroids, Dmax};
+                a.sb = SubSrc{w.csel_ids, Dmax, w.ccounts, w.cs, st->coarse_sizes, st->coarse_value_centroids, Dmax};
+                a.n_sub = want_pseudo ? 2 : 0;
+                a.pseudo[0] = PseudoArgs{nullptr, 0, st->n_coarse, nullptr, w.cs, st->coarse_sizes,
+                                         st->coarse_value_centroids, Dmax, w.part_ml, w.part_acc, P, S,
+                                         score_chunks(st->n_coarse)};
+                a.pseudo[1] = PseudoArgs{w.fids, Cmax, bound, w.ccounts, w.s, st->sizes, st->value_centroids, Cmax,
+                                         w.part_ml, w.part_acc, P, S + score_chunks(st->n_coarse),
+                                         score_chunks(bound)};
                 a.n_pseudo = want_pseudo ? 2 : 0;
             } else {
-                a.pa = PseudoSrc{nullptr, 0, C, nullptr, w.selmask, w.Cw, w.s, st->sizes, st->value_centroids, Cmax};
+                a.n_sub = want_pseudo ? 1 : 0;
+                a.pseudo[0] = PseudoArgs{nullptr, 0, C, nullptr, w.s, st->sizes, st->value_centroids, Cmax,
+                                         w.part_ml, w.part_acc, P, S, score_chunks(C)};
                 a.n_pseudo = want_pseudo ? 1 : 0;
             }
             a.Hq = p->n_q_heads;
@@ -379,9 +392,10 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
             a.S = S;
             a.part_ml = w.part_ml;
             a.part_acc = w.part_acc;
+            a.part_stride = P;
             MPA_TRY(launch_attend(p->dtype, G, a, U, s));
         } else if (merge) {
-            MPA_TRY(launch_merge(w.part_ml, w.part_acc, U, G, S, p->n_kv_heads, out, s));
+            MPA_TRY(launch_merge(w.part_ml, w.part_acc, U, G, P, p->n_kv_heads, out, s));
         }
     }
     // optional inspection copies once the selection exists

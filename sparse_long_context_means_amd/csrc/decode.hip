@@ -8,17 +8,34 @@
 // n_c * exp(q . Kbar_c / sqrt(d)) on Vbar_c, in numerator and denominator.
 //
 // Launches:
-//   score  -- s[c][g] = q_g . Kbar_c / sqrt(d), the group-mean ranking key and
-//             the cluster size, packed per item for the cut;
-//   select -- one workgroup per unit takes the budget cut (longest prefix of
-//             the (key desc, id asc) order whose sizes fit the budget) with a
-//             radix select, and writes the selected clusters (id, first member
-//             position, prefix of member rows) and a bitmask of them;
-//   attend -- split-K online softmax over the exact rows of the selected
-//             clusters (gathered K/V), the unclustered tail and every
-//             non-empty unselected cluster (logit s + ln n, value Vbar), in
-//             base-2 exponent units, fp32 partials;
-//   merge  -- log-sum-exp merge of the splits.
+//   score   -- s[c][g] = q_g . Kbar_c / sqrt(d) for every item, and one
+//              16-byte record per item for the cut: group-mean ranking key,
+//              budget weight (size), first member position, member rows;
+//   select  -- one workgroup per unit takes the budget cut (longest prefix of
+//              the (key desc, id asc) order whose weights fit the budget) with
+//              a radix select, and writes the selected clusters (id, first
+//              member position, prefix of member rows) and a bitmask of them;
+//              the SAME launch carries the approximate term: further
+//              workgroups stream Vbar and add the term of EVERY non-empty
+//              cluster (logit s + ln n, value Vbar) into one partial softmax
+//              state per chunk of 256 clusters, so the cut's latency hides
+//              behind that stream;
+//   attend  -- split-K online softmax over the exact rows of the selected
+//              clusters (gathered K/V) and the unclustered tail, minus the
+//              approximate terms of the selected clusters;
+//   merge   -- log-sum-exp merge of the attend splits and the chunk partials.
+// All softmax states are kept in base-2 exponent units with fp32 sums.
+//
+// Adding every cluster's approximate term and removing the selected ones
+// afterwards makes the approximate term a dense, selection-independent
+// stream.  The cancellation is harmless: by convexity of exp, a cluster's
+// approximate term never exceeds the sum of its members' exact terms (up to
+// the storage rounding of the centroids), so the removed mass is at most the
+// exact mass that replaces it and the rounding error of the difference stays
+// within a few fp32 units of the final denominator.  The removed term is
+// recomputed from the same stored score and size, so it matches the added one
+// to the last rounding of exp2.
+//
 // Kernel boundaries carry the cross-workgroup dependencies: a device-scope
 // fence per workgroup (write back + invalidate of an XCD's L2) serialises and
 // costs far more than a launch on this chip.
@@ -52,11 +69,144 @@ __device__ __forceinline__ int upper_index(const int32_t* pre, int n, int x) {
     return lo;
 }
 
+// log2 of a positive count, as both the adding and the removing side take it.
+__device__ __forceinline__ float log2_count(int n) { return __builtin_amdgcn_logf((float)n); }
+
+// ---------------------------------------------------------------------------
+// Online softmax state of a 16-lane row group: per query head g the reference
+// exponent m, the sum l of 2^(logit - m) and the weighted value sum acc (the
+// lane's 8 dimensions).  The reference is only raised when a logit exceeds it
+// by more than 2^8 (every weight stays <= 256 in fp32), so rescaling is rare.
+// ---------------------------------------------------------------------------
+constexpr float kLazyMax = 8.0f;
+
+template <int G>
+struct SoftState {
+    float m[G], l[G], acc[G][8];
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            m[g] = -INFINITY;
+            l[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+        }
+    }
+};
+
+// Adds (NEG: removes) 2 rows with base-2 logits lg[u][g] (-inf: absent row).
+template <typename T, int G, bool NEG>
+__device__ __forceinline__ void absorb2(SoftState<G>& st, const float (&lg)[2][G], const Slice8<T> (&v)[2]) {
+    float x0[8], x1[8];
+    v[0].unpack(x0);
+    v[1].unpack(x1);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float mx = fmaxf(lg[0][g], lg[1][g]);
+        if (mx == -INFINITY) continue;
+        if (mx > st.m[g] + kLazyMax) {  // rare: raise the reference
+            const float sc = __builtin_amdgcn_exp2f(st.m[g] - mx);
+            st.l[g] *= sc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
+            st.m[g] = mx;
+        }
+        float p0 = __builtin_amdgcn_exp2f(lg[0][g] - st.m[g]);
+        float p1 = __builtin_amdgcn_exp2f(lg[1][g] - st.m[g]);
+        if (NEG) {
+            p0 = -p0;
+            p1 = -p1;
+        }
+        st.l[g] += p0 + p1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(p1, x1[e], fmaf(p0, x0[e], st.acc[g][e]));
+    }
+}
+
+// Merge another partial state (om, ol, oacc) into st.
+template <int G>
+__device__ __forceinline__ void merge_state(SoftState<G>& st, const float* om, const float* ol, const float (*oacc)[8]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float M = fmaxf(st.m[g], om[g]);
+        if (M == -INFINITY) continue;
+        const float wa = __builtin_amdgcn_exp2f(st.m[g] - M);
+        const float wb = __builtin_amdgcn_exp2f(om[g] - M);
+        st.l[g] = st.l[g] * wa + ol[g] * wb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.acc[g][e] = st.acc[g][e] * wa + oacc[g][e] * wb;
+        st.m[g] = M;
+    }
+}
+
+// Partial (m, l, acc) of query head g of a unit in slot `slot` of P.
+__device__ __forceinline__ size_t part_index(int unit, int G, int g, int P, int slot) {
+    return ((size_t)unit * G + g) * P + slot;
+}
+
+// Combines the 16 row groups of a 256-thread workgroup (4 per wave through
+// lane shuffles, then the 4 waves through LDS, in wave order) and writes the
+// workgroup's partial to slot `slot`.  Every thread of the workgroup calls it.
+template <int G>
+__device__ __forceinline__ void finish_partial(SoftState<G>& st, float (*s_red)[G][kHeadDim + 2], float* part_ml,
+                                               float* part_acc, int unit, int slot, int P) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rg = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int step = 16; step <= 32; step <<= 1) {
+        float om[G], ol[G], oacc[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            om[g] = shfl_xor_f(st.m[g], step);
+            ol[g] = shfl_xor_f(st.l[g], step);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
+        }
+        merge_state<G>(st, om, ol, oacc);
+    }
+    __syncthreads();
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
+            if (li == 0) {
+                s_red[wave][g][kHeadDim] = st.m[g];
+                s_red[wave][g][kHeadDim + 1] = st.l[g];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kHeadDim; e += 256) {
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
+                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
+                acc = fmaf(s_red[w][g][dd], wt, acc);
+            }
+        }
+        const size_t pidx = part_index(unit, G, g, P, slot);
+        part_acc[pidx * kHeadDim + dd] = acc;
+        if (dd == 0) {
+            part_ml[pidx * 2] = M;
+            part_ml[pidx * 2 + 1] = l;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // score: workgroup (chunk, unit) scores 256 items, 16 lanes per centroid row,
-// 8 rows per lane group in flight, two passes.  Items are cluster ids, or the
-// member rows of a previous selection (the fine clusters inside the coarse
-// candidates of the two-level method).
+// 16 rows per lane group in flight (8 in fp32, two passes).  Items are
+// cluster ids, or the member rows of a previous selection (the fine clusters
+// inside the coarse candidates of the two-level method).  Thread t writes the
+// cut record of item t of the chunk (its fields load at the start; the key
+// comes through LDS).
 // ---------------------------------------------------------------------------
 constexpr int kScoreChunk = 256;  // items per workgroup (64 per wave)
 constexpr int kListCap = 1024;    // selection-list entries staged in LDS
@@ -65,13 +215,15 @@ template <typename T, int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     __shared__ int32_t s_pre[kListCap + 1];
     __shared__ int32_t s_off[kListCap];
+    __shared__ float s_key[kScoreChunk];
     const int unit = blockIdx.y;
     int n = a.n_items;
     if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, li = lane & 15;
-    const int i0 = blockIdx.x * kScoreChunk + wave * 64;
-    if (blockIdx.x * kScoreChunk >= n) return;  // uniform across the workgroup
+    const int c0 = blockIdx.x * kScoreChunk;
+    const int i0 = c0 + wave * 64;
+    if (c0 >= n) return;  // uniform across the workgroup
 
     // items through a selection list: stage its member-row prefix
     const int32_t* mem = a.members ? a.members + (size_t)unit * a.cent_rows : nullptr;
@@ -83,7 +235,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const int32_t* gpre = a.list_pre + (size_t)unit * (a.list_stride + 1);
         const int32_t* goff = a.list_off + (size_t)unit * a.list_stride;
         if (nl <= kListCap) {
-            for (int k = threadIdx.x; k <= nl; k += 256) {
+            for (int k = tid; k <= nl; k += 256) {
                 s_pre[k] = gpre[k];
                 if (k < nl) s_off[k] = goff[k];
             }
@@ -95,70 +247,83 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             loff = goff;
         }
     }
-    if (i0 >= n) return;
+    auto item_id = [&](int i) -> int {
+        if (!lpre) return i;
+        const int k = upper_index(lpre, nl, i);
+        return mem[loff[k] + i - lpre[k]];
+    };
+    // record fields of item c0 + tid, loaded up front
+    const int my_item = c0 + tid;
+    int my_id = 0, my_sz = 0, my_o0 = 0, my_o1 = 0;
+    if (my_item < n) {
+        my_id = item_id(my_item);
+        const int32_t* ofu = a.offsets + (size_t)unit * a.off_stride;
+        my_sz = a.sizes[(size_t)unit * a.cent_rows + my_id];
+        my_o0 = ofu[my_id];
+        my_o1 = ofu[my_id + 1];
+    }
 
-    const int b = unit / a.Hkv, h = unit % a.Hkv;
-    QSlice<T> qv[G];
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
+    if (i0 < n) {
+        const int b = unit / a.Hkv, h = unit % a.Hkv;
+        QSlice<T> qv[G];
+        const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
 #pragma unroll
-    for (int g = 0; g < G; ++g) qv[g].load(qb + (size_t)g * kHeadDim);
-    const T* cu = reinterpret_cast<const T*>(a.cent) + (size_t)unit * a.cent_rows * kHeadDim + li * 8;
-    const int32_t* szu = a.sizes + (size_t)unit * a.cent_rows;
+        for (int g = 0; g < G; ++g) qv[g].load(qb + (size_t)g * kHeadDim);
+        const T* cu = reinterpret_cast<const T*>(a.cent) + (size_t)unit * a.cent_rows * kHeadDim + li * 8;
+        constexpr int R = sizeof(T) == 2 ? 16 : 8;
 #pragma unroll 1
-    for (int half = 0; half < 2; ++half) {  // 2 x 8 rows per lane group in flight
-        const int ib = i0 + half * 32;
-        int cid[8];
-        Slice8<T> row[8];
+        for (int pass = 0; pass < 16 / R; ++pass) {
+            const int ib = i0 + pass * 4 * R;
+            if (ib >= n) break;  // uniform across the wave
+            int cid[R];
+            Slice8<T> row[R];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = ib + u * 4 + rg;
-            const int ii = i < n ? i : i0;
-            if (lpre) {
-                const int k = upper_index(lpre, nl, ii);
-                cid[u] = mem[loff[k] + ii - lpre[k]];
-            } else {
-                cid[u] = ii;
+            for (int u = 0; u < R; ++u) {
+                const int i = ib + u * 4 + rg;
+                cid[u] = item_id(i < n ? i : ib);
+            }
+#pragma unroll
+            for (int u = 0; u < R; ++u) row[u].load(cu + (size_t)cid[u] * kHeadDim);
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const int i = ib + u * 4 + rg;
+                float sg[G];
+                float r = 0.f;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    sg[g] = row16_sum(dot8(qv[g], row[u])) * kInvSqrtD;
+                    r += sg[g];
+                }
+                r *= 1.0f / G;
+                if (i < n) {
+                    float* so = a.s_out + ((size_t)unit * a.cent_rows + cid[u]) * G;
+                    float mine = sg[0];
+#pragma unroll
+                    for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
+                    if (li < G) so[li] = mine;
+                    if (li == 0) s_key[i - c0] = r;
+                }
             }
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) row[u].load(cu + (size_t)cid[u] * kHeadDim);
-        int sz[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) sz[u] = li == 0 ? szu[cid[u]] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = ib + u * 4 + rg;
-            float sg[G];
-            float r = 0.f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                sg[g] = row16_sum(dot8(qv[g], row[u])) * kInvSqrtD;
-                r += sg[g];
-            }
-            r *= 1.0f / G;
-            if (i < n) {
-                float* so = a.s_out + ((size_t)unit * a.cent_rows + cid[u]) * G;
-                float mine = sg[0];
-#pragma unroll
-                for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
-                if (li < G) so[li] = mine;
-                if (li == 0) a.rs_out[(size_t)unit * a.rs_stride + i] = make_int2(__float_as_int(r), sz[u]);
-                if (a.ids_out && li == 15) a.ids_out[(size_t)unit * a.rs_stride + i] = cid[u];
-            }
-        }
+    }
+    __syncthreads();
+    if (my_item < n) {
+        const size_t o = (size_t)unit * a.rs_stride + my_item;
+        a.rs_out[o] = make_int4(__float_as_int(s_key[tid]), my_sz, my_o0, my_o1 - my_o0);
+        if (a.ids_out) a.ids_out[o] = my_id;
     }
 }
 
 // ---------------------------------------------------------------------------
 // select: budget cut of one unit by one 256-thread workgroup.  Thread t owns
-// items 8 t .. 8 t + 7 of each tile of 2048 (key and size in registers).
-// Four 8-bit radix passes over the order-preserving key bits find the cut
-// value: pass p adds the sizes of the items still matching the prefix into
-// its own LDS histogram (all four are cleared up front, so a pass needs one
-// barrier), then every wave scans that histogram from the top digit down to
-// the budget left, and all reach the same digit.  Items above the cut value
-// are selected; items equal to it are taken in item order while they fit.
-// One workgroup scan places the selected items in item order.
+// items 8 t .. 8 t + 7 of each tile of 2048 (record in registers).  Four
+// 8-bit radix passes over the order-preserving key bits find the cut value:
+// pass p adds the weights of the items still matching the prefix into its own
+// LDS histogram (all four are cleared up front, so a pass needs one barrier),
+// then every wave scans that histogram from the top digit down to the budget
+// left, and all reach the same digit.  Items above the cut value are
+// selected; items equal to it are taken in item order while they fit.  One
+// workgroup scan places the selected items in item order.
 // ---------------------------------------------------------------------------
 constexpr int kSelItems = 8;                 // items per thread per tile
 constexpr int kSelTileN = 256 * kSelItems;   // items per tile
@@ -166,25 +331,26 @@ constexpr int kMaskWords = 1024;             // LDS bitmask capacity (32768 ids)
 
 struct SelItems {
     uint32_t key[kSelItems];
-    int32_t sz[kSelItems];
+    int32_t sz[kSelItems], off[kSelItems], rows[kSelItems];
 };
 
 __device__ __forceinline__ void load_items(const SelectArgs& a, int unit, int n, int base, SelItems& it) {
-    const int2* rs = a.rs + (size_t)unit * a.rs_stride;
+    const int4* rs = a.rs + (size_t)unit * a.rs_stride;
     const int t0 = base + threadIdx.x * kSelItems;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-        const int2 v = t0 + j < n ? rs[t0 + j] : make_int2(0, 0);
+        const int4 v = t0 + j < n ? rs[t0 + j] : make_int4(0, 0, 0, 0);
         it.key[j] = order_key(__int_as_float(v.x));
         it.sz[j] = v.y;
+        it.off[j] = v.z;
+        it.rows[j] = v.w;
     }
 }
 
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+__device__ __forceinline__ void select_unit(const SelectArgs& a, int unit) {
     __shared__ int hist[4][256];
     __shared__ int scan_lds[16];
     __shared__ uint32_t s_mask[kMaskWords];
-    const int unit = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     int n = a.n_items;
     if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
@@ -240,7 +406,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     const uint32_t tau = prefix;
 
     const int32_t* gids = a.ids ? a.ids + (size_t)unit * a.rs_stride : nullptr;
-    const int32_t* goff = a.offsets + (size_t)unit * a.off_stride;
     int32_t* sid = a.sel_ids + (size_t)unit * a.sel_stride;
     int32_t* soff = a.sel_off + (size_t)unit * a.sel_stride;
     int32_t* spre = a.sel_rowpre + (size_t)unit * (a.sel_stride + 1);
@@ -266,7 +431,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
             }
         }
         uint32_t selbits = 0;
-        int s_local = 0;
+        int s_local = 0, rows_local = 0;
 #pragma unroll
         for (int j = 0; j < kSelItems; ++j) {
             const int sz = it.sz[j];
@@ -282,21 +447,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
             sel = sel && sz > 0;
             selbits |= (uint32_t)sel << j;
             s_local += sel;
+            rows_local += sel ? it.rows[j] : 0;
         }
-        // member rows of the selected items (offsets read only for those)
-        int id[kSelItems], off[kSelItems], nr[kSelItems];
-        int rows_local = 0;
+        int id[kSelItems];
 #pragma unroll
-        for (int j = 0; j < kSelItems; ++j) {
-            id[j] = t0 + j < n ? (gids ? gids[t0 + j] : t0 + j) : 0;
-            off[j] = 0;
-            nr[j] = 0;
-            if ((selbits >> j) & 1u) {
-                off[j] = goff[id[j]];
-                nr[j] = goff[id[j] + 1] - off[j];
-                rows_local += nr[j];
-            }
-        }
+        for (int j = 0; j < kSelItems; ++j) id[j] = t0 + j < n ? (gids ? gids[t0 + j] : t0 + j) : 0;
         int4 tot;
         const int4 ex = block256_exclusive_sum4(make_int4(s_local, rows_local, 0, 0), tot, scan_lds);
         int k = carry_sel + ex.x, ro = carry_rows + ex.y;
@@ -304,10 +459,10 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
         for (int j = 0; j < kSelItems; ++j) {
             if ((selbits >> j) & 1u) {
                 sid[k] = id[j];
-                soff[k] = off[j];
+                soff[k] = it.off[j];
                 spre[k] = ro;
                 ++k;
-                ro += nr[j];
+                ro += it.rows[j];
                 atomicOr(&s_mask[id[j] >> 5], 1u << (id[j] & 31));
             }
             if (dbg && t0 + j < n) dbg[id[j]] = (selbits >> j) & 1u;
@@ -329,65 +484,140 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// attend: workgroup (split, unit), 4 waves, 16 lanes per row, 8 dims a lane.
-// A row group (16 lanes) keeps its own online-softmax state (m, l, acc[8] per
-// head) over the rows it visits, 2 rows per step with the next step's rows
-// already in flight.  The running maximum is only raised when a logit exceeds
-// it by more than 2^8 (every weight stays <= 256 in fp32), so rescaling is
-// rare.  Exact rows: split s takes rows [E s / S, E (s + 1) / S) of the
-// selected clusters' member rows (found by binary search of the row prefix).
-// Approximated clusters: split s takes items [P s / S, P (s + 1) / S) of the
-// cluster range and keeps the non-empty unselected ones (bitmask), compacted
-// in LDS with their weights n 2^(lambda - M) (M the chunk maximum).
+// Approximate term of every non-empty item of a chunk of 256 (one workgroup):
+// thread t takes item t's logits lambda_g = s_g log2(e) + log2(n) (base 2);
+// the chunk maximum M_g is the fixed reference, the weights 2^(lambda - M)
+// go to LDS, and row group (wave, rg) accumulates the value centroids of
+// items 64 wave + 4 u + rg (u < 16), whose loads are in flight from the start.
 // ---------------------------------------------------------------------------
-constexpr int kAttCap = 512;       // staged items per list and pass
-constexpr float kLazyMax = 8.0f;   // base-2 headroom before the running max moves
-
 template <int G>
-struct SoftState {
-    float m[G], l[G], acc[G][8];
-};
+constexpr int pseudo_lds_bytes() {
+    return (kScoreChunk * G + 4 * G + 4 * G * (kHeadDim + 1)) * 4;
+}
 
-// Adds 2 rows with base-2 logits lg[u][g] (-inf for an absent row).
 template <typename T, int G>
-__device__ __forceinline__ void absorb2(SoftState<G>& st, const float (&lg)[2][G], const Slice8<T> (&v)[2]) {
-    float x0[8], x1[8];
-    v[0].unpack(x0);
-    v[1].unpack(x1);
+__device__ __forceinline__ void pseudo_chunk(const PseudoArgs& a, int unit, int chunk, char* lds) {
+    float (*s_w)[G] = reinterpret_cast<float (*)[G]>(lds);
+    float (*s_wmax)[G] = reinterpret_cast<float (*)[G]>(lds + kScoreChunk * G * 4);
+    float (*s_red)[G][kHeadDim + 1] = reinterpret_cast<float (*)[G][kHeadDim + 1]>(lds + (kScoreChunk + 4) * G * 4);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rg = lane >> 4, li = lane & 15;
+    int n = a.n_items;
+    if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
+    const int slot = a.part_base + chunk;
+    const int c0 = chunk * kScoreChunk;
+    const int32_t* ids = a.ids ? a.ids + (size_t)unit * a.ids_stride : nullptr;
+    const float* su = a.s + (size_t)unit * a.rows * G;
+    const int32_t* szu = a.sizes + (size_t)unit * a.rows;
+
+    // value centroid rows of this row group (absent items read item c0)
+    const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.rows * kHeadDim + li * 8;
+    const int ib = c0 + wave * 64;
+    Slice8<T> vrow[16];
+    if (c0 < n) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = ib + u * 4 + rg;
+            const int c = i < n ? (ids ? ids[i] : i) : (ids ? ids[c0] : c0);
+            vrow[u].load(vb + (size_t)c * kHeadDim);
+        }
+    }
+    // logits of item c0 + tid
+    float lg[G];
+    {
+        const int i = c0 + tid;
+        int nn = 0, c = 0;
+        if (i < n) {
+            c = ids ? ids[i] : i;
+            nn = szu[c];
+        }
+        const float l2n = log2_count(nn > 0 ? nn : 1);
+#pragma unroll
+        for (int g = 0; g < G; ++g) lg[g] = nn > 0 ? fmaf(su[(size_t)c * G + g], kLog2e, l2n) : -INFINITY;
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const float mx = fmaxf(lg[0][g], lg[1][g]);
-        if (mx == -INFINITY) continue;
-        if (mx > st.m[g] + kLazyMax) {  // rare: raise the reference maximum
-            const float sc = __builtin_amdgcn_exp2f(st.m[g] - mx);
-            st.l[g] *= sc;
+        float m = lg[g];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
-            st.m[g] = mx;
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
+        if (lane == 0) s_wmax[wave][g] = m;
+    }
+    __syncthreads();
+    float M[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        M[g] = fmaxf(fmaxf(s_wmax[0][g], s_wmax[1][g]), fmaxf(s_wmax[2][g], s_wmax[3][g]));
+        s_w[tid][g] = lg[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[g] - M[g]);
+    }
+    __syncthreads();
+    float l[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    }
+    if (c0 < n) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = wave * 64 + u * 4 + rg;
+            float x[8];
+            vrow[u].unpack(x);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float w = s_w[r][g];
+                l[g] += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(w, x[e], acc[g][e]);
+            }
         }
-        const float p0 = __builtin_amdgcn_exp2f(lg[0][g] - st.m[g]);
-        const float p1 = __builtin_amdgcn_exp2f(lg[1][g] - st.m[g]);
-        st.l[g] += p0 + p1;
+    }
+    // same reference everywhere: plain sums over row groups, then waves
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(p1, x1[e], fmaf(p0, x0[e], st.acc[g][e]));
+    for (int step = 16; step <= 32; step <<= 1)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            l[g] += shfl_xor_f(l[g], step);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] += shfl_xor_f(acc[g][e], step);
+        }
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = acc[g][e];
+            if (li == 0) s_red[wave][g][kHeadDim] = l[g];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kHeadDim; e += 256) {
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        const float sum = (s_red[0][g][dd] + s_red[1][g][dd]) + (s_red[2][g][dd] + s_red[3][g][dd]);
+        const size_t pidx = part_index(unit, G, g, a.part_stride, slot);
+        a.part_acc[pidx * kHeadDim + dd] = sum;
+        if (dd == 0) {
+            a.part_ml[pidx * 2] = M[g];
+            a.part_ml[pidx * 2 + 1] =
+                (s_red[0][g][kHeadDim] + s_red[1][g][kHeadDim]) + (s_red[2][g][kHeadDim] + s_red[3][g][kHeadDim]);
+        }
     }
 }
 
-// Merge another partial state (om, ol, oacc) into st.
-template <int G>
-__device__ __forceinline__ void merge_state(SoftState<G>& st, const float* om, const float* ol, const float (*oacc)[8]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float M = fmaxf(st.m[g], om[g]);
-        if (M == -INFINITY) continue;
-        const float wa = __builtin_amdgcn_exp2f(st.m[g] - M);
-        const float wb = __builtin_amdgcn_exp2f(om[g] - M);
-        st.l[g] = st.l[g] * wa + ol[g] * wb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[g][e] = st.acc[g][e] * wa + oacc[g][e] * wb;
-        st.m[g] = M;
-    }
-}
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs sa) { select_unit(sa, blockIdx.x); }
+
+// ---------------------------------------------------------------------------
+// attend: workgroup (split, unit), 4 waves, 16 lanes per row, 8 dims a lane.
+// Each row group keeps its own softmax state over the rows it visits, 2 rows
+// per step with the next steps' rows already in flight.  Exact rows: split s
+// takes rows [E s / S, E (s + 1) / S) of the selected clusters' member rows
+// (found by binary search of the row prefix) and its share of the unclustered
+// tail; it also removes, for its share of each selected list, the
+// approximate terms added for those clusters (the first step's loads go out
+// ahead of the exact rows).
+// ---------------------------------------------------------------------------
+constexpr int kAttCap = 512;   // staged exact rows per pass
+constexpr int kAttDepth = 2;   // row steps in flight per wave
+constexpr int kSpec = 256;     // selection entries staged before the counts are known
 
 template <typename T>
 struct RowBuf {
@@ -420,44 +650,7 @@ __device__ __forceinline__ void exact_step(SoftState<G>& st, const QSlice<T> (&q
             const float d = row16_sum(dot8(qs[g], bf.k[u])) * qscale;
             lg[u][g] = bf.ok[u] ? d : -INFINITY;
         }
-    absorb2<T, G>(st, lg, bf.v);
-}
-
-template <typename T>
-struct PseudoBuf {
-    Slice8<T> v[2];
-    bool ok[2];
-    int i[2];
-};
-
-template <typename T>
-__device__ __forceinline__ void load_pseudo(PseudoBuf<T>& bf, const int32_t* s_pid, int cnt, int it, int wave, int rg,
-                                            const T* vbar) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = it * 32 + wave * 8 + u * 4 + rg;
-        bf.ok[u] = i < cnt;
-        bf.i[u] = bf.ok[u] ? i : 0;
-        bf.v[u].load(vbar + (size_t)s_pid[bf.i[u]] * kHeadDim);
-    }
-}
-
-// Adds 2 approximated clusters: staged weights (relative to the chunk
-// reference) times the row group's factor f.
-template <typename T, int G>
-__device__ __forceinline__ void pseudo_step(SoftState<G>& st, const float (*s_w)[G], const float (&f)[G],
-                                            const PseudoBuf<T>& bf) {
-    float x0[8], x1[8];
-    bf.v[0].unpack(x0);
-    bf.v[1].unpack(x1);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float p0 = bf.ok[0] ? s_w[bf.i[0]][g] * f[g] : 0.f;
-        const float p1 = bf.ok[1] ? s_w[bf.i[1]][g] * f[g] : 0.f;
-        st.l[g] += p0 + p1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(p1, x1[e], fmaf(p0, x0[e], st.acc[g][e]));
-    }
+    absorb2<T, G, false>(st, lg, bf.v);
 }
 
 // Stages exact rows [c0, c0 + cnt) of the unit's selection: row i belongs to
@@ -473,105 +666,46 @@ __device__ __forceinline__ void stage_exact(int32_t* s_row, const int32_t* pre, 
     }
 }
 
-// Stages the approximated clusters among items [c0, c0 + cnt) (cnt <= 512)
-// of a source: non-empty and not selected, compacted in item order; for each,
-// per head the weight n * 2^(lambda - M) with lambda = s * log2(e) (base-2
-// logit) and M the chunk's largest log2(n) + lambda, left in s_pm[g].
-// Returns the number staged.  Ends with a barrier.
-template <int G>
-__device__ __forceinline__ int stage_pseudo(int32_t* s_pid, float (*s_w)[G], float* s_pm, float (*s_wmax)[G],
-                                            int* s_cnt, const PseudoSrc& ps, int unit, int c0, int cnt) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t* ids = ps.ids ? ps.ids + (size_t)unit * ps.ids_stride : nullptr;
-    const uint32_t* msk = ps.selmask + (size_t)unit * ps.mask_stride;
-    const float* su = ps.s + (size_t)unit * ps.rows * G;
-    const int32_t* szu = ps.sizes + (size_t)unit * ps.rows;
+// Removal data of 2 selected clusters per row group: list entries base + 4 u
+// + rg (u = 0, 1) of [k0, k1).
+template <typename T, int G>
+struct SubBuf {
+    Slice8<T> v[2];
     float lg[2][G];
-    int cid[2];
-    bool keep[2];
-    float mx[G];
+};
+
+template <typename T, int G>
+__device__ __forceinline__ void load_sub(SubBuf<T, G>& sb, const SubSrc& ss, const int32_t* ids, int unit, int k0,
+                                         int k1, int base, int rg, int li) {
+    const float* su = ss.s + (size_t)unit * ss.rows * G;
+    const int32_t* szu = ss.sizes + (size_t)unit * ss.rows;
+    const T* vb = reinterpret_cast<const T*>(ss.vbar) + (size_t)unit * ss.rows * kHeadDim + li * 8;
 #pragma unroll
-    for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
+    for (int u = 0; u < 2; ++u) {
+        const int k = base + u * 4 + rg;
+        const bool ok = k < k1;
+        const int c = ids[ok ? k : k0];
+        const float l2n = log2_count(szu[c]);  // selected: n >= 1
+        sb.v[u].load(vb + (size_t)c * kHeadDim);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int i = tid + 256 * k;
-        keep[k] = false;
-        cid[k] = 0;
-        if (i < cnt) {
-            const int c = ids ? ids[c0 + i] : c0 + i;
-            const int n = szu[c];
-            cid[k] = c;
-            keep[k] = n > 0 && !((msk[c >> 5] >> (c & 31)) & 1u);
-            if (keep[k]) {
-                const float ln2n = __builtin_amdgcn_logf((float)n);  // log2(n)
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    lg[k][g] = fmaf(su[(size_t)c * G + g], kLog2e, ln2n);
-                    mx[g] = fmaxf(mx[g], lg[k][g]);
-                }
-            }
-        }
+        for (int g = 0; g < G; ++g) sb.lg[u][g] = ok ? fmaf(su[(size_t)c * G + g], kLog2e, l2n) : -INFINITY;
     }
-    // per-wave maxima and kept counts; one barrier
-    const uint64_t b0 = __ballot(keep[0]), b1 = __ballot(keep[1]);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float m = mx[g];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
-        if (lane == 0) s_wmax[wave][g] = m;
-    }
-    if (lane == 0) {
-        s_cnt[wave] = __popcll(b0);
-        s_cnt[4 + wave] = __popcll(b1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        mx[g] = fmaxf(fmaxf(s_wmax[0][g], s_wmax[1][g]), fmaxf(s_wmax[2][g], s_wmax[3][g]));
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        if (tid == g) s_pm[g] = mx[g];
-    // item order: k = 0 items (threads 0..255) first, then k = 1
-    int base0 = 0, base1 = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        base0 += w < wave ? s_cnt[w] : 0;
-        total += s_cnt[w];
-    }
-    base1 = total;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        base1 += w < wave ? s_cnt[4 + w] : 0;
-        total += s_cnt[4 + w];
-    }
-    const uint64_t below = (1ull << lane) - 1;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (keep[k]) {
-            const int slot = (k == 0 ? base0 + __popcll(b0 & below) : base1 + __popcll(b1 & below));
-            s_pid[slot] = cid[k];
-#pragma unroll
-            for (int g = 0; g < G; ++g) s_w[slot][g] = __builtin_amdgcn_exp2f(lg[k][g] - mx[g]);
-        }
-    }
-    __syncthreads();
-    return total;
+}
+
+template <int G>
+constexpr int attend_lds_bytes() {
+    return (kAttCap + (kListCap + 1) + 2 * kListCap + 4 * G * (kHeadDim + 2)) * 4;
 }
 
 template <typename T, int G>
-__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
-    __shared__ int32_t s_row[kAttCap];
-    __shared__ int32_t s_pid[kAttCap];
-    __shared__ float s_w[kAttCap][G];
-    __shared__ float s_pm[G];
-    __shared__ float s_wmax[4][G];
-    __shared__ int s_cnt[8];
-    __shared__ int32_t s_pre[kListCap + 1];
-    __shared__ int32_t s_off[kListCap];
-    __shared__ float s_red[4][G][kHeadDim + 2];
+__device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int unit, char* lds) {
+    constexpr int D = kAttDepth;
+    int32_t* s_row = reinterpret_cast<int32_t*>(lds);
+    int32_t* s_pre = s_row + kAttCap;
+    int32_t* s_off = s_pre + kListCap + 1;
+    int32_t* s_ids = s_off + kListCap;
+    float (*s_red)[G][kHeadDim + 2] = reinterpret_cast<float (*)[G][kHeadDim + 2]>(s_ids + kListCap);
 
-    const int split = blockIdx.x, unit = blockIdx.y;
     const int S = a.S;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -579,56 +713,93 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int b = unit / a.Hkv, h = unit % a.Hkv;
     const float qscale = kInvSqrtD * kLog2e;
 
-    // selection of the unit: member-row prefix and first member of each
-    // selected cluster (staged when small enough)
-    const int E = a.counts[unit * 4];
-    const int nsel = a.counts[unit * 4 + 1];
-    const int e0 = (int)((int64_t)E * split / S), e1 = (int)((int64_t)E * (split + 1) / S);
+    // selection of the unit: member-row prefix, first member and id of each
+    // selected cluster.  The first kSpec entries load beside the counts.
     const int32_t* gpre = a.sel_rowpre + (size_t)unit * (a.sel_stride + 1);
     const int32_t* goff = a.sel_off + (size_t)unit * a.sel_stride;
-    const int32_t* pre = gpre;
-    const int32_t* off = goff;
-    if (nsel <= kListCap) {
-        for (int k = tid; k <= nsel; k += 256) {
-            s_pre[k] = gpre[k];
-            if (k < nsel) s_off[k] = goff[k];
-        }
-        pre = s_pre;
-        off = s_off;
+    const int32_t* gids = a.n_sub > 0 ? a.sa.ids + (size_t)unit * a.sa.ids_stride : nullptr;
+    const int spec = min(kSpec, a.sel_stride);
+    if (tid < spec) {
+        s_off[tid] = goff[tid];
+        if (gids) s_ids[tid] = gids[tid];
     }
+    if (tid <= spec) s_pre[tid] = gpre[tid];
+    if (tid == 0 && spec == kSpec) s_pre[kSpec] = gpre[kSpec];
+    const int E = a.counts[unit * 4];
+    const int nsel = a.counts[unit * 4 + 1];
+    const bool staged = nsel <= kListCap;
+    if (staged && nsel > spec) {
+        for (int k = spec + 1 + tid; k <= nsel; k += 256) s_pre[k] = gpre[k];
+        for (int k = spec + tid; k < nsel; k += 256) {
+            s_off[k] = goff[k];
+            if (gids) s_ids[k] = gids[k];
+        }
+    }
+    const int32_t* pre = staged ? s_pre : gpre;
+    const int32_t* off = staged ? s_off : goff;
+    const int32_t* sids = staged ? s_ids : gids;
+    const int e0 = (int)((int64_t)E * split / S), e1 = (int)((int64_t)E * (split + 1) / S);
     const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
     QSlice<T> qs[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
     SoftState<G> st;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        st.m[g] = -INFINITY;
-        st.l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[g][e] = 0.f;
-    }
+    st.init();
     const size_t ubase = (size_t)unit * a.Nmax * kHeadDim + li * 8;
     const T* Kx = reinterpret_cast<const T*>(a.Kx) + ubase;
     const T* Vx = reinterpret_cast<const T*>(a.Vx) + ubase;
     const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
     __syncthreads();
 
+    // ---- removals of the first list, first step: loads issued first -------
+    SubBuf<T, G> sub;
+    int sk0 = 0, sk1 = 0;
+    if (a.n_sub > 0) {
+        sk0 = (int)((int64_t)nsel * split / S);
+        sk1 = (int)((int64_t)nsel * (split + 1) / S);
+        if (sk0 < sk1) load_sub<T, G>(sub, a.sa, sids, unit, sk0, sk1, sk0 + wave * 8, rg, li);
+    }
+    const bool sub_pending = a.n_sub > 0 && sk0 < sk1;
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- exact rows of selected clusters -------------------------------
-    for (int c0 = e0; c0 < e1; c0 += kAttCap) {
-        const int cnt = min(kAttCap, e1 - c0);
-        if (c0 != e0) __syncthreads();
+    // Batches of kAttCap staged rows, each streamed through a ring of D
+    // steps in flight.  The ring loop has no branches, so the compiler's
+    // wait counts stay exact: steps past the end load a valid row (staged
+    // row 0) and are masked out.  The removal data is consumed once the
+    // first batch's loads are out, so it is dead inside the ring loop.
+    RowBuf<T> ring[D];
+    int c0 = e0, cnt = min(kAttCap, e1 - e0);
+    if (c0 < e1) {
         stage_exact(s_row, pre, off, nsel, tids, c0, cnt);
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (sub_pending) absorb2<T, G, true>(st, sub.lg, sub.v);
+    while (c0 < e1) {
         const int steps = (cnt + 31) / 32;
-        RowBuf<T> A, B;
-        if (steps > 0) load_rows<T>(A, s_row, cnt, 0, wave, rg, Kx, Vx);
-        for (int it = 0; it < steps; it += 2) {
-            if (it + 1 < steps) load_rows<T>(B, s_row, cnt, it + 1, wave, rg, Kx, Vx);
-            exact_step<T, G>(st, qs, qscale, A);
-            if (it + 1 < steps) {
-                if (it + 2 < steps) load_rows<T>(A, s_row, cnt, it + 2, wave, rg, Kx, Vx);
-                exact_step<T, G>(st, qs, qscale, B);
+        for (int it = 0; it < steps; it += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                exact_step<T, G>(st, qs, qscale, ring[j]);
+                load_rows<T>(ring[j], s_row, cnt, it + j + D, wave, rg, Kx, Vx);
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring order: no load sinks
+            }
+        }
+        c0 += kAttCap;
+        if (c0 < e1) {
+            cnt = min(kAttCap, e1 - c0);
+            __syncthreads();
+            stage_exact(s_row, pre, off, nsel, tids, c0, cnt);
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -651,110 +822,77 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             exact_step<T, G>(st, qs, qscale, bf);
         }
     }
-    // ---- approximated clusters: logit s + ln n, value Vbar ----------------
-#pragma unroll 1
-    for (int which = 0; which < a.n_pseudo; ++which) {
-        const PseudoSrc& ps = which == 0 ? a.pa : a.pb;
-        const int P = ps.n_dev ? min(ps.n_host, ps.n_dev[unit * 4]) : ps.n_host;
-        const int p0 = (int)((int64_t)P * split / S), p1 = (int)((int64_t)P * (split + 1) / S);
-        const T* vbar = reinterpret_cast<const T*>(ps.vbar) + (size_t)unit * ps.rows * kHeadDim + li * 8;
-        for (int c0 = p0; c0 < p1; c0 += kAttCap) {
-            __syncthreads();
-            const int cnt = stage_pseudo<G>(s_pid, s_w, s_pm, s_wmax, s_cnt, ps, unit, c0, min(kAttCap, p1 - c0));
-            // move this row group's state to reference max(m, M) once; the
-            // staged weights are relative to M
-            float f[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float M = s_pm[g];
-                if (M > st.m[g]) {
-                    const float sc = __builtin_amdgcn_exp2f(st.m[g] - M);
-                    st.l[g] *= sc;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
-                    st.m[g] = M;
-                }
-                f[g] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - st.m[g]);
-            }
-            const int steps = (cnt + 31) / 32;
-            PseudoBuf<T> A, B;
-            if (steps > 0) load_pseudo<T>(A, s_pid, cnt, 0, wave, rg, vbar);
-            for (int it = 0; it < steps; it += 2) {
-                if (it + 1 < steps) load_pseudo<T>(B, s_pid, cnt, it + 1, wave, rg, vbar);
-                pseudo_step<T, G>(st, s_w, f, A);
-                if (it + 1 < steps) {
-                    if (it + 2 < steps) load_pseudo<T>(A, s_pid, cnt, it + 2, wave, rg, vbar);
-                    pseudo_step<T, G>(st, s_w, f, B);
-                }
-            }
+    // ---- the remaining removals (past the first step, second list) -------
+    if (a.n_sub > 0)
+        for (int base = sk0 + 32 + wave * 8; base < sk1; base += 32) {
+            load_sub<T, G>(sub, a.sa, sids, unit, sk0, sk1, base, rg, li);
+            absorb2<T, G, true>(st, sub.lg, sub.v);
+        }
+    if (a.n_sub > 1) {
+        const int nk = a.sb.counts[unit * 4 + 1];
+        const int k0 = (int)((int64_t)nk * split / S), k1 = (int)((int64_t)nk * (split + 1) / S);
+        const int32_t* ids = a.sb.ids + (size_t)unit * a.sb.ids_stride;
+        for (int base = k0 + wave * 8; base < k1; base += 32) {
+            load_sub<T, G>(sub, a.sb, ids, unit, k0, k1, base, rg, li);
+            absorb2<T, G, true>(st, sub.lg, sub.v);
         }
     }
+    finish_partial<G>(st, s_red, a.part_ml, a.part_acc, unit, split, a.part_stride);
+}
 
-    // ---- merge the 4 row groups of the wave, then the 4 waves --------------
-#pragma unroll
-    for (int step = 16; step <= 32; step <<= 1) {
-        float om[G], ol[G], oacc[G][8];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            om[g] = shfl_xor_f(st.m[g], step);
-            ol[g] = shfl_xor_f(st.l[g], step);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
-        }
-        merge_state<G>(st, om, ol, oacc);
+// Workgroup (x, unit): x < S attends split x; the other columns add the
+// approximate terms of every non-empty cluster, one chunk of 256 each, for the
+// sources in a.pseudo (the coarse level, then the fine level).  The
+// approximate term does not depend on the cut, so it streams beside the exact
+// rows.
+template <typename T, int G>
+__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+    constexpr int kLds = attend_lds_bytes<G>() > pseudo_lds_bytes<G>() ? attend_lds_bytes<G>() : pseudo_lds_bytes<G>();
+    __shared__ __align__(16) char lds[kLds];
+    const int x = blockIdx.x, unit = blockIdx.y;
+    if (x < a.S) {
+        attend_split<T, G>(a, x, unit, lds);
+        return;
     }
-    __syncthreads();
-    if (rg == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
-            if (li == 0) {
-                s_red[wave][g][kHeadDim] = st.m[g];
-                s_red[wave][g][kHeadDim + 1] = st.l[g];
-            }
+    int c = x - a.S;
+    for (int k = 0; k < a.n_pseudo; ++k) {
+        if (c < a.pseudo[k].chunks) {
+            pseudo_chunk<T, G>(a.pseudo[k], unit, c, lds);
+            return;
         }
-    }
-    __syncthreads();
-    // thread -> (g, dim) pairs; waves merged in order 0..3
-    for (int e = tid; e < G * kHeadDim; e += 256) {
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
-        float l = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
-                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
-                acc = fmaf(s_red[w][g][dd], wt, acc);
-            }
-        }
-        const size_t pidx = ((size_t)unit * G + g) * S + split;
-        a.part_acc[pidx * kHeadDim + dd] = acc;
-        if (dd == 0) {
-            a.part_ml[pidx * 2] = M;
-            a.part_ml[pidx * 2 + 1] = l;
-        }
+        c -= a.pseudo[k].chunks;
     }
 }
 
-// merge: one 128-thread workgroup per (unit, query head of the group).
+// merge: one 128-thread workgroup per (unit, query head of the group) over the
+// P partials of the unit, 8 partials loaded per round.
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_ml,
-                                                    const float* __restrict__ part_acc, int G, int S, int Hkv,
+                                                    const float* __restrict__ part_acc, int G, int P, int Hkv,
                                                     float* __restrict__ out) {
     const int unit = blockIdx.x / G, g = blockIdx.x % G;
     const int dd = threadIdx.x;
-    const size_t base = ((size_t)unit * G + g) * S;
+    const size_t base = ((size_t)unit * G + g) * P;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[(base + s) * 2]);
+    for (int s = 0; s < P; ++s) M = fmaxf(M, part_ml[(base + s) * 2]);
     float l = 0.f, acc = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float w = __builtin_amdgcn_exp2f(part_ml[(base + s) * 2] - M);
-            l = fmaf(part_ml[(base + s) * 2 + 1], w, l);
-            acc = fmaf(part_acc[(base + s) * kHeadDim + dd], w, acc);
+        for (int s0 = 0; s0 < P; s0 += 8) {
+            float ml[8], lv[8], av[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int s = min(s0 + k, P - 1);
+                ml[k] = part_ml[(base + s) * 2];
+                lv[k] = part_ml[(base + s) * 2 + 1];
+                av[k] = part_acc[(base + s) * kHeadDim + dd];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (s0 + k < P) {
+                    const float w = __builtin_amdgcn_exp2f(ml[k] - M);
+                    l = fmaf(lv[k], w, l);
+                    acc = fmaf(av[k], w, acc);
+                }
+            }
         }
     }
     const int b = unit / Hkv, h = unit % Hkv;
@@ -776,9 +914,11 @@ static hipError_t score_dispatch(int G, const ScoreArgs& a, dim3 grid, hipStream
     return hipGetLastError();
 }
 
+int score_chunks(int n_items) { return n_items > 0 ? (n_items + kScoreChunk - 1) / kScoreChunk : 0; }
+
 hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st) {
     if (a.n_items <= 0) return hipSuccess;
-    dim3 grid((a.n_items + kScoreChunk - 1) / kScoreChunk, units);
+    dim3 grid(score_chunks(a.n_items), units);
     return dtype == 1 ? score_dispatch<bf16_t>(G, a, grid, st) : score_dispatch<float>(G, a, grid, st);
 }
 
@@ -801,13 +941,23 @@ static hipError_t attend_dispatch(int G, const AttendArgs& a, dim3 grid, hipStre
 }
 
 hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipStream_t st) {
-    dim3 grid(a.S, units);
+    if (a.S < 1 || a.S > a.part_stride || a.n_sub < 0 || a.n_sub > 2 || a.sel_stride < 1) return hipErrorInvalidValue;
+    if (a.n_sub > 0 && a.sa.ids_stride != a.sel_stride) return hipErrorInvalidValue;
+    if (a.n_pseudo < 0 || a.n_pseudo > 2) return hipErrorInvalidValue;
+    // pseudo workgroups are laid out as columns S, S + 1, ... of the (x, unit) grid
+    int cols = 0;
+    for (int k = 0; k < a.n_pseudo; ++k) {
+        const PseudoArgs& p = a.pseudo[k];
+        if (p.chunks != score_chunks(p.n_items) || p.part_base + p.chunks > p.part_stride) return hipErrorInvalidValue;
+        cols += p.chunks;
+    }
+    dim3 grid(a.S + cols, units);
     return dtype == 1 ? attend_dispatch<bf16_t>(G, a, grid, st) : attend_dispatch<float>(G, a, grid, st);
 }
 
-hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int S, int Hkv, float* out,
+hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int P, int Hkv, float* out,
                         hipStream_t st) {
-    hipLaunchKernelGGL(merge_kernel, dim3(units * G), dim3(kHeadDim), 0, st, part_ml, part_acc, G, S, Hkv, out);
+    hipLaunchKernelGGL(merge_kernel, dim3(units * G), dim3(kHeadDim), 0, st, part_ml, part_acc, G, P, Hkv, out);
     return hipGetLastError();
 }
 

@@ -68,21 +68,23 @@ struct ScoreArgs {
     const int32_t* list_counts;  // [U][4]
     int32_t list_stride;
     const int32_t* members;      // [U][cent_rows] position -> cluster id
-    const int32_t* sizes;        // [U][cent_rows] cluster sizes
+    const int32_t* sizes;        // [U][cent_rows] cluster sizes (budget weights)
+    const int32_t* offsets;      // [U][off_stride] member start by cluster id (CSR)
+    int32_t off_stride;
     float* s_out;                // [U][cent_rows][G] scores by cluster id
-    int2* rs_out;                // [U][rs_stride] (group-mean key bits, size) by item
+    int4* rs_out;                // [U][rs_stride] (key bits, weight, first member, member rows) by item
     int32_t rs_stride;
     int32_t* ids_out;            // optional [U][rs_stride]: cluster id of each item
     int32_t Hq, Hkv;
 };
+// Workgroups (chunks) of a score launch over n_items items.
+int score_chunks(int n_items);
 hipError_t launch_score(int dtype, int G, const ScoreArgs& a, int units, hipStream_t st);
 
 struct SelectArgs {
-    const int2* rs;              // [U][rs_stride] (key bits, size) per item
+    const int4* rs;              // [U][rs_stride] records of the score pass
     int32_t rs_stride;
     const int32_t* ids;          // optional [U][rs_stride]: cluster id per item (else id = item)
-    const int32_t* offsets;      // [U][off_stride] member start by cluster id (CSR)
-    int32_t off_stride;
     int32_t n_items;             // host count (bound when n_items_dev is set)
     const int32_t* n_items_dev;  // optional per-unit count at n_items_dev[unit * 4]
     int32_t budget;
@@ -97,20 +99,31 @@ struct SelectArgs {
     int32_t* dbg_selected;       // optional [U][dbg_stride] by cluster id
     int32_t dbg_stride;
 };
-// Budget cut of every unit (one workgroup each).  Rows of a selected item are
-// its member positions offsets[id] .. offsets[id + 1]; its budget weight is
-// its size.
+// Approximate term of every non-empty item, one partial per chunk of 256
+// items: chunk j of a unit writes slot part_base + j of part_stride.
+struct PseudoArgs {
+    const int32_t* ids;          // optional [U][ids_stride]: cluster id per item
+    int32_t ids_stride;
+    int32_t n_items;             // host count (bound when n_items_dev is set)
+    const int32_t* n_items_dev;  // optional per-unit count at n_items_dev[unit * 4]
+    const float* s;              // [U][rows][G] scores by cluster id
+    const int32_t* sizes;        // [U][rows]
+    const void* vbar;            // [U][rows][d]
+    int32_t rows;
+    float* part_ml;              // [U][G][part_stride][2]
+    float* part_acc;             // [U][G][part_stride][d]
+    int32_t part_stride, part_base;
+    int32_t chunks;              // score_chunks(n_items)
+};
+// Budget cut of every unit (one workgroup each).
 hipError_t launch_select(const SelectArgs& a, int units, hipStream_t st);
 
-// Approximated clusters: the non-empty, unselected clusters among a set of
-// items (ids [0, n) or an id list).
-struct PseudoSrc {
-    const int32_t* ids;          // optional [U][ids_stride]
+// Selected clusters whose approximate term the score pass added and attend
+// removes again.
+struct SubSrc {
+    const int32_t* ids;          // [U][ids_stride] selected cluster ids
     int32_t ids_stride;
-    int32_t n_host;              // item count (bound when n_dev is set)
-    const int32_t* n_dev;        // optional count at n_dev[unit * 4]
-    const uint32_t* selmask;     // [U][mask_stride] selected bits by id
-    int32_t mask_stride;
+    const int32_t* counts;       // count at counts[unit * 4 + 1]
     const float* s;              // [U][rows][G] scores
     const int32_t* sizes;        // [U][rows]
     const void* vbar;            // [U][rows][d]
@@ -129,14 +142,18 @@ struct AttendArgs {
     const int32_t* counts;       // [U][4] of the (fine) select
     int32_t Nmax;
     int32_t n_clustered, n_total;
-    int32_t n_pseudo;            // sources used (0, 1 or 2)
-    PseudoSrc pa, pb;
+    int32_t n_sub;               // lists removed (0, 1 or 2)
+    SubSrc sa, sb;
     int32_t Hq, Hkv, S;
-    float* part_ml;              // [U][G][S][2]
-    float* part_acc;             // [U][G][S][d]
+    int32_t n_pseudo;            // approximate-term sources streamed in the same launch (0 .. 2)
+    PseudoArgs pseudo[2];
+    float* part_ml;              // [U][G][part_stride][2], slots 0 .. S-1
+    float* part_acc;             // [U][G][part_stride][d]
+    int32_t part_stride;
 };
 hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipStream_t st);
-hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int S, int Hkv,
+// Merges the P partial slots of every (unit, query head).
+hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int P, int Hkv,
                         float* out, hipStream_t st);
 
 // ---- measurement (probe.hip) ----------------------------------------------
