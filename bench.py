@@ -114,20 +114,18 @@ def main():
     ws = M.Workspace().get(p, state, dev)  # zero-filled
     out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
     dbg = M.DecodeDebug.allocate(p, state, dev)
-    sizes = state.sizes[:, :, :C].cpu().numpy()
-    live = sizes > 0
-    exact_rows, pseudo_items = [], []
+    exact_rows = []
     for s in range(n_q):
         M.decode(p, qs[s], Kd, Vd, N, state, T, out=out, workspace=ws, debug=dbg)
-        sel = dbg.selected.cpu().numpy().astype(bool)
         exact_rows.append(int(dbg.exact_tokens.sum()))
-        pseudo_items.append(int((live & ~sel).sum()))
     torch.cuda.synchronize()
 
     def bytes_of(step):
-        e, pc = exact_rows[step], pseudo_items[step]
+        e = exact_rows[step]
         score = B * Hq * d * 2 + U * C * d * 2            # queries + key centroids
-        attend = e * d * 2 * 2 + e * 4 + pc * d * 2        # exact K/V rows + their ids + value centroids
+        # exact K/V rows + their ids + every value centroid (the attend launch
+        # streams the approximate term of all clusters and removes the selected)
+        attend = e * d * 2 * 2 + e * 4 + U * C * d * 2
         other = U * C * 4 + B * Hq * d * 4                 # sizes + output
         return score, attend, other
 
