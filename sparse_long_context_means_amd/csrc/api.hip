@@ -57,6 +57,20 @@ int splits_of(const mpattn_params* p) {
     return p->splits > 0 ? p->splits : default_splits(p->batch * p->n_kv_heads);
 }
 
+// Attend splits of a decode: the requested count, raised to the number of
+// 256-cluster chunks of the approximate term (each split streams one).
+int decode_splits(const mpattn_params* p, int32_t chunks) {
+    const int s = splits_of(p);
+    return s > chunks ? s : chunks;
+}
+
+// Most chunks a decode on a state of these capacities can stream.
+int32_t max_chunks(const mpattn_params* p, int32_t Cmax, int32_t Dmax) {
+    if (!is_hier(p)) return score_chunks(Cmax);
+    const int32_t fine = Cmax < p->coarse_candidate_tokens ? Cmax : p->coarse_candidate_tokens;
+    return score_chunks(Dmax) + score_chunks(fine);
+}
+
 // Decode workspace regions.
 struct DecodeWs {
     float* s;             // [U][Cmax][G] scores by cluster id
@@ -66,9 +80,8 @@ struct DecodeWs {
     int32_t* sel_off;     // [U][Cmax]
     int32_t* sel_pre;     // [U][Cmax + 1]
     int32_t* counts;      // [U][4]
-    float* part_ml;       // [U][G][P][2]: attend splits, then score chunks
-    float* part_acc;      // [U][G][P][d]
-    int32_t P;            // partial slots available
+    float* part_ml;       // [U][G][S][2]: one partial per attend split
+    float* part_acc;      // [U][G][S][d]
     // hierarchy: coarse level and the fine items inside the candidates
     float* cs;            // [U][Dmax][G]
     int4* crs;            // [U][Dmax]
@@ -85,7 +98,7 @@ struct DecodeWs {
 DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char* base) {
     const size_t U = (size_t)p->batch * p->n_kv_heads;
     const size_t G = (size_t)(p->n_q_heads / p->n_kv_heads);
-    const size_t S = (size_t)splits_of(p);
+    const size_t S = (size_t)decode_splits(p, max_chunks(p, Cmax, Dmax));
     DecodeWs w{};
     w.Cw = (Cmax + 31) / 32;
     w.Dw = (Dmax + 31) / 32;
@@ -102,9 +115,8 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
     w.sel_off = (int32_t*)take(U * Cmax * 4);
     w.sel_pre = (int32_t*)take(U * (Cmax + 1) * 4);
     w.counts = (int32_t*)take(U * 4 * 4);
-    w.P = (int32_t)S + score_chunks(Cmax) + (is_hier(p) ? score_chunks(Dmax) : 0);
-    w.part_ml = (float*)take(U * G * w.P * 2 * 4);
-    w.part_acc = (float*)take(U * G * w.P * kD * 4);
+    w.part_ml = (float*)take(U * G * S * 2 * 4);
+    w.part_acc = (float*)take(U * G * S * kD * 4);
     if (is_hier(p)) {
         w.cs = (float*)take(U * Dmax * G * 4);
         w.crs = (int4*)take(U * Dmax * 16);
@@ -313,15 +325,17 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const hipStream_t s = (hipStream_t)stream;
     const int U = p->batch * p->n_kv_heads;
     const int G = p->n_q_heads / p->n_kv_heads;
-    const int S = splits_of(p);
+    const int32_t bound0 = st->n_clusters < p->coarse_candidate_tokens ? st->n_clusters : p->coarse_candidate_tokens;
+    const int32_t chunks = mode != MPATTN_MODE_MULTIPOLE
+                               ? 0
+                               : (hier ? score_chunks(st->n_coarse) + score_chunks(bound0) : score_chunks(st->n_clusters));
+    const int S = decode_splits(p, chunks);
     const int32_t Cmax = st->capacity_clusters, Dmax = st->capacity_coarse, N = p->capacity_tokens;
     const int32_t C = st->n_clusters;
     const bool sorted = st->sorted_keys != nullptr;
     const int32_t want_pseudo = mode == MPATTN_MODE_MULTIPOLE ? 1 : 0;
     const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
-    // partial slots: attend splits, then the score chunks (coarse, then fine)
-    const int32_t P = S + (want_pseudo ? (hier ? score_chunks(st->n_coarse) + score_chunks(bound) : score_chunks(C)) : 0);
-    if (P > w.P) return MPATTN_ERR_WORKSPACE;
+    const int32_t P = S;  // partial slots: one per attend split
 
     for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
         const char* name = hier ? kHierStages[stage] : kFlatStages[stage];
@@ -375,16 +389,14 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
                 a.sb = SubSrc{w.csel_ids, Dmax, w.ccounts, w.cs, st->coarse_sizes, st->coarse_value_centroids, Dmax};
                 a.n_sub = want_pseudo ? 2 : 0;
                 a.pseudo[0] = PseudoArgs{nullptr, 0, st->n_coarse, nullptr, w.cs, st->coarse_sizes,
-                                         st->coarse_value_centroids, Dmax, w.part_ml, w.part_acc, P, S,
-                                         score_chunks(st->n_coarse)};
+                                         st->coarse_value_centroids, Dmax, score_chunks(st->n_coarse)};
                 a.pseudo[1] = PseudoArgs{w.fids, Cmax, bound, w.ccounts, w.s, st->sizes, st->value_centroids, Cmax,
-                                         w.part_ml, w.part_acc, P, S + score_chunks(st->n_coarse),
                                          score_chunks(bound)};
                 a.n_pseudo = want_pseudo ? 2 : 0;
             } else {
                 a.n_sub = want_pseudo ? 1 : 0;
                 a.pseudo[0] = PseudoArgs{nullptr, 0, C, nullptr, w.s, st->sizes, st->value_centroids, Cmax,
-                                         w.part_ml, w.part_acc, P, S, score_chunks(C)};
+                                         score_chunks(C)};
                 a.n_pseudo = want_pseudo ? 1 : 0;
             }
             a.Hq = p->n_q_heads;

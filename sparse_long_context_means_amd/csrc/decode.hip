@@ -484,57 +484,44 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int unit) {
 }
 
 // ---------------------------------------------------------------------------
-// Approximate term of every non-empty item of a chunk of 256 (one workgroup):
-// thread t takes item t's logits lambda_g = s_g log2(e) + log2(n) (base 2);
-// the chunk maximum M_g is the fixed reference, the weights 2^(lambda - M)
-// go to LDS, and row group (wave, rg) accumulates the value centroids of
-// items 64 wave + 4 u + rg (u < 16), whose loads are in flight from the start.
+// Approximate term of every non-empty item of a chunk of 256 items, folded
+// into the softmax state of the attend workgroup that owns the chunk.  Thread
+// t takes item t's logits lambda_g = s_g log2(e) + log2(n) (base 2) and, after
+// a workgroup maximum, its weights 2^(lambda - m) go to LDS (0 for absent or
+// empty items); the row groups then add the value centroids they loaded at
+// the start of the workgroup.
 // ---------------------------------------------------------------------------
 template <int G>
-constexpr int pseudo_lds_bytes() {
-    return (kScoreChunk * G + 4 * G + 4 * G * (kHeadDim + 1)) * 4;
+struct ChunkMeta {  // item c0 + tid of a chunk
+    float s[G];
+    int n, c;
+};
+
+template <int G>
+__device__ __forceinline__ void chunk_meta_issue(ChunkMeta<G>& cm, const PseudoArgs& a, int unit, int chunk, int n) {
+    const int c0 = chunk * kScoreChunk, i = c0 + threadIdx.x;
+    const int32_t* ids = a.ids ? a.ids + (size_t)unit * a.ids_stride : nullptr;
+    // absent items read item c0's row (weight 0)
+    cm.c = ids ? ids[i < n ? i : c0] : (i < n ? i : c0);
+    cm.n = i < n ? a.sizes[(size_t)unit * a.rows + cm.c] : 0;
+    const float* su = a.s + ((size_t)unit * a.rows + cm.c) * G;
+#pragma unroll
+    for (int g = 0; g < G; ++g) cm.s[g] = su[g];
 }
 
-template <typename T, int G>
-__device__ __forceinline__ void pseudo_chunk(const PseudoArgs& a, int unit, int chunk, char* lds) {
-    float (*s_w)[G] = reinterpret_cast<float (*)[G]>(lds);
-    float (*s_wmax)[G] = reinterpret_cast<float (*)[G]>(lds + kScoreChunk * G * 4);
-    float (*s_red)[G][kHeadDim + 1] = reinterpret_cast<float (*)[G][kHeadDim + 1]>(lds + (kScoreChunk + 4) * G * 4);
+// Weights and ids of the chunk to LDS.  The state's reference first moves to
+// max(m, M) (M = the chunk maximum per head; the reference is the same in
+// every row group while only chunks have been added), and the weights are
+// 2^(lambda - m) relative to it (0 for absent or empty items).  Ends with a
+// barrier.
+template <int G>
+__device__ __forceinline__ void chunk_weights(SoftState<G>& st, const ChunkMeta<G>& cm, float (*s_w)[G],
+                                              float (*s_wmax)[G]) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int rg = lane >> 4, li = lane & 15;
-    int n = a.n_items;
-    if (a.n_items_dev) n = min(n, a.n_items_dev[unit * 4]);
-    const int slot = a.part_base + chunk;
-    const int c0 = chunk * kScoreChunk;
-    const int32_t* ids = a.ids ? a.ids + (size_t)unit * a.ids_stride : nullptr;
-    const float* su = a.s + (size_t)unit * a.rows * G;
-    const int32_t* szu = a.sizes + (size_t)unit * a.rows;
-
-    // value centroid rows of this row group (absent items read item c0)
-    const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.rows * kHeadDim + li * 8;
-    const int ib = c0 + wave * 64;
-    Slice8<T> vrow[16];
-    if (c0 < n) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int i = ib + u * 4 + rg;
-            const int c = i < n ? (ids ? ids[i] : i) : (ids ? ids[c0] : c0);
-            vrow[u].load(vb + (size_t)c * kHeadDim);
-        }
-    }
-    // logits of item c0 + tid
     float lg[G];
-    {
-        const int i = c0 + tid;
-        int nn = 0, c = 0;
-        if (i < n) {
-            c = ids ? ids[i] : i;
-            nn = szu[c];
-        }
-        const float l2n = log2_count(nn > 0 ? nn : 1);
+    const float l2n = log2_count(cm.n > 0 ? cm.n : 1);
 #pragma unroll
-        for (int g = 0; g < G; ++g) lg[g] = nn > 0 ? fmaf(su[(size_t)c * G + g], kLog2e, l2n) : -INFINITY;
-    }
+    for (int g = 0; g < G; ++g) lg[g] = cm.n > 0 ? fmaf(cm.s[g], kLog2e, l2n) : -INFINITY;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         float m = lg[g];
@@ -543,67 +530,28 @@ __device__ __forceinline__ void pseudo_chunk(const PseudoArgs& a, int unit, int 
         if (lane == 0) s_wmax[wave][g] = m;
     }
     __syncthreads();
-    float M[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        M[g] = fmaxf(fmaxf(s_wmax[0][g], s_wmax[1][g]), fmaxf(s_wmax[2][g], s_wmax[3][g]));
-        s_w[tid][g] = lg[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[g] - M[g]);
+        const float M = fmaxf(fmaxf(s_wmax[0][g], s_wmax[1][g]), fmaxf(s_wmax[2][g], s_wmax[3][g]));
+        if (M > st.m[g]) {
+            const float sc = __builtin_amdgcn_exp2f(st.m[g] - M);
+            st.l[g] *= sc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
+            st.m[g] = M;
+        }
+        s_w[tid][g] = lg[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[g] - st.m[g]);
     }
     __syncthreads();
-    float l[G], acc[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-    }
-    if (c0 < n) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int r = wave * 64 + u * 4 + rg;
-            float x[8];
-            vrow[u].unpack(x);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float w = s_w[r][g];
-                l[g] += w;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(w, x[e], acc[g][e]);
-            }
-        }
-    }
-    // same reference everywhere: plain sums over row groups, then waves
-#pragma unroll
-    for (int step = 16; step <= 32; step <<= 1)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            l[g] += shfl_xor_f(l[g], step);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] += shfl_xor_f(acc[g][e], step);
-        }
-    if (rg == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = acc[g][e];
-            if (li == 0) s_red[wave][g][kHeadDim] = l[g];
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < G * kHeadDim; e += 256) {
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        const float sum = (s_red[0][g][dd] + s_red[1][g][dd]) + (s_red[2][g][dd] + s_red[3][g][dd]);
-        const size_t pidx = part_index(unit, G, g, a.part_stride, slot);
-        a.part_acc[pidx * kHeadDim + dd] = sum;
-        if (dd == 0) {
-            a.part_ml[pidx * 2] = M[g];
-            a.part_ml[pidx * 2 + 1] =
-                (s_red[0][g][kHeadDim] + s_red[1][g][kHeadDim]) + (s_red[2][g][kHeadDim] + s_red[3][g][kHeadDim]);
-        }
-    }
 }
 
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs sa) { select_unit(sa, blockIdx.x); }
+
+template <typename T>
+struct RowBuf {
+    Slice8<T> k[2], v[2];
+    bool ok[2];
+};
 
 // ---------------------------------------------------------------------------
 // attend: workgroup (split, unit), 4 waves, 16 lanes per row, 8 dims a lane.
@@ -618,12 +566,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs sa) { select_uni
 constexpr int kAttCap = 512;   // staged exact rows per pass
 constexpr int kAttDepth = 2;   // row steps in flight per wave
 constexpr int kSpec = 256;     // selection entries staged before the counts are known
-
-template <typename T>
-struct RowBuf {
-    Slice8<T> k[2], v[2];
-    bool ok[2];
-};
 
 // Loads rows it * 32 + wave * 8 + u * 4 + rg (u = 0, 1) of a staged list.
 template <typename T>
@@ -694,6 +636,8 @@ __device__ __forceinline__ void load_sub(SubBuf<T, G>& sb, const SubSrc& ss, con
 
 template <int G>
 constexpr int attend_lds_bytes() {
+    // the chunk weights and their maxima alias the final reduction area
+    static_assert(4 * (kHeadDim + 2) >= kScoreChunk + 4, "chunk weights must fit the reduction area");
     return (kAttCap + (kListCap + 1) + 2 * kListCap + 4 * G * (kHeadDim + 2)) * 4;
 }
 
@@ -705,6 +649,8 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
     int32_t* s_off = s_pre + kListCap + 1;
     int32_t* s_ids = s_off + kListCap;
     float (*s_red)[G][kHeadDim + 2] = reinterpret_cast<float (*)[G][kHeadDim + 2]>(s_ids + kListCap);
+    float (*s_w)[G] = reinterpret_cast<float (*)[G]>(&s_red[0][0][0]);
+    float (*s_wmax)[G] = s_w + kScoreChunk;
 
     const int S = a.S;
     const int tid = threadIdx.x;
@@ -712,6 +658,42 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
     const int rg = lane >> 4, li = lane & 15;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
     const float qscale = kInvSqrtD * kLog2e;
+
+    // approximate-term chunk of this split: chunk s over the sources (the
+    // launcher makes S >= the number of chunks)
+    int n_chunks = 0;
+    for (int k = 0; k < a.n_pseudo; ++k) n_chunks += a.pseudo[k].chunks;
+    auto locate = [&](int cg, int& k, int& ch) {
+        k = 0;
+        ch = cg;
+        while (k + 1 < a.n_pseudo && ch >= a.pseudo[k].chunks) ch -= a.pseudo[k++].chunks;
+    };
+    auto items_of = [&](const PseudoArgs& ps) {
+        return ps.n_items_dev ? min(ps.n_items, ps.n_items_dev[unit * 4]) : ps.n_items;
+    };
+    int rk = 0, rch = 0, rn = 0;
+    bool has_chunk = false;
+    ChunkMeta<G> cm;
+    Slice8<T> pv[16];  // value centroids of items 64 wave + 4 u + rg of the chunk
+    if (split < n_chunks) {
+        locate(split, rk, rch);
+        const PseudoArgs& ps = a.pseudo[rk];
+        rn = items_of(ps);
+        has_chunk = rch * kScoreChunk < rn;
+        if (has_chunk) {
+            // loads first: they are in flight while the selection is staged
+            const int c0 = rch * kScoreChunk;
+            const int32_t* pids = ps.ids ? ps.ids + (size_t)unit * ps.ids_stride : nullptr;
+            const T* vb = reinterpret_cast<const T*>(ps.vbar) + (size_t)unit * ps.rows * kHeadDim + li * 8;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int i = c0 + wave * 64 + u * 4 + rg;
+                const int ii = i < rn ? i : c0;  // absent items read item c0 (weight 0)
+                pv[u].load(vb + (size_t)(pids ? pids[ii] : ii) * kHeadDim);
+            }
+            chunk_meta_issue<G>(cm, ps, unit, rch, rn);
+        }
+    }
 
     // selection of the unit: member-row prefix, first member and id of each
     // selected cluster.  The first kSpec entries load beside the counts.
@@ -739,10 +721,6 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
     const int32_t* off = staged ? s_off : goff;
     const int32_t* sids = staged ? s_ids : gids;
     const int e0 = (int)((int64_t)E * split / S), e1 = (int)((int64_t)E * (split + 1) / S);
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
-    QSlice<T> qs[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
     SoftState<G> st;
     st.init();
     const size_t ubase = (size_t)unit * a.Nmax * kHeadDim + li * 8;
@@ -750,6 +728,34 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
     const T* Vx = reinterpret_cast<const T*>(a.Vx) + ubase;
     const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
     __syncthreads();
+
+    // ---- the chunk's approximate terms: weights to LDS, then the rows ------
+    if (has_chunk) {
+        chunk_weights<G>(st, cm, s_w, s_wmax);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            float x[8];
+            pv[u].unpack(x);
+            const int r = wave * 64 + u * 4 + rg;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float w = s_w[r][g];
+                st.l[g] += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+            }
+        }
+    }
+    // ---- the first batch of exact rows ------------------------------------
+    int c0 = e0, cnt = min(kAttCap, e1 - e0);
+    if (cnt > 0) stage_exact(s_row, pre, off, nsel, tids, c0, cnt);
+    else if (tid == 0) s_row[0] = tids ? tids[0] : 0;  // masked ring steps read a valid row
+    __syncthreads();
+
+    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
+    QSlice<T> qs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
 
     // ---- removals of the first list, first step: loads issued first -------
     SubBuf<T, G> sub;
@@ -762,25 +768,17 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
     const bool sub_pending = a.n_sub > 0 && sk0 < sk1;
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- exact rows of selected clusters -------------------------------
-    // Batches of kAttCap staged rows, each streamed through a ring of D
-    // steps in flight.  The ring loop has no branches, so the compiler's
-    // wait counts stay exact: steps past the end load a valid row (staged
-    // row 0) and are masked out.  The removal data is consumed once the
-    // first batch's loads are out, so it is dead inside the ring loop.
+    // ---- exact rows through a ring of D steps in flight.  The loop body has
+    //      no branches, so the compiler's wait counts stay exact: steps past
+    //      the end load a valid row (staged row 0) and are masked out. ------
     RowBuf<T> ring[D];
-    int c0 = e0, cnt = min(kAttCap, e1 - e0);
-    if (c0 < e1) {
-        stage_exact(s_row, pre, off, nsel, tids, c0, cnt);
-        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int j = 0; j < D; ++j) {
+        load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx);
+        __builtin_amdgcn_sched_barrier(0);
     }
     if (sub_pending) absorb2<T, G, true>(st, sub.lg, sub.v);
-    while (c0 < e1) {
+    {
         const int steps = (cnt + 31) / 32;
         for (int it = 0; it < steps; it += D) {
 #pragma unroll
@@ -790,15 +788,24 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order: no load sinks
             }
         }
-        c0 += kAttCap;
-        if (c0 < e1) {
-            cnt = min(kAttCap, e1 - c0);
-            __syncthreads();
-            stage_exact(s_row, pre, off, nsel, tids, c0, cnt);
-            __syncthreads();
+    }
+    // ---- further batches of exact rows ------------------------------------
+    for (c0 += kAttCap; c0 < e1; c0 += kAttCap) {
+        cnt = min(kAttCap, e1 - c0);
+        __syncthreads();
+        stage_exact(s_row, pre, off, nsel, tids, c0, cnt);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int steps = (cnt + 31) / 32;
+        for (int it = 0; it < steps; it += D) {
 #pragma unroll
             for (int j = 0; j < D; ++j) {
-                load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx);
+                exact_step<T, G>(st, qs, qscale, ring[j]);
+                load_rows<T>(ring[j], s_row, cnt, it + j + D, wave, rg, Kx, Vx);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -837,31 +844,19 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
             absorb2<T, G, true>(st, sub.lg, sub.v);
         }
     }
+    __syncthreads();  // the chunk staging (aliasing the reduction area) is consumed
     finish_partial<G>(st, s_red, a.part_ml, a.part_acc, unit, split, a.part_stride);
 }
 
-// Workgroup (x, unit): x < S attends split x; the other columns add the
-// approximate terms of every non-empty cluster, one chunk of 256 each, for the
-// sources in a.pseudo (the coarse level, then the fine level).  The
-// approximate term does not depend on the cut, so it streams beside the exact
-// rows.
+// Workgroup (split, unit).  The approximate term does not depend on the cut:
+// split s also streams chunk s of the sources in a.pseudo (the coarse level,
+// then the fine level; S is at least their chunk count) and folds it into its
+// state.  The bf16 variants with up to 4 query heads per group are held to
+// 128 registers so that 4 workgroups fit on a CU.
 template <typename T, int G>
-__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
-    constexpr int kLds = attend_lds_bytes<G>() > pseudo_lds_bytes<G>() ? attend_lds_bytes<G>() : pseudo_lds_bytes<G>();
-    __shared__ __align__(16) char lds[kLds];
-    const int x = blockIdx.x, unit = blockIdx.y;
-    if (x < a.S) {
-        attend_split<T, G>(a, x, unit, lds);
-        return;
-    }
-    int c = x - a.S;
-    for (int k = 0; k < a.n_pseudo; ++k) {
-        if (c < a.pseudo[k].chunks) {
-            pseudo_chunk<T, G>(a.pseudo[k], unit, c, lds);
-            return;
-        }
-        c -= a.pseudo[k].chunks;
-    }
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && G <= 4) ? 4 : 1) void attend_kernel(AttendArgs a) {
+    __shared__ __align__(16) char lds[attend_lds_bytes<G>()];
+    attend_split<T, G>(a, blockIdx.x, blockIdx.y, lds);
 }
 
 // merge: one 128-thread workgroup per (unit, query head of the group) over the
@@ -944,14 +939,13 @@ hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipSt
     if (a.S < 1 || a.S > a.part_stride || a.n_sub < 0 || a.n_sub > 2 || a.sel_stride < 1) return hipErrorInvalidValue;
     if (a.n_sub > 0 && a.sa.ids_stride != a.sel_stride) return hipErrorInvalidValue;
     if (a.n_pseudo < 0 || a.n_pseudo > 2) return hipErrorInvalidValue;
-    // pseudo workgroups are laid out as columns S, S + 1, ... of the (x, unit) grid
-    int cols = 0;
+    int chunks = 0;
     for (int k = 0; k < a.n_pseudo; ++k) {
-        const PseudoArgs& p = a.pseudo[k];
-        if (p.chunks != score_chunks(p.n_items) || p.part_base + p.chunks > p.part_stride) return hipErrorInvalidValue;
-        cols += p.chunks;
+        if (a.pseudo[k].chunks != score_chunks(a.pseudo[k].n_items)) return hipErrorInvalidValue;
+        chunks += a.pseudo[k].chunks;
     }
-    dim3 grid(a.S + cols, units);
+    if (chunks > a.S) return hipErrorInvalidValue;  // one chunk per split at most
+    dim3 grid(a.S, units);
     return dtype == 1 ? attend_dispatch<bf16_t>(G, a, grid, st) : attend_dispatch<float>(G, a, grid, st);
 }
 

@@ -99,8 +99,8 @@ struct SelectArgs {
     int32_t* dbg_selected;       // optional [U][dbg_stride] by cluster id
     int32_t dbg_stride;
 };
-// Approximate term of every non-empty item, one partial per chunk of 256
-// items: chunk j of a unit writes slot part_base + j of part_stride.
+// Approximate term of every non-empty item, streamed by the attend launch in
+// chunks of 256 items.
 struct PseudoArgs {
     const int32_t* ids;          // optional [U][ids_stride]: cluster id per item
     int32_t ids_stride;
@@ -110,9 +110,6 @@ struct PseudoArgs {
     const int32_t* sizes;        // [U][rows]
     const void* vbar;            // [U][rows][d]
     int32_t rows;
-    float* part_ml;              // [U][G][part_stride][2]
-    float* part_acc;             // [U][G][part_stride][d]
-    int32_t part_stride, part_base;
     int32_t chunks;              // score_chunks(n_items)
 };
 // Budget cut of every unit (one workgroup each).
@@ -145,7 +142,7 @@ struct AttendArgs {
     int32_t n_sub;               // lists removed (0, 1 or 2)
     SubSrc sa, sb;
     int32_t Hq, Hkv, S;
-    int32_t n_pseudo;            // approximate-term sources streamed in the same launch (0 .. 2)
+    int32_t n_pseudo;            // approximate-term sources, spread over the splits (0 .. 2)
     PseudoArgs pseudo[2];
     float* part_ml;              // [U][G][part_stride][2], slots 0 .. S-1
     float* part_acc;             // [U][G][part_stride][d]
