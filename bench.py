@@ -206,10 +206,17 @@ def main():
 
     steps_idx = range(args.warmup, args.warmup + args.steps)
     byts = np.array([sum(bytes_of(s)) for s in steps_idx], dtype=np.float64)
-    att_bytes = np.array([bytes_of(s)[1] for s in steps_idx], dtype=np.float64)
+    # dominant kernel: the per-unit kernel (the whole step but the merge) or
+    # the split attend kernel
+    if "unit" in stage_names:
+        dom = "unit"
+        att_bytes = np.array([sum(bytes_of(s)) - B * Hq * d * 4 for s in steps_idx], dtype=np.float64)
+    else:
+        dom = "attend"
+        att_bytes = np.array([bytes_of(s)[1] for s in steps_idx], dtype=np.float64)
     cold_us = float(step_ms.mean() * 1e3)
     eff_gbps = float((byts / (step_ms * 1e-3)).mean() / 1e9)
-    att_k = stage_names.index("attend")
+    att_k = stage_names.index(dom)
     att_ms = stage_ms[:, att_k]
     att_gbps = float(att_bytes.mean() / (att_ms.mean() * 1e-3) / 1e9)
     log(f"[bench] cold {cold_us:.1f} us/step  warm {warm_us:.1f} us/step  "
@@ -280,7 +287,7 @@ def main():
         "timed_wall_ms_incl_cache_flush": round(wall_ms, 2),
         "build_ms": round(build_ms, 2),
         "build_assign_TFLOPs_lower_bound": round(assign_flop / (build_ms * 1e-3) / 1e12, 1),
-        "roofline": {"bound": "hbm", "kernel": "attend", "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},

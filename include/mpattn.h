@@ -79,7 +79,8 @@ typedef struct mpattn_params {
                                            ceil(L / this) coarse clusters (default 128) */
     int32_t coarse_iters;               /* weighted Lloyd rounds of the coarse level, >= 1 (default 10) */
     int32_t coarse_candidate_tokens;    /* hierarchical decode: token budget of the coarse candidates */
-    int32_t splits;                     /* decode work splits per unit; 0 = chosen by the library */
+    int32_t splits;                     /* decode work splits per unit; 0 = chosen by the library
+                                           (> 0 also selects the split launches of the flat method) */
     uint64_t seed;                      /* seeds the k-means initialisation */
 } mpattn_params;
 
@@ -208,9 +209,12 @@ mpattn_status mpattn_decode(const mpattn_params* params, const void* q, const vo
                             int32_t mode, float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of kernel stages one decode enqueues (for timing stage by stage):
- * 4 for the flat method (score, select, attend, merge), 6 for the
- * hierarchical one (coarse_score, coarse_select, fine_score, fine_select,
- * attend, merge). */
+ * 6 for the hierarchical method (coarse_score, coarse_select, fine_score,
+ * fine_select, attend, merge); for the flat method 2 (unit, merge) when the
+ * whole step of a unit runs in one workgroup -- bf16 storage, splits = 0, at
+ * least 64 units and at most 4096 clusters per unit -- else 4 (score,
+ * select, attend, merge).  Both forms compute the same cut and, up to fp32
+ * summation order, the same output. */
 int32_t mpattn_decode_stage_count(const mpattn_params* params);
 
 /* Name of decode stage i (static storage), NULL if out of range. */

@@ -10,6 +10,8 @@
 
 using namespace mpa;
 
+extern "C" int32_t mpattn_max_clusters(const mpattn_params* p);
+
 namespace {
 
 constexpr int kD = 128;
@@ -185,6 +187,15 @@ mpattn_status run_blocks(const mpattn_params* p, const void* k, const void* v, m
 }
 
 const char* kFlatStages[] = {"score", "select", "attend", "merge"};
+const char* kUnitStages[] = {"unit", "merge"};
+
+// The whole flat decode step of a unit in one workgroup (unit.hip) when the
+// batch has enough units to fill the GPU and the split count is automatic.
+bool unit_path(const mpattn_params* p) {
+    if (is_hier(p) || p->splits > 0 || p->dtype != MPATTN_BF16) return false;
+    const int G = p->n_q_heads / p->n_kv_heads;
+    return unit_path_fits(p->dtype, G, mpattn_max_clusters(p)) && p->batch * p->n_kv_heads >= 64;
+}
 const char* kHierStages[] = {"coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"};
 
 }  // namespace
@@ -290,13 +301,13 @@ mpattn_status mpattn_update_window(const mpattn_params* p, const void* k, const 
 
 int32_t mpattn_decode_stage_count(const mpattn_params* p) {
     if (check_params(p) != MPATTN_OK) return 0;
-    return is_hier(p) ? 6 : 4;
+    return is_hier(p) ? 6 : unit_path(p) ? 2 : 4;
 }
 
 const char* mpattn_decode_stage_name(const mpattn_params* p, int32_t stage) {
     const int32_t n = mpattn_decode_stage_count(p);
     if (stage < 0 || stage >= n) return nullptr;
-    return is_hier(p) ? kHierStages[stage] : kFlatStages[stage];
+    return is_hier(p) ? kHierStages[stage] : unit_path(p) ? kUnitStages[stage] : kFlatStages[stage];
 }
 
 mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void* k, const void* v,
@@ -316,7 +327,7 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     if (st->capacity_clusters > kMaxDecodeClusters || st->capacity_coarse > kMaxDecodeClusters)
         return MPATTN_ERR_UNSUPPORTED;
     if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
-    const int32_t n_stages = hier ? 6 : 4;
+    const int32_t n_stages = mpattn_decode_stage_count(p);
     if (first_stage < 0 || last_stage >= n_stages || first_stage > last_stage) return MPATTN_ERR_INVALID_ARG;
     const DecodeWs need = layout_decode(p, st->capacity_clusters, st->capacity_coarse, nullptr);
     if (!workspace || workspace_bytes < need.bytes) return MPATTN_ERR_WORKSPACE;
@@ -336,6 +347,46 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const int32_t want_pseudo = mode == MPATTN_MODE_MULTIPOLE ? 1 : 0;
     const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
     const int32_t P = S;  // partial slots: one per attend split
+
+    if (unit_path(p)) {
+        const int R = unit_replicas(C);
+        if (R > S) return MPATTN_ERR_WORKSPACE;
+        for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
+            if (stage == 0) {
+                UnitArgs a{};
+                a.q = q;
+                a.kbar = st->key_centroids;
+                a.vbar = st->value_centroids;
+                a.sizes = st->sizes;
+                a.offsets = st->offsets;
+                a.Kx = sorted ? st->sorted_keys : k;
+                a.Vx = sorted ? st->sorted_values : v;
+                a.token_ids = sorted ? nullptr : st->token_ids;
+                a.K = k;
+                a.V = v;
+                a.Cmax = Cmax;
+                a.C = C;
+                a.Nmax = N;
+                a.n_clustered = st->n_clustered;
+                a.n_total = n_tokens_total;
+                a.budget = token_budget;
+                a.pseudo = want_pseudo;
+                a.Hq = p->n_q_heads;
+                a.Hkv = p->n_kv_heads;
+                a.out = out;
+                a.part_ml = w.part_ml;
+                a.part_acc = w.part_acc;
+                a.part_stride = R;
+                a.dbg_scores = debug ? debug->scores : nullptr;
+                a.dbg_selected = debug ? debug->selected : nullptr;
+                a.dbg_exact = debug ? debug->exact_tokens : nullptr;
+                MPA_TRY(launch_unit_decode(p->dtype, G, a, U, R, s));
+            } else if (R > 1) {
+                MPA_TRY(launch_merge(w.part_ml, w.part_acc, U, G, R, p->n_kv_heads, out, s));
+            }
+        }
+        return MPATTN_OK;
+    }
 
     for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
         const char* name = hier ? kHierStages[stage] : kFlatStages[stage];

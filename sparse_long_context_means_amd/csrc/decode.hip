@@ -41,108 +41,11 @@
 // costs far more than a launch on this chip.
 #include <math.h>
 
+#include "attn.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace mpa {
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0;  // -0 ranks as +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ int wave_exclusive_sum(int v, int& total) {
-    const int inc = wave_inclusive_sum(v);
-    total = lane_value(inc, kWave - 1);
-    return inc - v;
-}
-
-// Largest k with pre[k] <= x, for pre[0] = 0 <= x < pre[n] (n >= 1).
-__device__ __forceinline__ int upper_index(const int32_t* pre, int n, int x) {
-    int lo = 0, hi = n;  // pre[lo] <= x < pre[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] <= x) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
-
-// log2 of a positive count, as both the adding and the removing side take it.
-__device__ __forceinline__ float log2_count(int n) { return __builtin_amdgcn_logf((float)n); }
-
-// ---------------------------------------------------------------------------
-// Online softmax state of a 16-lane row group: per query head g the reference
-// exponent m, the sum l of 2^(logit - m) and the weighted value sum acc (the
-// lane's 8 dimensions).  The reference is only raised when a logit exceeds it
-// by more than 2^8 (every weight stays <= 256 in fp32), so rescaling is rare.
-// ---------------------------------------------------------------------------
-constexpr float kLazyMax = 8.0f;
-
-template <int G>
-struct SoftState {
-    float m[G], l[G], acc[G][8];
-    __device__ __forceinline__ void init() {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            m[g] = -INFINITY;
-            l[g] = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-        }
-    }
-};
-
-// Adds (NEG: removes) 2 rows with base-2 logits lg[u][g] (-inf: absent row).
-template <typename T, int G, bool NEG>
-__device__ __forceinline__ void absorb2(SoftState<G>& st, const float (&lg)[2][G], const Slice8<T> (&v)[2]) {
-    float x0[8], x1[8];
-    v[0].unpack(x0);
-    v[1].unpack(x1);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float mx = fmaxf(lg[0][g], lg[1][g]);
-        if (mx == -INFINITY) continue;
-        if (mx > st.m[g] + kLazyMax) {  // rare: raise the reference
-            const float sc = __builtin_amdgcn_exp2f(st.m[g] - mx);
-            st.l[g] *= sc;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st.acc[g][e] *= sc;
-            st.m[g] = mx;
-        }
-        float p0 = __builtin_amdgcn_exp2f(lg[0][g] - st.m[g]);
-        float p1 = __builtin_amdgcn_exp2f(lg[1][g] - st.m[g]);
-        if (NEG) {
-            p0 = -p0;
-            p1 = -p1;
-        }
-        st.l[g] += p0 + p1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(p1, x1[e], fmaf(p0, x0[e], st.acc[g][e]));
-    }
-}
-
-// Merge another partial state (om, ol, oacc) into st.
-template <int G>
-__device__ __forceinline__ void merge_state(SoftState<G>& st, const float* om, const float* ol, const float (*oacc)[8]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float M = fmaxf(st.m[g], om[g]);
-        if (M == -INFINITY) continue;
-        const float wa = __builtin_amdgcn_exp2f(st.m[g] - M);
-        const float wb = __builtin_amdgcn_exp2f(om[g] - M);
-        st.l[g] = st.l[g] * wa + ol[g] * wb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[g][e] = st.acc[g][e] * wa + oacc[g][e] * wb;
-        st.m[g] = M;
-    }
-}
-
-// Partial (m, l, acc) of query head g of a unit in slot `slot` of P.
-__device__ __forceinline__ size_t part_index(int unit, int G, int g, int P, int slot) {
-    return ((size_t)unit * G + g) * P + slot;
-}
 
 // Combines the 16 row groups of a 256-thread workgroup (4 per wave through
 // lane shuffles, then the 4 waves through LDS, in wave order) and writes the
@@ -202,13 +105,15 @@ __device__ __forceinline__ void finish_partial(SoftState<G>& st, float (*s_red)[
 
 // ---------------------------------------------------------------------------
 // score: workgroup (chunk, unit) scores 256 items, 16 lanes per centroid row,
-// 16 rows per lane group in flight (8 in fp32, two passes).  Items are
+// 16 rows per lane group in flight (8 in fp32, two passes); row group (wave,
+// rg) takes items 16 u + 4 wave + rg, so the waves read one interleaved
+// stream (separate per-wave streams cost HBM efficiency).  Items are
 // cluster ids, or the member rows of a previous selection (the fine clusters
 // inside the coarse candidates of the two-level method).  Thread t writes the
 // cut record of item t of the chunk (its fields load at the start; the key
 // comes through LDS).
 // ---------------------------------------------------------------------------
-constexpr int kScoreChunk = 256;  // items per workgroup (64 per wave)
+constexpr int kScoreChunk = 256;  // items per workgroup
 constexpr int kListCap = 1024;    // selection-list entries staged in LDS
 
 template <typename T, int G>
@@ -222,7 +127,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, li = lane & 15;
     const int c0 = blockIdx.x * kScoreChunk;
-    const int i0 = c0 + wave * 64;
+    const int i0 = c0 + wave * 4;  // the waves interleave by 4 items: one stream per workgroup
     if (c0 >= n) return;  // uniform across the workgroup
 
     // items through a selection list: stage its member-row prefix
@@ -273,20 +178,20 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         constexpr int R = sizeof(T) == 2 ? 16 : 8;
 #pragma unroll 1
         for (int pass = 0; pass < 16 / R; ++pass) {
-            const int ib = i0 + pass * 4 * R;
+            const int ib = i0 + pass * 16 * R;
             if (ib >= n) break;  // uniform across the wave
             int cid[R];
             Slice8<T> row[R];
 #pragma unroll
             for (int u = 0; u < R; ++u) {
-                const int i = ib + u * 4 + rg;
+                const int i = ib + u * 16 + rg;
                 cid[u] = item_id(i < n ? i : ib);
             }
 #pragma unroll
             for (int u = 0; u < R; ++u) row[u].load(cu + (size_t)cid[u] * kHeadDim);
 #pragma unroll
             for (int u = 0; u < R; ++u) {
-                const int i = ib + u * 4 + rg;
+                const int i = ib + u * 16 + rg;
                 float sg[G];
                 float r = 0.f;
 #pragma unroll
@@ -547,12 +452,6 @@ __device__ __forceinline__ void chunk_weights(SoftState<G>& st, const ChunkMeta<
 
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs sa) { select_unit(sa, blockIdx.x); }
 
-template <typename T>
-struct RowBuf {
-    Slice8<T> k[2], v[2];
-    bool ok[2];
-};
-
 // ---------------------------------------------------------------------------
 // attend: workgroup (split, unit), 4 waves, 16 lanes per row, 8 dims a lane.
 // Each row group keeps its own softmax state over the rows it visits, 2 rows
@@ -566,47 +465,6 @@ struct RowBuf {
 constexpr int kAttCap = 512;   // staged exact rows per pass
 constexpr int kAttDepth = 2;   // row steps in flight per wave
 constexpr int kSpec = 256;     // selection entries staged before the counts are known
-
-// Loads rows it * 32 + wave * 8 + u * 4 + rg (u = 0, 1) of a staged list.
-template <typename T>
-__device__ __forceinline__ void load_rows(RowBuf<T>& bf, const int32_t* s_row, int cnt, int it, int wave, int rg,
-                                          const T* Kx, const T* Vx) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = it * 32 + wave * 8 + u * 4 + rg;
-        bf.ok[u] = i < cnt;
-        const int r = s_row[bf.ok[u] ? i : 0];
-        bf.k[u].load(Kx + (size_t)r * kHeadDim);
-        bf.v[u].load(Vx + (size_t)r * kHeadDim);
-    }
-}
-
-template <typename T, int G>
-__device__ __forceinline__ void exact_step(SoftState<G>& st, const QSlice<T> (&qs)[G], float qscale,
-                                           const RowBuf<T>& bf) {
-    float lg[2][G];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float d = row16_sum(dot8(qs[g], bf.k[u])) * qscale;
-            lg[u][g] = bf.ok[u] ? d : -INFINITY;
-        }
-    absorb2<T, G, false>(st, lg, bf.v);
-}
-
-// Stages exact rows [c0, c0 + cnt) of the unit's selection: row i belongs to
-// selected cluster k with pre[k] <= i < pre[k + 1] and sits at member position
-// off[k] + i - pre[k] (through token ids when rows are gathered from K/V).
-__device__ __forceinline__ void stage_exact(int32_t* s_row, const int32_t* pre, const int32_t* off, int nsel,
-                                            const int32_t* tids, int c0, int cnt) {
-    for (int i = threadIdx.x; i < cnt; i += 256) {
-        const int r = c0 + i;
-        const int k = upper_index(pre, nsel, r);
-        const int pos = off[k] + r - pre[k];
-        s_row[i] = tids ? tids[pos] : pos;
-    }
-}
 
 // Removal data of 2 selected clusters per row group: list entries base + 4 u
 // + rg (u = 0, 1) of [k0, k1).
@@ -674,7 +532,7 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
     int rk = 0, rch = 0, rn = 0;
     bool has_chunk = false;
     ChunkMeta<G> cm;
-    Slice8<T> pv[16];  // value centroids of items 64 wave + 4 u + rg of the chunk
+    Slice8<T> pv[16];  // value centroids of chunk items 16 u + 4 wave + rg
     if (split < n_chunks) {
         locate(split, rk, rch);
         const PseudoArgs& ps = a.pseudo[rk];
@@ -687,7 +545,7 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
             const T* vb = reinterpret_cast<const T*>(ps.vbar) + (size_t)unit * ps.rows * kHeadDim + li * 8;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                const int i = c0 + wave * 64 + u * 4 + rg;
+                const int i = c0 + u * 16 + wave * 4 + rg;
                 const int ii = i < rn ? i : c0;  // absent items read item c0 (weight 0)
                 pv[u].load(vb + (size_t)(pids ? pids[ii] : ii) * kHeadDim);
             }
@@ -736,7 +594,7 @@ __device__ __forceinline__ void attend_split(const AttendArgs& a, int split, int
         for (int u = 0; u < 16; ++u) {
             float x[8];
             pv[u].unpack(x);
-            const int r = wave * 64 + u * 4 + rg;
+            const int r = u * 16 + wave * 4 + rg;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float w = s_w[r][g];

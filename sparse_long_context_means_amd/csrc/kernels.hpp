@@ -153,6 +153,36 @@ hipError_t launch_attend(int dtype, int G, const AttendArgs& a, int units, hipSt
 hipError_t launch_merge(const float* part_ml, const float* part_acc, int units, int G, int P, int Hkv,
                         float* out, hipStream_t st);
 
+// ---- whole decode step per unit (unit.hip) ---------------------------------
+struct UnitArgs {
+    const void* q;               // [B][Hq][d]
+    const void* kbar;            // [U][Cmax][d]
+    const void* vbar;            // [U][Cmax][d]
+    const int32_t* sizes;        // [U][Cmax]
+    const int32_t* offsets;      // [U][Cmax + 1]
+    const void* Kx;              // exact-row source: sorted copy or K
+    const void* Vx;
+    const int32_t* token_ids;    // non-null: member positions go through token ids
+    const void* K;               // tail rows
+    const void* V;
+    int32_t Cmax, C, Nmax, n_clustered, n_total, budget;
+    int32_t pseudo;              // 1: approximate unselected clusters; 0: omit them
+    int32_t Hq, Hkv;
+    float* out;                  // [B][Hq][d] when one replica
+    float* part_ml;              // [U][G][part_stride][2] when several
+    float* part_acc;             // [U][G][part_stride][d]
+    int32_t part_stride;
+    float* dbg_scores;           // optional [U][C][G]
+    int32_t* dbg_selected;       // optional [U][C]
+    int32_t* dbg_exact;          // optional [U]
+};
+// Fewest replicas (workgroups per unit) the per-unit path needs for C clusters.
+int unit_replicas(int n_clusters);
+// Whether the per-unit path supports this storage dtype, group size and
+// cluster capacity.
+bool unit_path_fits(int dtype, int G, int cmax);
+hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st);
+
 // ---- measurement (probe.hip) ----------------------------------------------
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 

@@ -1,0 +1,506 @@
+// unit.hip -- one Multipole Attention decode step of a (sequence, KV head)
+// unit in ONE 1024-thread workgroup (or R replicas of it).
+//
+// Pages: atlas.scime.ai summary, opening sentence (exact attention on the
+// top-scoring clusters, centroid attention for the rest) and "Approach"
+// (value centroids stand in for the unselected clusters); mlsanity.com paper
+// page, "Abstract (arXiv)" (centroids pick the important keys).
+//
+// Each replica scores every cluster of its unit and takes the budget cut in
+// LDS (the replicas compute the same keys with the same operations, so they
+// reach the same cut); replica r then attends its share of the work: the
+// approximate terms of clusters [C r / R, C (r + 1) / R) (selected clusters
+// skipped through the LDS bitmask) and exact rows [E r / R, E (r + 1) / R) of
+// the selected clusters, plus its share of the unclustered tail.  With R = 1
+// the workgroup writes the normalised output; otherwise one partial per
+// replica goes to the merge launch.  No cut record, score or selection list
+// leaves the workgroup, and there is no launch boundary between the steps.
+// This path is meant for batches with many units (one workgroup per CU);
+// the split launches in decode.hip serve the rest.
+#include <math.h>
+
+#include "attn.hpp"
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace mpa {
+
+constexpr int kUnitThreads = 512;
+constexpr int kUnitWaves = kUnitThreads / kWave;  // 8
+constexpr int kUnitTiles = 8;                     // cut items per thread
+constexpr int kUnitMaxC = kUnitTiles * kUnitThreads;  // clusters per unit
+constexpr int kUnitShare = 1024;                  // approximate-term clusters per replica
+constexpr int kUnitRowBatch = 1024;               // staged exact rows per pass
+constexpr int kUnitRowsPerWave = kUnitMaxC / kUnitWaves;    // scored clusters per wave
+constexpr int kUnitSharePerWave = kUnitShare / kUnitWaves;  // approximate-term clusters per wave
+
+// Exclusive workgroup scan of two counters; totals in tot.
+template <int NW>
+__device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int ix = wave_inclusive_sum(v.x), iy = wave_inclusive_sum(v.y);
+    if (lane == kWave - 1) {
+        lds[2 * wave] = ix;
+        lds[2 * wave + 1] = iy;
+    }
+    __syncthreads();
+    int bx = 0, by = 0, tx = 0, ty = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int p = lds[2 * w], q = lds[2 * w + 1];
+        if (w < wave) {
+            bx += p;
+            by += q;
+        }
+        tx += p;
+        ty += q;
+    }
+    __syncthreads();  // lds may be reused right after
+    tot = make_int2(tx, ty);
+    return make_int2(bx + ix - v.x, by + iy - v.y);
+}
+
+// LDS layout (bytes).  The final reduction of the waves' states reuses the
+// "big" region once the selection lists, weights and row stage are dead.
+template <int G>
+struct UnitLds {
+    static constexpr int key = 0;                                    // float [MaxC]
+    static constexpr int sz = key + kUnitMaxC * 4;                   // int [MaxC]: sizes
+    static constexpr int off = sz + kUnitMaxC * 4;                   // int [MaxC]: first member
+    static constexpr int rows = off + kUnitMaxC * 4;                 // int [MaxC]: member rows
+    static constexpr int hist = rows + kUnitMaxC * 4;                // int [4][256]
+    static constexpr int scan = hist + 4 * 256 * 4;                  // int [64]
+    static constexpr int mask = scan + 64 * 4;                       // uint32 [MaxC / 32]
+    static constexpr int misc = mask + (kUnitMaxC / 32) * 4;         // int [8]
+    static constexpr int gmax = misc + 8 * 4;                        // float [waves][G]
+    static constexpr int big = gmax + kUnitWaves * G * 4;
+    static constexpr int sid = big;                                  // int [MaxC]
+    static constexpr int soff = sid + kUnitMaxC * 4;                 // int [MaxC]
+    static constexpr int spre = soff + kUnitMaxC * 4;                // int [MaxC + 1]
+    static constexpr int lg = spre + (kUnitMaxC + 4) * 4;            // float [Share][G]
+    static constexpr int row = lg + kUnitShare * G * 4;              // int [RowBatch]
+    static constexpr int big_end = row + kUnitRowBatch * 4;
+    static constexpr int red_bytes = kUnitWaves * G * (kHeadDim + 2) * 4;
+    static constexpr int bytes = (big_end > big + red_bytes ? big_end : big + red_bytes);
+};
+
+constexpr int kUnitCutItems = kUnitMaxC / kUnitThreads;  // consecutive cut items per thread (8)
+constexpr int kScoreDepth = 4;                           // score steps in flight per wave
+constexpr int kPseudoDepth = 2;                          // value-centroid steps in flight per wave
+constexpr int kExactDepth = 4;                           // exact-row steps in flight per wave
+
+// Four rows of a row group (one ring step of the score or the value-centroid
+// stream).
+template <typename T>
+struct Rows4 {
+    Slice8<T> r[4];
+};
+
+template <typename T, int G>
+__global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
+    using L = UnitLds<G>;
+    __shared__ __align__(16) char lds[L::bytes];
+    float* s_key = reinterpret_cast<float*>(lds + L::key);
+    int32_t* s_sz = reinterpret_cast<int32_t*>(lds + L::sz);
+    int32_t* s_off = reinterpret_cast<int32_t*>(lds + L::off);
+    int32_t* s_rows = reinterpret_cast<int32_t*>(lds + L::rows);
+    int(*hist)[256] = reinterpret_cast<int(*)[256]>(lds + L::hist);
+    int* s_scan = reinterpret_cast<int*>(lds + L::scan);
+    uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + L::mask);
+    int* s_misc = reinterpret_cast<int*>(lds + L::misc);
+    float(*s_gmax)[G] = reinterpret_cast<float(*)[G]>(lds + L::gmax);
+    int32_t* s_sid = reinterpret_cast<int32_t*>(lds + L::sid);
+    int32_t* s_soff = reinterpret_cast<int32_t*>(lds + L::soff);
+    int32_t* s_spre = reinterpret_cast<int32_t*>(lds + L::spre);
+    float(*s_lg)[G] = reinterpret_cast<float(*)[G]>(lds + L::lg);
+    int32_t* s_row = reinterpret_cast<int32_t*>(lds + L::row);
+    float(*s_red)[G][kHeadDim + 2] = reinterpret_cast<float(*)[G][kHeadDim + 2]>(lds + L::big);
+
+    const int rep = blockIdx.x, unit = blockIdx.y, R = gridDim.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rg = lane >> 4, li = lane & 15;
+    const int C = a.C;
+    const int b = unit / a.Hkv, h = unit % a.Hkv;
+    const int32_t* szu = a.sizes + (size_t)unit * a.Cmax;
+    const int32_t* ofu = a.offsets + (size_t)unit * (a.Cmax + 1);
+    const int cs = (int)((int64_t)C * rep / R), ce = (int)((int64_t)C * (rep + 1) / R);  // approximate-term share
+
+    // ---- cluster records to LDS (sizes, first member, member rows) --------
+    for (int i = tid; i < C; i += kUnitThreads) {
+        const int o0 = ofu[i];
+        s_sz[i] = szu[i];
+        s_off[i] = o0;
+        s_rows[i] = ofu[i + 1] - o0;
+    }
+    for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
+    for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
+    __syncthreads();
+
+    // ---- scores through a ring of kScoreDepth steps: step s of wave w takes
+    //      clusters 128 s + 16 w + 4 u + rg (u < 4).  The ranking key goes to
+    //      LDS, the share's base-2 logits s log2(e) + log2(n) too.  The ring
+    //      body has no data-dependent branch (steps past the end load row 0
+    //      and store nothing), so the compiler's wait counts stay exact. ----
+    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
+    {
+        QSlice<T> qv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) qv[g].load(qb + (size_t)g * kHeadDim);
+        const T* cu = reinterpret_cast<const T*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+        // the waves interleave: one step of the workgroup reads 128
+        // consecutive clusters (32 KB), so the workgroup is a single stream
+        const int steps = (C + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
+        auto cluster = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
+        Rows4<T> ring[kScoreDepth];
+#pragma unroll
+        for (int j = 0; j < kScoreDepth; ++j) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = cluster(j, u);
+                ring[j].r[u].load(cu + (size_t)(i < C ? i : 0) * kHeadDim);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int it = 0; it < steps; it += kScoreDepth) {
+#pragma unroll
+            for (int j = 0; j < kScoreDepth; ++j) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = cluster(it + j, u);
+                    float sg[G];
+                    float r = 0.f;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        sg[g] = row16_sum(dot8(qv[g], ring[j].r[u])) * kInvSqrtD;
+                        r += sg[g];
+                    }
+                    r *= 1.0f / G;
+                    if (i < C) {
+                        float mine = sg[0];
+#pragma unroll
+                        for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
+                        if (li == 0) s_key[i] = r;
+                        if (li < G) {
+                            if (a.dbg_scores && rep == 0) a.dbg_scores[((size_t)unit * C + i) * G + li] = mine;
+                            if (i >= cs && i < ce) {
+                                const int n = s_sz[i];
+                                s_lg[i - cs][li] = n > 0 ? fmaf(mine, kLog2e, log2_count(n)) : -INFINITY;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = cluster(it + j + kScoreDepth, u);
+                    ring[j].r[u].load(cu + (size_t)(i < C ? i : 0) * kHeadDim);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- budget cut: four 8-bit radix passes over the keys (weights =
+    //      sizes), thread t owning items 8 t .. 8 t + 7; one workgroup scan
+    //      places the selected items in item order --------------------------
+    uint32_t key[kUnitCutItems];
+    int isz[kUnitCutItems];
+#pragma unroll
+    for (int j = 0; j < kUnitCutItems; ++j) {
+        const int i = tid * kUnitCutItems + j;
+        key[j] = i < C ? order_key(s_key[i]) : 0u;
+        isz[j] = i < C ? s_sz[i] : 0;
+    }
+    uint32_t prefix = 0, pmask = 0;
+    int Rb = a.budget;
+    bool done = false;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+#pragma unroll
+        for (int j = 0; j < kUnitCutItems; ++j)
+            if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
+        __syncthreads();
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = hist[p][255 - (4 * lane + j)];
+        int total;
+        int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
+        if (total <= Rb) {  // the same in every wave
+            done = true;
+            break;
+        }
+        int found = -1, cum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (found < 0 && run <= Rb && Rb < run + v[j]) {
+                found = 255 - (4 * lane + j);
+                cum = run;
+            }
+            run += v[j];
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = __ffsll((long long)bal) - 1;
+        const int digit = lane_value(found, src);
+        Rb -= lane_value(cum, src);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xFFu << shift;
+    }
+    const uint32_t tau = prefix;
+    uint32_t selbits = 0;
+    int s_local = 0, rows_local = 0;
+    {
+        int tie_local = 0;
+        if (!done) {
+#pragma unroll
+            for (int j = 0; j < kUnitCutItems; ++j)
+                if (isz[j] > 0 && key[j] == tau) tie_local += isz[j];
+        }
+        int run_tie = 0;
+        if (!done && __syncthreads_count(tie_local > 0) > 1) {  // uniform
+            int2 tt;
+            run_tie = block_exclusive_sum2<kUnitWaves>(make_int2(tie_local, 0), tt, s_scan).x;
+        }
+#pragma unroll
+        for (int j = 0; j < kUnitCutItems; ++j) {
+            bool sel;
+            if (done) {
+                sel = key[j] >= prefix;
+            } else {
+                const bool tie = key[j] == tau;
+                sel = key[j] > tau || (tie && run_tie + isz[j] <= Rb);
+                if (tie) run_tie += isz[j];
+            }
+            sel = sel && isz[j] > 0;
+            selbits |= (uint32_t)sel << j;
+            s_local += sel;
+            rows_local += sel ? s_rows[tid * kUnitCutItems + j] : 0;
+        }
+    }
+    int2 tot;
+    const int2 ex = block_exclusive_sum2<kUnitWaves>(make_int2(s_local, rows_local), tot, s_scan);
+    {
+        int k = ex.x, ro = ex.y;
+#pragma unroll
+        for (int j = 0; j < kUnitCutItems; ++j) {
+            const int i = tid * kUnitCutItems + j;
+            if ((selbits >> j) & 1u) {
+                s_sid[k] = i;
+                s_soff[k] = s_off[i];
+                s_spre[k] = ro;
+                ++k;
+                ro += s_rows[i];
+                atomicOr(&s_mask[i >> 5], 1u << (i & 31));
+            }
+            if (a.dbg_selected && rep == 0 && i < C) a.dbg_selected[(size_t)unit * C + i] = (selbits >> j) & 1u;
+        }
+    }
+    const int nsel = tot.x, E = tot.y;
+    if (tid == 0) {
+        s_spre[nsel] = E;
+        if (a.dbg_exact && rep == 0) a.dbg_exact[unit] = E;
+    }
+    __syncthreads();
+
+    // ---- approximate terms of the share (unselected, non-empty clusters):
+    //      the share maximum is the reference of every row group; the value
+    //      centroids stream through a ring of kPseudoDepth steps of 4 rows
+    //      (share items 128 s + 16 w + 4 u + rg) ----------------------------
+    SoftState<G> st;
+    st.init();
+    if (a.pseudo) {
+        float M[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float m = -INFINITY;
+            for (int t = tid; t < kUnitShare; t += kUnitThreads) {
+                const int c = cs + t;
+                if (c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u)) m = fmaxf(m, s_lg[t][g]);
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
+            if (lane == 0) s_gmax[wave][g] = m;
+        }
+        __syncthreads();
+        if (tid < G) {  // the share maximum of head tid
+            float m = s_gmax[0][tid];
+            for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][tid]);
+            s_misc[tid] = __float_as_int(m);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            M[g] = __int_as_float(s_misc[g]);
+            st.m[g] = M[g];
+        }
+        const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+        constexpr int kSteps = kUnitSharePerWave / 16;
+        auto item = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
+        Rows4<T> ring[kPseudoDepth];
+#pragma unroll
+        for (int j = 0; j < kPseudoDepth; ++j) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = cs + item(j, u);
+                ring[j].r[u].load(vb + (size_t)(c < ce ? c : cs) * kHeadDim);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int it = 0; it < kSteps; it += kPseudoDepth) {
+#pragma unroll
+            for (int j = 0; j < kPseudoDepth; ++j) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = item(it + j, u);
+                    const int cc = cs + r;
+                    const bool ok = cc < ce && !((s_mask[cc >> 5] >> (cc & 31)) & 1u);
+                    float x[8];
+                    ring[j].r[u].unpack(x);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float lgv = ok ? s_lg[r][g] : -INFINITY;
+                        const float w = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - M[g]);
+                        st.l[g] += w;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = cs + item(it + j + kPseudoDepth, u);
+                    ring[j].r[u].load(vb + (size_t)(c < ce && it + j + kPseudoDepth < kSteps ? c : cs) * kHeadDim);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+            }
+        }
+    }
+
+    // ---- exact rows of the replica's share, staged in batches, through a
+    //      ring of kExactDepth steps of 64 rows (branch-free body: exact wait
+    //      counts; steps past the end load staged row 0 and are masked) ------
+    QSlice<T> qs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
+    const float qscale = kInvSqrtD * kLog2e;
+    const size_t ubase = (size_t)unit * a.Nmax * kHeadDim + li * 8;
+    const T* Kx = reinterpret_cast<const T*>(a.Kx) + ubase;
+    const T* Vx = reinterpret_cast<const T*>(a.Vx) + ubase;
+    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
+    const int e0 = (int)((int64_t)E * rep / R), e1 = (int)((int64_t)E * (rep + 1) / R);
+    for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
+        const int cnt = min(kUnitRowBatch, e1 - c0);
+        __syncthreads();  // the previous batch is consumed
+        stage_exact(s_row, s_spre, s_soff, nsel, tids, c0, cnt);
+        __syncthreads();
+        RowBuf<T> ring[kExactDepth];
+#pragma unroll
+        for (int j = 0; j < kExactDepth; ++j) {
+            load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx, kUnitWaves);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int steps = (cnt + 8 * kUnitWaves - 1) / (8 * kUnitWaves);
+        for (int it = 0; it < steps; it += kExactDepth) {
+#pragma unroll
+            for (int j = 0; j < kExactDepth; ++j) {
+                exact_step<T, G>(st, qs, qscale, ring[j]);
+                load_rows<T>(ring[j], s_row, cnt, it + j + kExactDepth, wave, rg, Kx, Vx, kUnitWaves);
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+            }
+        }
+    }
+    // ---- unclustered tail, exactly -----------------------------------------
+    {
+        const int Tn = a.n_total - a.n_clustered;
+        const int t0 = (int)((int64_t)Tn * rep / R), t1 = (int)((int64_t)Tn * (rep + 1) / R);
+        const T* Kt = reinterpret_cast<const T*>(a.K) + ubase;
+        const T* Vt = reinterpret_cast<const T*>(a.V) + ubase;
+        for (int base = t0 + wave * 8; base < t1; base += 8 * kUnitWaves) {
+            RowBuf<T> bf;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = base + u * 4 + rg;
+                bf.ok[u] = i < t1;
+                const int r = a.n_clustered + (bf.ok[u] ? i : t0);
+                bf.k[u].load(Kt + (size_t)r * kHeadDim);
+                bf.v[u].load(Vt + (size_t)r * kHeadDim);
+            }
+            exact_step<T, G>(st, qs, qscale, bf);
+        }
+    }
+
+    // ---- combine the row groups: 4 per wave by shuffles, then the waves
+    //      through LDS (in wave order) ---------------------------------------
+#pragma unroll
+    for (int step = 16; step <= 32; step <<= 1) {
+        float om[G], ol[G], oacc[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            om[g] = shfl_xor_f(st.m[g], step);
+            ol[g] = shfl_xor_f(st.l[g], step);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
+        }
+        merge_state<G>(st, om, ol, oacc);
+    }
+    __syncthreads();  // the big region is free
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
+            if (li == 0) {
+                s_red[wave][g][kHeadDim] = st.m[g];
+                s_red[wave][g][kHeadDim + 1] = st.l[g];
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kHeadDim; e += kUnitThreads) {
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kUnitWaves; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kUnitWaves; ++w) {
+                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
+                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
+                acc = fmaf(s_red[w][g][dd], wt, acc);
+            }
+        }
+        if (R == 1) {
+            a.out[((size_t)b * a.Hq + (size_t)h * G + g) * kHeadDim + dd] = l > 0.f ? acc / l : 0.f;
+        } else {
+            const size_t pidx = ((size_t)unit * G + g) * a.part_stride + rep;
+            a.part_acc[pidx * kHeadDim + dd] = acc;
+            if (dd == 0) {
+                a.part_ml[pidx * 2] = M;
+                a.part_ml[pidx * 2 + 1] = l;
+            }
+        }
+    }
+}
+
+int unit_replicas(int n_clusters) { return (n_clusters + kUnitShare - 1) / kUnitShare; }
+
+bool unit_path_fits(int dtype, int G, int max_clusters) {
+    return dtype == 1 && (G == 1 || G == 2 || G == 4 || G == 8) && max_clusters >= 1 && max_clusters <= kUnitMaxC;
+}
+
+hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
+    if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < unit_replicas(a.C) ||
+        (replicas > 1 && (!a.part_ml || !a.part_acc || a.part_stride < replicas)) || (replicas == 1 && !a.out))
+        return hipErrorInvalidValue;
+    dim3 grid(replicas, units);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 1>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 2>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 4>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 8>), grid, dim3(kUnitThreads), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mpa

@@ -3,12 +3,14 @@ declares, its struct layouts match the header as a C compiler sees it, and
 every validation error is returned before anything touches a GPU (all pointers
 below are fake and never dereferenced)."""
 import ctypes
+import dataclasses
 import os
 import re
 import subprocess
 import tempfile
 
 import pytest
+import torch
 
 from sparse_long_context_means_amd import mpattn as M
 
@@ -183,6 +185,11 @@ def test_workspace_and_stages():
     assert p.decode_stages() == ["score", "select", "attend", "merge"]
     ph = _params(coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
     assert ph.decode_stages() == ["coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"]
+    # many units, automatic splits, bf16: the whole step of a unit in one workgroup
+    many = M.Params(batch=16, n_q_heads=32, n_kv_heads=8, capacity_tokens=32768)
+    assert many.decode_stages() == ["unit", "merge"]
+    assert dataclasses.replace(many, splits=8).decode_stages() == ["score", "select", "attend", "merge"]
+    assert dataclasses.replace(many, dtype=torch.float32).decode_stages() == ["score", "select", "attend", "merge"]
     small = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=1).c()), 2053, 0, M.OP_DECODE)
     big = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=64).c()), 2053, 0, M.OP_DECODE)
     assert big > small

@@ -49,6 +49,9 @@ DECODE_CASES = [
     ("fp32", 1, 1, 1, 4096, 4096, 8192, 16, [128], True, 0),
     ("bf16", 1, 8, 1, 2000, 2000, 512, 8, [200], True, 0),
     ("bf16", 1, 2, 1, 777, 777, 256, 4, [50, 0], False, 0),
+    # many units: the whole step of a unit in one workgroup
+    ("bf16", 16, 32, 8, 2048, 2048, 1024, 16, [0, 40, 300, 2048], True, 0),
+    ("bf16", 8, 16, 8, 3000, 3300, 1024, 16, [100, 3000], False, 0),
 ]
 
 
@@ -326,3 +329,31 @@ def test_omit_mode_matches_oracle():
             ref = O.decode_unit(q[0, h * G:(h + 1) * G], K[0, h], V[0, h], p.capacity_tokens, st, T, mode=1)
             ok, ea, er = close(out[0, h * G:(h + 1) * G], ref.out)
             assert ok, (h, T, ea)
+
+
+# ---------------------------------------------------------------------------
+# the per-unit path (one workgroup per unit) against the split launches
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["multipole", "omit"])
+def test_unit_path_matches_split_path_and_oracle(mode):
+    mp, w, K, V, means, p, state = _built(B=16, Hq=32, Hkv=8, N=3000, Bc=1024)
+    md = mp.MODE_MULTIPOLE if mode == "multipole" else mp.MODE_OMIT
+    ps = dataclasses.replace(p, splits=8)
+    G = p.group
+    for step, T in enumerate((64, 700)):
+        q = queries(w, means, 10 + step)
+        du, ds = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+        ou = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 3000, state, T, mode=md, debug=du).cpu().numpy()
+        os_ = mp.decode(ps, q.to(DEV), K.to(DEV), V.to(DEV), 3000, state, T, mode=md, debug=ds).cpu().numpy()
+        # same keys, same cut, same exact-token counts on both paths
+        assert torch.equal(du.scores.cpu(), ds.scores.cpu())
+        assert torch.equal(du.selected.cpu(), ds.selected.cpu())
+        assert torch.equal(du.exact_tokens.cpu(), ds.exact_tokens.cpu())
+        np.testing.assert_allclose(ou, os_, rtol=1e-4, atol=1e-5)
+        for u in (0, 37, 127):
+            b, h = divmod(u, p.n_kv_heads)
+            st = oracle_state_from_gpu(state, b, h, p)
+            ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], 3000, st, T,
+                                mode=0 if mode == "multipole" else 1)
+            ok, ea, er = close(ou[b, h * G:(h + 1) * G], ref.out)
+            assert ok, (u, T, ea, er)
