@@ -349,7 +349,7 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const int32_t P = S;  // partial slots: one per attend split
 
     if (unit_path(p)) {
-        const int R = unit_replicas(C);
+        const int R = unit_replicas(C, U);
         if (R > S) return MPATTN_ERR_WORKSPACE;
         for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
             if (stage == 0) {

@@ -176,8 +176,10 @@ struct UnitArgs {
     int32_t* dbg_selected;       // optional [U][C]
     int32_t* dbg_exact;          // optional [U]
 };
-// Fewest replicas (workgroups per unit) the per-unit path needs for C clusters.
-int unit_replicas(int n_clusters);
+// Replicas (workgroups per unit) of the per-unit path for C clusters: one when
+// C <= 2048 and there are at least 256 units, else at least two, shares of
+// <= 1024 clusters and at least 256 workgroups in all (up to 8 per unit).
+int unit_replicas(int n_clusters, int units);
 // Whether the per-unit path supports this storage dtype, group size and
 // cluster capacity.
 bool unit_path_fits(int dtype, int G, int cmax);

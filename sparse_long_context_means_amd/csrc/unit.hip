@@ -27,12 +27,12 @@ namespace mpa {
 
 constexpr int kUnitThreads = 512;
 constexpr int kUnitWaves = kUnitThreads / kWave;  // 8
-constexpr int kUnitTiles = 8;                     // cut items per thread
-constexpr int kUnitMaxC = kUnitTiles * kUnitThreads;  // clusters per unit
-constexpr int kUnitShare = 1024;                  // approximate-term clusters per replica
 constexpr int kUnitRowBatch = 1024;               // staged exact rows per pass
-constexpr int kUnitRowsPerWave = kUnitMaxC / kUnitWaves;    // scored clusters per wave
-constexpr int kUnitSharePerWave = kUnitShare / kUnitWaves;  // approximate-term clusters per wave
+// Two shapes: up to 2048 clusters with one replica per unit (the whole
+// approximate term in one workgroup), or up to 4096 clusters with shares of
+// 1024 per replica.
+constexpr int kUnitMaxCSmall = 2048, kUnitShareSmall = 2048;
+constexpr int kUnitMaxCLarge = 4096, kUnitShareLarge = 1024;
 
 // Exclusive workgroup scan of two counters; totals in tot.
 template <int NW>
@@ -62,7 +62,7 @@ __device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds
 
 // LDS layout (bytes).  The final reduction of the waves' states reuses the
 // "big" region once the selection lists, weights and row stage are dead.
-template <int G>
+template <int G, int kUnitMaxC, int kUnitShare>
 struct UnitLds {
     static constexpr int key = 0;                                    // float [MaxC]
     static constexpr int sz = key + kUnitMaxC * 4;                   // int [MaxC]: sizes
@@ -84,7 +84,6 @@ struct UnitLds {
     static constexpr int bytes = (big_end > big + red_bytes ? big_end : big + red_bytes);
 };
 
-constexpr int kUnitCutItems = kUnitMaxC / kUnitThreads;  // consecutive cut items per thread (8)
 constexpr int kScoreDepth = 4;                           // score steps in flight per wave
 constexpr int kPseudoDepth = 2;                          // value-centroid steps in flight per wave
 constexpr int kExactDepth = 4;                           // exact-row steps in flight per wave
@@ -96,9 +95,11 @@ struct Rows4 {
     Slice8<T> r[4];
 };
 
-template <typename T, int G>
+template <typename T, int G, int kUnitMaxC, int kUnitShare>
 __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
-    using L = UnitLds<G>;
+    constexpr int kUnitCutItems = kUnitMaxC / kUnitThreads;        // consecutive cut items per thread
+    constexpr int kUnitSharePerWave = kUnitShare / kUnitWaves;     // approximate-term clusters per wave
+    using L = UnitLds<G, kUnitMaxC, kUnitShare>;
     __shared__ __align__(16) char lds[L::bytes];
     float* s_key = reinterpret_cast<float*>(lds + L::key);
     int32_t* s_sz = reinterpret_cast<int32_t*>(lds + L::sz);
@@ -116,7 +117,10 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     int32_t* s_row = reinterpret_cast<int32_t*>(lds + L::row);
     float(*s_red)[G][kHeadDim + 2] = reinterpret_cast<float(*)[G][kHeadDim + 2]>(lds + L::big);
 
-    const int rep = blockIdx.x, unit = blockIdx.y, R = gridDim.x;
+    // grid (unit, replica): the replicas of a unit are U workgroups apart in
+    // dispatch order, so with U a multiple of 8 they land on the same XCD and
+    // share its L2 for the key centroids both of them read
+    const int unit = blockIdx.x, rep = blockIdx.y, R = gridDim.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int rg = lane >> 4, li = lane & 15;
     const int C = a.C;
@@ -124,17 +128,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     const int32_t* szu = a.sizes + (size_t)unit * a.Cmax;
     const int32_t* ofu = a.offsets + (size_t)unit * (a.Cmax + 1);
     const int cs = (int)((int64_t)C * rep / R), ce = (int)((int64_t)C * (rep + 1) / R);  // approximate-term share
-
-    // ---- cluster records to LDS (sizes, first member, member rows) --------
-    for (int i = tid; i < C; i += kUnitThreads) {
-        const int o0 = ofu[i];
-        s_sz[i] = szu[i];
-        s_off[i] = o0;
-        s_rows[i] = ofu[i + 1] - o0;
-    }
-    for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
-    for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
-    __syncthreads();
 
     // ---- scores through a ring of kScoreDepth steps: step s of wave w takes
     //      clusters 128 s + 16 w + 4 u + rg (u < 4).  The ranking key goes to
@@ -161,6 +154,17 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // cluster records to LDS (sizes, first member, member rows) while the
+        // first centroid rows are in flight
+        for (int i = tid; i < C; i += kUnitThreads) {
+            const int o0 = ofu[i];
+            s_sz[i] = szu[i];
+            s_off[i] = o0;
+            s_rows[i] = ofu[i + 1] - o0;
+        }
+        for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
+        for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
+        __syncthreads();
         for (int it = 0; it < steps; it += kScoreDepth) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
@@ -199,6 +203,24 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
     }
     __syncthreads();
+
+    // ---- the first value-centroid steps of the share go out now: they do not
+    //      depend on the cut and arrive while it is taken ---------------------
+    const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+    constexpr int kSteps = kUnitSharePerWave / 16;
+    auto item = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
+    Rows4<T> pring[kPseudoDepth];
+    if (a.pseudo) {
+#pragma unroll
+        for (int j = 0; j < kPseudoDepth; ++j) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = cs + item(j, u);
+                pring[j].r[u].load(vb + (size_t)(c < ce ? c : cs) * kHeadDim);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 
     // ---- budget cut: four 8-bit radix passes over the keys (weights =
     //      sizes), thread t owning items 8 t .. 8 t + 7; one workgroup scan
@@ -333,19 +355,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             M[g] = __int_as_float(s_misc[g]);
             st.m[g] = M[g];
         }
-        const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
-        constexpr int kSteps = kUnitSharePerWave / 16;
-        auto item = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
-        Rows4<T> ring[kPseudoDepth];
-#pragma unroll
-        for (int j = 0; j < kPseudoDepth; ++j) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = cs + item(j, u);
-                ring[j].r[u].load(vb + (size_t)(c < ce ? c : cs) * kHeadDim);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
         for (int it = 0; it < kSteps; it += kPseudoDepth) {
 #pragma unroll
             for (int j = 0; j < kPseudoDepth; ++j) {
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                     const int cc = cs + r;
                     const bool ok = cc < ce && !((s_mask[cc >> 5] >> (cc & 31)) & 1u);
                     float x[8];
-                    ring[j].r[u].unpack(x);
+                    pring[j].r[u].unpack(x);
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
                         const float lgv = ok ? s_lg[r][g] : -INFINITY;
@@ -368,7 +377,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int c = cs + item(it + j + kPseudoDepth, u);
-                    ring[j].r[u].load(vb + (size_t)(c < ce && it + j + kPseudoDepth < kSteps ? c : cs) * kHeadDim);
+                    pring[j].r[u].load(vb + (size_t)(c < ce && it + j + kPseudoDepth < kSteps ? c : cs) * kHeadDim);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
@@ -482,25 +491,44 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     }
 }
 
-int unit_replicas(int n_clusters) { return (n_clusters + kUnitShare - 1) / kUnitShare; }
-
-bool unit_path_fits(int dtype, int G, int max_clusters) {
-    return dtype == 1 && (G == 1 || G == 2 || G == 4 || G == 8) && max_clusters >= 1 && max_clusters <= kUnitMaxC;
+// One replica per unit only once the units alone give a workgroup to every CU
+// (reading the key centroids twice costs less than leaving half the CUs idle).
+int unit_replicas(int n_clusters, int units) {
+    constexpr int kWorkgroups = 256;
+    if (n_clusters <= kUnitMaxCSmall && units >= kWorkgroups) return 1;
+    int r = (n_clusters + kUnitShareLarge - 1) / kUnitShareLarge;
+    if (r < 2) r = 2;
+    while (units * r < kWorkgroups && r < 8) ++r;
+    return r;
 }
 
-hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
-    if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < unit_replicas(a.C) ||
-        (replicas > 1 && (!a.part_ml || !a.part_acc || a.part_stride < replicas)) || (replicas == 1 && !a.out))
-        return hipErrorInvalidValue;
-    dim3 grid(replicas, units);
+bool unit_path_fits(int dtype, int G, int max_clusters) {
+    return dtype == 1 && (G == 1 || G == 2 || G == 4 || G == 8) && max_clusters >= 1 && max_clusters <= kUnitMaxCLarge;
+}
+
+template <int MAXC, int SHARE>
+static hipError_t unit_dispatch(int G, const UnitArgs& a, dim3 grid, hipStream_t st) {
     switch (G) {
-        case 1: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 1>), grid, dim3(kUnitThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 2>), grid, dim3(kUnitThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 4>), grid, dim3(kUnitThreads), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 8>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 1, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 2, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 4, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 8, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
+    if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < 1 ||
+        (replicas > 1 && (!a.part_ml || !a.part_acc || a.part_stride < replicas)) || (replicas == 1 && !a.out))
+        return hipErrorInvalidValue;
+    dim3 grid(units, replicas);
+    if (replicas == 1) {
+        if (a.C > kUnitShareSmall) return hipErrorInvalidValue;
+        return unit_dispatch<kUnitMaxCSmall, kUnitShareSmall>(G, a, grid, st);
+    }
+    if ((a.C + replicas - 1) / replicas > kUnitShareLarge) return hipErrorInvalidValue;
+    return unit_dispatch<kUnitMaxCLarge, kUnitShareLarge>(G, a, grid, st);
 }
 
 }  // namespace mpa
