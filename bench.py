@@ -206,11 +206,11 @@ def main():
 
     steps_idx = range(args.warmup, args.warmup + args.steps)
     byts = np.array([sum(bytes_of(s)) for s in steps_idx], dtype=np.float64)
-    # dominant kernel: the per-unit kernel (the whole step but the merge) or
-    # the split attend kernel
+    # dominant kernel: the per-unit kernel (the whole step) or the split
+    # attend kernel
     if "unit" in stage_names:
         dom = "unit"
-        att_bytes = np.array([sum(bytes_of(s)) - B * Hq * d * 4 for s in steps_idx], dtype=np.float64)
+        att_bytes = byts.copy()
     else:
         dom = "attend"
         att_bytes = np.array([bytes_of(s)[1] for s in steps_idx], dtype=np.float64)

@@ -129,6 +129,9 @@ typedef struct mpattn_decode_debug {
     int32_t* selected;      /* device [B][Hkv][n_clusters]: 1 for clusters attended exactly      */
     int32_t* candidates;    /* device [B][Hkv][n_coarse]: 1 for coarse candidates (hierarchical) */
     int32_t* exact_tokens;  /* device [B][Hkv]: tokens of the selected clusters                   */
+    int32_t rescore;        /* nonzero: in the one-launch flat decode, every workgroup of a unit
+                               scores all of its clusters instead of taking the other workgroups'
+                               keys (the path taken when they are late); the result is the same */
 } mpattn_decode_debug;
 
 /* Human-readable text of a status code (static storage). */
@@ -145,7 +148,10 @@ int32_t mpattn_max_coarse(const mpattn_params* params);
 /* Workspace bytes an operation needs for a state of `capacity_clusters`
  * clusters (and `capacity_coarse` coarse clusters).  0 means no workspace.
  * Returns (size_t)-1 when the parameters are invalid.  Decodes that share a
- * workspace must not overlap in time. */
+ * workspace must not overlap in time.  A decode workspace must hold zeros
+ * before its first decode and must not be written by anything else between
+ * decodes (the workgroups of a unit exchange tagged words through it; a
+ * decode leaves it valid for the next one). */
 size_t mpattn_workspace_bytes(const mpattn_params* params, int32_t capacity_clusters, int32_t capacity_coarse,
                               int32_t op);
 
@@ -210,11 +216,11 @@ mpattn_status mpattn_decode(const mpattn_params* params, const void* q, const vo
 
 /* Number of kernel stages one decode enqueues (for timing stage by stage):
  * 6 for the hierarchical method (coarse_score, coarse_select, fine_score,
- * fine_select, attend, merge); for the flat method 2 (unit, merge) when the
- * whole step of a unit runs in one workgroup -- bf16 storage, splits = 0, at
- * least 64 units and at most 4096 clusters per unit -- else 4 (score,
- * select, attend, merge).  Both forms compute the same cut and, up to fp32
- * summation order, the same output. */
+ * fine_select, attend, merge); for the flat method 1 (unit) when the whole
+ * step of a unit runs in one launch -- bf16 storage, splits = 0, at least 64
+ * units and at most 4096 clusters per unit -- else 4 (score, select, attend,
+ * merge).  Both forms compute the same cut and, up to fp32 summation order,
+ * the same output. */
 int32_t mpattn_decode_stage_count(const mpattn_params* params);
 
 /* Name of decode stage i (static storage), NULL if out of range. */

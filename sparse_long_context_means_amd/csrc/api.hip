@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/mpattn.h"
 #include "kernels.hpp"
 
@@ -73,8 +75,16 @@ int32_t max_chunks(const mpattn_params* p, int32_t Cmax, int32_t Dmax) {
     return score_chunks(Dmax) + score_chunks(fine);
 }
 
+bool unit_path(const mpattn_params* p);
+
 // Decode workspace regions.
 struct DecodeWs {
+    // per-unit path with several replicas: exchange words (tag << 32 | value);
+    // they rely on the workspace holding zeros before its first decode
+    uint64_t* xch;        // [U][Rx][Cmax] keys
+    uint64_t* xpart;      // [U][Rx][G][d + 2] partials
+    uint64_t* xcount;     // [U] arrival words
+    int32_t Rx;           // most replicas a decode on this layout uses
     float* s;             // [U][Cmax][G] scores by cluster id
     int4* rs;             // [U][Cmax] cut records by item
     uint32_t* selmask;    // [U][Cw] selected clusters
@@ -110,6 +120,14 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
         off += align_up(bytes);
         return ptr;
     };
+    if (unit_path(p)) {
+        w.Rx = unit_replicas(mpattn_max_clusters(p), (int)U);
+        if (w.Rx > 1) {
+            w.xch = (uint64_t*)take(U * w.Rx * Cmax * 8);
+            w.xpart = (uint64_t*)take(U * w.Rx * G * (kD + 2) * 8);
+            w.xcount = (uint64_t*)take(U * 8);
+        }
+    }
     w.s = (float*)take(U * Cmax * G * 4);
     w.rs = (int4*)take(U * Cmax * 16);
     w.selmask = (uint32_t*)take(U * w.Cw * 4);
@@ -131,6 +149,22 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
     }
     w.bytes = off;
     return w;
+}
+
+// Tag of one decode call: a bijective 32-bit mix (the MurmurHash3 finalizer)
+// of a per-process call counter, never zero, so no two calls of the last 2^32
+// share one and a zeroed word never matches.
+uint32_t next_tag() {
+    static std::atomic<uint32_t> counter{0};
+    for (;;) {
+        uint32_t h = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+        h ^= h >> 16;
+        h *= 0x85ebca6bu;
+        h ^= h >> 13;
+        h *= 0xc2b2ae35u;
+        h ^= h >> 16;
+        if (h != 0u) return h;
+    }
 }
 
 mpattn_status hip_status(hipError_t e) { return e == hipSuccess ? MPATTN_OK : MPATTN_ERR_HIP; }
@@ -187,7 +221,7 @@ mpattn_status run_blocks(const mpattn_params* p, const void* k, const void* v, m
 }
 
 const char* kFlatStages[] = {"score", "select", "attend", "merge"};
-const char* kUnitStages[] = {"unit", "merge"};
+const char* kUnitStages[] = {"unit"};
 
 // The whole flat decode step of a unit in one workgroup (unit.hip) when the
 // batch has enough units to fill the GPU and the split count is automatic.
@@ -301,7 +335,7 @@ mpattn_status mpattn_update_window(const mpattn_params* p, const void* k, const 
 
 int32_t mpattn_decode_stage_count(const mpattn_params* p) {
     if (check_params(p) != MPATTN_OK) return 0;
-    return is_hier(p) ? 6 : unit_path(p) ? 2 : 4;
+    return is_hier(p) ? 6 : unit_path(p) ? 1 : 4;
 }
 
 const char* mpattn_decode_stage_name(const mpattn_params* p, int32_t stage) {
@@ -348,43 +382,39 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
     const int32_t P = S;  // partial slots: one per attend split
 
-    if (unit_path(p)) {
+    if (unit_path(p)) {  // one stage
         const int R = unit_replicas(C, U);
-        if (R > S) return MPATTN_ERR_WORKSPACE;
-        for (int32_t stage = first_stage; stage <= last_stage; ++stage) {
-            if (stage == 0) {
-                UnitArgs a{};
-                a.q = q;
-                a.kbar = st->key_centroids;
-                a.vbar = st->value_centroids;
-                a.sizes = st->sizes;
-                a.offsets = st->offsets;
-                a.Kx = sorted ? st->sorted_keys : k;
-                a.Vx = sorted ? st->sorted_values : v;
-                a.token_ids = sorted ? nullptr : st->token_ids;
-                a.K = k;
-                a.V = v;
-                a.Cmax = Cmax;
-                a.C = C;
-                a.Nmax = N;
-                a.n_clustered = st->n_clustered;
-                a.n_total = n_tokens_total;
-                a.budget = token_budget;
-                a.pseudo = want_pseudo;
-                a.Hq = p->n_q_heads;
-                a.Hkv = p->n_kv_heads;
-                a.out = out;
-                a.part_ml = w.part_ml;
-                a.part_acc = w.part_acc;
-                a.part_stride = R;
-                a.dbg_scores = debug ? debug->scores : nullptr;
-                a.dbg_selected = debug ? debug->selected : nullptr;
-                a.dbg_exact = debug ? debug->exact_tokens : nullptr;
-                MPA_TRY(launch_unit_decode(p->dtype, G, a, U, R, s));
-            } else if (R > 1) {
-                MPA_TRY(launch_merge(w.part_ml, w.part_acc, U, G, R, p->n_kv_heads, out, s));
-            }
-        }
+        if (R > 1 && R > w.Rx) return MPATTN_ERR_WORKSPACE;
+        UnitArgs a{};
+        a.q = q;
+        a.kbar = st->key_centroids;
+        a.vbar = st->value_centroids;
+        a.sizes = st->sizes;
+        a.offsets = st->offsets;
+        a.Kx = sorted ? st->sorted_keys : k;
+        a.Vx = sorted ? st->sorted_values : v;
+        a.token_ids = sorted ? nullptr : st->token_ids;
+        a.K = k;
+        a.V = v;
+        a.Cmax = Cmax;
+        a.C = C;
+        a.Nmax = N;
+        a.n_clustered = st->n_clustered;
+        a.n_total = n_tokens_total;
+        a.budget = token_budget;
+        a.pseudo = want_pseudo;
+        a.Hq = p->n_q_heads;
+        a.Hkv = p->n_kv_heads;
+        a.out = out;
+        a.xch = w.xch;
+        a.xpart = w.xpart;
+        a.xcount = w.xcount;
+        a.tag = next_tag();
+        a.dbg_scores = debug ? debug->scores : nullptr;
+        a.dbg_selected = debug ? debug->selected : nullptr;
+        a.dbg_exact = debug ? debug->exact_tokens : nullptr;
+        a.rescore = debug ? debug->rescore : 0;
+        MPA_TRY(launch_unit_decode(p->dtype, G, a, U, R, s));
         return MPATTN_OK;
     }
 

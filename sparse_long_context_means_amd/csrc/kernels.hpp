@@ -168,10 +168,13 @@ struct UnitArgs {
     int32_t Cmax, C, Nmax, n_clustered, n_total, budget;
     int32_t pseudo;              // 1: approximate unselected clusters; 0: omit them
     int32_t Hq, Hkv;
-    float* out;                  // [B][Hq][d] when one replica
-    float* part_ml;              // [U][G][part_stride][2] when several
-    float* part_acc;             // [U][G][part_stride][d]
-    int32_t part_stride;
+    float* out;                  // [B][Hq][d]
+    // replica exchange (several replicas): words are (tag << 32 | 32-bit value)
+    uint64_t* xch;               // [U][R][Cmax]: keys, slot r read by replica r
+    uint64_t* xpart;             // [U][R][G][d + 2]: partial sums, m, l of each replica
+    uint64_t* xcount;            // [U]: arrival word (tag << 32 | replicas counted in)
+    uint32_t tag;                // nonzero, distinct for every call
+    int32_t rescore;             // nonzero: skip the key exchange, score every cluster
     float* dbg_scores;           // optional [U][C][G]
     int32_t* dbg_selected;       // optional [U][C]
     int32_t* dbg_exact;          // optional [U]

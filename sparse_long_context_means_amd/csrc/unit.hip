@@ -87,6 +87,11 @@ struct UnitLds {
 constexpr int kScoreDepth = 4;                           // score steps in flight per wave
 constexpr int kPseudoDepth = 2;                          // value-centroid steps in flight per wave
 constexpr int kExactDepth = 4;                           // exact-row steps in flight per wave
+// Waits on the other replicas of a unit, in ticks of the 100 MHz constant
+// clock: for their keys (then the workgroup scores them itself) and for the
+// partial words of replicas that have already counted in.
+constexpr uint64_t kExchangeWaitTicks = 2000;
+constexpr uint64_t kPartialWaitTicks = 100000;
 
 // Four rows of a row group (one ring step of the score or the value-centroid
 // stream).
@@ -135,36 +140,40 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      body has no data-dependent branch (steps past the end load row 0
     //      and store nothing), so the compiler's wait counts stay exact. ----
     const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
-    {
+    const T* cu = reinterpret_cast<const T*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+    // one pass over clusters [lo, hi); the first pass also brings the cluster
+    // records to LDS while its first centroid rows are in flight, and only it
+    // writes the share's logits (the approximate term may have replaced them
+    // with its weights by the time a later pass runs)
+    auto score_pass = [&](int lo, int hi, bool first) {
         QSlice<T> qv[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) qv[g].load(qb + (size_t)g * kHeadDim);
-        const T* cu = reinterpret_cast<const T*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
         // the waves interleave: one step of the workgroup reads 128
         // consecutive clusters (32 KB), so the workgroup is a single stream
-        const int steps = (C + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
-        auto cluster = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
+        const int steps = (hi - lo + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
+        auto cluster = [&](int step, int u) { return lo + step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
         Rows4<T> ring[kScoreDepth];
 #pragma unroll
         for (int j = 0; j < kScoreDepth; ++j) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int i = cluster(j, u);
-                ring[j].r[u].load(cu + (size_t)(i < C ? i : 0) * kHeadDim);
+                ring[j].r[u].load(cu + (size_t)(i < hi ? i : 0) * kHeadDim);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // cluster records to LDS (sizes, first member, member rows) while the
-        // first centroid rows are in flight
-        for (int i = tid; i < C; i += kUnitThreads) {
-            const int o0 = ofu[i];
-            s_sz[i] = szu[i];
-            s_off[i] = o0;
-            s_rows[i] = ofu[i + 1] - o0;
+        if (first) {
+            for (int i = tid; i < C; i += kUnitThreads) {
+                const int o0 = ofu[i];
+                s_sz[i] = szu[i];
+                s_off[i] = o0;
+                s_rows[i] = ofu[i + 1] - o0;
+            }
+            for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
+            for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
+            __syncthreads();
         }
-        for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
-        for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
-        __syncthreads();
         for (int it = 0; it < steps; it += kScoreDepth) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
@@ -179,14 +188,14 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                         r += sg[g];
                     }
                     r *= 1.0f / G;
-                    if (i < C) {
+                    if (i < hi) {
                         float mine = sg[0];
 #pragma unroll
                         for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
                         if (li == 0) s_key[i] = r;
                         if (li < G) {
-                            if (a.dbg_scores && rep == 0) a.dbg_scores[((size_t)unit * C + i) * G + li] = mine;
-                            if (i >= cs && i < ce) {
+                            if (a.dbg_scores) a.dbg_scores[((size_t)unit * C + i) * G + li] = mine;
+                            if (first && i >= cs && i < ce) {  // later passes keep them
                                 const int n = s_sz[i];
                                 s_lg[i - cs][li] = n > 0 ? fmaf(mine, kLog2e, log2_count(n)) : -INFINITY;
                             }
@@ -196,21 +205,37 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int i = cluster(it + j + kScoreDepth, u);
-                    ring[j].r[u].load(cu + (size_t)(i < C ? i : 0) * kHeadDim);
+                    ring[j].r[u].load(cu + (size_t)(i < hi ? i : 0) * kHeadDim);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
-    }
+    };
+
+    // ---- scores through a ring of kScoreDepth steps: step s of wave w takes
+    //      clusters lo + 128 s + 16 w + 4 u + rg (u < 4).  The ranking key goes
+    //      to LDS, the share's base-2 logits s log2(e) + log2(n) too.  The ring
+    //      body has no data-dependent branch (steps past the end load row 0
+    //      and store nothing), so the compiler's wait counts stay exact.  With
+    //      several replicas each scores only its share and the keys of the
+    //      others come through the exchange below. ------------------------------
+    score_pass(R > 1 ? cs : 0, R > 1 ? ce : C, true);
     __syncthreads();
 
-    // ---- the first value-centroid steps of the share go out now: they do not
-    //      depend on the cut and arrive while it is taken ---------------------
+    // ---- approximate terms of the share: the value centroids of clusters
+    //      [cs, ce) not marked in the selection mask, weighted by
+    //      2^(lg - M) with M the share maximum over those clusters, stream
+    //      through a ring of kPseudoDepth steps of 4 rows (share items
+    //      128 s + 16 w + 4 u + rg).  Run after the cut, the mask holds the
+    //      selected clusters; run before it (odd replicas, below) the mask is
+    //      still empty and the selected clusters are taken out afterwards. ----
     const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
     constexpr int kSteps = kUnitSharePerWave / 16;
     auto item = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
     Rows4<T> pring[kPseudoDepth];
-    if (a.pseudo) {
+    SoftState<G> st;
+    st.init();
+    auto pseudo_issue = [&]() {  // the first ring steps
 #pragma unroll
         for (int j = 0; j < kPseudoDepth; ++j) {
 #pragma unroll
@@ -219,6 +244,136 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 pring[j].r[u].load(vb + (size_t)(c < ce ? c : cs) * kHeadDim);
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    float Mref[G];  // reference exponent of the approximate-term weights
+    auto pseudo_pass = [&]() {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float m = -INFINITY;
+            for (int t = tid; t < kUnitShare; t += kUnitThreads) {
+                const int c = cs + t;
+                if (c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u)) m = fmaxf(m, s_lg[t][g]);
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
+            if (lane == 0) s_gmax[wave][g] = m;
+        }
+        __syncthreads();
+        if (tid < G) {  // the share maximum of head tid
+            float m = s_gmax[0][tid];
+            for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][tid]);
+            s_misc[tid] = __float_as_int(m);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            Mref[g] = __int_as_float(s_misc[g]);
+            st.m[g] = Mref[g];
+        }
+        // the weights, once per cluster and head, replace the logits in LDS
+        // (0 for clusters outside the share, masked or empty)
+        for (int t = tid; t < kUnitShare; t += kUnitThreads) {
+            const int c = cs + t;
+            const bool ok = c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float lgv = ok ? s_lg[t][g] : -INFINITY;
+                s_lg[t][g] = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - Mref[g]);
+            }
+        }
+        __syncthreads();
+        for (int it = 0; it < kSteps; it += kPseudoDepth) {
+#pragma unroll
+            for (int j = 0; j < kPseudoDepth; ++j) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = item(it + j, u);
+                    float x[8];
+                    pring[j].r[u].unpack(x);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float w = s_lg[r][g];
+                        st.l[g] += w;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = cs + item(it + j + kPseudoDepth, u);
+                    pring[j].r[u].load(vb + (size_t)(c < ce && it + j + kPseudoDepth < kSteps ? c : cs) * kHeadDim);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+            }
+        }
+    };
+    // Odd replicas stream the approximate term of every cluster of their share
+    // while the even ones take the cut, and the other way round afterwards,
+    // so the memory pipe is not idle while every workgroup takes its cut.
+    const bool early = R > 1 && a.pseudo && (rep & 1);
+
+    // ---- key exchange between the replicas of the unit.  Every replica
+    //      writes the keys of its share into each other replica's slot as
+    //      64-bit words (call tag << 32 | key bits) with agent-scope atomic
+    //      stores, then reads its own slot: a word counts once it carries this
+    //      call's tag, so no fence or flag orders the words.  A word still
+    //      missing after kExchangeWaitTicks (a replica not yet running) makes
+    //      the workgroup score every cluster itself with the same operations,
+    //      which gives the same keys.  Consumed words are reset to zero. ------
+    bool miss = a.rescore != 0;
+    const bool xchg = R > 1 && !miss;
+    uint64_t* xu = a.xch + (size_t)unit * R * a.Cmax;
+    uint64_t* slot = xu + (size_t)rep * a.Cmax;
+    const uint64_t tagw = (uint64_t)a.tag << 32;
+    if (xchg) {
+        for (int i = cs + tid; i < ce; i += kUnitThreads) {
+            const uint64_t w = tagw | __float_as_uint(s_key[i]);
+            for (int r2 = 0; r2 < R; ++r2)
+                if (r2 != rep)
+                    __hip_atomic_store(xu + (size_t)r2 * a.Cmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (early) {
+        pseudo_issue();
+        pseudo_pass();
+    }
+    uint64_t xw[kUnitCutItems];
+    if (xchg) {
+#pragma unroll
+        for (int j = 0; j < kUnitCutItems; ++j) {
+            const int i = tid + j * kUnitThreads;
+            xw[j] = (i < C && (i < cs || i >= ce))
+                        ? __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : tagw;
+        }
+    }
+    // the first value-centroid steps of the even replicas go out behind the
+    // exchange reads: they do not depend on the cut and arrive while it is taken
+    if (!early && a.pseudo) pseudo_issue();
+    if (xchg) {
+        const uint64_t t0 = wall_clock64();
+#pragma unroll
+        for (int j = 0; j < kUnitCutItems; ++j) {
+            const int i = tid + j * kUnitThreads;
+            while (!miss && (uint32_t)(xw[j] >> 32) != a.tag) {
+                if (wall_clock64() - t0 > kExchangeWaitTicks) {
+                    miss = true;
+                } else {
+                    __builtin_amdgcn_s_sleep(2);
+                    xw[j] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            if (i < C && (i < cs || i >= ce) && (uint32_t)(xw[j] >> 32) == a.tag) {
+                s_key[i] = __uint_as_float((uint32_t)xw[j]);
+                __hip_atomic_store(slot + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (R > 1) {
+        if (__syncthreads_or(miss)) {
+            score_pass(0, C, false);
+            __syncthreads();
         }
     }
 
@@ -324,62 +479,44 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     }
     __syncthreads();
 
-    // ---- approximate terms of the share (unselected, non-empty clusters):
-    //      the share maximum is the reference of every row group; the value
-    //      centroids stream through a ring of kPseudoDepth steps of 4 rows
-    //      (share items 128 s + 16 w + 4 u + rg) ----------------------------
-    SoftState<G> st;
-    st.init();
-    if (a.pseudo) {
-        float M[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float m = -INFINITY;
-            for (int t = tid; t < kUnitShare; t += kUnitThreads) {
-                const int c = cs + t;
-                if (c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u)) m = fmaxf(m, s_lg[t][g]);
+    if (a.pseudo && !early) pseudo_pass();
+    if (early) {
+        // take the selected clusters of the share [cs, ce) (a contiguous run
+        // of the ascending selected list) back out of the approximate term,
+        // with the same weights
+        int k_lo = 0, k_hi = nsel;
+        {
+            int lo = 0, hi = nsel;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_sid[mid] < cs) lo = mid + 1; else hi = mid;
             }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
-            if (lane == 0) s_gmax[wave][g] = m;
+            k_lo = lo;
+            hi = nsel;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_sid[mid] < ce) lo = mid + 1; else hi = mid;
+            }
+            k_hi = lo;
         }
-        __syncthreads();
-        if (tid < G) {  // the share maximum of head tid
-            float m = s_gmax[0][tid];
-            for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][tid]);
-            s_misc[tid] = __float_as_int(m);
-        }
-        __syncthreads();
+        const int rgi = wave * 4 + rg;  // 32 row groups, one row each per pass
+        float back[G];  // weight scale from the reference Mref to the state's
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            M[g] = __int_as_float(s_misc[g]);
-            st.m[g] = M[g];
-        }
-        for (int it = 0; it < kSteps; it += kPseudoDepth) {
+        for (int g = 0; g < G; ++g) back[g] = __builtin_amdgcn_exp2f(Mref[g] - st.m[g]);
+        for (int k0 = k_lo; k0 < k_hi; k0 += 4 * kUnitWaves) {
+            const int k = k0 + rgi;
+            const bool ok = k < k_hi;
+            const int c = ok ? s_sid[k] : cs;
+            Slice8<T> v;
+            v.load(vb + (size_t)c * kHeadDim);
+            float x[8];
+            v.unpack(x);
 #pragma unroll
-            for (int j = 0; j < kPseudoDepth; ++j) {
+            for (int g = 0; g < G; ++g) {
+                const float p = ok ? s_lg[c - cs][g] * back[g] : 0.f;
+                st.l[g] -= p;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = item(it + j, u);
-                    const int cc = cs + r;
-                    const bool ok = cc < ce && !((s_mask[cc >> 5] >> (cc & 31)) & 1u);
-                    float x[8];
-                    pring[j].r[u].unpack(x);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float lgv = ok ? s_lg[r][g] : -INFINITY;
-                        const float w = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - M[g]);
-                        st.l[g] += w;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int c = cs + item(it + j + kPseudoDepth, u);
-                    pring[j].r[u].load(vb + (size_t)(c < ce && it + j + kPseudoDepth < kSteps ? c : cs) * kHeadDim);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+                for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(-p, x[e], st.acc[g][e]);
             }
         }
     }
@@ -464,7 +601,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
     }
     __syncthreads();
-    for (int e = tid; e < G * kHeadDim; e += kUnitThreads) {
+    // thread tid owns outputs e = tid + kUnitThreads k of the unit's G heads
+    constexpr int kOut = (G * kHeadDim + kUnitThreads - 1) / kUnitThreads;
+    float oM[kOut], oL[kOut], oA[kOut];
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kUnitThreads;
+        if (e >= G * kHeadDim) break;
         const int g = e / kHeadDim, dd = e % kHeadDim;
         float M = -INFINITY;
 #pragma unroll
@@ -478,16 +621,90 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 acc = fmaf(s_red[w][g][dd], wt, acc);
             }
         }
-        if (R == 1) {
-            a.out[((size_t)b * a.Hq + (size_t)h * G + g) * kHeadDim + dd] = l > 0.f ? acc / l : 0.f;
-        } else {
-            const size_t pidx = ((size_t)unit * G + g) * a.part_stride + rep;
-            a.part_acc[pidx * kHeadDim + dd] = acc;
-            if (dd == 0) {
-                a.part_ml[pidx * 2] = M;
-                a.part_ml[pidx * 2 + 1] = l;
+        oM[k] = M;
+        oL[k] = l;
+        oA[k] = acc;
+    }
+    float* outu = a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
+    if (R == 1) {
+#pragma unroll
+        for (int k = 0; k < kOut; ++k) {
+            const int e = tid + k * kUnitThreads;
+            if (e < G * kHeadDim) outu[e] = oL[k] > 0.f ? oA[k] / oL[k] : 0.f;
+        }
+        return;
+    }
+
+    // ---- several replicas: each posts its partial (per head: the state m, l
+    //      and the 128 sums) as tagged words, then counts itself in on the
+    //      unit's arrival word (call tag << 32 | count, compare-and-swap; a
+    //      stale tag counts as zero).  The replica that arrives last reads the
+    //      others' partials (waiting only for words already stored) and writes
+    //      the normalised output, merging in replica order. -------------------
+    constexpr int kPart = G * (kHeadDim + 2);
+    uint64_t* xp = a.xpart + (size_t)unit * R * kPart;
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kUnitThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
+        __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (dd == 0) {
+            __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t* cnt = a.xcount + unit;
+        uint64_t old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t arrived;
+        for (;;) {
+            arrived = ((uint32_t)(old >> 32) == a.tag ? (uint32_t)old : 0u) + 1u;
+            if (__hip_atomic_compare_exchange_strong(cnt, &old, tagw | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+        s_misc[0] = arrived == (uint32_t)R;
+    }
+    __syncthreads();
+    if (!s_misc[0]) return;
+    const uint64_t t0 = wall_clock64();
+    bool late = false;
+    auto take = [&](const uint64_t* p) {  // a partner word of this call
+        uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while ((uint32_t)(v >> 32) != a.tag && !late) {
+            if (wall_clock64() - t0 > kPartialWaitTicks) late = true;
+            __builtin_amdgcn_s_sleep(1);
+            v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return (uint32_t)(v >> 32) == a.tag ? __uint_as_float((uint32_t)v) : NAN;
+    };
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kUnitThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        float M = -INFINITY;
+        for (int r2 = 0; r2 < R; ++r2) {
+            const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+            M = fmaxf(M, r2 == rep ? oM[k] : take(pg + kHeadDim));
+        }
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+            for (int r2 = 0; r2 < R; ++r2) {
+                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                const float m = r2 == rep ? oM[k] : take(pg + kHeadDim);
+                const float wt = __builtin_amdgcn_exp2f(m - M);
+                l = fmaf(r2 == rep ? oL[k] : take(pg + kHeadDim + 1), wt, l);
+                acc = fmaf(r2 == rep ? oA[k] : take(pg + dd), wt, acc);
             }
         }
+        // a partial that never arrived (cannot happen once its replica has
+        // counted in) poisons the output instead of hanging
+        outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
     }
 }
 
@@ -520,7 +737,7 @@ static hipError_t unit_dispatch(int G, const UnitArgs& a, dim3 grid, hipStream_t
 
 hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
     if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < 1 ||
-        (replicas > 1 && (!a.part_ml || !a.part_acc || a.part_stride < replicas)) || (replicas == 1 && !a.out))
+        !a.out || (replicas > 1 && (!a.xch || !a.xpart || !a.xcount || a.tag == 0u)))
         return hipErrorInvalidValue;
     dim3 grid(units, replicas);
     if (replicas == 1) {

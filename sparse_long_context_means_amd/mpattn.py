@@ -50,7 +50,7 @@ class CState(ctypes.Structure):
 
 
 class CDebug(ctypes.Structure):
-    _fields_ = [(n, _VP) for n in ("scores", "selected", "candidates", "exact_tokens")]
+    _fields_ = [(n, _VP) for n in ("scores", "selected", "candidates", "exact_tokens")] + [("rescore", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -266,6 +266,7 @@ class DecodeDebug:
     selected: Optional[torch.Tensor] = None      # [B][Hkv][n_clusters] int32
     candidates: Optional[torch.Tensor] = None    # [B][Hkv][n_coarse] int32
     exact_tokens: Optional[torch.Tensor] = None  # [B][Hkv] int32
+    rescore: bool = False                        # every workgroup of a unit scores all clusters
 
     @staticmethod
     def allocate(p: Params, state: ClusterState, device="cuda") -> "DecodeDebug":
@@ -278,7 +279,8 @@ class DecodeDebug:
             exact_tokens=torch.zeros(B, H, dtype=torch.int32, device=device))
 
     def c(self) -> CDebug:
-        return CDebug(_ptr(self.scores), _ptr(self.selected), _ptr(self.candidates), _ptr(self.exact_tokens))
+        return CDebug(_ptr(self.scores), _ptr(self.selected), _ptr(self.candidates), _ptr(self.exact_tokens),
+                      int(self.rescore))
 
 
 def decode(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens_total: int,

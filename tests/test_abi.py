@@ -187,7 +187,7 @@ def test_workspace_and_stages():
     assert ph.decode_stages() == ["coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"]
     # many units, automatic splits, bf16: the whole step of a unit in one workgroup
     many = M.Params(batch=16, n_q_heads=32, n_kv_heads=8, capacity_tokens=32768)
-    assert many.decode_stages() == ["unit", "merge"]
+    assert many.decode_stages() == ["unit"]
     assert dataclasses.replace(many, splits=8).decode_stages() == ["score", "select", "attend", "merge"]
     assert dataclasses.replace(many, dtype=torch.float32).decode_stages() == ["score", "select", "attend", "merge"]
     small = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=1).c()), 2053, 0, M.OP_DECODE)

@@ -357,3 +357,27 @@ def test_unit_path_matches_split_path_and_oracle(mode):
                                 mode=0 if mode == "multipole" else 1)
             ok, ea, er = close(ou[b, h * G:(h + 1) * G], ref.out)
             assert ok, (u, T, ea, er)
+
+
+def test_unit_path_rescore_gives_the_same_result():
+    """The one-launch decode splits a unit over several workgroups that take
+    each other's cluster keys; the path they take when a partner is late
+    (every workgroup scores all clusters itself) must give bit-identical keys,
+    cut and output.  Forced here through the debug flag, at 128 units (two
+    workgroups per unit) and 64 units (four)."""
+    for B, Hkv in ((16, 8), (8, 8)):
+        mp, w, K, V, means, p, state = _built(B=B, Hq=4 * Hkv, Hkv=Hkv, N=3000, Bc=1024)
+        assert p.decode_stages() == ["unit"]
+        for step, T in enumerate((64, 700)):
+            q = queries(w, means, 20 + step).to(DEV)
+            outs, dbgs = [], []
+            for rescore in (False, True, False):
+                d = mp.DecodeDebug.allocate(p, state, DEV)
+                d.rescore = rescore
+                outs.append(mp.decode(p, q, K.to(DEV), V.to(DEV), 3000, state, T, debug=d).cpu())
+                dbgs.append(d)
+            for o, d in zip(outs[1:], dbgs[1:]):
+                assert torch.equal(o, outs[0]), (B, T)
+                assert torch.equal(d.scores.cpu(), dbgs[0].scores.cpu())
+                assert torch.equal(d.selected.cpu(), dbgs[0].selected.cpu())
+                assert torch.equal(d.exact_tokens.cpu(), dbgs[0].exact_tokens.cpu())
