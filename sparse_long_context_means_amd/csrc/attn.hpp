@@ -110,6 +110,56 @@ __device__ __forceinline__ size_t part_index(int unit, int G, int g, int P, int 
     return ((size_t)unit * G + g) * P + slot;
 }
 
+// ---------------------------------------------------------------------------
+// Scores on the matrix cores: v_mfma_f32_16x16x32_bf16 multiplies 16 key rows
+// (A: lane l holds row l % 16, dimensions 32 kk + 8 (l / 16) .. + 8 of k-block
+// kk) by the query heads of a group (B: lane l holds head l % 16 at the same
+// dimensions, zero for heads >= G); lane l receives the dot products of rows
+// 4 (l / 16) + i, i < 4, with head l % 16.  Four k-blocks cover d = 128.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+
+struct QOperand {
+    uint4 b[4];
+};
+
+// qg: head 0 of the group, [G][d] contiguous.
+template <int G>
+__device__ __forceinline__ void load_qop(QOperand& q, const bf16_t* qg, int lane) {
+    const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        q.b[kk] = n < G ? *reinterpret_cast<const uint4*>(qg + (size_t)n * kHeadDim + kk * 32 + grp * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The lane's share of its row (row l % 16 of the 16): 4 loads of 16 bytes.
+__device__ __forceinline__ void load_row_blocks(Slice8<bf16_t> (&a)[4], const bf16_t* row, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk].load(row + kk * 32 + (lane >> 4) * 8);
+}
+
+__device__ __forceinline__ f32x4v mfma_scores(const Slice8<bf16_t> (&a)[4], const QOperand& q) {
+    f32x4v d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a[kk].raw),
+                                                    __builtin_bit_cast(bf16x8v, q.b[kk]), d, 0, 0, 0);
+    return d;
+}
+
+// Mean of a row's scores over the G heads (lanes l % 16 < G); the result is
+// valid in lanes with l % 16 == 0.  The same operations on every path give
+// the same ranking keys.
+template <int G>
+__device__ __forceinline__ float head_mean(float s) {
+    if (G >= 2) s += MPA_DPP(s, 0xB1);   // quad_perm [1,0,3,2]
+    if (G >= 4) s += MPA_DPP(s, 0x4E);   // quad_perm [2,3,0,1]
+    if (G >= 8) s += MPA_DPP(s, 0x141);  // row_half_mirror: lane 0 takes lane 7
+    return s * (1.0f / G);
+}
+
 template <typename T>
 struct RowBuf {
     Slice8<T> k[2], v[2];

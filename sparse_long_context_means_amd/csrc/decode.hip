@@ -168,7 +168,40 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         my_o1 = ofu[my_id + 1];
     }
 
-    if (i0 < n) {
+    if constexpr (sizeof(T) == 2) {
+        // bf16: 16 items per matrix-core product; group u of wave w holds
+        // items c0 + 64 u + 16 w .. + 16 (lane l loads item l % 16 of them)
+        const int b = unit / a.Hkv, h = unit % a.Hkv;
+        const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
+        QOperand qop;
+        load_qop<G>(qop, qg, lane);
+        const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.cent) + (size_t)unit * a.cent_rows * kHeadDim;
+        int cid[4];
+        Slice8<bf16_t> rows[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = c0 + u * 64 + wave * 16 + li;
+            cid[u] = item_id(i < n ? i : c0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_row_blocks(rows[u], cu + (size_t)cid[u] * kHeadDim, lane);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4v d = mfma_scores(rows[u], qop);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e;  // item of the 16 whose scores lane (rg, li) holds
+                const int i = c0 + u * 64 + wave * 16 + r;
+                const int id = __shfl(cid[u], r, kWave);
+                const float sv = d[e] * kInvSqrtD;
+                const float key = head_mean<G>(sv);
+                if (i < n) {
+                    if (li < G) a.s_out[((size_t)unit * a.cent_rows + id) * G + li] = sv;
+                    if (li == 0) s_key[i - c0] = key;
+                }
+            }
+        }
+    } else if (i0 < n) {
         const int b = unit / a.Hkv, h = unit % a.Hkv;
         QSlice<T> qv[G];
         const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;

@@ -73,7 +73,8 @@ struct UnitLds {
     static constexpr int mask = scan + 64 * 4;                       // uint32 [MaxC / 32]
     static constexpr int misc = mask + (kUnitMaxC / 32) * 4;         // int [8]
     static constexpr int gmax = misc + 8 * 4;                        // float [waves][G]
-    static constexpr int big = gmax + kUnitWaves * G * 4;
+    static constexpr int pexp = gmax + kUnitWaves * G * 4;          // float [waves][16][G]
+    static constexpr int big = pexp + kUnitWaves * 16 * G * 4;
     static constexpr int sid = big;                                  // int [MaxC]
     static constexpr int soff = sid + kUnitMaxC * 4;                 // int [MaxC]
     static constexpr int spre = soff + kUnitMaxC * 4;                // int [MaxC + 1]
@@ -86,12 +87,18 @@ struct UnitLds {
 
 constexpr int kScoreDepth = 4;                           // score steps in flight per wave
 constexpr int kPseudoDepth = 2;                          // value-centroid steps in flight per wave
-constexpr int kExactDepth = 4;                           // exact-row steps in flight per wave
+constexpr int kExactDepth = 2;                           // exact-row steps (16 rows) in flight per wave
 // Waits on the other replicas of a unit, in ticks of the 100 MHz constant
 // clock: for their keys (then the workgroup scores them itself) and for the
 // partial words of replicas that have already counted in.
 constexpr uint64_t kExchangeWaitTicks = 2000;
 constexpr uint64_t kPartialWaitTicks = 100000;
+
+// One ring step of 16 exact rows of a wave: the lane's blocks of key row
+// l % 16 (matrix-core operand) and value rows 4 (l / 16) + e.
+struct ExactRows16 {
+    Slice8<bf16_t> k[4], v[4];
+};
 
 // Four rows of a row group (one ring step of the score or the value-centroid
 // stream).
@@ -115,6 +122,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + L::mask);
     int* s_misc = reinterpret_cast<int*>(lds + L::misc);
     float(*s_gmax)[G] = reinterpret_cast<float(*)[G]>(lds + L::gmax);
+    float* s_p = reinterpret_cast<float*>(lds + L::pexp);
     int32_t* s_sid = reinterpret_cast<int32_t*>(lds + L::sid);
     int32_t* s_soff = reinterpret_cast<int32_t*>(lds + L::soff);
     int32_t* s_spre = reinterpret_cast<int32_t*>(lds + L::spre);
@@ -134,33 +142,26 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     const int32_t* ofu = a.offsets + (size_t)unit * (a.Cmax + 1);
     const int cs = (int)((int64_t)C * rep / R), ce = (int)((int64_t)C * (rep + 1) / R);  // approximate-term share
 
-    // ---- scores through a ring of kScoreDepth steps: step s of wave w takes
-    //      clusters 128 s + 16 w + 4 u + rg (u < 4).  The ranking key goes to
-    //      LDS, the share's base-2 logits s log2(e) + log2(n) too.  The ring
-    //      body has no data-dependent branch (steps past the end load row 0
-    //      and store nothing), so the compiler's wait counts stay exact. ----
     const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
-    const T* cu = reinterpret_cast<const T*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+    const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
+    const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim;
     // one pass over clusters [lo, hi); the first pass also brings the cluster
     // records to LDS while its first centroid rows are in flight, and only it
     // writes the share's logits (the approximate term may have replaced them
     // with its weights by the time a later pass runs)
     auto score_pass = [&](int lo, int hi, bool first) {
-        QSlice<T> qv[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) qv[g].load(qb + (size_t)g * kHeadDim);
+        QOperand qop;
+        load_qop<G>(qop, qg, lane);
         // the waves interleave: one step of the workgroup reads 128
-        // consecutive clusters (32 KB), so the workgroup is a single stream
+        // consecutive clusters (32 KB), so the workgroup is a single stream;
+        // lane l loads row l % 16 of its wave's 16
         const int steps = (hi - lo + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
-        auto cluster = [&](int step, int u) { return lo + step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
-        Rows4<T> ring[kScoreDepth];
+        auto base = [&](int step) { return lo + step * 16 * kUnitWaves + wave * 16; };
+        Rows4<bf16_t> ring[kScoreDepth];
 #pragma unroll
         for (int j = 0; j < kScoreDepth; ++j) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = cluster(j, u);
-                ring[j].r[u].load(cu + (size_t)(i < hi ? i : 0) * kHeadDim);
-            }
+            const int i = base(j) + li;
+            load_row_blocks(ring[j].r, cu + (size_t)(i < hi ? i : 0) * kHeadDim, lane);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (first) {
@@ -177,48 +178,39 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         for (int it = 0; it < steps; it += kScoreDepth) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
+                // lane (rg, li) receives rows 4 rg + e of the 16 for head li
+                const f32x4v d = mfma_scores(ring[j].r, qop);
+                const int cb = base(it + j) + 4 * rg;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = cluster(it + j, u);
-                    float sg[G];
-                    float r = 0.f;
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        sg[g] = row16_sum(dot8(qv[g], ring[j].r[u])) * kInvSqrtD;
-                        r += sg[g];
-                    }
-                    r *= 1.0f / G;
+                for (int e = 0; e < 4; ++e) {
+                    const float sv = d[e] * kInvSqrtD;
+                    const float key = head_mean<G>(sv);
+                    const int i = cb + e;
                     if (i < hi) {
-                        float mine = sg[0];
-#pragma unroll
-                        for (int g = 1; g < G; ++g) mine = li == g ? sg[g] : mine;
-                        if (li == 0) s_key[i] = r;
+                        if (li == 0) s_key[i] = key;
                         if (li < G) {
-                            if (a.dbg_scores) a.dbg_scores[((size_t)unit * C + i) * G + li] = mine;
+                            if (a.dbg_scores) a.dbg_scores[((size_t)unit * C + i) * G + li] = sv;
                             if (first && i >= cs && i < ce) {  // later passes keep them
                                 const int n = s_sz[i];
-                                s_lg[i - cs][li] = n > 0 ? fmaf(mine, kLog2e, log2_count(n)) : -INFINITY;
+                                s_lg[i - cs][li] = n > 0 ? fmaf(sv, kLog2e, log2_count(n)) : -INFINITY;
                             }
                         }
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int i = cluster(it + j + kScoreDepth, u);
-                    ring[j].r[u].load(cu + (size_t)(i < hi ? i : 0) * kHeadDim);
-                }
+                const int i = base(it + j + kScoreDepth) + li;
+                load_row_blocks(ring[j].r, cu + (size_t)(i < hi ? i : 0) * kHeadDim, lane);
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
     };
 
-    // ---- scores through a ring of kScoreDepth steps: step s of wave w takes
-    //      clusters lo + 128 s + 16 w + 4 u + rg (u < 4).  The ranking key goes
-    //      to LDS, the share's base-2 logits s log2(e) + log2(n) too.  The ring
-    //      body has no data-dependent branch (steps past the end load row 0
-    //      and store nothing), so the compiler's wait counts stay exact.  With
-    //      several replicas each scores only its share and the keys of the
-    //      others come through the exchange below. ------------------------------
+    // ---- scores on the matrix cores through a ring of kScoreDepth steps:
+    //      step s of wave w takes clusters lo + 128 s + 16 w .. + 16.  The
+    //      ranking key goes to LDS, the share's base-2 logits s log2(e) +
+    //      log2(n) too.  The ring body has no data-dependent branch (steps
+    //      past the end load row 0 and store nothing), so the compiler's wait
+    //      counts stay exact.  With several replicas each scores only its
+    //      share and the keys of the others come through the exchange below.
     score_pass(R > 1 ? cs : 0, R > 1 ? ce : C, true);
     __syncthreads();
 
@@ -521,37 +513,116 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
     }
 
-    // ---- exact rows of the replica's share, staged in batches, through a
-    //      ring of kExactDepth steps of 64 rows (branch-free body: exact wait
-    //      counts; steps past the end load staged row 0 and are masked) ------
+    // ---- exact rows of the replica's share, staged in batches, 16 rows per
+    //      wave step through a ring of kExactDepth steps (branch-free body:
+    //      exact wait counts; rows past the end load staged row 0 and are
+    //      masked).  The scores of a step come from the matrix cores (lane
+    //      (rg, li) receives rows 4 rg + e for head li); the wave keeps one
+    //      reference exponent per head, raised lazily as in SoftState; the
+    //      weights go through a per-wave LDS tile to the row groups, which
+    //      accumulate rows 4 rg + e of the step into their value sums. -------
     QSlice<T> qs[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
     const float qscale = kInvSqrtD * kLog2e;
     const size_t ubase = (size_t)unit * a.Nmax * kHeadDim + li * 8;
-    const T* Kx = reinterpret_cast<const T*>(a.Kx) + ubase;
-    const T* Vx = reinterpret_cast<const T*>(a.Vx) + ubase;
     const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
     const int e0 = (int)((int64_t)E * rep / R), e1 = (int)((int64_t)E * (rep + 1) / R);
-    for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
-        const int cnt = min(kUnitRowBatch, e1 - c0);
-        __syncthreads();  // the previous batch is consumed
-        stage_exact(s_row, s_spre, s_soff, nsel, tids, c0, cnt);
-        __syncthreads();
-        RowBuf<T> ring[kExactDepth];
+    {
+        const bf16_t* Kx = reinterpret_cast<const bf16_t*>(a.Kx) + (size_t)unit * a.Nmax * kHeadDim;
+        const bf16_t* Vx = reinterpret_cast<const bf16_t*>(a.Vx) + ubase;
+        QOperand qop;
+        load_qop<G>(qop, qg, lane);
+        // the wave's reference exponent of head li (entering: the same in
+        // every row group) and the lane's weight sum of rows 4 rg + e, head li
+        float mv = 0.f;
 #pragma unroll
-        for (int j = 0; j < kExactDepth; ++j) {
-            load_rows<T>(ring[j], s_row, cnt, j, wave, rg, Kx, Vx, kUnitWaves);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const int steps = (cnt + 8 * kUnitWaves - 1) / (8 * kUnitWaves);
-        for (int it = 0; it < steps; it += kExactDepth) {
+        for (int g = 0; g < G; ++g) mv = li == g ? st.m[g] : mv;
+        float lp = 0.f;
+        float* sp = s_p + wave * 16 * G;  // [16][G] weights of the step
+        for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
+            const int cnt = min(kUnitRowBatch, e1 - c0);
+            __syncthreads();  // the previous batch is consumed
+            stage_exact(s_row, s_spre, s_soff, nsel, tids, c0, cnt);
+            __syncthreads();
+            auto load_step = [&](ExactRows16& rr, int step) {
+                const int ib = step * 16 * kUnitWaves + wave * 16;
+                const int ik = ib + li;
+                load_row_blocks(rr.k, Kx + (size_t)s_row[ik < cnt ? ik : 0] * kHeadDim, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int iv = ib + 4 * rg + e;
+                    rr.v[e].load(Vx + (size_t)s_row[iv < cnt ? iv : 0] * kHeadDim);
+                }
+            };
+            ExactRows16 ring[kExactDepth];
 #pragma unroll
             for (int j = 0; j < kExactDepth; ++j) {
-                exact_step<T, G>(st, qs, qscale, ring[j]);
-                load_rows<T>(ring[j], s_row, cnt, it + j + kExactDepth, wave, rg, Kx, Vx, kUnitWaves);
-                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+                load_step(ring[j], j);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            const int steps = (cnt + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
+            for (int it = 0; it < steps; it += kExactDepth) {
+#pragma unroll
+                for (int j = 0; j < kExactDepth; ++j) {
+                    const f32x4v d = mfma_scores(ring[j].k, qop);
+                    const int ib = (it + j) * 16 * kUnitWaves + wave * 16 + 4 * rg;
+                    float sv[4];
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sv[e] = ib + e < cnt ? d[e] * qscale : -INFINITY;
+                        mx = fmaxf(mx, sv[e]);
+                    }
+                    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+                    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+                    const bool raise = li < G && mx > mv + kLazyMax;
+                    if (__builtin_amdgcn_ballot_w64(raise)) {  // rare, wave-uniform
+                        const float sc = raise ? __builtin_amdgcn_exp2f(mv - mx) : 1.f;
+                        mv = raise ? mx : mv;
+                        lp *= sc;
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), g));
+                            st.l[g] *= sg;
+#pragma unroll
+                            for (int x = 0; x < 8; ++x) st.acc[g][x] *= sg;
+                        }
+                    }
+                    float pe[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pe[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - mv);
+                        lp += pe[e];
+                    }
+                    if (li < G) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sp[(4 * rg + e) * G + li] = pe[e];
+                    }
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float pg[G];
+#pragma unroll
+                        for (int g = 0; g < G; ++g) pg[g] = sp[(4 * rg + e) * G + g];
+                        float x[8];
+                        ring[j].v[e].unpack(x);
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) st.acc[g][q] = fmaf(pg[g], x[q], st.acc[g][q]);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    load_step(ring[j], it + j + kExactDepth);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+                }
+            }
+        }
+        // back to the row-group form: reference of the wave, row-group sums
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            st.m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), g));
+            st.l[g] += __shfl(lp, rg * 16 + g, kWave);
         }
     }
     // ---- unclustered tail, exactly -----------------------------------------
