@@ -31,6 +31,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
+
+# HBM bytes per launch of the per-unit decode kernel on this workload, from
+# two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for a 256 MiB device copy
+# (FETCH_SIZE reads 131085 KiB there: x2.0; WRITE_SIZE 262144 KiB: x1.0).
+# Valid only for the kernel sources they were taken on (sha256 over unit.hip,
+# attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
+UNIT_TRAFFIC = {
+    "sources_sha256": "3e1a2e8d5f1e92ddbbac7ee57b3a4a4b69384d945e76fb23f153b5c7c73c793c",
+    "fetch_bytes": int(121485.77 * 2.0 * 1024),
+    "write_bytes": int(7146.96 * 1.0 * 1024),
+    "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
+}
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
@@ -43,7 +57,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3-8b-layer-b16-32k-s95")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=8, help="oracle decode steps timed for the CPU baseline")
     ap.add_argument("--splits", type=int, default=0)
@@ -288,12 +302,27 @@ def main():
         "build_ms": round(build_ms, 2),
         "build_assign_TFLOPs_lower_bound": round(assign_flop / (build_ms * 1e-3) / 1e12, 1),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": _unit_traffic_bytes() if dom == "unit" and args.workload == DEFAULT_WORKLOAD else None,
                      "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def _unit_traffic_bytes():
+    """Counter-derived HBM bytes per launch of the per-unit kernel, or None
+    when its sources differ from the ones the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_long_context_means_amd", "csrc")
+    for fn in ("unit.hip", "attn.hpp", "device.hpp", "kernels.hpp"):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != UNIT_TRAFFIC["sources_sha256"]:
+        return None
+    return UNIT_TRAFFIC["fetch_bytes"] + UNIT_TRAFFIC["write_bytes"]
 
 
 def _cpu_model():
