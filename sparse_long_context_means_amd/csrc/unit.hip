@@ -34,6 +34,30 @@ constexpr int kUnitRowBatch = 1024;               // staged exact rows per pass
 constexpr int kUnitMaxCSmall = 2048, kUnitShareSmall = 2048;
 constexpr int kUnitMaxCLarge = 4096, kUnitShareLarge = 1024;
 
+// Workgroup barrier ordering LDS only: global loads and stores in flight are
+// not waited for (every barrier here publishes LDS data; a plain
+// __syncthreads() after a global store would also drain the load rings).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Number of threads of the workgroup with p set (one barrier; `lds` holds a
+// slot per wave and may be reused after the next barrier; it must not be the
+// area of a scan that follows without a barrier).
+template <int NW>
+__device__ __forceinline__ int block_count(bool p, int* lds) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int c = __popcll(__ballot(p));
+    if (lane == 0) lds[wave] = c;
+    lds_barrier();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += lds[w];
+    return t;
+}
+
 // Exclusive workgroup scan of two counters; totals in tot.
 template <int NW>
 __device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds) {
@@ -43,7 +67,7 @@ __device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds
         lds[2 * wave] = ix;
         lds[2 * wave + 1] = iy;
     }
-    __syncthreads();
+    lds_barrier();
     int bx = 0, by = 0, tx = 0, ty = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -55,7 +79,7 @@ __device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds
         tx += p;
         ty += q;
     }
-    __syncthreads();  // lds may be reused right after
+    lds_barrier();  // lds may be reused right after
     tot = make_int2(tx, ty);
     return make_int2(bx + ix - v.x, by + iy - v.y);
 }
@@ -150,6 +174,19 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     // writes the share's logits (the approximate term may have replaced them
     // with its weights by the time a later pass runs)
     auto score_pass = [&](int lo, int hi, bool first) {
+        // the cluster records (first pass) go out ahead of the centroid rows,
+        // as unconditional loads (clamped index), so writing them to LDS waits
+        // for them alone and not for the ring behind them
+        int rsz[kUnitCutItems], ro0[kUnitCutItems], ro1[kUnitCutItems];
+        if (first) {
+#pragma unroll
+            for (int j = 0; j < kUnitCutItems; ++j) {
+                const int i = min(tid + j * kUnitThreads, C - 1);
+                rsz[j] = szu[i];
+                ro0[j] = ofu[i];
+                ro1[j] = ofu[i + 1];
+            }
+        }
         QOperand qop;
         load_qop<G>(qop, qg, lane);
         // the waves interleave: one step of the workgroup reads 128
@@ -165,15 +202,18 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         if (first) {
-            for (int i = tid; i < C; i += kUnitThreads) {
-                const int o0 = ofu[i];
-                s_sz[i] = szu[i];
-                s_off[i] = o0;
-                s_rows[i] = ofu[i + 1] - o0;
+#pragma unroll
+            for (int j = 0; j < kUnitCutItems; ++j) {
+                const int i = tid + j * kUnitThreads;
+                if (i < C) {
+                    s_sz[i] = rsz[j];
+                    s_off[i] = ro0[j];
+                    s_rows[i] = ro1[j] - ro0[j];
+                }
             }
             for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
             for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
-            __syncthreads();
+            lds_barrier();
         }
         for (int it = 0; it < steps; it += kScoreDepth) {
 #pragma unroll
@@ -212,7 +252,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      counts stay exact.  With several replicas each scores only its
     //      share and the keys of the others come through the exchange below.
     score_pass(R > 1 ? cs : 0, R > 1 ? ce : C, true);
-    __syncthreads();
+    lds_barrier();
 
     // ---- approximate terms of the share: the value centroids of clusters
     //      [cs, ce) not marked in the selection mask, weighted by
@@ -251,13 +291,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
             if (lane == 0) s_gmax[wave][g] = m;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < G) {  // the share maximum of head tid
             float m = s_gmax[0][tid];
             for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][tid]);
             s_misc[tid] = __float_as_int(m);
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             Mref[g] = __int_as_float(s_misc[g]);
@@ -274,7 +314,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 s_lg[t][g] = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - Mref[g]);
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int it = 0; it < kSteps; it += kPseudoDepth) {
 #pragma unroll
             for (int j = 0; j < kPseudoDepth; ++j) {
@@ -312,7 +352,8 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      call's tag, so no fence or flag orders the words.  A word still
     //      missing after kExchangeWaitTicks (a replica not yet running) makes
     //      the workgroup score every cluster itself with the same operations,
-    //      which gives the same keys.  Consumed words are reset to zero. ------
+    //      which gives the same keys.  Words of earlier calls carry other tags,
+    //      so none needs clearing. ----------------------------------------------
     bool miss = a.rescore != 0;
     const bool xchg = R > 1 && !miss;
     uint64_t* xu = a.xch + (size_t)unit * R * a.Cmax;
@@ -344,28 +385,36 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     // exchange reads: they do not depend on the cut and arrive while it is taken
     if (!early && a.pseudo) pseudo_issue();
     if (xchg) {
-        const uint64_t t0 = wall_clock64();
+        // straight-line check first: the compiler waits for the exchange
+        // words alone, not for the value-centroid rows issued behind them
+        bool fresh = true;
+#pragma unroll
+        for (int j = 0; j < kUnitCutItems; ++j) fresh = fresh && (uint32_t)(xw[j] >> 32) == a.tag;
+        if (!fresh) {  // a partner is behind: poll its words, for a bounded time
+            const uint64_t t0 = wall_clock64();
+#pragma unroll
+            for (int j = 0; j < kUnitCutItems; ++j) {
+                const int i = tid + j * kUnitThreads;
+                while (!miss && (uint32_t)(xw[j] >> 32) != a.tag) {
+                    if (wall_clock64() - t0 > kExchangeWaitTicks) {
+                        miss = true;
+                    } else {
+                        __builtin_amdgcn_s_sleep(2);
+                        xw[j] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kUnitCutItems; ++j) {
             const int i = tid + j * kUnitThreads;
-            while (!miss && (uint32_t)(xw[j] >> 32) != a.tag) {
-                if (wall_clock64() - t0 > kExchangeWaitTicks) {
-                    miss = true;
-                } else {
-                    __builtin_amdgcn_s_sleep(2);
-                    xw[j] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            if (i < C && (i < cs || i >= ce) && (uint32_t)(xw[j] >> 32) == a.tag) {
-                s_key[i] = __uint_as_float((uint32_t)xw[j]);
-                __hip_atomic_store(slot + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (i < C && (i < cs || i >= ce) && (uint32_t)(xw[j] >> 32) == a.tag) s_key[i] = __uint_as_float((uint32_t)xw[j]);
         }
     }
     if (R > 1) {
-        if (__syncthreads_or(miss)) {
+        if (block_count<kUnitWaves>(miss, s_scan + 32) > 0) {
             score_pass(0, C, false);
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -389,7 +438,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
         for (int j = 0; j < kUnitCutItems; ++j)
             if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
-        __syncthreads();
+        lds_barrier();
         int v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = hist[p][255 - (4 * lane + j)];
@@ -426,7 +475,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 if (isz[j] > 0 && key[j] == tau) tie_local += isz[j];
         }
         int run_tie = 0;
-        if (!done && __syncthreads_count(tie_local > 0) > 1) {  // uniform
+        if (!done && block_count<kUnitWaves>(tie_local > 0, s_scan + 32) > 1) {  // uniform
             int2 tt;
             run_tie = block_exclusive_sum2<kUnitWaves>(make_int2(tie_local, 0), tt, s_scan).x;
         }
@@ -469,7 +518,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         s_spre[nsel] = E;
         if (a.dbg_exact && rep == 0) a.dbg_exact[unit] = E;
     }
-    __syncthreads();
+    lds_barrier();
 
     if (a.pseudo && !early) pseudo_pass();
     if (early) {
@@ -542,11 +591,22 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         float* sp = s_p + wave * 16 * G;  // [16][G] weights of the step
         for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
             const int cnt = min(kUnitRowBatch, e1 - c0);
-            __syncthreads();  // the previous batch is consumed
+            lds_barrier();  // the previous batch is consumed
             stage_exact(s_row, s_spre, s_soff, nsel, tids, c0, cnt);
-            __syncthreads();
+            lds_barrier();
+            // 16-row blocks: the older waves 0-3 (first in issue order on
+            // their SIMDs, measured to finish their share ~25% sooner) take
+            // the first 9/16 of the blocks, waves 4-7 the rest; each half
+            // interleaves its blocks over its four waves
+            const int nb = (cnt + 15) / 16;
+            const int na = (nb * 9 + 8) / 16;
+            const int hb = wave < 4 ? 0 : na, hn = wave < 4 ? na : nb - na, hw = wave & 3;
+            auto blk = [&](int step) {
+                const int q = step * 4 + hw;
+                return q < hn ? hb + q : nb;  // nb: past the end, masked
+            };
             auto load_step = [&](ExactRows16& rr, int step) {
-                const int ib = step * 16 * kUnitWaves + wave * 16;
+                const int ib = blk(step) * 16;
                 const int ik = ib + li;
                 load_row_blocks(rr.k, Kx + (size_t)s_row[ik < cnt ? ik : 0] * kHeadDim, lane);
 #pragma unroll
@@ -561,12 +621,12 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 load_step(ring[j], j);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const int steps = (cnt + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
+            const int steps = (hn + 3) / 4;  // per wave
             for (int it = 0; it < steps; it += kExactDepth) {
 #pragma unroll
                 for (int j = 0; j < kExactDepth; ++j) {
                     const f32x4v d = mfma_scores(ring[j].k, qop);
-                    const int ib = (it + j) * 16 * kUnitWaves + wave * 16 + 4 * rg;
+                    const int ib = blk(it + j) * 16 + 4 * rg;
                     float sv[4];
                     float mx = -INFINITY;
 #pragma unroll
@@ -659,7 +719,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
         merge_state<G>(st, om, ol, oacc);
     }
-    __syncthreads();  // the big region is free
+    lds_barrier();  // the big region is free
     if (rg == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -671,7 +731,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // thread tid owns outputs e = tid + kUnitThreads k of the unit's G heads
     constexpr int kOut = (G * kHeadDim + kUnitThreads - 1) / kUnitThreads;
     float oM[kOut], oL[kOut], oA[kOut];
@@ -727,7 +787,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         uint64_t* cnt = a.xcount + unit;
         uint64_t old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -740,12 +800,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
         s_misc[0] = arrived == (uint32_t)R;
     }
-    __syncthreads();
+    lds_barrier();
     if (!s_misc[0]) return;
     const uint64_t t0 = wall_clock64();
     bool late = false;
-    auto take = [&](const uint64_t* p) {  // a partner word of this call
-        uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // a partner word of this call (all of them are issued before the first
+    // is checked, so the reads take one round trip)
+    auto fresh = [&](uint64_t v, const uint64_t* p) {
         while ((uint32_t)(v >> 32) != a.tag && !late) {
             if (wall_clock64() - t0 > kPartialWaitTicks) late = true;
             __builtin_amdgcn_s_sleep(1);
@@ -753,24 +814,49 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
         return (uint32_t)(v >> 32) == a.tag ? __uint_as_float((uint32_t)v) : NAN;
     };
+    constexpr int kMaxR = 8;
 #pragma unroll
     for (int k = 0; k < kOut; ++k) {
         const int e = tid + k * kUnitThreads;
         if (e >= G * kHeadDim) break;
         const int g = e / kHeadDim, dd = e % kHeadDim;
+        uint64_t wm[kMaxR], wl[kMaxR], wa[kMaxR];
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R && r2 != rep) {
+                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                wm[r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wl[r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wa[r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        float pm[kMaxR], pl[kMaxR], pa[kMaxR];
         float M = -INFINITY;
-        for (int r2 = 0; r2 < R; ++r2) {
-            const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-            M = fmaxf(M, r2 == rep ? oM[k] : take(pg + kHeadDim));
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R) {
+                if (r2 == rep) {
+                    pm[r2] = oM[k];
+                    pl[r2] = oL[k];
+                    pa[r2] = oA[k];
+                } else {
+                    const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                    pm[r2] = fresh(wm[r2], pg + kHeadDim);
+                    pl[r2] = fresh(wl[r2], pg + kHeadDim + 1);
+                    pa[r2] = fresh(wa[r2], pg + dd);
+                }
+                M = fmaxf(M, pm[r2]);
+            }
         }
         float l = 0.f, acc = 0.f;
         if (M != -INFINITY) {
-            for (int r2 = 0; r2 < R; ++r2) {
-                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                const float m = r2 == rep ? oM[k] : take(pg + kHeadDim);
-                const float wt = __builtin_amdgcn_exp2f(m - M);
-                l = fmaf(r2 == rep ? oL[k] : take(pg + kHeadDim + 1), wt, l);
-                acc = fmaf(r2 == rep ? oA[k] : take(pg + dd), wt, acc);
+#pragma unroll
+            for (int r2 = 0; r2 < kMaxR; ++r2) {
+                if (r2 < R) {
+                    const float wt = __builtin_amdgcn_exp2f(pm[r2] - M);
+                    l = fmaf(pl[r2], wt, l);
+                    acc = fmaf(pa[r2], wt, acc);
+                }
             }
         }
         // a partial that never arrived (cannot happen once its replica has
