@@ -173,6 +173,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     // records to LDS while its first centroid rows are in flight, and only it
     // writes the share's logits (the approximate term may have replaced them
     // with its weights by the time a later pass runs)
+    float lgmax = -INFINITY;  // the lane's maximum share logit (head li)
     auto score_pass = [&](int lo, int hi, bool first) {
         // the cluster records (first pass) go out ahead of the centroid rows,
         // as unconditional loads (clamped index), so writing them to LDS waits
@@ -232,7 +233,9 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                             if (a.dbg_scores) a.dbg_scores[((size_t)unit * C + i) * G + li] = sv;
                             if (first && i >= cs && i < ce) {  // later passes keep them
                                 const int n = s_sz[i];
-                                s_lg[i - cs][li] = n > 0 ? fmaf(sv, kLog2e, log2_count(n)) : -INFINITY;
+                                const float lgv = n > 0 ? fmaf(sv, kLog2e, log2_count(n)) : -INFINITY;
+                                s_lg[i - cs][li] = lgv;
+                                lgmax = fmaxf(lgmax, lgv);
                             }
                         }
                     }
@@ -241,6 +244,11 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 load_row_blocks(ring[j].r, cu + (size_t)(i < hi ? i : 0) * kHeadDim, lane);
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
+        }
+        if (first) {  // the wave's maximum logit of head li over the share
+            lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 16));
+            lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 32));
+            if (lane < G) s_gmax[wave][lane] = lgmax;
         }
     };
 
@@ -278,33 +286,22 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    float Mref[G];  // reference exponent of the approximate-term weights
-    auto pseudo_pass = [&]() {
+    // reference exponent of the approximate-term weights: the share's
+    // maximum logit over all its clusters (from the score pass), so every
+    // weight is at most 1 whichever clusters the cut removes
+    float Mref[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float m = -INFINITY;
-            for (int t = tid; t < kUnitShare; t += kUnitThreads) {
-                const int c = cs + t;
-                if (c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u)) m = fmaxf(m, s_lg[t][g]);
-            }
+    for (int g = 0; g < G; ++g) {
+        float m = s_gmax[0][g];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
-            if (lane == 0) s_gmax[wave][g] = m;
-        }
-        lds_barrier();
-        if (tid < G) {  // the share maximum of head tid
-            float m = s_gmax[0][tid];
-            for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][tid]);
-            s_misc[tid] = __float_as_int(m);
-        }
-        lds_barrier();
+        for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][g]);
+        Mref[g] = m;
+    }
+    // the weights, once per cluster and head, replace the logits in LDS (0 for
+    // clusters outside the share, masked or empty)
+    auto pseudo_weights = [&]() {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            Mref[g] = __int_as_float(s_misc[g]);
-            st.m[g] = Mref[g];
-        }
-        // the weights, once per cluster and head, replace the logits in LDS
-        // (0 for clusters outside the share, masked or empty)
+        for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
         for (int t = tid; t < kUnitShare; t += kUnitThreads) {
             const int c = cs + t;
             const bool ok = c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u);
@@ -315,6 +312,8 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
         }
         lds_barrier();
+    };
+    auto pseudo_loop = [&]() {
         for (int it = 0; it < kSteps; it += kPseudoDepth) {
 #pragma unroll
             for (int j = 0; j < kPseudoDepth; ++j) {
@@ -367,23 +366,30 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                     __hip_atomic_store(xu + (size_t)r2 * a.Cmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (early) {
-        pseudo_issue();
-        pseudo_pass();
-    }
+    // exchange reads: unconditional (clamped index) so that the compiler
+    // counts them exactly; words of this replica's own share are not used
     uint64_t xw[kUnitCutItems];
-    if (xchg) {
+    auto poll_issue = [&]() {
 #pragma unroll
         for (int j = 0; j < kUnitCutItems; ++j) {
             const int i = tid + j * kUnitThreads;
-            xw[j] = (i < C && (i < cs || i >= ce))
-                        ? __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : tagw;
+            const uint64_t v = __hip_atomic_load(slot + min(i, C - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            xw[j] = (i < C && (i < cs || i >= ce)) ? v : tagw;
         }
+    };
+    if (early) {
+        // the reads go out just before this replica's stream: by the time it
+        // is through, its partners' words have long arrived
+        pseudo_issue();
+        pseudo_weights();
+        if (xchg) poll_issue();
+        pseudo_loop();
+    } else {
+        if (xchg) poll_issue();
+        // the first value-centroid steps go out behind the exchange reads:
+        // they do not depend on the cut and arrive while it is taken
+        if (a.pseudo) pseudo_issue();
     }
-    // the first value-centroid steps of the even replicas go out behind the
-    // exchange reads: they do not depend on the cut and arrive while it is taken
-    if (!early && a.pseudo) pseudo_issue();
     if (xchg) {
         // straight-line check first: the compiler waits for the exchange
         // words alone, not for the value-centroid rows issued behind them
@@ -520,7 +526,10 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     }
     lds_barrier();
 
-    if (a.pseudo && !early) pseudo_pass();
+    if (a.pseudo && !early) {
+        pseudo_weights();
+        pseudo_loop();
+    }
     if (early) {
         // take the selected clusters of the share [cs, ce) (a contiguous run
         // of the ascending selected list) back out of the approximate term,
