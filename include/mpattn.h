@@ -129,9 +129,11 @@ typedef struct mpattn_decode_debug {
     int32_t* selected;      /* device [B][Hkv][n_clusters]: 1 for clusters attended exactly      */
     int32_t* candidates;    /* device [B][Hkv][n_coarse]: 1 for coarse candidates (hierarchical) */
     int32_t* exact_tokens;  /* device [B][Hkv]: tokens of the selected clusters                   */
-    int32_t rescore;        /* nonzero: in the one-launch flat decode, every workgroup of a unit
-                               scores all of its clusters instead of taking the other workgroups'
-                               keys (the path taken when they are late); the result is the same */
+    int32_t rescore;        /* one-launch flat decode only; 0: normal.  1: every workgroup of a
+                               unit scores all of its clusters instead of taking the other
+                               workgroups' keys.  2: as if those keys never arrived (the path taken
+                               when a workgroup is late: one wave scores them).  The result is the
+                               same bits in all three cases. */
 } mpattn_decode_debug;
 
 /* Human-readable text of a status code (static storage). */

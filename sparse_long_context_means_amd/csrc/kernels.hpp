@@ -174,7 +174,7 @@ struct UnitArgs {
     uint64_t* xpart;             // [U][R][G][d + 2]: partial sums, m, l of each replica
     uint64_t* xcount;            // [U]: arrival word (tag << 32 | replicas counted in)
     uint32_t tag;                // nonzero, distinct for every call
-    int32_t rescore;             // nonzero: skip the key exchange, score every cluster
+    int32_t rescore;             // 1: every workgroup scores every cluster; 2: one wave does, as after a timeout
     float* dbg_scores;           // optional [U][C][G]
     int32_t* dbg_selected;       // optional [U][C]
     int32_t* dbg_exact;          // optional [U]

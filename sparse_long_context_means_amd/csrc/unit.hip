@@ -28,9 +28,9 @@ namespace mpa {
 constexpr int kUnitThreads = 512;
 constexpr int kUnitWaves = kUnitThreads / kWave;  // 8
 constexpr int kUnitRowBatch = 1024;               // staged exact rows per pass
-// Two shapes: up to 2048 clusters with one replica per unit (the whole
-// approximate term in one workgroup), or up to 4096 clusters with shares of
-// 1024 per replica.
+// Three shapes: up to 2048 clusters with one replica per unit (the whole
+// approximate term in one workgroup), up to 2048 or 4096 clusters with
+// shares of up to 1024 per replica.
 constexpr int kUnitMaxCSmall = 2048, kUnitShareSmall = 2048;
 constexpr int kUnitMaxCLarge = 4096, kUnitShareLarge = 1024;
 
@@ -43,31 +43,44 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Number of threads of the workgroup with p set (one barrier; `lds` holds a
-// slot per wave and may be reused after the next barrier; it must not be the
-// area of a scan that follows without a barrier).
+// Barrier of waves 0 .. NW-1 of the workgroup through an LDS counter, the
+// other waves running on.  Each of those waves passes the same sequence of
+// these barriers (gen counts them), and all of them are resident, so the
+// wait always ends.
 template <int NW>
-__device__ __forceinline__ int block_count(bool p, int* lds) {
+__device__ __forceinline__ void group_barrier(int* ctr, int& gen) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    ++gen;
+    if ((threadIdx.x & (kWave - 1)) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NW * gen) __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Number of threads of waves 0 .. NW-1 with p set (`lds`: NW ints, free
+// again after the next group barrier).
+template <int NW>
+__device__ __forceinline__ int group_count(bool p, int* lds, int* ctr, int& gen) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int c = __popcll(__ballot(p));
     if (lane == 0) lds[wave] = c;
-    lds_barrier();
+    group_barrier<NW>(ctr, gen);
     int t = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) t += lds[w];
     return t;
 }
 
-// Exclusive workgroup scan of two counters; totals in tot.
+// Exclusive scan of two counters over waves 0 .. NW-1 in thread order;
+// totals in tot (`lds`: 2 NW ints).
 template <int NW>
-__device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds) {
+__device__ __forceinline__ int2 group_exclusive_sum2(int2 v, int2& tot, int* lds, int* ctr, int& gen) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int ix = wave_inclusive_sum(v.x), iy = wave_inclusive_sum(v.y);
     if (lane == kWave - 1) {
         lds[2 * wave] = ix;
         lds[2 * wave + 1] = iy;
     }
-    lds_barrier();
+    group_barrier<NW>(ctr, gen);
     int bx = 0, by = 0, tx = 0, ty = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -79,9 +92,121 @@ __device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds
         tx += p;
         ty += q;
     }
-    lds_barrier();  // lds may be reused right after
+    group_barrier<NW>(ctr, gen);  // lds may be reused right after
     tot = make_int2(tx, ty);
     return make_int2(bx + ix - v.x, by + iy - v.y);
+}
+
+// Budget cut taken by waves 0 .. NW-1 (the others run on): the longest prefix
+// of the non-empty clusters in (key desc, id asc) order whose sizes sum to at
+// most `budget`.  Thread t owns clusters ITEMS t .. ITEMS t + ITEMS - 1.  Four
+// 8-bit radix passes over the order-preserving key bits, weighted by size,
+// into LDS histograms find the cut value (every wave scans the histogram and
+// reaches the same digit); clusters above it are selected, clusters equal to
+// it in id order while they fit.  One group scan places the selected clusters
+// in id order: ids, first members, member-row prefix (s_spre[nsel] = E), and
+// nsel, E in out[0], out[1].
+template <int NW, int ITEMS>
+__device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_sz, const int32_t* s_off,
+                                          const int32_t* s_rows, int C, int budget, int (*hist)[256], int* s_scan,
+                                          int* ctr, int& gen, int32_t* s_sid, int32_t* s_soff, int32_t* s_spre,
+                                          int* out, int32_t* dbg_sel) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    uint32_t key[ITEMS];
+    int isz[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int i = tid * ITEMS + j;
+        key[j] = i < C ? order_key(s_key[i]) : 0u;
+        isz[j] = i < C ? s_sz[i] : 0;
+    }
+    for (int k = tid; k < 4 * 256; k += NW * kWave) reinterpret_cast<int*>(hist)[k] = 0;
+    group_barrier<NW>(ctr, gen);
+    uint32_t prefix = 0, pmask = 0;
+    int Rb = budget;
+    bool done = false;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j)
+            if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
+        group_barrier<NW>(ctr, gen);
+        int v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = hist[p][255 - (4 * lane + q)];
+        int total;
+        int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
+        if (total <= Rb) {  // the same in every wave: every candidate left fits
+            done = true;
+            break;
+        }
+        int found = -1, cum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (found < 0 && run <= Rb && Rb < run + v[q]) {
+                found = 255 - (4 * lane + q);
+                cum = run;
+            }
+            run += v[q];
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = __ffsll((long long)bal) - 1;
+        const int digit = lane_value(found, src);
+        Rb -= lane_value(cum, src);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xFFu << shift;
+    }
+    uint32_t selbits = 0;
+    int s_local = 0, rows_local = 0;
+    {
+        int tie_local = 0;
+        if (!done) {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j)
+                if (isz[j] > 0 && key[j] == prefix) tie_local += isz[j];
+        }
+        int run_tie = 0;
+        if (!done && group_count<NW>(tie_local > 0, s_scan + 32, ctr, gen) > 1) {  // uniform
+            int2 tt;
+            run_tie = group_exclusive_sum2<NW>(make_int2(tie_local, 0), tt, s_scan, ctr, gen).x;
+        }
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            bool sel;
+            if (done) {
+                sel = key[j] >= prefix;  // prefix: the digits fixed so far, low bits zero
+            } else {
+                const bool tie = key[j] == prefix;
+                sel = key[j] > prefix || (tie && run_tie + isz[j] <= Rb);
+                if (tie) run_tie += isz[j];
+            }
+            sel = sel && isz[j] > 0;
+            selbits |= (uint32_t)sel << j;
+            s_local += sel;
+            rows_local += sel ? s_rows[tid * ITEMS + j] : 0;
+        }
+    }
+    int2 tot;
+    const int2 ex = group_exclusive_sum2<NW>(make_int2(s_local, rows_local), tot, s_scan, ctr, gen);
+    int k = ex.x, ro = ex.y;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int i = tid * ITEMS + j;
+        if ((selbits >> j) & 1u) {
+            s_sid[k] = i;
+            s_soff[k] = s_off[i];
+            s_spre[k] = ro;
+            ++k;
+            ro += s_rows[i];
+        }
+        if (dbg_sel && i < C) dbg_sel[i] = (selbits >> j) & 1u;
+    }
+    if (tid == 0) {
+        s_spre[tot.x] = tot.y;
+        out[0] = tot.x;
+        out[1] = tot.y;
+    }
 }
 
 // LDS layout (bytes).  The final reduction of the waves' states reuses the
@@ -94,8 +219,7 @@ struct UnitLds {
     static constexpr int rows = off + kUnitMaxC * 4;                 // int [MaxC]: member rows
     static constexpr int hist = rows + kUnitMaxC * 4;                // int [4][256]
     static constexpr int scan = hist + 4 * 256 * 4;                  // int [64]
-    static constexpr int mask = scan + 64 * 4;                       // uint32 [MaxC / 32]
-    static constexpr int misc = mask + (kUnitMaxC / 32) * 4;         // int [8]
+    static constexpr int misc = scan + 64 * 4;                       // int [8]
     static constexpr int gmax = misc + 8 * 4;                        // float [waves][G]
     static constexpr int pexp = gmax + kUnitWaves * G * 4;          // float [waves][16][G]
     static constexpr int big = pexp + kUnitWaves * 16 * G * 4;
@@ -133,7 +257,7 @@ struct Rows4 {
 
 template <typename T, int G, int kUnitMaxC, int kUnitShare>
 __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
-    constexpr int kUnitCutItems = kUnitMaxC / kUnitThreads;        // consecutive cut items per thread
+    constexpr int kUnitRecItems = kUnitMaxC / kUnitThreads;        // cluster records per thread
     constexpr int kUnitSharePerWave = kUnitShare / kUnitWaves;     // approximate-term clusters per wave
     using L = UnitLds<G, kUnitMaxC, kUnitShare>;
     __shared__ __align__(16) char lds[L::bytes];
@@ -143,7 +267,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     int32_t* s_rows = reinterpret_cast<int32_t*>(lds + L::rows);
     int(*hist)[256] = reinterpret_cast<int(*)[256]>(lds + L::hist);
     int* s_scan = reinterpret_cast<int*>(lds + L::scan);
-    uint32_t* s_mask = reinterpret_cast<uint32_t*>(lds + L::mask);
     int* s_misc = reinterpret_cast<int*>(lds + L::misc);
     float(*s_gmax)[G] = reinterpret_cast<float(*)[G]>(lds + L::gmax);
     float* s_p = reinterpret_cast<float*>(lds + L::pexp);
@@ -169,19 +292,20 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
     const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
     const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim;
-    // one pass over clusters [lo, hi); the first pass also brings the cluster
-    // records to LDS while its first centroid rows are in flight, and only it
-    // writes the share's logits (the approximate term may have replaced them
-    // with its weights by the time a later pass runs)
+    // one pass over clusters [lo, hi) by nw waves (this one is wave wv of
+    // them); the first pass (all waves) also brings the cluster records to
+    // LDS while its first centroid rows are in flight, and only it writes the
+    // share's logits (the approximate term may have replaced them with its
+    // weights by the time a later pass runs)
     float lgmax = -INFINITY;  // the lane's maximum share logit (head li)
-    auto score_pass = [&](int lo, int hi, bool first) {
+    auto score_pass = [&](int lo, int hi, bool first, int nw, int wv) {
         // the cluster records (first pass) go out ahead of the centroid rows,
         // as unconditional loads (clamped index), so writing them to LDS waits
         // for them alone and not for the ring behind them
-        int rsz[kUnitCutItems], ro0[kUnitCutItems], ro1[kUnitCutItems];
+        int rsz[kUnitRecItems], ro0[kUnitRecItems], ro1[kUnitRecItems];
         if (first) {
 #pragma unroll
-            for (int j = 0; j < kUnitCutItems; ++j) {
+            for (int j = 0; j < kUnitRecItems; ++j) {
                 const int i = min(tid + j * kUnitThreads, C - 1);
                 rsz[j] = szu[i];
                 ro0[j] = ofu[i];
@@ -190,11 +314,11 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
         QOperand qop;
         load_qop<G>(qop, qg, lane);
-        // the waves interleave: one step of the workgroup reads 128
-        // consecutive clusters (32 KB), so the workgroup is a single stream;
-        // lane l loads row l % 16 of its wave's 16
-        const int steps = (hi - lo + 16 * kUnitWaves - 1) / (16 * kUnitWaves);
-        auto base = [&](int step) { return lo + step * 16 * kUnitWaves + wave * 16; };
+        // the waves interleave: one step of the workgroup reads 16 nw
+        // consecutive clusters, so the workgroup is a single stream; lane l
+        // loads row l % 16 of its wave's 16
+        const int steps = (hi - lo + 16 * nw - 1) / (16 * nw);
+        auto base = [&](int step) { return lo + step * 16 * nw + wv * 16; };
         Rows4<bf16_t> ring[kScoreDepth];
 #pragma unroll
         for (int j = 0; j < kScoreDepth; ++j) {
@@ -204,7 +328,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
         if (first) {
 #pragma unroll
-            for (int j = 0; j < kUnitCutItems; ++j) {
+            for (int j = 0; j < kUnitRecItems; ++j) {
                 const int i = tid + j * kUnitThreads;
                 if (i < C) {
                     s_sz[i] = rsz[j];
@@ -213,7 +337,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 }
             }
             for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
-            for (int k = tid; k < kUnitMaxC / 32; k += kUnitThreads) s_mask[k] = 0;
             lds_barrier();
         }
         for (int it = 0; it < steps; it += kScoreDepth) {
@@ -259,23 +382,160 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      past the end load row 0 and store nothing), so the compiler's wait
     //      counts stay exact.  With several replicas each scores only its
     //      share and the keys of the others come through the exchange below.
-    score_pass(R > 1 ? cs : 0, R > 1 ? ce : C, true);
+    score_pass(R > 1 ? cs : 0, R > 1 ? ce : C, true, kUnitWaves, wave);
     lds_barrier();
 
     // ---- approximate terms of the share: the value centroids of clusters
-    //      [cs, ce) not marked in the selection mask, weighted by
-    //      2^(lg - M) with M the share maximum over those clusters, stream
-    //      through a ring of kPseudoDepth steps of 4 rows (share items
-    //      128 s + 16 w + 4 u + rg).  Run after the cut, the mask holds the
-    //      selected clusters; run before it (odd replicas, below) the mask is
-    //      still empty and the selected clusters are taken out afterwards. ----
+    //      [cs, ce), weighted by 2^(lg - M) with M the share's maximum logit
+    //      over all its clusters (from the score pass; every weight is at most
+    //      1), stream through a ring of kPseudoDepth steps of 4 rows per row
+    //      group.  Waves 4-7 run it over every cluster of the share while
+    //      waves 0-3 take the cut; the selected clusters are taken out after.
     const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
-    constexpr int kSteps = kUnitSharePerWave / 16;
-    auto item = [&](int step, int u) { return step * 16 * kUnitWaves + wave * 16 + u * 4 + rg; };
+    constexpr int kCutWaves = 4, kStreamWaves = kUnitWaves - kCutWaves;
+    constexpr int kSteps = (kUnitShare + 16 * kStreamWaves - 1) / (16 * kStreamWaves);
+    const int sw = wave - kCutWaves;  // stream wave index (waves 4-7)
+    auto item = [&](int step, int u) { return step * 16 * kStreamWaves + sw * 16 + u * 4 + rg; };
     Rows4<T> pring[kPseudoDepth];
     SoftState<G> st;
     st.init();
-    auto pseudo_issue = [&]() {  // the first ring steps
+    float Mref[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float m = s_gmax[0][g];
+#pragma unroll
+        for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][g]);
+        Mref[g] = m;
+    }
+
+    // ---- key exchange between the replicas of the unit.  Every replica
+    //      writes the keys of its share into each other replica's slot as
+    //      64-bit words (call tag << 32 | key bits) with agent-scope atomic
+    //      stores; waves 0-3 then read its own slot: a word counts once it
+    //      carries this call's tag, so no fence or flag orders the words, and
+    //      words of earlier calls (other tags) need no clearing.  A word still
+    //      missing after kExchangeWaitTicks (a replica not yet running) makes
+    //      waves 0-3 score every cluster themselves with the same operations,
+    //      which gives the same keys. ------------------------------------------
+    const uint64_t tagw = (uint64_t)a.tag << 32;
+    uint64_t* xu = a.xch + (size_t)unit * R * a.Cmax;
+    if (R > 1 && !a.rescore) {
+        for (int i = cs + tid; i < ce; i += kUnitThreads) {
+            const uint64_t w = tagw | __float_as_uint(s_key[i]);
+            for (int r2 = 0; r2 < R; ++r2)
+                if (r2 != rep)
+                    __hip_atomic_store(xu + (size_t)r2 * a.Cmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (a.pseudo) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
+    }
+    if (R > 1 && a.rescore == 1) {  // every wave scores the other shares too
+        score_pass(0, C, false, kUnitWaves, wave);
+    }
+    int* gctr = s_misc + 5;  // group barrier counters: waves 0-3, waves 4-7
+    int* sctr = s_misc + 4;
+    if (tid == 0) {
+        *gctr = 0;
+        *sctr = 0;
+    }
+    lds_barrier();
+
+    if (wave < kCutWaves) {
+        // ---- waves 0-3: the other replicas' keys, then the budget cut -------
+        int gen = 0;
+        if (R > 1 && a.rescore != 1) {
+            bool miss = a.rescore == 2;  // 2: as if the other keys never came
+            if (!miss) {
+                constexpr int kPoll = kUnitMaxC / (kCutWaves * kWave);  // words per thread
+                uint64_t* slot = xu + (size_t)rep * a.Cmax;
+                uint64_t w[kPoll];
+#pragma unroll
+                for (int q = 0; q < kPoll; ++q)  // unconditional (clamped): exact wait counts
+                    w[q] = __hip_atomic_load(slot + min(tid + q * kCutWaves * kWave, C - 1), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                bool fresh = true;
+#pragma unroll
+                for (int q = 0; q < kPoll; ++q) {
+                    const int i = tid + q * kCutWaves * kWave;
+                    fresh = fresh && (!(i < C && (i < cs || i >= ce)) || (uint32_t)(w[q] >> 32) == a.tag);
+                }
+                if (!fresh) {  // a partner is behind: poll its words, for a bounded time
+                    const uint64_t t0 = wall_clock64();
+#pragma unroll
+                    for (int q = 0; q < kPoll; ++q) {
+                        const int i = tid + q * kCutWaves * kWave;
+                        const bool need = i < C && (i < cs || i >= ce);
+                        while (need && !miss && (uint32_t)(w[q] >> 32) != a.tag) {
+                            if (wall_clock64() - t0 > kExchangeWaitTicks) {
+                                miss = true;
+                            } else {
+                                __builtin_amdgcn_s_sleep(2);
+                                w[q] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kPoll; ++q) {
+                    const int i = tid + q * kCutWaves * kWave;
+                    if (i < C && (i < cs || i >= ce) && (uint32_t)(w[q] >> 32) == a.tag)
+                        s_key[i] = __uint_as_float((uint32_t)w[q]);
+                }
+            }
+            if (group_count<kCutWaves>(miss, s_scan + 32, gctr, gen) > 0) {
+                score_pass(0, C, false, kCutWaves, wave);  // these four waves
+            }
+            group_barrier<kCutWaves>(gctr, gen);
+        }
+        group_cut<kCutWaves, kUnitMaxC / (kCutWaves * kWave)>(
+            s_key, s_sz, s_off, s_rows, C, a.budget, hist, s_scan, gctr, gen, s_sid, s_soff, s_spre, s_misc + 6,
+            a.dbg_selected && rep == 0 ? a.dbg_selected + (size_t)unit * C : nullptr);
+        if (a.pseudo) {
+            // take the selected clusters of the share [cs, ce) (a contiguous
+            // run of the ascending selected list) back out of the approximate
+            // term, with the weights waves 4-7 computed (their first barrier)
+            group_barrier<kCutWaves>(gctr, gen);  // the whole list is written
+            while (__hip_atomic_load(sctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kStreamWaves)
+                __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            const int nsel = s_misc[6];
+            int k_lo = 0, k_hi = nsel;
+            {
+                int lo = 0, hi = nsel;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_sid[mid] < cs) lo = mid + 1; else hi = mid;
+                }
+                k_lo = lo;
+                hi = nsel;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_sid[mid] < ce) lo = mid + 1; else hi = mid;
+                }
+                k_hi = lo;
+            }
+            const int rgi = wave * 4 + rg;  // 16 row groups, one row each per pass
+            for (int k0 = k_lo; k0 < k_hi; k0 += 4 * kCutWaves) {
+                const int k = k0 + rgi;
+                const bool ok = k < k_hi;
+                const int c = ok ? s_sid[k] : cs;
+                Slice8<T> v;
+                v.load(vb + (size_t)c * kHeadDim);
+                float x[8];
+                v.unpack(x);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float p = ok ? s_lg[c - cs][g] : 0.f;  // every state's reference is still Mref
+                    st.l[g] -= p;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(-p, x[e], st.acc[g][e]);
+                }
+            }
+        }
+    } else if (a.pseudo) {
+        // ---- waves 4-7: the approximate term of every cluster of the share --
 #pragma unroll
         for (int j = 0; j < kPseudoDepth; ++j) {
 #pragma unroll
@@ -285,46 +545,31 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    // reference exponent of the approximate-term weights: the share's
-    // maximum logit over all its clusters (from the score pass), so every
-    // weight is at most 1 whichever clusters the cut removes
-    float Mref[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float m = s_gmax[0][g];
-#pragma unroll
-        for (int w = 1; w < kUnitWaves; ++w) m = fmaxf(m, s_gmax[w][g]);
-        Mref[g] = m;
-    }
-    // the weights, once per cluster and head, replace the logits in LDS (0 for
-    // clusters outside the share, masked or empty)
-    auto pseudo_weights = [&]() {
-#pragma unroll
-        for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
-        for (int t = tid; t < kUnitShare; t += kUnitThreads) {
+        // the weights, once per cluster and head, replace the logits in LDS (0
+        // for clusters outside the share or empty), while the first rows fly
+        for (int t = tid - kCutWaves * kWave; t < kUnitShare; t += kStreamWaves * kWave) {
             const int c = cs + t;
-            const bool ok = c < ce && !((s_mask[c >> 5] >> (c & 31)) & 1u);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float lgv = ok ? s_lg[t][g] : -INFINITY;
+                const float lgv = c < ce ? s_lg[t][g] : -INFINITY;
                 s_lg[t][g] = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - Mref[g]);
             }
         }
-        lds_barrier();
-    };
-    auto pseudo_loop = [&]() {
+        int sgen = 0;
+        group_barrier<kStreamWaves>(sctr, sgen);
+#pragma unroll 1
         for (int it = 0; it < kSteps; it += kPseudoDepth) {
 #pragma unroll
             for (int j = 0; j < kPseudoDepth; ++j) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int r = item(it + j, u);
+                    const int rr = r < kUnitShare ? r : kUnitShare - 1;  // past the share: weight 0
                     float x[8];
                     pring[j].r[u].unpack(x);
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        const float w = s_lg[r][g];
+                        const float w = r < kUnitShare ? s_lg[rr][g] : 0.f;
                         st.l[g] += w;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
@@ -338,238 +583,10 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
-    };
-    // Odd replicas stream the approximate term of every cluster of their share
-    // while the even ones take the cut, and the other way round afterwards,
-    // so the memory pipe is not idle while every workgroup takes its cut.
-    const bool early = R > 1 && a.pseudo && (rep & 1);
-
-    // ---- key exchange between the replicas of the unit.  Every replica
-    //      writes the keys of its share into each other replica's slot as
-    //      64-bit words (call tag << 32 | key bits) with agent-scope atomic
-    //      stores, then reads its own slot: a word counts once it carries this
-    //      call's tag, so no fence or flag orders the words.  A word still
-    //      missing after kExchangeWaitTicks (a replica not yet running) makes
-    //      the workgroup score every cluster itself with the same operations,
-    //      which gives the same keys.  Words of earlier calls carry other tags,
-    //      so none needs clearing. ----------------------------------------------
-    bool miss = a.rescore != 0;
-    const bool xchg = R > 1 && !miss;
-    uint64_t* xu = a.xch + (size_t)unit * R * a.Cmax;
-    uint64_t* slot = xu + (size_t)rep * a.Cmax;
-    const uint64_t tagw = (uint64_t)a.tag << 32;
-    if (xchg) {
-        for (int i = cs + tid; i < ce; i += kUnitThreads) {
-            const uint64_t w = tagw | __float_as_uint(s_key[i]);
-            for (int r2 = 0; r2 < R; ++r2)
-                if (r2 != rep)
-                    __hip_atomic_store(xu + (size_t)r2 * a.Cmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    // exchange reads: unconditional (clamped index) so that the compiler
-    // counts them exactly; words of this replica's own share are not used
-    uint64_t xw[kUnitCutItems];
-    auto poll_issue = [&]() {
-#pragma unroll
-        for (int j = 0; j < kUnitCutItems; ++j) {
-            const int i = tid + j * kUnitThreads;
-            const uint64_t v = __hip_atomic_load(slot + min(i, C - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            xw[j] = (i < C && (i < cs || i >= ce)) ? v : tagw;
-        }
-    };
-    if (early) {
-        // the reads go out just before this replica's stream: by the time it
-        // is through, its partners' words have long arrived
-        pseudo_issue();
-        pseudo_weights();
-        if (xchg) poll_issue();
-        pseudo_loop();
-    } else {
-        if (xchg) poll_issue();
-        // the first value-centroid steps go out behind the exchange reads:
-        // they do not depend on the cut and arrive while it is taken
-        if (a.pseudo) pseudo_issue();
-    }
-    if (xchg) {
-        // straight-line check first: the compiler waits for the exchange
-        // words alone, not for the value-centroid rows issued behind them
-        bool fresh = true;
-#pragma unroll
-        for (int j = 0; j < kUnitCutItems; ++j) fresh = fresh && (uint32_t)(xw[j] >> 32) == a.tag;
-        if (!fresh) {  // a partner is behind: poll its words, for a bounded time
-            const uint64_t t0 = wall_clock64();
-#pragma unroll
-            for (int j = 0; j < kUnitCutItems; ++j) {
-                const int i = tid + j * kUnitThreads;
-                while (!miss && (uint32_t)(xw[j] >> 32) != a.tag) {
-                    if (wall_clock64() - t0 > kExchangeWaitTicks) {
-                        miss = true;
-                    } else {
-                        __builtin_amdgcn_s_sleep(2);
-                        xw[j] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kUnitCutItems; ++j) {
-            const int i = tid + j * kUnitThreads;
-            if (i < C && (i < cs || i >= ce) && (uint32_t)(xw[j] >> 32) == a.tag) s_key[i] = __uint_as_float((uint32_t)xw[j]);
-        }
-    }
-    if (R > 1) {
-        if (block_count<kUnitWaves>(miss, s_scan + 32) > 0) {
-            score_pass(0, C, false);
-            lds_barrier();
-        }
-    }
-
-    // ---- budget cut: four 8-bit radix passes over the keys (weights =
-    //      sizes), thread t owning items 8 t .. 8 t + 7; one workgroup scan
-    //      places the selected items in item order --------------------------
-    uint32_t key[kUnitCutItems];
-    int isz[kUnitCutItems];
-#pragma unroll
-    for (int j = 0; j < kUnitCutItems; ++j) {
-        const int i = tid * kUnitCutItems + j;
-        key[j] = i < C ? order_key(s_key[i]) : 0u;
-        isz[j] = i < C ? s_sz[i] : 0;
-    }
-    uint32_t prefix = 0, pmask = 0;
-    int Rb = a.budget;
-    bool done = false;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int shift = 24 - 8 * p;
-#pragma unroll
-        for (int j = 0; j < kUnitCutItems; ++j)
-            if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
-        lds_barrier();
-        int v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = hist[p][255 - (4 * lane + j)];
-        int total;
-        int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
-        if (total <= Rb) {  // the same in every wave
-            done = true;
-            break;
-        }
-        int found = -1, cum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (found < 0 && run <= Rb && Rb < run + v[j]) {
-                found = 255 - (4 * lane + j);
-                cum = run;
-            }
-            run += v[j];
-        }
-        const uint64_t bal = __ballot(found >= 0);
-        const int src = __ffsll((long long)bal) - 1;
-        const int digit = lane_value(found, src);
-        Rb -= lane_value(cum, src);
-        prefix |= (uint32_t)digit << shift;
-        pmask |= 0xFFu << shift;
-    }
-    const uint32_t tau = prefix;
-    uint32_t selbits = 0;
-    int s_local = 0, rows_local = 0;
-    {
-        int tie_local = 0;
-        if (!done) {
-#pragma unroll
-            for (int j = 0; j < kUnitCutItems; ++j)
-                if (isz[j] > 0 && key[j] == tau) tie_local += isz[j];
-        }
-        int run_tie = 0;
-        if (!done && block_count<kUnitWaves>(tie_local > 0, s_scan + 32) > 1) {  // uniform
-            int2 tt;
-            run_tie = block_exclusive_sum2<kUnitWaves>(make_int2(tie_local, 0), tt, s_scan).x;
-        }
-#pragma unroll
-        for (int j = 0; j < kUnitCutItems; ++j) {
-            bool sel;
-            if (done) {
-                sel = key[j] >= prefix;
-            } else {
-                const bool tie = key[j] == tau;
-                sel = key[j] > tau || (tie && run_tie + isz[j] <= Rb);
-                if (tie) run_tie += isz[j];
-            }
-            sel = sel && isz[j] > 0;
-            selbits |= (uint32_t)sel << j;
-            s_local += sel;
-            rows_local += sel ? s_rows[tid * kUnitCutItems + j] : 0;
-        }
-    }
-    int2 tot;
-    const int2 ex = block_exclusive_sum2<kUnitWaves>(make_int2(s_local, rows_local), tot, s_scan);
-    {
-        int k = ex.x, ro = ex.y;
-#pragma unroll
-        for (int j = 0; j < kUnitCutItems; ++j) {
-            const int i = tid * kUnitCutItems + j;
-            if ((selbits >> j) & 1u) {
-                s_sid[k] = i;
-                s_soff[k] = s_off[i];
-                s_spre[k] = ro;
-                ++k;
-                ro += s_rows[i];
-                atomicOr(&s_mask[i >> 5], 1u << (i & 31));
-            }
-            if (a.dbg_selected && rep == 0 && i < C) a.dbg_selected[(size_t)unit * C + i] = (selbits >> j) & 1u;
-        }
-    }
-    const int nsel = tot.x, E = tot.y;
-    if (tid == 0) {
-        s_spre[nsel] = E;
-        if (a.dbg_exact && rep == 0) a.dbg_exact[unit] = E;
     }
     lds_barrier();
-
-    if (a.pseudo && !early) {
-        pseudo_weights();
-        pseudo_loop();
-    }
-    if (early) {
-        // take the selected clusters of the share [cs, ce) (a contiguous run
-        // of the ascending selected list) back out of the approximate term,
-        // with the same weights
-        int k_lo = 0, k_hi = nsel;
-        {
-            int lo = 0, hi = nsel;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (s_sid[mid] < cs) lo = mid + 1; else hi = mid;
-            }
-            k_lo = lo;
-            hi = nsel;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (s_sid[mid] < ce) lo = mid + 1; else hi = mid;
-            }
-            k_hi = lo;
-        }
-        const int rgi = wave * 4 + rg;  // 32 row groups, one row each per pass
-        float back[G];  // weight scale from the reference Mref to the state's
-#pragma unroll
-        for (int g = 0; g < G; ++g) back[g] = __builtin_amdgcn_exp2f(Mref[g] - st.m[g]);
-        for (int k0 = k_lo; k0 < k_hi; k0 += 4 * kUnitWaves) {
-            const int k = k0 + rgi;
-            const bool ok = k < k_hi;
-            const int c = ok ? s_sid[k] : cs;
-            Slice8<T> v;
-            v.load(vb + (size_t)c * kHeadDim);
-            float x[8];
-            v.unpack(x);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float p = ok ? s_lg[c - cs][g] * back[g] : 0.f;
-                st.l[g] -= p;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(-p, x[e], st.acc[g][e]);
-            }
-        }
-    }
+    const int nsel = s_misc[6], E = s_misc[7];
+    if (tid == 0 && a.dbg_exact && rep == 0) a.dbg_exact[unit] = E;
 
     // ---- exact rows of the replica's share, staged in batches, 16 rows per
     //      wave step through a ring of kExactDepth steps (branch-free body:
@@ -911,6 +928,7 @@ hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, in
         return unit_dispatch<kUnitMaxCSmall, kUnitShareSmall>(G, a, grid, st);
     }
     if ((a.C + replicas - 1) / replicas > kUnitShareLarge) return hipErrorInvalidValue;
+    if (a.C <= kUnitMaxCSmall) return unit_dispatch<kUnitMaxCSmall, kUnitShareLarge>(G, a, grid, st);
     return unit_dispatch<kUnitMaxCLarge, kUnitShareLarge>(G, a, grid, st);
 }
 

@@ -266,7 +266,7 @@ class DecodeDebug:
     selected: Optional[torch.Tensor] = None      # [B][Hkv][n_clusters] int32
     candidates: Optional[torch.Tensor] = None    # [B][Hkv][n_coarse] int32
     exact_tokens: Optional[torch.Tensor] = None  # [B][Hkv] int32
-    rescore: bool = False                        # every workgroup of a unit scores all clusters
+    rescore: int = 0                             # 1: every workgroup scores all clusters; 2: late-partner path
 
     @staticmethod
     def allocate(p: Params, state: ClusterState, device="cuda") -> "DecodeDebug":

@@ -361,17 +361,17 @@ def test_unit_path_matches_split_path_and_oracle(mode):
 
 def test_unit_path_rescore_gives_the_same_result():
     """The one-launch decode splits a unit over several workgroups that take
-    each other's cluster keys; the path they take when a partner is late
-    (every workgroup scores all clusters itself) must give bit-identical keys,
-    cut and output.  Forced here through the debug flag, at 128 units (two
-    workgroups per unit) and 64 units (four)."""
+    each other's cluster keys; the paths that score the other shares locally
+    (all waves: rescore 1; one wave, as when a partner is late: rescore 2)
+    must give bit-identical keys, cut and output.  Forced through the debug
+    flag, at 128 units (two workgroups per unit) and 64 units (four)."""
     for B, Hkv in ((16, 8), (8, 8)):
         mp, w, K, V, means, p, state = _built(B=B, Hq=4 * Hkv, Hkv=Hkv, N=3000, Bc=1024)
         assert p.decode_stages() == ["unit"]
         for step, T in enumerate((64, 700)):
             q = queries(w, means, 20 + step).to(DEV)
             outs, dbgs = [], []
-            for rescore in (False, True, False):
+            for rescore in (0, 1, 2, 0):
                 d = mp.DecodeDebug.allocate(p, state, DEV)
                 d.rescore = rescore
                 outs.append(mp.decode(p, q, K.to(DEV), V.to(DEV), 3000, state, T, debug=d).cpu())
