@@ -246,12 +246,12 @@ def test_tiny_config_free_running():
 # reductions, determinism, split invariance
 # ---------------------------------------------------------------------------
 
-def _built(B=2, Hq=8, Hkv=2, N=4500, Bc=2048, splits=0, dt=torch.bfloat16, sorted_copy=True, iters=4):
+def _built(B=2, Hq=8, Hkv=2, N=4500, Bc=2048, splits=0, dt=torch.bfloat16, sorted_copy=True, iters=4, r=16):
     mp = M()
     w = small_workload(B, Hq, Hkv, N, 200, dt, outliers=4)
     K, V, means = workloads.make_cache(w)
     p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=dt, cluster_block=Bc,
-                  build_iters=iters, splits=splits, seed=1)
+                  build_iters=iters, splits=splits, seed=1, tokens_per_centroid=r)
     state = mp.ClusterState(p, DEV, sorted_copy=sorted_copy)
     mp.build_clusters(p, K.to(DEV), V.to(DEV), N, state)
     return mp, w, K, V, means, p, state
@@ -355,6 +355,32 @@ def test_unit_path_matches_split_path_and_oracle(mode):
             st = oracle_state_from_gpu(state, b, h, p)
             ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], 3000, st, T,
                                 mode=0 if mode == "multipole" else 1)
+            ok, ea, er = close(ou[b, h * G:(h + 1) * G], ref.out)
+            assert ok, (u, T, ea, er)
+
+
+def test_unit_path_over_2048_clusters_matches_split_path_and_oracle():
+    """The one-launch decode at more than 2048 clusters per unit (the
+    4096-cluster shape, four workgroups per unit at 64 units): same keys, cut
+    and exact-token counts as the split launches, outputs within tolerance of
+    them and of the oracle on sampled units."""
+    mp, w, K, V, means, p, state = _built(B=8, Hq=32, Hkv=8, N=10000, Bc=8192, r=4, iters=2)
+    assert p.decode_stages() == ["unit"] and state.n_clusters > 2048
+    ps = dataclasses.replace(p, splits=8)
+    G = p.group
+    for step, T in enumerate((500, 3000)):
+        q = queries(w, means, 30 + step)
+        du, ds = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+        ou = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 10000, state, T, debug=du).cpu().numpy()
+        os_ = mp.decode(ps, q.to(DEV), K.to(DEV), V.to(DEV), 10000, state, T, debug=ds).cpu().numpy()
+        assert torch.equal(du.scores.cpu(), ds.scores.cpu())
+        assert torch.equal(du.selected.cpu(), ds.selected.cpu())
+        assert torch.equal(du.exact_tokens.cpu(), ds.exact_tokens.cpu())
+        np.testing.assert_allclose(ou, os_, rtol=1e-4, atol=1e-5)
+        for u in (0, 63):
+            b, h = divmod(u, p.n_kv_heads)
+            st = oracle_state_from_gpu(state, b, h, p)
+            ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], 10000, st, T, mode=0)
             ok, ea, er = close(ou[b, h * G:(h + 1) * G], ref.out)
             assert ok, (u, T, ea, er)
 
