@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=8, help="oracle decode steps timed for the CPU baseline")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--gather", action="store_true", help="decode by token-id gather instead of the sorted copy")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the online-update and hierarchical-decode measurements")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -236,6 +238,8 @@ def main():
     log(f"[bench] cold {cold_us:.1f} us/step  warm {warm_us:.1f} us/step  "
         f"stages(us) " + " ".join(f"{n}={stage_ms[:, k].mean() * 1e3:.1f}" for k, n in enumerate(stage_names)))
 
+    rows = None if args.no_rows else measure_rows(M, workloads, dev, evict)
+
     # ---- CPU baseline: the oracle on the machine's host cores --------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -307,8 +311,126 @@ def main():
                      "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
+        "rows": rows,
     }
     print(json.dumps(res), flush=True)
+
+
+def _params_for(M, w, **kw):
+    base = dict(batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, capacity_tokens=w.capacity,
+                dtype=w.dtype, tokens_per_centroid=w.tokens_per_centroid, cluster_block=w.cluster_block,
+                build_iters=w.build_iters, update_iters=w.update_iters,
+                coarse_tokens_per_centroid=w.coarse_tokens_per_centroid,
+                coarse_candidate_tokens=w.coarse_candidate_tokens, seed=0)
+    base.update(kw)
+    return M.Params(**base)
+
+
+def _cold_decode_us(M, p, qs, Kd, Vd, n_total, state, T, ws, evict):
+    """Median cold decode time (µs) over the given queries, caches evicted
+    before each step, events on the launch stream."""
+    import numpy as np
+    import torch
+    ts = []
+    for q in qs:
+        evict()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        M.decode(p, q, Kd, Vd, n_total, state, T, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return float(np.median(ts))
+
+
+def measure_rows(M, workloads, dev, evict):
+    """The other rows of the path on their own workloads: the online window
+    update (a new 8192-token block clustered, 5 rounds, batch 4) with a decode
+    over the unclustered tail, and the hierarchical decode at 131072 tokens.
+    Rooflines: the update's assign contraction against the bf16 matrix-core
+    peak, the decodes against HBM."""
+    import numpy as np
+    import torch
+    rows = {}
+    d = 128
+    # ---- online update (H3) and decode with a tail ----------------------------
+    w = workloads.WORKLOADS["qwen3-8b-layer-b4-online"]
+    K, V, means = workloads.make_cache(w)
+    Kd, Vd = K.to(dev), V.to(dev)
+    p = _params_for(M, w)
+    st = M.ClusterState(p, dev)
+    M.build_clusters(p, Kd, Vd, w.n_tokens, st)
+    n = w.n_tokens
+    U = p.units
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    M.update_window(p, Kd, Vd, n + w.cluster_block, st)
+    b.record()
+    torch.cuda.synchronize()
+    upd_ms = a.elapsed_time(b)
+    n += w.cluster_block
+    flop = 2.0 * U * w.cluster_block * (w.cluster_block // w.tokens_per_centroid) * d * w.update_iters
+    tail = 4096
+    M.update_window(p, Kd, Vd, n + tail, st)  # tail only: no block completes
+    T = w.budgets[0]
+    ws = M.Workspace().get(p, st, dev)
+    qs = [workloads.make_queries(w, means, s).to(dev) for s in range(12)]
+    dbg = M.DecodeDebug.allocate(p, st, dev)
+    M.decode(p, qs[0], Kd, Vd, n + tail, st, T, workspace=ws, debug=dbg)
+    E = int(dbg.exact_tokens.sum())
+    C = st.n_clusters
+    byts = p.batch * p.n_q_heads * d * (2 + 4) + U * C * (2 * d * 2 + 4) + E * 2 * d * 2 + U * tail * 2 * d * 2
+    us = _cold_decode_us(M, p, qs[2:], Kd, Vd, n + tail, st, T, ws, evict)
+    rows["H3_online_update"] = {
+        "workload": w.name, "block_tokens": w.cluster_block, "rounds": w.update_iters, "ms": round(upd_ms, 3),
+        "roofline": {"bound": "mfma", "achieved": round(flop / (upd_ms * 1e-3) / 1e12, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(flop / (upd_ms * 1e-3) / 1e12 / 2500.0, 4)}}
+    rows["H3_decode_with_tail"] = {
+        "workload": w.name, "n_clustered": n, "tail_tokens": tail, "token_budget": T, "us_per_step": round(us, 2),
+        "algorithmic_MB": round(byts / 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(byts / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+    log(f"[bench] H3 update {upd_ms:.3f} ms, decode with {tail}-token tail {us:.1f} us")
+    del K, V, Kd, Vd, st, ws
+    torch.cuda.empty_cache()
+    # ---- hierarchical decode (H8) ---------------------------------------------
+    w = workloads.WORKLOADS["qwen3-8b-layer-b4-128k-hier"]
+    K, V, means = workloads.make_cache(w)
+    Kd, Vd = K.to(dev), V.to(dev)
+    p = _params_for(M, w)
+    st = M.ClusterState(p, dev)
+    M.build_clusters(p, Kd, Vd, w.n_tokens, st)
+    torch.cuda.synchronize()
+    a.record()
+    M.build_clusters(p, Kd, Vd, w.n_tokens, st)
+    b.record()
+    torch.cuda.synchronize()
+    build_ms = a.elapsed_time(b)
+    U, N, T = p.units, w.n_tokens, w.budgets[0]
+    ws = M.Workspace().get(p, st, dev)
+    qs = [workloads.make_queries(w, means, s).to(dev) for s in range(12)]
+    dbg = M.DecodeDebug.allocate(p, st, dev)
+    M.decode(p, qs[0], Kd, Vd, N, st, T, workspace=ws, debug=dbg)
+    E = int(dbg.exact_tokens.sum())
+    cand = dbg.candidates.cpu().numpy().astype(bool)           # [B][Hkv][D]
+    coff = st.coarse_offsets.cpu().numpy()                      # [B][Hkv][D+1]
+    D = st.n_coarse
+    fine_in_cand = int(((coff[..., 1:D + 1] - coff[..., :D]) * cand[..., :D]).sum())
+    # coarse K̄ and V̄ and sizes of every coarse cluster; fine K̄, V̄ and sizes of
+    # the fine clusters inside the candidates; the exact rows; queries, output
+    byts = U * D * (2 * d * 2 + 4) + fine_in_cand * (2 * d * 2 + 4 + 4) + E * 2 * d * 2 \
+        + p.batch * p.n_q_heads * d * (2 + 4)
+    us = _cold_decode_us(M, p, qs[2:], Kd, Vd, N, st, T, ws, evict)
+    rows["H8_hierarchical_decode"] = {
+        "workload": w.name, "token_budget": T, "coarse_candidate_tokens": w.coarse_candidate_tokens,
+        "build_ms": round(build_ms, 2), "us_per_step": round(us, 2), "algorithmic_MB": round(byts / 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(byts / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+    log(f"[bench] H8 build {build_ms:.1f} ms, hierarchical decode {us:.1f} us ({byts / 1e6:.1f} MB)")
+    del K, V, Kd, Vd, st, ws
+    torch.cuda.empty_cache()
+    return rows
 
 
 def _unit_traffic_bytes():

@@ -21,6 +21,7 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxFinePerBlockHier = 2048;
 constexpr int kMaxCoarsePerBlock = 64;
 constexpr int kMaxDecodeClusters = 32768;  // selection bitmask held in LDS
+constexpr int kUnitPathMinUnits = 16;      // fewer units: the split launches
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -228,7 +229,7 @@ const char* kUnitStages[] = {"unit"};
 bool unit_path(const mpattn_params* p) {
     if (is_hier(p) || p->splits > 0 || p->dtype != MPATTN_BF16) return false;
     const int G = p->n_q_heads / p->n_kv_heads;
-    return unit_path_fits(p->dtype, G, mpattn_max_clusters(p)) && p->batch * p->n_kv_heads >= 64;
+    return unit_path_fits(p->dtype, G, mpattn_max_clusters(p)) && p->batch * p->n_kv_heads >= kUnitPathMinUnits;
 }
 const char* kHierStages[] = {"coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"};
 

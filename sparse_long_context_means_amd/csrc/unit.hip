@@ -289,7 +289,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     const int32_t* ofu = a.offsets + (size_t)unit * (a.Cmax + 1);
     const int cs = (int)((int64_t)C * rep / R), ce = (int)((int64_t)C * (rep + 1) / R);  // approximate-term share
 
-    const T* qb = reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim + li * 8;
     const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
     const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim;
     // one pass over clusters [lo, hi) by nw waves (this one is wave wv of
@@ -595,17 +594,21 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      (rg, li) receives rows 4 rg + e for head li); the wave keeps one
     //      reference exponent per head, raised lazily as in SoftState; the
     //      weights go through a per-wave LDS tile to the row groups, which
-    //      accumulate rows 4 rg + e of the step into their value sums. -------
-    QSlice<T> qs[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) qs[g].load(qb + (size_t)g * kHeadDim);
+    //      accumulate rows 4 rg + e of the step into their value sums.  The
+    //      rows are the selected clusters' members [0, E) followed by the
+    //      unclustered tail [E, E + Tn); a staged tail row holds -1 - token
+    //      and is read from K, V instead of the exact-row source. ------------
     const float qscale = kInvSqrtD * kLog2e;
-    const size_t ubase = (size_t)unit * a.Nmax * kHeadDim + li * 8;
+    const size_t ubase = (size_t)unit * a.Nmax * kHeadDim;
     const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
-    const int e0 = (int)((int64_t)E * rep / R), e1 = (int)((int64_t)E * (rep + 1) / R);
+    const int Tn = a.n_total - a.n_clustered;
+    const int Et = E + Tn;
+    const int e0 = (int)((int64_t)Et * rep / R), e1 = (int)((int64_t)Et * (rep + 1) / R);
     {
-        const bf16_t* Kx = reinterpret_cast<const bf16_t*>(a.Kx) + (size_t)unit * a.Nmax * kHeadDim;
-        const bf16_t* Vx = reinterpret_cast<const bf16_t*>(a.Vx) + ubase;
+        const bf16_t* Kx = reinterpret_cast<const bf16_t*>(a.Kx) + ubase;
+        const bf16_t* Vx = reinterpret_cast<const bf16_t*>(a.Vx) + ubase + li * 8;
+        const bf16_t* Kt = reinterpret_cast<const bf16_t*>(a.K) + ubase;
+        const bf16_t* Vt = reinterpret_cast<const bf16_t*>(a.V) + ubase + li * 8;
         QOperand qop;
         load_qop<G>(qop, qg, lane);
         // the wave's reference exponent of head li (entering: the same in
@@ -618,7 +621,18 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
             const int cnt = min(kUnitRowBatch, e1 - c0);
             lds_barrier();  // the previous batch is consumed
-            stage_exact(s_row, s_spre, s_soff, nsel, tids, c0, cnt);
+            for (int i = tid; i < cnt; i += kUnitThreads) {
+                const int r = c0 + i;
+                int v;
+                if (r < E) {  // member r - pre[k] of selected cluster k
+                    const int k = upper_index(s_spre, nsel, r);
+                    const int pos = s_soff[k] + r - s_spre[k];
+                    v = tids ? tids[pos] : pos;
+                } else {
+                    v = -1 - (a.n_clustered + r - E);
+                }
+                s_row[i] = v;
+            }
             lds_barrier();
             // 16-row blocks: the older waves 0-3 (first in issue order on
             // their SIMDs, measured to finish their share ~25% sooner) take
@@ -634,11 +648,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             auto load_step = [&](ExactRows16& rr, int step) {
                 const int ib = blk(step) * 16;
                 const int ik = ib + li;
-                load_row_blocks(rr.k, Kx + (size_t)s_row[ik < cnt ? ik : 0] * kHeadDim, lane);
+                const int rk = s_row[ik < cnt ? ik : 0];
+                load_row_blocks(rr.k, rk >= 0 ? Kx + (size_t)rk * kHeadDim : Kt + (size_t)(-1 - rk) * kHeadDim, lane);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int iv = ib + 4 * rg + e;
-                    rr.v[e].load(Vx + (size_t)s_row[iv < cnt ? iv : 0] * kHeadDim);
+                    const int rv = s_row[iv < cnt ? iv : 0];
+                    rr.v[e].load(rv >= 0 ? Vx + (size_t)rv * kHeadDim : Vt + (size_t)(-1 - rv) * kHeadDim);
                 }
             };
             ExactRows16 ring[kExactDepth];
@@ -711,26 +727,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             st.l[g] += __shfl(lp, rg * 16 + g, kWave);
         }
     }
-    // ---- unclustered tail, exactly -----------------------------------------
-    {
-        const int Tn = a.n_total - a.n_clustered;
-        const int t0 = (int)((int64_t)Tn * rep / R), t1 = (int)((int64_t)Tn * (rep + 1) / R);
-        const T* Kt = reinterpret_cast<const T*>(a.K) + ubase;
-        const T* Vt = reinterpret_cast<const T*>(a.V) + ubase;
-        for (int base = t0 + wave * 8; base < t1; base += 8 * kUnitWaves) {
-            RowBuf<T> bf;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = base + u * 4 + rg;
-                bf.ok[u] = i < t1;
-                const int r = a.n_clustered + (bf.ok[u] ? i : t0);
-                bf.k[u].load(Kt + (size_t)r * kHeadDim);
-                bf.v[u].load(Vt + (size_t)r * kHeadDim);
-            }
-            exact_step<T, G>(st, qs, qscale, bf);
-        }
-    }
-
     // ---- combine the row groups: 4 per wave by shuffles, then the waves
     //      through LDS (in wave order) ---------------------------------------
 #pragma unroll
