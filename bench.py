@@ -238,6 +238,30 @@ def main():
     log(f"[bench] cold {cold_us:.1f} us/step  warm {warm_us:.1f} us/step  "
         f"stages(us) " + " ".join(f"{n}={stage_ms[:, k].mean() * 1e3:.1f}" for k, n in enumerate(stage_names)))
 
+    # ---- dense split-K decode of the same step (the pages' comparison point) --
+    dense = None
+    if not args.no_rows:
+        dws = torch.empty(int(M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 1, 0, M.OP_DENSE)), dtype=torch.uint8,
+                          device=dev)
+        dts = []
+        for i in range(min(10, args.steps)):
+            evict()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            M.dense_decode(p, qs[args.warmup + i], Kd, Vd, N, out=out, workspace=dws)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            dts.append(a_.elapsed_time(b_) * 1e3)
+        dense_us = float(np.median(dts))
+        dense_bytes = U * N * d * 2 * 2 + B * Hq * d * (2 + 4)
+        dense = {"us_per_step": round(dense_us, 2), "algorithmic_MB": round(dense_bytes / 1e6, 1),
+                 "roofline": {"bound": "hbm", "achieved": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(dense_bytes / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+                 "sparse_speedup": round(dense_us / cold_us, 2)}
+        log(f"[bench] dense split-K decode {dense_us:.1f} us/step ({dense_us / cold_us:.2f}x the sparse step)")
+        del dws
+
     rows = None if args.no_rows else measure_rows(M, workloads, dev, evict)
 
     # ---- CPU baseline: the oracle on the machine's host cores --------------------
@@ -311,6 +335,7 @@ def main():
                      "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
+        "dense_reference": dense,
         "rows": rows,
     }
     print(json.dumps(res), flush=True)

@@ -56,7 +56,7 @@ typedef enum {
 
 typedef enum { MPATTN_F32 = 0, MPATTN_BF16 = 1 } mpattn_dtype;
 
-typedef enum { MPATTN_OP_BUILD = 0, MPATTN_OP_UPDATE = 1, MPATTN_OP_DECODE = 2 } mpattn_op;
+typedef enum { MPATTN_OP_BUILD = 0, MPATTN_OP_UPDATE = 1, MPATTN_OP_DECODE = 2, MPATTN_OP_DENSE = 3 } mpattn_op;
 
 typedef enum {
     MPATTN_MODE_MULTIPOLE = 0, /* unselected clusters approximated by their value centroids */
@@ -215,6 +215,23 @@ mpattn_status mpattn_update_window(const mpattn_params* params, const void* k, c
 mpattn_status mpattn_decode(const mpattn_params* params, const void* q, const void* k, const void* v,
                             int32_t n_tokens_total, const mpattn_state* state, int32_t token_budget,
                             int32_t mode, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense decode: exact attention of every query head over all tokens
+ * [0, n_tokens) of its KV head, the comparison point of the sparse decode
+ * (pages: atlas summary, "Key results": the speedups are quoted against a
+ * split-K dense decode).  out[b][hq] = sum_i e^{l_i} v_i / sum_i e^{l_i} with
+ * l_i = q_hq . k_i / sqrt(d).  The tokens are split into ranges processed in
+ * parallel, then merged (log-sum-exp).  bf16 storage only.
+ *   q: device [B][Hq][d]; k, v: device [B][Hkv][capacity_tokens][d];
+ *   out: device [B][Hq][d] fp32.  workspace: mpattn_workspace_bytes(...,
+ *   MPATTN_OP_DENSE) bytes, no initial contents needed.
+ * Errors: INVALID_ARG (null, n_tokens < 1 or > capacity_tokens), UNSUPPORTED
+ * (fp32 storage), WORKSPACE, HIP.
+ */
+mpattn_status mpattn_dense_decode(const mpattn_params* params, const void* q, const void* k, const void* v,
+                                  int32_t n_tokens, float* out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Number of kernel stages one decode enqueues (for timing stage by stage):
  * 6 for the hierarchical method (coarse_score, coarse_select, fine_score,

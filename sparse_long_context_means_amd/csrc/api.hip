@@ -168,6 +168,13 @@ uint32_t next_tag() {
     }
 }
 
+// Dense decode workspace: partials [U][G][S][2] and [U][G][S][d].
+size_t dense_ws_bytes(const mpattn_params* p) {
+    const size_t U = (size_t)p->batch * p->n_kv_heads, G = (size_t)(p->n_q_heads / p->n_kv_heads);
+    const size_t S = (size_t)dense_splits((int)U);
+    return align_up(U * G * S * 2 * 4) + align_up(U * G * S * kD * 4);
+}
+
 mpattn_status hip_status(hipError_t e) { return e == hipSuccess ? MPATTN_OK : MPATTN_ERR_HIP; }
 
 #define MPA_TRY(expr)                                  \
@@ -267,6 +274,7 @@ size_t mpattn_workspace_bytes(const mpattn_params* p, int32_t capacity_clusters,
                               int32_t op) {
     if (check_params(p) != MPATTN_OK || capacity_clusters < 1 || capacity_coarse < 0) return (size_t)-1;
     if (op == MPATTN_OP_BUILD || op == MPATTN_OP_UPDATE) return 0;
+    if (op == MPATTN_OP_DENSE) return dense_ws_bytes(p);
     if (op != MPATTN_OP_DECODE) return (size_t)-1;
     return layout_decode(p, capacity_clusters, capacity_coarse, nullptr).bytes;
 }
@@ -510,6 +518,27 @@ mpattn_status mpattn_decode(const mpattn_params* p, const void* q, const void* k
     if (n == 0) return check_params(p) == MPATTN_OK ? MPATTN_ERR_INVALID_ARG : check_params(p);
     return mpattn_decode_ex(p, q, k, v, n_tokens_total, st, token_budget, mode, out, workspace, workspace_bytes,
                             stream, nullptr, 0, n - 1);
+}
+
+mpattn_status mpattn_dense_decode(const mpattn_params* p, const void* q, const void* k, const void* v,
+                                  int32_t n_tokens, float* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    mpattn_status rc = check_params(p);
+    if (rc != MPATTN_OK) return rc;
+    if (!q || !k || !v || !out) return MPATTN_ERR_INVALID_ARG;
+    if (n_tokens < 1 || n_tokens > p->capacity_tokens) return MPATTN_ERR_INVALID_ARG;
+    if (p->dtype != MPATTN_BF16) return MPATTN_ERR_UNSUPPORTED;
+    const size_t need = dense_ws_bytes(p);
+    if (!workspace || workspace_bytes < need) return MPATTN_ERR_WORKSPACE;
+    const int U = p->batch * p->n_kv_heads, G = p->n_q_heads / p->n_kv_heads;
+    const int S = dense_splits(U);
+    float* part_ml = (float*)workspace;
+    float* part_acc = (float*)((char*)workspace + align_up((size_t)U * G * S * 2 * 4));
+    DenseArgs a{q, k, v, p->capacity_tokens, n_tokens, p->n_q_heads, p->n_kv_heads, part_ml, part_acc};
+    const hipStream_t s = (hipStream_t)stream;
+    MPA_TRY(launch_dense(G, a, U, S, s));
+    MPA_TRY(launch_merge(part_ml, part_acc, U, G, S, p->n_kv_heads, out, s));
+    return MPATTN_OK;
 }
 
 mpattn_status mpattn_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -160,6 +160,95 @@ __device__ __forceinline__ float head_mean(float s) {
     return s * (1.0f / G);
 }
 
+// ---------------------------------------------------------------------------
+// Exact rows on the matrix cores, 16 per wave step.  Lane l loads the blocks
+// of key row l % 16 (the A operand) and the 8-element slices of value rows
+// 4 (l / 16) + e (e < 4), so row group l / 16 accumulates those four rows.  The
+// wave keeps one reference exponent per head (mv in lane l for head l % 16,
+// the same in every row group, raised lazily as in SoftState) and each lane
+// the weight sum lp of its rows 4 (l / 16) + e for head l % 16; the weights
+// reach the row groups through a per-wave LDS tile sp[16][G].
+// ---------------------------------------------------------------------------
+struct ExactRows16 {
+    Slice8<bf16_t> k[4], v[4];
+};
+
+// Matrix-core form of the state on entry (st.m the same in every row group).
+template <int G>
+__device__ __forceinline__ float exact16_enter(const SoftState<G>& st) {
+    const int li = threadIdx.x & 15;
+    float mv = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) mv = li == g ? st.m[g] : mv;
+    return mv;
+}
+
+// One step: rows first_row + e (e < 4) of row group l / 16 count while below
+// `cnt`; the others weigh nothing.
+template <int G>
+__device__ __forceinline__ void exact16_step(SoftState<G>& st, float& mv, float& lp, float* sp, const QOperand& qop,
+                                             const ExactRows16& rr, int first_row, int cnt, float qscale) {
+    const int lane = threadIdx.x & (kWave - 1), rg = lane >> 4, li = lane & 15;
+    const f32x4v d = mfma_scores(rr.k, qop);
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sv[e] = first_row + e < cnt ? d[e] * qscale : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const bool raise = li < G && mx > mv + kLazyMax;
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // rare, wave-uniform
+        const float sc = raise ? __builtin_amdgcn_exp2f(mv - mx) : 1.f;
+        mv = raise ? mx : mv;
+        lp *= sc;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), g));
+            st.l[g] *= sg;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) st.acc[g][x] *= sg;
+        }
+    }
+    float pe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pe[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - mv);
+        lp += pe[e];
+    }
+    if (li < G) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[(4 * rg + e) * G + li] = pe[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float pg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pg[g] = sp[(4 * rg + e) * G + g];
+        float x[8];
+        rr.v[e].unpack(x);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) st.acc[g][q] = fmaf(pg[g], x[q], st.acc[g][q]);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Back to the row-group form: the wave's reference, the row groups' sums.
+template <int G>
+__device__ __forceinline__ void exact16_leave(SoftState<G>& st, float mv, float lp) {
+    const int rg = (threadIdx.x & (kWave - 1)) >> 4;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        st.m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), g));
+        st.l[g] += __shfl(lp, rg * 16 + g, kWave);
+    }
+}
+
 template <typename T>
 struct RowBuf {
     Slice8<T> k[2], v[2];

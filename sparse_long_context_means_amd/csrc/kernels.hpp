@@ -188,6 +188,19 @@ int unit_replicas(int n_clusters, int units);
 bool unit_path_fits(int dtype, int G, int cmax);
 hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st);
 
+// ---- dense decode (dense.hip) ----------------------------------------------
+struct DenseArgs {
+    const void* q;               // [B][Hq][d] bf16
+    const void* K;               // [U][Nmax][d] bf16
+    const void* V;
+    int32_t Nmax, n_tokens, Hq, Hkv;
+    float* part_ml;              // [U][G][S][2]
+    float* part_acc;             // [U][G][S][d]
+};
+// Token splits of the dense decode for this many units.
+int dense_splits(int units);
+hipError_t launch_dense(int G, const DenseArgs& a, int units, int splits, hipStream_t st);
+
 // ---- measurement (probe.hip) ----------------------------------------------
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 

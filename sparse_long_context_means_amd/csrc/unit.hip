@@ -242,12 +242,6 @@ constexpr int kExactDepth = 2;                           // exact-row steps (16 
 constexpr uint64_t kExchangeWaitTicks = 2000;
 constexpr uint64_t kPartialWaitTicks = 100000;
 
-// One ring step of 16 exact rows of a wave: the lane's blocks of key row
-// l % 16 (matrix-core operand) and value rows 4 (l / 16) + e.
-struct ExactRows16 {
-    Slice8<bf16_t> k[4], v[4];
-};
-
 // Four rows of a row group (one ring step of the score or the value-centroid
 // stream).
 template <typename T>
@@ -613,9 +607,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         load_qop<G>(qop, qg, lane);
         // the wave's reference exponent of head li (entering: the same in
         // every row group) and the lane's weight sum of rows 4 rg + e, head li
-        float mv = 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) mv = li == g ? st.m[g] : mv;
+        float mv = exact16_enter<G>(st);
         float lp = 0.f;
         float* sp = s_p + wave * 16 * G;  // [16][G] weights of the step
         for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
@@ -667,65 +659,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             for (int it = 0; it < steps; it += kExactDepth) {
 #pragma unroll
                 for (int j = 0; j < kExactDepth; ++j) {
-                    const f32x4v d = mfma_scores(ring[j].k, qop);
-                    const int ib = blk(it + j) * 16 + 4 * rg;
-                    float sv[4];
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sv[e] = ib + e < cnt ? d[e] * qscale : -INFINITY;
-                        mx = fmaxf(mx, sv[e]);
-                    }
-                    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-                    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-                    const bool raise = li < G && mx > mv + kLazyMax;
-                    if (__builtin_amdgcn_ballot_w64(raise)) {  // rare, wave-uniform
-                        const float sc = raise ? __builtin_amdgcn_exp2f(mv - mx) : 1.f;
-                        mv = raise ? mx : mv;
-                        lp *= sc;
-#pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), g));
-                            st.l[g] *= sg;
-#pragma unroll
-                            for (int x = 0; x < 8; ++x) st.acc[g][x] *= sg;
-                        }
-                    }
-                    float pe[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pe[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - mv);
-                        lp += pe[e];
-                    }
-                    if (li < G) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sp[(4 * rg + e) * G + li] = pe[e];
-                    }
-                    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float pg[G];
-#pragma unroll
-                        for (int g = 0; g < G; ++g) pg[g] = sp[(4 * rg + e) * G + g];
-                        float x[8];
-                        ring[j].v[e].unpack(x);
-#pragma unroll
-                        for (int g = 0; g < G; ++g)
-#pragma unroll
-                            for (int q = 0; q < 8; ++q) st.acc[g][q] = fmaf(pg[g], x[q], st.acc[g][q]);
-                    }
-                    __builtin_amdgcn_wave_barrier();
+                    exact16_step<G>(st, mv, lp, sp, qop, ring[j], blk(it + j) * 16 + 4 * rg, cnt, qscale);
                     load_step(ring[j], it + j + kExactDepth);
                     __builtin_amdgcn_sched_barrier(0);  // keep the ring order
                 }
             }
         }
-        // back to the row-group form: reference of the wave, row-group sums
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            st.m[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), g));
-            st.l[g] += __shfl(lp, rg * 16 + g, kWave);
-        }
+        exact16_leave<G>(st, mv, lp);
     }
     // ---- combine the row groups: 4 per wave by shuffles, then the waves
     //      through LDS (in wave order) ---------------------------------------

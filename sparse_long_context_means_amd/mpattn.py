@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmpattn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-OP_BUILD, OP_UPDATE, OP_DECODE = 0, 1, 2
+OP_BUILD, OP_UPDATE, OP_DECODE, OP_DENSE = 0, 1, 2, 3
 MODE_MULTIPOLE, MODE_OMIT = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.mpattn_decode_stage_count.argtypes = [P]
     lib.mpattn_decode_stage_name.restype = ctypes.c_char_p
     lib.mpattn_decode_stage_name.argtypes = [P, i32]
+    lib.mpattn_dense_decode.restype = ctypes.c_int
+    lib.mpattn_dense_decode.argtypes = [P, _VP, _VP, _VP, i32, _VP, _VP, sz, _VP]
     lib.mpattn_read_probe.restype = ctypes.c_int
     lib.mpattn_read_probe.argtypes = [_VP, sz, _VP, _VP]
     return lib
@@ -309,6 +311,28 @@ def decode(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_token
                               token_budget, mode, _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(q.device), ctypes.byref(dbg) if dbg is not None else None, first, last)
     _raise(st, "mpattn_decode")
+    return out
+
+
+def dense_decode(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens: int,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense decode over tokens [0, n_tokens) (see mpattn_dense_decode);
+    returns out [B][Hq][d] float32."""
+    _check_cache(p, k, v)
+    qshape = (p.batch, p.n_q_heads, p.head_dim)
+    if tuple(q.shape) != qshape or q.dtype != p.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError(f"q must be a contiguous {p.dtype} CUDA tensor of shape {qshape}")
+    if out is None:
+        out = torch.empty(qshape, dtype=torch.float32, device=q.device)
+    cp = p.c()
+    if workspace is None:
+        n = int(lib.mpattn_workspace_bytes(ctypes.byref(cp), 1, 0, OP_DENSE))
+        if n == (1 << 64) - 1:
+            raise MpattnError(ERR_INVALID_ARG, "mpattn_workspace_bytes")
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = lib.mpattn_dense_decode(ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), n_tokens, _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(q.device))
+    _raise(st, "mpattn_dense_decode")
     return out
 
 

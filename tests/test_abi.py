@@ -193,3 +193,21 @@ def test_workspace_and_stages():
     small = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=1).c()), 2053, 0, M.OP_DECODE)
     big = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=64).c()), 2053, 0, M.OP_DECODE)
     assert big > small
+
+
+def test_dense_decode_validation():
+    p = _params()
+    cp = p.c()
+    need = M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 1, 0, M.OP_DENSE)
+    assert 0 < need < (1 << 40)
+    dense = lambda n, ws=1 << 40, q=FAKE, par=ctypes.byref(cp): M.lib.mpattn_dense_decode(
+        par, q, FAKE, FAKE, n, FAKE, FAKE, ws, None)
+    assert dense(0) == M.ERR_INVALID_ARG
+    assert dense(p.capacity_tokens + 1) == M.ERR_INVALID_ARG
+    assert dense(16, q=None) == M.ERR_INVALID_ARG
+    assert dense(16, ws=need - 1) == M.ERR_WORKSPACE
+    assert dense(16, par=None) == M.ERR_INVALID_ARG
+    pf = _params(dtype=torch.float32)
+    cpf = pf.c()
+    assert M.lib.mpattn_dense_decode(ctypes.byref(cpf), FAKE, FAKE, FAKE, 16, FAKE, FAKE, 1 << 40, None) == \
+        M.ERR_UNSUPPORTED

@@ -257,6 +257,26 @@ def _built(B=2, Hq=8, Hkv=2, N=4500, Bc=2048, splits=0, dt=torch.bfloat16, sorte
     return mp, w, K, V, means, p, state
 
 
+def test_dense_decode_matches_oracle():
+    """The dense split-K decode (the comparison point) against textbook
+    softmax attention on every head, with a token count that leaves a
+    ragged last tile, and against the sparse decode at a full budget."""
+    mp, w, K, V, means, p, state = _built(B=2, Hq=8, Hkv=2, N=4500)
+    G = p.group
+    for n_tok in (4500, 4433, 70):
+        q = queries(w, means, 40 + n_tok % 7)
+        out = mp.dense_decode(p, q.to(DEV), K.to(DEV), V.to(DEV), n_tok).cpu().numpy()
+        for b in range(p.batch):
+            for h in range(p.n_kv_heads):
+                ref = O.dense(q[b, h * G:(h + 1) * G], K[b, h, :n_tok], V[b, h, :n_tok])
+                ok, ea, er = close(out[b, h * G:(h + 1) * G], ref)
+                assert ok, (n_tok, b, h, ea, er)
+    q = queries(w, means, 50)
+    od = mp.dense_decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 4500).cpu().numpy()
+    of = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 4500, state, 4500).cpu().numpy()
+    np.testing.assert_allclose(od, of, rtol=1e-3, atol=2e-4)
+
+
 def test_full_budget_is_dense_attention():
     mp, w, K, V, means, p, state = _built()
     q = queries(w, means, 3)
