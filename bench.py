@@ -417,6 +417,47 @@ def measure_rows(M, workloads, dev, evict):
         "roofline": {"bound": "hbm", "achieved": round(byts / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
     log(f"[bench] H3 update {upd_ms:.3f} ms, decode with {tail}-token tail {us:.1f} us")
+    # ---- the update on a second stream while decodes continue on the first ---
+    main, side = torch.cuda.current_stream(dev), torch.cuda.Stream(dev)
+    n_total = w.n_tokens + w.cluster_block  # the new block is the tail until clustered
+    dq = qs[:8] * 4
+
+    def decodes(view):
+        evs = []
+        for q in dq:
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_a.record(main)
+            M.decode(p, q, Kd, Vd, n_total, view, T, workspace=ws)
+            e_b.record(main)
+            evs.append((e_a, e_b))
+        return evs
+
+    alone_st = M.ClusterState(p, dev)
+    M.build_clusters(p, Kd, Vd, w.n_tokens, alone_st)
+    evs = decodes(alone_st)
+    torch.cuda.synchronize()
+    dec_alone = float(np.median([x.elapsed_time(y) * 1e3 for x, y in evs]))
+    conc_st = M.ClusterState(p, dev)
+    M.build_clusters(p, Kd, Vd, w.n_tokens, conc_st)
+    origin = torch.cuda.Event(enable_timing=True)
+    origin.record(main)
+    side.wait_event(origin)
+    view, done, _ = M.update_window_concurrent(p, Kd, Vd, n_total, conc_st, side)
+    evs = decodes(view)
+    end = torch.cuda.Event(enable_timing=True)
+    end.record(side)
+    torch.cuda.synchronize()
+    upd_conc = origin.elapsed_time(end)
+    during = [x.elapsed_time(y) * 1e3 for x, y in evs if origin.elapsed_time(x) < upd_conc]
+    rows["H3_concurrent_update"] = {
+        "workload": w.name, "decodes_enqueued": len(dq),
+        "decode_us_alone": round(dec_alone, 2),
+        "decode_us_during_update": round(float(np.median(during)), 2) if during else None,
+        "decodes_during_update": len(during),
+        "update_ms_alone": round(upd_ms, 3), "update_ms_beside_decodes": round(upd_conc, 3)}
+    log(f"[bench] H3 concurrent: decode {dec_alone:.1f} us alone, "
+        f"{(np.median(during) if during else float('nan')):.1f} us during the update ({len(during)} decodes); "
+        f"update {upd_ms:.3f} ms alone, {upd_conc:.3f} ms beside decodes")
     del K, V, Kd, Vd, st, ws
     torch.cuda.empty_cache()
     # ---- hierarchical decode (H8) ---------------------------------------------

@@ -111,7 +111,7 @@ typedef struct mpattn_state {
     int32_t* coarse_sizes;           /* device [B][Hkv][Dmax]: member tokens of each coarse cluster */
     int32_t* coarse_offsets;         /* device [B][Hkv][Dmax+1]: start in coarse_members          */
     int32_t* coarse_members;         /* device [B][Hkv][Cmax]: non-empty fine ids by (coarse, fine);
-                                        a block's list starts at its first fine cluster id */
+                                        the blocks' lists follow each other */
     int32_t* parent;                 /* device [B][Hkv][Cmax]: coarse id of each fine cluster, -1 if empty */
     int32_t capacity_clusters;       /* Cmax >= mpattn_max_clusters(params) is always enough */
     int32_t capacity_coarse;         /* Dmax (0 for the flat method) */

@@ -320,18 +320,19 @@ def build_coarse(st: UnitState, *, coarse_tokens_per_centroid: int = 128, iters:
     st.coffsets = np.zeros(cap + 1, np.int32)
     st.cmembers = np.zeros(st.capacity_clusters, np.int32)
     st.cJ = []
-    g0 = 0
+    g0, pos = 0, 0
     for b in st.blocks:
         D = clusters_for(b.L, coarse_tokens_per_centroid)
         J = np.zeros(max(iters, 1))
         s0 = block_stream(seed, unit, b.index, 1)
-        # the block's member list starts at its first fine cluster id
+        # the blocks' member lists follow each other (non-empty fine ids only)
         n = _lib.orc_coarse_block(_d(st.kbar), _d(st.vbar), _i(st.sizes), d, b.c0, b.C, g0, D, iters,
-                                  st.storage, s0, b.c0, _d(st.cmu), _d(st.ckbar), _d(st.cvbar),
+                                  st.storage, s0, pos, _d(st.cmu), _d(st.ckbar), _d(st.cvbar),
                                   _i(st.csizes), _i(st.parent), _i(st.coffsets), _i(st.cmembers), _d(J))
         if n < 0:
             raise RuntimeError("orc_coarse_block failed (fewer non-empty fine clusters than coarse ones?)")
         g0 += D
+        pos += n
         st.cJ.append(J[:iters])
     st.n_coarse = g0
 

@@ -429,6 +429,16 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
         if (live) ids[carry + ex.x] = c0 + c;
         carry += tot.x;
     }
+    // the lists of the blocks follow each other: this block's starts after
+    // the non-empty fine clusters of the earlier blocks (of this build or
+    // update alike), so a block's end offset is the next block's start
+    int before = 0;
+    for (int base = 0; base < c0; base += 256) {
+        const int c = base + threadIdx.x;
+        int4 tot;
+        block256_exclusive_sum4(make_int4(c < c0 && su[c] > 0 ? 1 : 0, 0, 0, 0), tot, scan_lds);
+        before += tot.x;
+    }
     if (threadIdx.x == 0) s_m = carry;
     __syncthreads();
     const int m = s_m;
@@ -535,11 +545,11 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
     for (int c = threadIdx.x; c < C; c += 256) pu[c0 + c] = -1;
     __syncthreads();
     for (int i = threadIdx.x; i < m; i += 256) pu[ids[i]] = g0 + loc[i];
-    // member lists by (coarse, fine): one thread per coarse cluster
+    // member lists by (coarse, fine), one thread for the block
     int32_t* ou = coffsets + (size_t)unit * (cr.Dmax + 1);
     int32_t* mu_ = cmembers + (size_t)unit * g.Cmax;
     if (threadIdx.x == 0) {
-        int pos = c0;
+        int pos = before;
         for (int gg = 0; gg < Dfull; ++gg) {
             ou[g0 + gg] = pos;
             int tot = 0;

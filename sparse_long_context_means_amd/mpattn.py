@@ -7,10 +7,11 @@ the library has not been built; there is no fallback path.
 """
 from __future__ import annotations
 
+import copy
 import ctypes
 import os
 from dataclasses import dataclass, field
-from typing import Dict, Optional, Sequence
+from typing import Dict, Optional, Sequence, Tuple
 
 import torch
 
@@ -238,6 +239,26 @@ def update_window(p: Params, k: torch.Tensor, v: torch.Tensor, n_tokens_total: i
     _raise(st, "mpattn_update_window")
     state._take(cs)
     return state.n_blocks - before
+
+
+def update_window_concurrent(p: Params, k: torch.Tensor, v: torch.Tensor, n_tokens_total: int, state: ClusterState,
+                             stream: torch.cuda.Stream) -> Tuple[ClusterState, torch.cuda.Event, int]:
+    """Enqueues mpattn_update_window on `stream` and returns (view, event,
+    blocks added).  `view` is the state as it was before the update: the same
+    device arrays with the old host counters.  Decodes on other streams may go
+    on using it while the update runs, because the update writes only past the
+    old clusters (new centroids, sizes, member lists, sorted rows) and
+    rewrites the old clusters' end offset with its own value.  Once `event`
+    has completed (e.g. after stream.wait_event(event) on the decode stream),
+    `state` holds the new clusters.  Flat method only."""
+    if p.hierarchical:
+        raise ValueError("concurrent window update: flat method only")
+    view = copy.copy(state)
+    with torch.cuda.stream(stream):
+        added = update_window(p, k, v, n_tokens_total, state)
+        event = torch.cuda.Event()
+        event.record(stream)
+    return view, event, added
 
 
 class Workspace:

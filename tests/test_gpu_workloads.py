@@ -203,6 +203,45 @@ def test_online_update_phases():
     check_decode_units(p, state, q, K, V, n, T, out, dbg.selected.cpu().numpy(), range(p.units))
 
 
+def test_concurrent_update_leaves_the_old_state_usable():
+    """The window update on a second stream while decodes continue on the
+    first with the state as it was: every decode during the update gives the
+    bits of the decode on the old state, and after the update's event the
+    decode gives the bits of a serial update."""
+    mp = M()
+    w = workloads.WORKLOADS["qwen3-8b-layer-b4-online"]
+    K, V, means = workloads.make_cache(w)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    p = params_for(w)
+    T = w.budgets[0]
+    n_prompt, n_total = w.n_tokens, w.n_tokens + w.cluster_block
+    q = workloads.make_queries(w, means, 0).to(DEV)
+    # serial reference: before and after the update
+    ref_state = mp.ClusterState(p, DEV)
+    mp.build_clusters(p, Kd, Vd, n_prompt, ref_state)
+    before = mp.decode(p, q, Kd, Vd, n_total, ref_state, T).clone()
+    assert mp.update_window(p, Kd, Vd, n_total, ref_state) == 1
+    after = mp.decode(p, q, Kd, Vd, n_total, ref_state, T).clone()
+    assert not torch.equal(before, after)
+    # concurrent: decodes on the current stream while the update runs
+    state = mp.ClusterState(p, DEV)
+    mp.build_clusters(p, Kd, Vd, n_prompt, state)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    view, done, added = mp.update_window_concurrent(p, Kd, Vd, n_total, state, side)
+    assert added == 1 and view.n_clustered == n_prompt and state.n_clustered == n_total
+    ws = mp.Workspace().get(p, view, DEV)
+    outs = [mp.decode(p, q, Kd, Vd, n_total, view, T, workspace=ws).clone() for _ in range(12)]
+    overlapped = not done.query()  # the update was still running after the decodes were enqueued
+    torch.cuda.current_stream().wait_event(done)
+    new = mp.decode(p, q, Kd, Vd, n_total, state, T, workspace=ws)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, before)
+    assert torch.equal(new, after)
+    print("update still running while the decodes were enqueued:", overlapped)
+
+
 def test_update_equals_build_on_gpu():
     """Clustering a prompt and then appending aligned blocks gives the state
     one build over the whole length gives, when the round counts agree."""
