@@ -260,6 +260,8 @@ def main():
                               "frac": round(dense_bytes / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
                  "sparse_speedup": round(dense_us / cold_us, 2)}
         log(f"[bench] dense split-K decode {dense_us:.1f} us/step ({dense_us / cold_us:.2f}x the sparse step)")
+        dense["ablation"] = measure_ablation(M, p, [qs[args.warmup + i] for i in range(min(8, args.steps))],
+                                             Kd, Vd, N, state, T, ws, dws, evict)
         del dws
 
     rows = None if args.no_rows else measure_rows(M, workloads, dev, evict)
@@ -351,7 +353,7 @@ def _params_for(M, w, **kw):
     return M.Params(**base)
 
 
-def _cold_decode_us(M, p, qs, Kd, Vd, n_total, state, T, ws, evict):
+def _cold_decode_us(M, p, qs, Kd, Vd, n_total, state, T, ws, evict, mode=0):
     """Median cold decode time (µs) over the given queries, caches evicted
     before each step, events on the launch stream."""
     import numpy as np
@@ -361,11 +363,45 @@ def _cold_decode_us(M, p, qs, Kd, Vd, n_total, state, T, ws, evict):
         evict()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        M.decode(p, q, Kd, Vd, n_total, state, T, workspace=ws)
+        M.decode(p, q, Kd, Vd, n_total, state, T, mode=mode, workspace=ws)
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b) * 1e3)
     return float(np.median(ts))
+
+
+def measure_ablation(M, p, qs, Kd, Vd, n_total, state, T, ws, dws, evict):
+    """Output error against exact dense attention, and cold time, of the
+    shared selection with centroid terms (the method), the same selection
+    with the unselected clusters dropped, and per-query-head selection with
+    centroid terms.  Error per query head: ||o - o_dense|| / ||o_dense||."""
+    import numpy as np
+    import torch
+    modes = {"multipole": M.MODE_MULTIPOLE, "omit": M.MODE_OMIT, "per_head": M.MODE_PER_HEAD}
+    errs = {k: [] for k in modes}
+    exact = {k: 0 for k in modes}
+    for q in qs:
+        ref = M.dense_decode(p, q, Kd, Vd, n_total, workspace=dws).double()
+        for name, md in modes.items():
+            dbg = M.DecodeDebug.allocate(p, state, q.device, per_head=md == M.MODE_PER_HEAD)
+            o = M.decode(p, q, Kd, Vd, n_total, state, T, mode=md, workspace=ws, debug=dbg).double()
+            e = (o - ref).norm(dim=-1) / ref.norm(dim=-1)
+            errs[name].append(e.flatten().cpu())
+            rows = int(dbg.exact_tokens.sum())
+            exact[name] += rows * (1 if md == M.MODE_PER_HEAD else p.group)
+    torch.cuda.synchronize()
+    res = {}
+    for name, md in modes.items():
+        e = torch.cat(errs[name]).numpy()
+        res[name] = {"rel_l2_err_mean": float(f"{e.mean():.4g}"), "rel_l2_err_p99": float(f"{np.percentile(e, 99):.4g}"),
+                     "rel_l2_err_max": float(f"{e.max():.4g}"),
+                     "exact_rows_per_query_head": round(exact[name] / (len(qs) * p.batch * p.n_q_heads), 1),
+                     "cold_us_per_step": round(_cold_decode_us(M, p, qs, Kd, Vd, n_total, state, T, ws, evict,
+                                                               mode=md), 2)}
+        log(f"[bench] ablation {name}: rel err mean {e.mean():.4f} max {e.max():.4f}  "
+            f"{res[name]['cold_us_per_step']:.1f} us/step")
+    res["queries"] = f"{len(qs)} decode steps x {p.batch * p.n_q_heads} query heads, budget {T} tokens"
+    return res
 
 
 def measure_rows(M, workloads, dev, evict):

@@ -60,7 +60,8 @@ typedef enum { MPATTN_OP_BUILD = 0, MPATTN_OP_UPDATE = 1, MPATTN_OP_DECODE = 2, 
 
 typedef enum {
     MPATTN_MODE_MULTIPOLE = 0, /* unselected clusters approximated by their value centroids */
-    MPATTN_MODE_OMIT = 1       /* unselected clusters dropped (the ablation the pages compare with) */
+    MPATTN_MODE_OMIT = 1,      /* unselected clusters dropped (the ablation the pages compare with) */
+    MPATTN_MODE_PER_HEAD = 2   /* as MULTIPOLE, but every query head ranks and cuts on its own scores */
 } mpattn_mode;
 
 /* Shape and method parameters (host struct, read-only for the library). */
@@ -202,7 +203,13 @@ mpattn_status mpattn_update_window(const mpattn_params* params, const void* k, c
  *       / (sum_exact e^{l_i}     + sum_unselected n_c e^{s_c})
  * where the exact set is every token of a selected cluster plus the
  * unclustered tail [n_clustered, n_tokens_total).  MPATTN_MODE_OMIT drops the
- * unselected terms.  The hierarchical method (coarse level present) first
+ * unselected terms.  MPATTN_MODE_PER_HEAD is the alternative to the shared
+ * selection (the pages do not say who selects under grouped-query attention):
+ * each query head ranks the clusters of its KV head by its own s_c and takes
+ * its own cut under token_budget, so one KV head may read up to G different
+ * exact sets; it runs on the one-launch path only (UNSUPPORTED elsewhere), and
+ * its inspection outputs are per query head ([B][Hq][C] selected, [B][Hq]
+ * exact_tokens, [B][Hq][C] scores).  The hierarchical method (coarse level present) first
  * selects coarse candidates under coarse_candidate_tokens, then selects fine
  * clusters inside them; unselected fine clusters of candidates and all
  * non-candidate coarse clusters give the approximate terms.
@@ -236,7 +243,7 @@ mpattn_status mpattn_dense_decode(const mpattn_params* params, const void* q, co
 /* Number of kernel stages one decode enqueues (for timing stage by stage):
  * 6 for the hierarchical method (coarse_score, coarse_select, fine_score,
  * fine_select, attend, merge); for the flat method 1 (unit) when the whole
- * step of a unit runs in one launch -- bf16 storage, splits = 0, at least 64
+ * step of a unit runs in one launch -- bf16 storage, splits = 0, at least 16
  * units and at most 4096 clusters per unit -- else 4 (score, select, attend,
  * merge).  Both forms compute the same cut and, up to fp32 summation order,
  * the same output. */

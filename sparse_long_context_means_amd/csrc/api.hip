@@ -86,6 +86,7 @@ struct DecodeWs {
     uint64_t* xpart;      // [U][Rx][G][d + 2] partials
     uint64_t* xcount;     // [U] arrival words
     int32_t Rx;           // most replicas a decode on this layout uses
+    int32_t Rxh;          // the same when each query head is its own unit
     float* s;             // [U][Cmax][G] scores by cluster id
     int4* rs;             // [U][Cmax] cut records by item
     uint32_t* selmask;    // [U][Cw] selected clusters
@@ -122,11 +123,17 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
         return ptr;
     };
     if (unit_path(p)) {
+        // sized for both unit layouts: one unit per KV head (G heads each),
+        // or one per query head (per-head selection)
         w.Rx = unit_replicas(mpattn_max_clusters(p), (int)U);
-        if (w.Rx > 1) {
-            w.xch = (uint64_t*)take(U * w.Rx * Cmax * 8);
-            w.xpart = (uint64_t*)take(U * w.Rx * G * (kD + 2) * 8);
-            w.xcount = (uint64_t*)take(U * 8);
+        w.Rxh = unit_replicas(mpattn_max_clusters(p), (int)(U * G));
+        const size_t r1 = w.Rx > 1 ? U * w.Rx : 0, rh = w.Rxh > 1 ? U * G * w.Rxh : 0;
+        if (r1 + rh > 0) {
+            const size_t words = r1 > rh ? r1 : rh;
+            const size_t parts = r1 * G > rh ? r1 * G : rh;
+            w.xch = (uint64_t*)take(words * Cmax * 8);
+            w.xpart = (uint64_t*)take(parts * (kD + 2) * 8);
+            w.xcount = (uint64_t*)take(U * G * 8);
         }
     }
     w.s = (float*)take(U * Cmax * G * 4);
@@ -364,9 +371,11 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     if (st->n_clusters < 1 || st->n_clusters > st->capacity_clusters) return MPATTN_ERR_INVALID_ARG;
     if (n_tokens_total < st->n_clustered || n_tokens_total > p->capacity_tokens) return MPATTN_ERR_INVALID_ARG;
     if (token_budget < 0) return MPATTN_ERR_INVALID_ARG;
-    if (mode != MPATTN_MODE_MULTIPOLE && mode != MPATTN_MODE_OMIT) return MPATTN_ERR_INVALID_ARG;
+    if (mode != MPATTN_MODE_MULTIPOLE && mode != MPATTN_MODE_OMIT && mode != MPATTN_MODE_PER_HEAD)
+        return MPATTN_ERR_INVALID_ARG;
     const bool hier = is_hier(p);
     if (hier && mode != MPATTN_MODE_MULTIPOLE) return MPATTN_ERR_UNSUPPORTED;
+    if (mode == MPATTN_MODE_PER_HEAD && !unit_path(p)) return MPATTN_ERR_UNSUPPORTED;
     if (st->capacity_clusters > kMaxDecodeClusters || st->capacity_coarse > kMaxDecodeClusters)
         return MPATTN_ERR_UNSUPPORTED;
     if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
@@ -387,13 +396,17 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const int32_t Cmax = st->capacity_clusters, Dmax = st->capacity_coarse, N = p->capacity_tokens;
     const int32_t C = st->n_clusters;
     const bool sorted = st->sorted_keys != nullptr;
-    const int32_t want_pseudo = mode == MPATTN_MODE_MULTIPOLE ? 1 : 0;
+    const int32_t want_pseudo = mode != MPATTN_MODE_OMIT ? 1 : 0;
     const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
     const int32_t P = S;  // partial slots: one per attend split
 
     if (unit_path(p)) {  // one stage
-        const int R = unit_replicas(C, U);
-        if (R > 1 && R > w.Rx) return MPATTN_ERR_WORKSPACE;
+        // per-head selection: each query head is a unit of one head that
+        // reads the clusters and cache of its KV head
+        const bool per_head = mode == MPATTN_MODE_PER_HEAD;
+        const int Uv = per_head ? U * G : U, Gv = per_head ? 1 : G;
+        const int R = unit_replicas(C, Uv);
+        if (R > 1 && R > (per_head ? w.Rxh : w.Rx)) return MPATTN_ERR_WORKSPACE;
         UnitArgs a{};
         a.q = q;
         a.kbar = st->key_centroids;
@@ -413,7 +426,8 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         a.budget = token_budget;
         a.pseudo = want_pseudo;
         a.Hq = p->n_q_heads;
-        a.Hkv = p->n_kv_heads;
+        a.Hkv = per_head ? p->n_q_heads : p->n_kv_heads;
+        a.ugroup = per_head ? G : 1;
         a.out = out;
         a.xch = w.xch;
         a.xpart = w.xpart;
@@ -423,7 +437,7 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         a.dbg_selected = debug ? debug->selected : nullptr;
         a.dbg_exact = debug ? debug->exact_tokens : nullptr;
         a.rescore = debug ? debug->rescore : 0;
-        MPA_TRY(launch_unit_decode(p->dtype, G, a, U, R, s));
+        MPA_TRY(launch_unit_decode(p->dtype, Gv, a, Uv, R, s));
         return MPATTN_OK;
     }
 

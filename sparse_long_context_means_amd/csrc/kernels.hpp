@@ -167,7 +167,8 @@ struct UnitArgs {
     const void* V;
     int32_t Cmax, C, Nmax, n_clustered, n_total, budget;
     int32_t pseudo;              // 1: approximate unselected clusters; 0: omit them
-    int32_t Hq, Hkv;
+    int32_t Hq, Hkv;             // Hkv: units per sequence
+    int32_t ugroup;              // units per state unit (1; G when each query head is its own unit)
     float* out;                  // [B][Hq][d]
     // replica exchange (several replicas): words are (tag << 32 | 32-bit value)
     uint64_t* xch;               // [U][R][Cmax]: keys, slot r read by replica r

@@ -279,12 +279,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     const int rg = lane >> 4, li = lane & 15;
     const int C = a.C;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
-    const int32_t* szu = a.sizes + (size_t)unit * a.Cmax;
-    const int32_t* ofu = a.offsets + (size_t)unit * (a.Cmax + 1);
+    const int su = unit / a.ugroup;  // the unit's clusters and cache (shared by a group when per head)
+    const int32_t* szu = a.sizes + (size_t)su * a.Cmax;
+    const int32_t* ofu = a.offsets + (size_t)su * (a.Cmax + 1);
     const int cs = (int)((int64_t)C * rep / R), ce = (int)((int64_t)C * (rep + 1) / R);  // approximate-term share
 
     const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
-    const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim;
+    const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)su * a.Cmax * kHeadDim;
     // one pass over clusters [lo, hi) by nw waves (this one is wave wv of
     // them); the first pass (all waves) also brings the cluster records to
     // LDS while its first centroid rows are in flight, and only it writes the
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      1), stream through a ring of kPseudoDepth steps of 4 rows per row
     //      group.  Waves 4-7 run it over every cluster of the share while
     //      waves 0-3 take the cut; the selected clusters are taken out after.
-    const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+    const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)su * a.Cmax * kHeadDim + li * 8;
     constexpr int kCutWaves = 4, kStreamWaves = kUnitWaves - kCutWaves;
     constexpr int kSteps = (kUnitShare + 16 * kStreamWaves - 1) / (16 * kStreamWaves);
     const int sw = wave - kCutWaves;  // stream wave index (waves 4-7)
@@ -593,8 +594,8 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      unclustered tail [E, E + Tn); a staged tail row holds -1 - token
     //      and is read from K, V instead of the exact-row source. ------------
     const float qscale = kInvSqrtD * kLog2e;
-    const size_t ubase = (size_t)unit * a.Nmax * kHeadDim;
-    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
+    const size_t ubase = (size_t)su * a.Nmax * kHeadDim;
+    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)su * a.Nmax : nullptr;
     const int Tn = a.n_total - a.n_clustered;
     const int Et = E + Tn;
     const int e0 = (int)((int64_t)Et * rep / R), e1 = (int)((int64_t)Et * (rep + 1) / R);
@@ -855,7 +856,7 @@ static hipError_t unit_dispatch(int G, const UnitArgs& a, dim3 grid, hipStream_t
 }
 
 hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
-    if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < 1 ||
+    if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < 1 || a.ugroup < 1 ||
         !a.out || (replicas > 1 && (!a.xch || !a.xpart || !a.xcount || a.tag == 0u)))
         return hipErrorInvalidValue;
     dim3 grid(units, replicas);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libmpattn.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 OP_BUILD, OP_UPDATE, OP_DECODE, OP_DENSE = 0, 1, 2, 3
-MODE_MULTIPOLE, MODE_OMIT = 0, 1
+MODE_MULTIPOLE, MODE_OMIT, MODE_PER_HEAD = 0, 1, 2
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 
@@ -285,6 +285,7 @@ _default_ws = Workspace()
 
 @dataclass
 class DecodeDebug:
+    # per-head selection: Hq in place of Hkv and 1 in place of G
     scores: Optional[torch.Tensor] = None        # [B][Hkv][n_clusters][G] float32
     selected: Optional[torch.Tensor] = None      # [B][Hkv][n_clusters] int32
     candidates: Optional[torch.Tensor] = None    # [B][Hkv][n_coarse] int32
@@ -292,10 +293,11 @@ class DecodeDebug:
     rescore: int = 0                             # 1: every workgroup scores all clusters; 2: late-partner path
 
     @staticmethod
-    def allocate(p: Params, state: ClusterState, device="cuda") -> "DecodeDebug":
-        B, H, C = p.batch, p.n_kv_heads, state.n_clusters
+    def allocate(p: Params, state: ClusterState, device="cuda", per_head: bool = False) -> "DecodeDebug":
+        B, C = p.batch, state.n_clusters
+        H, G = (p.n_q_heads, 1) if per_head else (p.n_kv_heads, p.group)
         return DecodeDebug(
-            scores=torch.zeros(B, H, C, p.group, dtype=torch.float32, device=device),
+            scores=torch.zeros(B, H, C, G, dtype=torch.float32, device=device),
             selected=torch.zeros(B, H, C, dtype=torch.int32, device=device),
             candidates=torch.zeros(B, H, max(state.n_coarse, 1), dtype=torch.int32, device=device)
             if p.hierarchical else None,
@@ -323,6 +325,14 @@ def decode(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_token
     if workspace is None:
         workspace = _default_ws.get(p, state, q.device)
     cp, cs = p.c(), state.c()
+    if debug is not None:
+        units = p.batch * (p.n_q_heads if mode == MODE_PER_HEAD else p.n_kv_heads)
+        per_unit = {"scores": state.n_clusters * p.n_q_heads * p.batch // units, "selected": state.n_clusters,
+                    "candidates": state.n_coarse, "exact_tokens": 1}
+        for name, n in per_unit.items():
+            t = getattr(debug, name)
+            if t is not None and (not t.is_contiguous() or t.numel() * t.element_size() < units * n * 4):
+                raise ValueError(f"debug.{name} must be contiguous and hold {units} x {n} 32-bit values")
     dbg = debug.c() if debug is not None else None
     if stages is None:
         first, last = 0, lib.mpattn_decode_stage_count(ctypes.byref(cp)) - 1

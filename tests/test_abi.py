@@ -174,7 +174,11 @@ def test_decode_validation():
     ph = _params(capacity_tokens=131072, coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
     sh = _fake_state(ph, n_clustered=8192, n_clusters=512, n_coarse=64, n_blocks=1)
     assert _decode(ph, sh, 8192, mode=M.MODE_OMIT) == M.ERR_UNSUPPORTED
+    assert _decode(ph, sh, 8192, mode=M.MODE_PER_HEAD) == M.ERR_UNSUPPORTED
     assert _decode(ph, sh, 8192, ws=10) == M.ERR_WORKSPACE
+    # per-head selection runs on the one-launch path only
+    assert p.decode_stages() != ["unit"]
+    assert _decode(p, st, 4096, mode=M.MODE_PER_HEAD) == M.ERR_UNSUPPORTED
 
 
 def test_workspace_and_stages():
@@ -190,6 +194,15 @@ def test_workspace_and_stages():
     assert many.decode_stages() == ["unit"]
     assert dataclasses.replace(many, splits=8).decode_stages() == ["score", "select", "attend", "merge"]
     assert dataclasses.replace(many, dtype=torch.float32).decode_stages() == ["score", "select", "attend", "merge"]
+    # the one-launch workspace also holds the exchange of the per-head units:
+    # eight workgroups per unit at 16 units of 4 heads, four per query head
+    # at 64 one-head units
+    few = M.Params(batch=2, n_q_heads=32, n_kv_heads=8, capacity_tokens=32768)
+    assert few.decode_stages() == ["unit"]
+    shared_only = 16 * 8 * 2048 * 8 + 16 * 8 * 4 * 130 * 8 + 16 * 8
+    per_head = 64 * 4 * 2048 * 8 + 64 * 4 * 130 * 8 + 64 * 8
+    ws = M.lib.mpattn_workspace_bytes(ctypes.byref(few.c()), 2048, 0, M.OP_DECODE)
+    assert ws >= per_head > shared_only
     small = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=1).c()), 2053, 0, M.OP_DECODE)
     big = M.lib.mpattn_workspace_bytes(ctypes.byref(_params(splits=64).c()), 2053, 0, M.OP_DECODE)
     assert big > small

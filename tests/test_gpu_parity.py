@@ -427,3 +427,89 @@ def test_unit_path_rescore_gives_the_same_result():
                 assert torch.equal(d.scores.cpu(), dbgs[0].scores.cpu())
                 assert torch.equal(d.selected.cpu(), dbgs[0].selected.cpu())
                 assert torch.equal(d.exact_tokens.cpu(), dbgs[0].exact_tokens.cpu())
+
+
+# ---------------------------------------------------------------------------
+# per-query-head selection (the alternative reading of who selects under
+# grouped-query attention): each query head is the oracle's decode of a
+# one-head group over its KV head's clusters
+# ---------------------------------------------------------------------------
+def test_per_head_selection_matches_oracle_on_oracle_state():
+    mp = M()
+    B, Hq, Hkv, n_tot, Bc, r = 8, 32, 8, 3000, 1024, 16
+    w = small_workload(B, Hq, Hkv, n_tot, max(8, n_tot // 16), outliers=4, index=91)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=n_tot, tokens_per_centroid=r,
+                  cluster_block=Bc, build_iters=3, seed=5)
+    assert p.decode_stages() == ["unit"]
+    units = O.parallel_map(lambda u: O.build_unit(K[u // Hkv, u % Hkv], V[u // Hkv, u % Hkv], n_tot,
+                                                  tokens_per_centroid=r, cluster_block_size=Bc, iters=3,
+                                                  storage=storage_of(torch.bfloat16), seed=5, unit=u,
+                                                  capacity_clusters=p.max_clusters()),
+                           range(B * Hkv))
+    state = mp.ClusterState(p, DEV)
+    load_oracle_states(state, p, units, K, V)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    G = Hq // Hkv
+    n_tie = 0
+    for step, T in enumerate((0, 40, 300, 3000)):
+        q = queries(w, means, 40 + step)
+        dbg = mp.DecodeDebug.allocate(p, state, DEV, per_head=True)
+        out = mp.decode(p, q.to(DEV), Kd, Vd, n_tot, state, T, mode=mp.MODE_PER_HEAD, debug=dbg).cpu().numpy()
+        sel_g = dbg.selected.cpu().numpy()       # [B][Hq][C]
+        s_g = dbg.scores.cpu().numpy()[..., 0]    # [B][Hq][C]
+        exact_g = dbg.exact_tokens.cpu().numpy()  # [B][Hq]
+        for b in range(B):
+            for hq in range(Hq):
+                st = units[b * Hkv + hq // G]
+                C = st.n_clusters
+                qu = q[b, hq:hq + 1]
+                ref = O.decode_unit(qu, K[b, hq // G], V[b, hq // G], n_tot, st, T)
+                q64 = O.f64(qu)
+                bound = gamma(136) * (np.abs(q64) @ np.abs(st.kbar[:C]).T)[0] / math.sqrt(128)
+                assert np.all(np.abs(s_g[b, hq, :C] - ref.s[0]) <= bound + 4 * U32 * np.abs(ref.s[0]) + 1e-30)
+                if np.array_equal(sel_g[b, hq, :C], ref.selected):
+                    want = ref.out
+                else:
+                    n_tie += 1
+                    tol = rank_tolerance(q64, st.kbar[:C])
+                    assert selection_is_valid(ref.r, tol, st.sizes[:C], T, sel_g[b, hq, :C]), (b, hq, T)
+                    want = O.decode_with_selection(qu, K[b, hq // G], V[b, hq // G], n_tot, st, sel_g[b, hq, :C])
+                ok, ea, er = close(out[b, hq:hq + 1], want)
+                assert ok, f"head ({b}, {hq}) T={T}: max abs {ea:.3g} max rel {er:.3g}"
+                assert exact_g[b, hq] == st.sizes[:C][sel_g[b, hq, :C].astype(bool)].sum()
+        # the heads of a group do not all take the shared cut
+        if T in (40, 300):
+            shared = mp.DecodeDebug.allocate(p, state, DEV)
+            mp.decode(p, q.to(DEV), Kd, Vd, n_tot, state, T, debug=shared)
+            per = sel_g.reshape(B, Hkv, G, -1)
+            assert np.any(per != shared.selected.cpu().numpy()[:, :, None, :])
+    assert n_tie <= 4
+
+
+def test_per_head_selection_with_one_head_per_group_is_the_shared_decode():
+    """With G = 1 the two readings coincide: same launch shape, same bits."""
+    mp, w, K, V, means, p, state = _built(B=16, Hq=8, Hkv=8, N=3000, Bc=1024)
+    assert p.group == 1 and p.decode_stages() == ["unit"]
+    q = queries(w, means, 50).to(DEV)
+    for T in (64, 700):
+        a = mp.decode(p, q, K.to(DEV), V.to(DEV), 3000, state, T).cpu()
+        b = mp.decode(p, q, K.to(DEV), V.to(DEV), 3000, state, T, mode=mp.MODE_PER_HEAD).cpu()
+        assert torch.equal(a, b)
+
+
+def test_per_head_selection_on_gpu_state_with_tail_and_replicas():
+    """GPU-built state, an unclustered tail, and few enough units that each
+    query head's step is split over several workgroups."""
+    mp, w, K, V, means, p, state = _built(B=2, Hq=32, Hkv=8, N=4500, Bc=1024)
+    assert p.decode_stages() == ["unit"]
+    G = p.group
+    n_cl = state.n_clustered
+    q = queries(w, means, 60)
+    for T in (100, 900):
+        out = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 4500, state, T, mode=mp.MODE_PER_HEAD).cpu().numpy()
+        for b, hq in ((0, 0), (0, 5), (1, 17), (1, 31)):
+            st = oracle_state_from_gpu(state, b, hq // G, p)
+            ref = O.decode_unit(q[b, hq:hq + 1], K[b, hq // G], V[b, hq // G], 4500, st, T)
+            ok, ea, er = close(out[b, hq:hq + 1], ref.out)
+            assert ok, (b, hq, T, ea, er, n_cl)
