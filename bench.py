@@ -260,8 +260,13 @@ def main():
                               "frac": round(dense_bytes / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
                  "sparse_speedup": round(dense_us / cold_us, 2)}
         log(f"[bench] dense split-K decode {dense_us:.1f} us/step ({dense_us / cold_us:.2f}x the sparse step)")
-        dense["ablation"] = measure_ablation(M, p, [qs[args.warmup + i] for i in range(min(8, args.steps))],
-                                             Kd, Vd, N, state, T, ws, dws, evict)
+        n_abl = min(8, args.steps)
+        dense["ablation"] = {
+            "independent_heads": measure_ablation(M, p, [qs[args.warmup + i] for i in range(n_abl)],
+                                                  Kd, Vd, N, state, T, ws, dws, evict),
+            "group_shared_component": measure_ablation(
+                M, p, [workloads.make_queries(w, means, args.warmup + i, group_shared=True).to(dev)
+                       for i in range(n_abl)], Kd, Vd, N, state, T, ws, dws, evict)}
         del dws
 
     rows = None if args.no_rows else measure_rows(M, workloads, dev, evict)
@@ -374,7 +379,9 @@ def measure_ablation(M, p, qs, Kd, Vd, n_total, state, T, ws, dws, evict):
     """Output error against exact dense attention, and cold time, of the
     shared selection with centroid terms (the method), the same selection
     with the unselected clusters dropped, and per-query-head selection with
-    centroid terms.  Error per query head: ||o - o_dense|| / ||o_dense||."""
+    centroid terms.  Error per query head: ||o - o_dense|| / ||o_dense||.
+    The same for both query recipes: heads of a group that look at unrelated
+    parts of the context, or at the same part."""
     import numpy as np
     import torch
     modes = {"multipole": M.MODE_MULTIPOLE, "omit": M.MODE_OMIT, "per_head": M.MODE_PER_HEAD}

@@ -491,3 +491,74 @@ def test_hierarchy_exact_weighted_objective_monotone():
     for c in range(10):
         if counts[c]:
             np.testing.assert_allclose(mu[c], (w[a == c, None] * x[a == c]).sum(0) / w[a == c].sum(), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) centroid codes with a power-of-two scale per 32 values
+# ---------------------------------------------------------------------------
+def test_e4m3_table_from_the_format_definition():
+    from oracle import centroid_codes as F
+    v = F.VALUES
+    assert len(v) == 127 and v[0] == 0.0
+    assert v[1] == 2.0 ** -9 and v[7] == 7 * 2.0 ** -9          # subnormals 0.m x 2^-6
+    assert v[8] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x7E] == 448.0
+    assert np.all(np.diff(v) > 0)                                # codes ordered by magnitude
+    # spacing doubles once per binade of 8 codes above the subnormals
+    for e in range(1, 15):
+        assert np.allclose(np.diff(v[8 * e:8 * e + 8]), 2.0 ** (e - 10))
+
+
+def test_e4m3_hand_derived_blocks(golden_dir):
+    from oracle import centroid_codes as F
+    g = json.load(open(os.path.join(golden_dir, "fp8_blocks.json")))
+    for case in g["cases"]:
+        codes, E = F.encode_block(case["x"])
+        assert E == case["E"], case["derivation"]
+        assert [int(c) for c in codes] == [int(c, 16) for c in case["codes"]], case["derivation"]
+
+
+def test_e4m3_every_value_round_trips_and_ties_go_even():
+    from oracle import centroid_codes as F
+    v = F.VALUES
+    # all 127 finite magnitudes, both signs, in blocks whose largest value is
+    # 448 (scale 2^0): each encodes to its own code
+    xs = np.concatenate([v, -v[1:]])
+    for s in range(0, len(xs), 31):
+        blk = np.zeros(32)
+        blk[:len(xs[s:s + 31])] = xs[s:s + 31]
+        blk[31] = 448.0
+        codes, E = F.encode_block(blk)
+        assert E == 0
+        assert np.array_equal(F.decode_rows(codes[None].astype(np.uint8), np.array([[127]]))[0], blk)
+    # midpoints go to the even code, anything above a midpoint goes up
+    for c in range(126):
+        mid = (v[c] + v[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert F.encode_magnitude(mid) == even
+        assert F.encode_magnitude(np.nextafter(mid, np.inf)) == c + 1
+        assert F.encode_magnitude(np.nextafter(mid, -np.inf)) == c
+
+
+def test_e4m3_scale_rule_and_error_bound():
+    from oracle import centroid_codes as F
+    assert F.scale_exponent(448.0) == 0 and F.scale_exponent(448.0001) == 1
+    assert F.scale_exponent(1.0) == -8 and F.scale_exponent(1.75) == -8 and F.scale_exponent(1.76) == -7
+    assert F.scale_exponent(0.0) == -126 and F.scale_exponent(2.0 ** -140) == -126
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((40, 128)) * np.exp2(rng.integers(-20, 20, (40, 1)))
+    X[3, 5:9] = 0.0
+    X[4, 32:64] *= 1e-45                              # below the floor of the scale
+    codes, scales = F.encode_rows(X)
+    Y = F.decode_rows(codes, scales)
+    E = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    a = np.abs(X) * np.exp2(-E)                       # magnitudes in code units
+    assert np.all(a <= 448.0)
+    # E is the least such exponent unless the floor -126 holds it
+    above = scales > 1
+    assert np.all((np.abs(X).reshape(40, 4, 32).max(-1) * np.exp2(-(scales.astype(np.int64) - 128)))[above] > 448.0)
+    assert not np.all(above)
+    err = np.abs(Y - X) * np.exp2(-E)
+    normal = a >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * a[normal])  # half an ulp of 3 mantissa bits
+    assert np.all(err[~normal] <= 2.0 ** -10)            # half the subnormal step
+    assert np.array_equal(np.signbit(Y[X != 0]), np.signbit(X[X != 0]))

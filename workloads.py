@@ -129,18 +129,23 @@ def make_cache(w: Workload, batch_ids: Optional[Sequence[int]] = None, n_tokens:
     return K, V, [s.means for s in seqs]
 
 
-def make_queries(w: Workload, means: List[List[torch.Tensor]], step: int, phase: int = -1) -> torch.Tensor:
+def make_queries(w: Workload, means: List[List[torch.Tensor]], step: int, phase: int = -1,
+                 group_shared: bool = False) -> torch.Tensor:
     """q [B][Hq][d]: a random component mean of the head's KV group (of the
-    given mixture phase, default the latest) + 0.1 * N(0, I)."""
-    g = torch.Generator("cpu").manual_seed(2000 * w.index + step)
+    given mixture phase, default the latest) + 0.1 * N(0, I).  Each query
+    head draws its own component; with group_shared the G heads of a group
+    draw one component together (and their own noise)."""
+    g = torch.Generator("cpu").manual_seed(2000 * w.index + step + (1000 if group_shared else 0))
     B = len(means)
     G = w.n_q_heads // w.n_kv_heads
     q = torch.empty(B, w.n_q_heads, w.head_dim, dtype=torch.float32)
     for b in range(B):
         mu = means[b][phase]
         M = mu.shape[1]
+        m = 0
         for hq in range(w.n_q_heads):
-            m = int(torch.randint(0, M, (1,), generator=g))
+            if not group_shared or hq % G == 0:
+                m = int(torch.randint(0, M, (1,), generator=g))
             q[b, hq] = mu[hq // G, m] + 0.1 * torch.randn(w.head_dim, generator=g)
     return q.to(w.dtype)
 
