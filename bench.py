@@ -20,6 +20,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import ctypes
+import dataclasses
 import json
 import math
 import os
@@ -239,7 +240,7 @@ def main():
         f"stages(us) " + " ".join(f"{n}={stage_ms[:, k].mean() * 1e3:.1f}" for k, n in enumerate(stage_names)))
 
     # ---- dense split-K decode of the same step (the pages' comparison point) --
-    dense = None
+    dense = fp8 = None
     if not args.no_rows:
         dws = torch.empty(int(M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 1, 0, M.OP_DENSE)), dtype=torch.uint8,
                           device=dev)
@@ -260,13 +261,31 @@ def main():
                               "frac": round(dense_bytes / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
                  "sparse_speedup": round(dense_us / cold_us, 2)}
         log(f"[bench] dense split-K decode {dense_us:.1f} us/step ({dense_us / cold_us:.2f}x the sparse step)")
+        # the same build with fp8 centroid copies (same seed: the same clusters)
+        p8 = dataclasses.replace(p, centroid_format=M.CENTROIDS_FP8)
+        state8 = M.ClusterState(p8, dev, sorted_copy=not args.gather)
+        M.build_clusters(p8, Kd, Vd, N, state8)
+        torch.cuda.synchronize()
+        variants = {"multipole": (p, state, M.MODE_MULTIPOLE), "omit": (p, state, M.MODE_OMIT),
+                    "per_head": (p, state, M.MODE_PER_HEAD), "fp8_centroids": (p8, state8, M.MODE_MULTIPOLE)}
         n_abl = min(8, args.steps)
         dense["ablation"] = {
-            "independent_heads": measure_ablation(M, p, [qs[args.warmup + i] for i in range(n_abl)],
-                                                  Kd, Vd, N, state, T, ws, dws, evict),
+            "independent_heads": measure_ablation(M, variants, [qs[args.warmup + i] for i in range(n_abl)],
+                                                  Kd, Vd, N, T, ws, dws, evict),
             "group_shared_component": measure_ablation(
-                M, p, [workloads.make_queries(w, means, args.warmup + i, group_shared=True).to(dev)
-                       for i in range(n_abl)], Kd, Vd, N, state, T, ws, dws, evict)}
+                M, variants, [workloads.make_queries(w, means, args.warmup + i, group_shared=True).to(dev)
+                              for i in range(n_abl)], Kd, Vd, N, T, ws, dws, evict)}
+        # fp8 centroid copies on the timed queries: bytes and roofline
+        f8_us = _cold_decode_us(M, p8, [qs[args.warmup + i] for i in range(args.steps)], Kd, Vd, N, state8, T, ws,
+                                evict)
+        f8_bytes = float(byts.mean()) - 2 * U * C * d * 2 + 2 * U * C * (d + d // 32)
+        fp8 = {"us_per_step": round(f8_us, 2), "algorithmic_MB": round(f8_bytes / 1e6, 2),
+               "roofline": {"bound": "hbm", "achieved": round(f8_bytes / (f8_us * 1e-6) / 1e9, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(f8_bytes / (f8_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+               "speedup_vs_stored_centroids": round(cold_us / f8_us, 3)}
+        log(f"[bench] fp8 centroids {f8_us:.1f} us/step ({fp8['roofline']['achieved']:.0f} GB/s algorithmic)")
+        del state8
         del dws
 
     rows = None if args.no_rows else measure_rows(M, workloads, dev, evict)
@@ -343,6 +362,7 @@ def main():
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
         "dense_reference": dense,
+        "fp8_centroids": fp8,
         "rows": rows,
     }
     print(json.dumps(res), flush=True)
@@ -375,21 +395,21 @@ def _cold_decode_us(M, p, qs, Kd, Vd, n_total, state, T, ws, evict, mode=0):
     return float(np.median(ts))
 
 
-def measure_ablation(M, p, qs, Kd, Vd, n_total, state, T, ws, dws, evict):
-    """Output error against exact dense attention, and cold time, of the
-    shared selection with centroid terms (the method), the same selection
-    with the unselected clusters dropped, and per-query-head selection with
-    centroid terms.  Error per query head: ||o - o_dense|| / ||o_dense||.
-    The same for both query recipes: heads of a group that look at unrelated
-    parts of the context, or at the same part."""
+def measure_ablation(M, variants, qs, Kd, Vd, n_total, T, ws, dws, evict):
+    """Output error against exact dense attention, and cold time, of decode
+    variants (name -> (params, state, mode)): the shared selection with
+    centroid terms (the method), the same selection with the unselected
+    clusters dropped, per-query-head selection with centroid terms, and the
+    method reading fp8 centroid copies.  Error per query head:
+    ||o - o_dense|| / ||o_dense||."""
     import numpy as np
     import torch
-    modes = {"multipole": M.MODE_MULTIPOLE, "omit": M.MODE_OMIT, "per_head": M.MODE_PER_HEAD}
-    errs = {k: [] for k in modes}
-    exact = {k: 0 for k in modes}
+    p0 = next(iter(variants.values()))[0]
+    errs = {k: [] for k in variants}
+    exact = {k: 0 for k in variants}
     for q in qs:
-        ref = M.dense_decode(p, q, Kd, Vd, n_total, workspace=dws).double()
-        for name, md in modes.items():
+        ref = M.dense_decode(p0, q, Kd, Vd, n_total, workspace=dws).double()
+        for name, (p, state, md) in variants.items():
             dbg = M.DecodeDebug.allocate(p, state, q.device, per_head=md == M.MODE_PER_HEAD)
             o = M.decode(p, q, Kd, Vd, n_total, state, T, mode=md, workspace=ws, debug=dbg).double()
             e = (o - ref).norm(dim=-1) / ref.norm(dim=-1)
@@ -398,7 +418,7 @@ def measure_ablation(M, p, qs, Kd, Vd, n_total, state, T, ws, dws, evict):
             exact[name] += rows * (1 if md == M.MODE_PER_HEAD else p.group)
     torch.cuda.synchronize()
     res = {}
-    for name, md in modes.items():
+    for name, (p, state, md) in variants.items():
         e = torch.cat(errs[name]).numpy()
         res[name] = {"rel_l2_err_mean": float(f"{e.mean():.4g}"), "rel_l2_err_p99": float(f"{np.percentile(e, 99):.4g}"),
                      "rel_l2_err_max": float(f"{e.max():.4g}"),
@@ -407,7 +427,7 @@ def measure_ablation(M, p, qs, Kd, Vd, n_total, state, T, ws, dws, evict):
                                                                mode=md), 2)}
         log(f"[bench] ablation {name}: rel err mean {e.mean():.4f} max {e.max():.4f}  "
             f"{res[name]['cold_us_per_step']:.1f} us/step")
-    res["queries"] = f"{len(qs)} decode steps x {p.batch * p.n_q_heads} query heads, budget {T} tokens"
+    res["queries"] = f"{len(qs)} decode steps x {p0.batch * p0.n_q_heads} query heads, budget {T} tokens"
     return res
 
 

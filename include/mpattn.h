@@ -56,6 +56,22 @@ typedef enum {
 
 typedef enum { MPATTN_F32 = 0, MPATTN_BF16 = 1 } mpattn_dtype;
 
+/* What the decode reads for the clusters' key and value centroids.  The
+ * pages keep the centroids in the cache's own precision; the fp8 format is
+ * a bandwidth option of this library (the centroids are over half of the
+ * bytes a decode step at 95% sparsity reads):
+ *   MPATTN_CENTROIDS_STORED: the stored centroids (dtype);
+ *   MPATTN_CENTROIDS_FP8: fp8 copies that the build and update write next
+ *     to the stored centroids: every run of 32 values of a centroid row
+ *     shares a scale 2^E, E the least integer >= -126 with
+ *     max|x| * 2^-E <= 448, stored as the byte E + 127; each value is the
+ *     E4M3 code (OCP 8-bit floating point: bias 7, 3 mantissa bits,
+ *     subnormals, largest finite 448) nearest to x * 2^-E, ties to the even
+ *     code, sign bit copied from x.  The decode computes with the decoded
+ *     values code * 2^E.  bf16 storage, flat method, one-launch decode
+ *     only.  The k-means itself always uses the stored centroids. */
+typedef enum { MPATTN_CENTROIDS_STORED = 0, MPATTN_CENTROIDS_FP8 = 1 } mpattn_centroid_format;
+
 typedef enum { MPATTN_OP_BUILD = 0, MPATTN_OP_UPDATE = 1, MPATTN_OP_DECODE = 2, MPATTN_OP_DENSE = 3 } mpattn_op;
 
 typedef enum {
@@ -82,6 +98,7 @@ typedef struct mpattn_params {
     int32_t coarse_candidate_tokens;    /* hierarchical decode: token budget of the coarse candidates */
     int32_t splits;                     /* decode work splits per unit; 0 = chosen by the library
                                            (> 0 also selects the split launches of the flat method) */
+    int32_t centroid_format;            /* an mpattn_centroid_format value; default STORED */
     uint64_t seed;                      /* seeds the k-means initialisation */
 } mpattn_params;
 
@@ -114,6 +131,11 @@ typedef struct mpattn_state {
     int32_t* coarse_members;         /* device [B][Hkv][Cmax]: non-empty fine ids by (coarse, fine);
                                         the blocks' lists follow each other */
     int32_t* parent;                 /* device [B][Hkv][Cmax]: coarse id of each fine cluster, -1 if empty */
+    /* fp8 copies of the centroids (MPATTN_CENTROIDS_FP8; else may be NULL) */
+    uint8_t* key_codes;              /* device [B][Hkv][Cmax][d]: E4M3 codes of key_centroids        */
+    uint8_t* key_scales;             /* device [B][Hkv][Cmax][d / 32]: scale bytes E + 127            */
+    uint8_t* value_codes;            /* device [B][Hkv][Cmax][d]: E4M3 codes of value_centroids      */
+    uint8_t* value_scales;           /* device [B][Hkv][Cmax][d / 32] */
     int32_t capacity_clusters;       /* Cmax >= mpattn_max_clusters(params) is always enough */
     int32_t capacity_coarse;         /* Dmax (0 for the flat method) */
     /* host counters, identical for every unit; set to 0 before the first build */

@@ -49,31 +49,29 @@ def scale_exponent(amax: float) -> int:
     return max(E, E_MIN)
 
 
-def encode_magnitude(y: float) -> int:
-    """Code of the table value nearest to |y| <= 448; ties go to the even code."""
-    a = abs(y)
-    i = int(np.searchsorted(VALUES, a))  # VALUES[i - 1] < a <= VALUES[i]
-    if i == 0:
-        return 0
-    if i >= len(VALUES):
+def encode_magnitudes(a) -> np.ndarray:
+    """Codes of the table values nearest to magnitudes a <= 448; ties go to
+    the even code."""
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    if np.any(a > MAX_FINITE):
         raise ValueError("magnitude above 448")
+    i = np.clip(np.searchsorted(VALUES, a), 1, len(VALUES) - 1)  # VALUES[i - 1] < a <= VALUES[i] (a > 0)
     lo, hi = VALUES[i - 1], VALUES[i]
-    if a - lo < hi - a:
-        return i - 1
-    if a - lo > hi - a:
-        return i
-    return i - 1 if (i - 1) % 2 == 0 else i
+    below, above = a - lo, hi - a
+    pick_hi = (above < below) | ((above == below) & (i % 2 == 0))
+    return np.where(a == 0, 0, np.where(pick_hi, i, i - 1)).astype(np.uint8)
+
+
+def encode_magnitude(y: float) -> int:
+    return int(encode_magnitudes([y])[0])
 
 
 def encode_block(x) -> tuple:
     """(codes uint8[n], E) of up to 32 values sharing one scale."""
     x = np.asarray(x, dtype=np.float64)
     E = scale_exponent(float(np.abs(x).max()) if x.size else 0.0)
-    codes = np.zeros(x.size, np.uint8)
-    for j, v in enumerate(x):
-        c = encode_magnitude(math.ldexp(float(v), -E))
-        codes[j] = c | (0x80 if math.copysign(1.0, v) < 0 else 0)
-    return codes, E
+    codes = encode_magnitudes(np.ldexp(x, -E)) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return codes.astype(np.uint8), E
 
 
 def encode_rows(X) -> tuple:

@@ -42,6 +42,10 @@ mpattn_status check_params(const mpattn_params* p) {
     if (p->cluster_block > kMaxBlock) return MPATTN_ERR_UNSUPPORTED;
     if (p->tokens_per_centroid > p->cluster_block) return MPATTN_ERR_INVALID_ARG;
     if ((int64_t)p->batch * p->n_kv_heads > 65535) return MPATTN_ERR_UNSUPPORTED;  // grid y
+    if (p->centroid_format != MPATTN_CENTROIDS_STORED && p->centroid_format != MPATTN_CENTROIDS_FP8)
+        return MPATTN_ERR_INVALID_ARG;
+    if (p->centroid_format == MPATTN_CENTROIDS_FP8 && (p->dtype != MPATTN_BF16 || is_hier(p)))
+        return MPATTN_ERR_UNSUPPORTED;
     if (is_hier(p)) {
         if (p->coarse_iters < 1 || p->coarse_candidate_tokens < 0) return MPATTN_ERR_INVALID_ARG;
         if (ceil_div(p->cluster_block, p->tokens_per_centroid) > kMaxFinePerBlockHier ||
@@ -196,6 +200,9 @@ mpattn_status check_state(const mpattn_params* p, const mpattn_state* st) {
         return MPATTN_ERR_INVALID_ARG;
     if ((st->sorted_keys == nullptr) != (st->sorted_values == nullptr)) return MPATTN_ERR_INVALID_ARG;
     if (st->capacity_clusters < 1) return MPATTN_ERR_INVALID_ARG;
+    if (p->centroid_format == MPATTN_CENTROIDS_FP8 &&
+        (!st->key_codes || !st->key_scales || !st->value_codes || !st->value_scales))
+        return MPATTN_ERR_INVALID_ARG;
     if (st->n_clustered < 0 || st->n_clusters < 0 || st->n_coarse < 0 || st->n_blocks < 0)
         return MPATTN_ERR_INVALID_ARG;
     if (is_hier(p)) {
@@ -221,6 +228,9 @@ mpattn_status run_blocks(const mpattn_params* p, const void* k, const void* v, m
     }
     MPA_TRY(launch_segmented_mean(p->dtype, v, g, br.c_base, n_new_clusters, st->sizes, st->offsets, st->token_ids,
                                   nullptr, st->value_centroids, true, s));
+    if (p->centroid_format == MPATTN_CENTROIDS_FP8)
+        MPA_TRY(launch_encode_codes(g, br.c_base, n_new_clusters, st->key_centroids, st->value_centroids,
+                                    st->key_codes, st->key_scales, st->value_codes, st->value_scales, s));
     if (st->sorted_keys)
         MPA_TRY(launch_sorted_copy(p->dtype, k, v, g, br.p_base, br.n_end - br.p_base, st->token_ids,
                                    st->sorted_keys, st->sorted_values, s));
@@ -375,7 +385,8 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         return MPATTN_ERR_INVALID_ARG;
     const bool hier = is_hier(p);
     if (hier && mode != MPATTN_MODE_MULTIPOLE) return MPATTN_ERR_UNSUPPORTED;
-    if (mode == MPATTN_MODE_PER_HEAD && !unit_path(p)) return MPATTN_ERR_UNSUPPORTED;
+    if ((mode == MPATTN_MODE_PER_HEAD || p->centroid_format == MPATTN_CENTROIDS_FP8) && !unit_path(p))
+        return MPATTN_ERR_UNSUPPORTED;
     if (st->capacity_clusters > kMaxDecodeClusters || st->capacity_coarse > kMaxDecodeClusters)
         return MPATTN_ERR_UNSUPPORTED;
     if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
@@ -428,6 +439,12 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         a.Hq = p->n_q_heads;
         a.Hkv = per_head ? p->n_q_heads : p->n_kv_heads;
         a.ugroup = per_head ? G : 1;
+        if (p->centroid_format == MPATTN_CENTROIDS_FP8) {
+            a.kcodes = st->key_codes;
+            a.kscales = st->key_scales;
+            a.vcodes = st->value_codes;
+            a.vscales = st->value_scales;
+        }
         a.out = out;
         a.xch = w.xch;
         a.xpart = w.xpart;

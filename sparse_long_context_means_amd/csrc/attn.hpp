@@ -119,6 +119,7 @@ __device__ __forceinline__ size_t part_index(int unit, int G, int g, int P, int 
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
 
 struct QOperand {
     uint4 b[4];
@@ -148,6 +149,68 @@ __device__ __forceinline__ f32x4v mfma_scores(const Slice8<bf16_t> (&a)[4], cons
                                                     __builtin_bit_cast(bf16x8v, q.b[kk]), d, 0, 0, 0);
     return d;
 }
+
+// ---------------------------------------------------------------------------
+// fp8 centroid copies: E4M3 codes with one scale byte (E + 127) per 32
+// values of a row.  The gfx950 scaled conversions decode code x 2^E exactly
+// (they take the exponent of the scale operand; 2^E is a normal float since
+// the byte is 1 .. 254).
+__device__ __forceinline__ float code_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// Score operand of a coded key-centroid row.  Lane (row l % 16, group l / 16)
+// holds the 32 codes of block l / 16 (one scale); operand kk is codes
+// 8 kk .. 8 kk + 7 of them, so the query operand must take its elements in
+// the same order (load_qop_blocks).
+struct KCodes {
+    uint4 lo, hi;
+    uint32_t sc;
+    __device__ __forceinline__ void load(const uint8_t* codes_row, const uint8_t* scales_row, int grp) {
+        lo = *reinterpret_cast<const uint4*>(codes_row + grp * 32);
+        hi = *reinterpret_cast<const uint4*>(codes_row + grp * 32 + 16);
+        sc = scales_row[grp];
+    }
+    __device__ __forceinline__ void operands(Slice8<bf16_t> (&a)[4]) const {
+        const float s = code_scale(sc);
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            a[kk].raw.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * kk], s, false));
+            a[kk].raw.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * kk], s, true));
+            a[kk].raw.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * kk + 1], s, false));
+            a[kk].raw.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * kk + 1], s, true));
+        }
+    }
+};
+
+// Query operand in the order of KCodes: operand kk of lane (n, grp) holds
+// elements 32 grp + 8 kk .. + 7 of head n.
+template <int G>
+__device__ __forceinline__ void load_qop_blocks(QOperand& q, const bf16_t* qg, int lane) {
+    const int n = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        q.b[kk] = n < G ? *reinterpret_cast<const uint4*>(qg + (size_t)n * kHeadDim + grp * 32 + kk * 8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Eight consecutive values of a coded value-centroid row (one scale).
+struct VCodes8 {
+    uint2 raw;
+    uint32_t sc;
+    __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scale) {
+        raw = *reinterpret_cast<const uint2*>(codes);
+        sc = *scale;
+    }
+    __device__ __forceinline__ void unpack(float* x) const {
+        const float s = code_scale(sc);
+        const f32x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.x, s, false);
+        const f32x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.x, s, true);
+        const f32x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.y, s, false);
+        const f32x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw.y, s, true);
+        x[0] = p0[0]; x[1] = p0[1]; x[2] = p1[0]; x[3] = p1[1];
+        x[4] = p2[0]; x[5] = p2[1]; x[6] = p3[0]; x[7] = p3[1];
+    }
+};
 
 // Mean of a row's scores over the G heads (lanes l % 16 < G); the result is
 // valid in lanes with l % 16 == 0.  The same operations on every path give

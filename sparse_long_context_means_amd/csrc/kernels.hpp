@@ -37,6 +37,9 @@ hipError_t launch_kmeans_csr(const int32_t* assign, UnitGeom g, BlockRange br, i
 hipError_t launch_segmented_mean(int dtype, const void* X, UnitGeom g, int c_begin, int c_count,
                                  const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
                                  float* master, void* store, bool empty_zero, hipStream_t st);
+// fp8 copies of centroid rows [c_begin, c_begin + c_count) of every unit (codes.hip)
+hipError_t launch_encode_codes(UnitGeom g, int c_begin, int c_count, const void* kbar, const void* vbar,
+                               uint8_t* kcodes, uint8_t* kscales, uint8_t* vcodes, uint8_t* vscales, hipStream_t st);
 hipError_t launch_sorted_copy(int dtype, const void* K, const void* V, UnitGeom g, int p_begin, int count,
                               const int32_t* token_ids, void* SK, void* SV, hipStream_t st);
 
@@ -169,6 +172,12 @@ struct UnitArgs {
     int32_t pseudo;              // 1: approximate unselected clusters; 0: omit them
     int32_t Hq, Hkv;             // Hkv: units per sequence
     int32_t ugroup;              // units per state unit (1; G when each query head is its own unit)
+    // fp8 copies of the centroids ([U][Cmax][d] codes, [U][Cmax][d / 32]
+    // scale bytes); when kcodes is set they replace kbar and vbar
+    const uint8_t* kcodes;
+    const uint8_t* kscales;
+    const uint8_t* vcodes;
+    const uint8_t* vscales;
     float* out;                  // [B][Hq][d]
     // replica exchange (several replicas): words are (tag << 32 | 32-bit value)
     uint64_t* xch;               // [U][R][Cmax]: keys, slot r read by replica r

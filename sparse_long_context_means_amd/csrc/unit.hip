@@ -19,6 +19,8 @@
 // the split launches in decode.hip serve the rest.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
@@ -249,7 +251,8 @@ struct Rows4 {
     Slice8<T> r[4];
 };
 
-template <typename T, int G, int kUnitMaxC, int kUnitShare>
+// F8: the centroids come from their fp8 copies (codes and scale bytes).
+template <typename T, int G, int kUnitMaxC, int kUnitShare, bool F8>
 __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     constexpr int kUnitRecItems = kUnitMaxC / kUnitThreads;        // cluster records per thread
     constexpr int kUnitSharePerWave = kUnitShare / kUnitWaves;     // approximate-term clusters per wave
@@ -286,6 +289,18 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 
     const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
     const bf16_t* cu = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)su * a.Cmax * kHeadDim;
+    constexpr int kScaleBytes = kHeadDim / 32;  // fp8 copies: one scale byte per 32 values
+    const uint8_t* kc = F8 ? a.kcodes + (size_t)su * a.Cmax * kHeadDim : nullptr;
+    const uint8_t* ksc = F8 ? a.kscales + (size_t)su * a.Cmax * kScaleBytes : nullptr;
+    // one key-centroid row of the score ring: the lane's 4 operand blocks, or
+    // its 32 codes and their scale
+    using KRow = std::conditional_t<F8, KCodes, Rows4<bf16_t>>;
+    auto kload = [&](KRow& r, int i) {
+        if constexpr (F8)
+            r.load(kc + (size_t)i * kHeadDim, ksc + (size_t)i * kScaleBytes, rg);
+        else
+            load_row_blocks(r.r, cu + (size_t)i * kHeadDim, lane);
+    };
     // one pass over clusters [lo, hi) by nw waves (this one is wave wv of
     // them); the first pass (all waves) also brings the cluster records to
     // LDS while its first centroid rows are in flight, and only it writes the
@@ -307,17 +322,20 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
         }
         QOperand qop;
-        load_qop<G>(qop, qg, lane);
+        if constexpr (F8)
+            load_qop_blocks<G>(qop, qg, lane);
+        else
+            load_qop<G>(qop, qg, lane);
         // the waves interleave: one step of the workgroup reads 16 nw
         // consecutive clusters, so the workgroup is a single stream; lane l
         // loads row l % 16 of its wave's 16
         const int steps = (hi - lo + 16 * nw - 1) / (16 * nw);
         auto base = [&](int step) { return lo + step * 16 * nw + wv * 16; };
-        Rows4<bf16_t> ring[kScoreDepth];
+        KRow ring[kScoreDepth];
 #pragma unroll
         for (int j = 0; j < kScoreDepth; ++j) {
             const int i = base(j) + li;
-            load_row_blocks(ring[j].r, cu + (size_t)(i < hi ? i : 0) * kHeadDim, lane);
+            kload(ring[j], i < hi ? i : 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (first) {
@@ -337,7 +355,14 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
             for (int j = 0; j < kScoreDepth; ++j) {
                 // lane (rg, li) receives rows 4 rg + e of the 16 for head li
-                const f32x4v d = mfma_scores(ring[j].r, qop);
+                f32x4v d;
+                if constexpr (F8) {
+                    Slice8<bf16_t> op[4];
+                    ring[j].operands(op);
+                    d = mfma_scores(op, qop);
+                } else {
+                    d = mfma_scores(ring[j].r, qop);
+                }
                 const int cb = base(it + j) + 4 * rg;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -358,7 +383,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                     }
                 }
                 const int i = base(it + j + kScoreDepth) + li;
-                load_row_blocks(ring[j].r, cu + (size_t)(i < hi ? i : 0) * kHeadDim, lane);
+                kload(ring[j], i < hi ? i : 0);
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
@@ -386,11 +411,24 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      group.  Waves 4-7 run it over every cluster of the share while
     //      waves 0-3 take the cut; the selected clusters are taken out after.
     const T* vb = reinterpret_cast<const T*>(a.vbar) + (size_t)su * a.Cmax * kHeadDim + li * 8;
+    const uint8_t* vc = F8 ? a.vcodes + (size_t)su * a.Cmax * kHeadDim + li * 8 : nullptr;
+    const uint8_t* vsc = F8 ? a.vscales + (size_t)su * a.Cmax * kScaleBytes + (li >> 2) : nullptr;
+    // values li * 8 .. + 7 of value-centroid row c
+    using VRow = std::conditional_t<F8, VCodes8, Slice8<T>>;
+    auto vload = [&](VRow& v, int c) {
+        if constexpr (F8)
+            v.load(vc + (size_t)c * kHeadDim, vsc + (size_t)c * kScaleBytes);
+        else
+            v.load(vb + (size_t)c * kHeadDim);
+    };
     constexpr int kCutWaves = 4, kStreamWaves = kUnitWaves - kCutWaves;
     constexpr int kSteps = (kUnitShare + 16 * kStreamWaves - 1) / (16 * kStreamWaves);
     const int sw = wave - kCutWaves;  // stream wave index (waves 4-7)
     auto item = [&](int step, int u) { return step * 16 * kStreamWaves + sw * 16 + u * 4 + rg; };
-    Rows4<T> pring[kPseudoDepth];
+    struct VRows4 {
+        VRow r[4];
+    };
+    VRows4 pring[kPseudoDepth];
     SoftState<G> st;
     st.init();
     float Mref[G];
@@ -515,8 +553,8 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 const int k = k0 + rgi;
                 const bool ok = k < k_hi;
                 const int c = ok ? s_sid[k] : cs;
-                Slice8<T> v;
-                v.load(vb + (size_t)c * kHeadDim);
+                VRow v;
+                vload(v, c);
                 float x[8];
                 v.unpack(x);
 #pragma unroll
@@ -535,7 +573,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = cs + item(j, u);
-                pring[j].r[u].load(vb + (size_t)(c < ce ? c : cs) * kHeadDim);
+                vload(pring[j].r[u], c < ce ? c : cs);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -572,7 +610,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int c = cs + item(it + j + kPseudoDepth, u);
-                    pring[j].r[u].load(vb + (size_t)(c < ce && it + j + kPseudoDepth < kSteps ? c : cs) * kHeadDim);
+                    vload(pring[j].r[u], c < ce && it + j + kPseudoDepth < kSteps ? c : cs);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
@@ -843,21 +881,28 @@ bool unit_path_fits(int dtype, int G, int max_clusters) {
     return dtype == 1 && (G == 1 || G == 2 || G == 4 || G == 8) && max_clusters >= 1 && max_clusters <= kUnitMaxCLarge;
 }
 
-template <int MAXC, int SHARE>
-static hipError_t unit_dispatch(int G, const UnitArgs& a, dim3 grid, hipStream_t st) {
+template <int MAXC, int SHARE, bool F8>
+static hipError_t unit_dispatch_g(int G, const UnitArgs& a, dim3 grid, hipStream_t st) {
     switch (G) {
-        case 1: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 1, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 2, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
-        case 4: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 4, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 8, MAXC, SHARE>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 1, MAXC, SHARE, F8>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 2, MAXC, SHARE, F8>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 4, MAXC, SHARE, F8>), grid, dim3(kUnitThreads), 0, st, a); break;
+        case 8: hipLaunchKernelGGL((unit_decode_kernel<bf16_t, 8, MAXC, SHARE, F8>), grid, dim3(kUnitThreads), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int MAXC, int SHARE>
+static hipError_t unit_dispatch(int G, const UnitArgs& a, dim3 grid, hipStream_t st) {
+    return a.kcodes ? unit_dispatch_g<MAXC, SHARE, true>(G, a, grid, st)
+                    : unit_dispatch_g<MAXC, SHARE, false>(G, a, grid, st);
+}
+
 hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
     if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < 1 || a.ugroup < 1 ||
-        !a.out || (replicas > 1 && (!a.xch || !a.xpart || !a.xcount || a.tag == 0u)))
+        !a.out || (replicas > 1 && (!a.xch || !a.xpart || !a.xcount || a.tag == 0u)) ||
+        (a.kcodes && (!a.kscales || !a.vcodes || !a.vscales)))
         return hipErrorInvalidValue;
     dim3 grid(units, replicas);
     if (replicas == 1) {

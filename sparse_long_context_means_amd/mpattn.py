@@ -22,6 +22,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_HIP = 0, 
 F32, BF16 = 0, 1
 OP_BUILD, OP_UPDATE, OP_DECODE, OP_DENSE = 0, 1, 2, 3
 MODE_MULTIPOLE, MODE_OMIT, MODE_PER_HEAD = 0, 1, 2
+CENTROIDS_STORED, CENTROIDS_FP8 = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 
@@ -35,7 +36,7 @@ class CParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "dtype", "capacity_tokens", "tokens_per_centroid",
         "cluster_block", "build_iters", "update_iters", "coarse_tokens_per_centroid", "coarse_iters",
-        "coarse_candidate_tokens", "splits")] + [("seed", ctypes.c_uint64)]
+        "coarse_candidate_tokens", "splits", "centroid_format")] + [("seed", ctypes.c_uint64)]
 
 
 _VP = ctypes.c_void_p
@@ -45,7 +46,8 @@ class CState(ctypes.Structure):
     _fields_ = [(n, _VP) for n in (
         "key_centroids", "value_centroids", "key_centroids_f32", "sizes", "offsets", "token_ids", "assign",
         "sorted_keys", "sorted_values", "coarse_key_centroids", "coarse_value_centroids",
-        "coarse_key_centroids_f32", "coarse_sizes", "coarse_offsets", "coarse_members", "parent")] + [
+        "coarse_key_centroids_f32", "coarse_sizes", "coarse_offsets", "coarse_members", "parent",
+        "key_codes", "key_scales", "value_codes", "value_scales")] + [
         (n, ctypes.c_int32) for n in (
             "capacity_clusters", "capacity_coarse", "n_clustered", "n_clusters", "n_coarse", "n_blocks")]
 
@@ -111,6 +113,7 @@ class Params:
     coarse_candidate_tokens: int = 0
     splits: int = 0
     seed: int = 0
+    centroid_format: int = CENTROIDS_STORED  # CENTROIDS_FP8: the decode reads fp8 copies
 
     @property
     def group(self) -> int:
@@ -128,7 +131,7 @@ class Params:
         return CParams(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, _DTYPES[self.dtype],
                        self.capacity_tokens, self.tokens_per_centroid, self.cluster_block, self.build_iters,
                        self.update_iters, self.coarse_tokens_per_centroid, self.coarse_iters,
-                       self.coarse_candidate_tokens, self.splits, self.seed & (2**64 - 1))
+                       self.coarse_candidate_tokens, self.splits, self.centroid_format, self.seed & (2**64 - 1))
 
     def max_clusters(self) -> int:
         return int(lib.mpattn_max_clusters(ctypes.byref(self.c())))
@@ -170,6 +173,12 @@ class ClusterState:
         self.assign = torch.zeros(p.batch, p.n_kv_heads, N, dtype=torch.int32, **kw)
         self.sorted_keys = torch.zeros(p.batch, p.n_kv_heads, N, d, dtype=dt, **kw) if sorted_copy else None
         self.sorted_values = torch.zeros(p.batch, p.n_kv_heads, N, d, dtype=dt, **kw) if sorted_copy else None
+        self.key_codes = self.key_scales = self.value_codes = self.value_scales = None
+        if p.centroid_format == CENTROIDS_FP8:
+            self.key_codes = torch.zeros(p.batch, p.n_kv_heads, C, d, dtype=torch.uint8, **kw)
+            self.value_codes = torch.zeros(p.batch, p.n_kv_heads, C, d, dtype=torch.uint8, **kw)
+            self.key_scales = torch.zeros(p.batch, p.n_kv_heads, C, d // 32, dtype=torch.uint8, **kw)
+            self.value_scales = torch.zeros(p.batch, p.n_kv_heads, C, d // 32, dtype=torch.uint8, **kw)
         self.capacity_coarse = 0
         self.coarse_key_centroids = self.coarse_value_centroids = self.coarse_key_centroids_f32 = None
         self.coarse_sizes = self.coarse_offsets = self.coarse_members = self.parent = None
@@ -194,7 +203,8 @@ class ClusterState:
                       _ptr(self.sorted_keys), _ptr(self.sorted_values), _ptr(self.coarse_key_centroids),
                       _ptr(self.coarse_value_centroids), _ptr(self.coarse_key_centroids_f32),
                       _ptr(self.coarse_sizes), _ptr(self.coarse_offsets), _ptr(self.coarse_members),
-                      _ptr(self.parent), self.capacity_clusters, self.capacity_coarse, self.n_clustered,
+                      _ptr(self.parent), _ptr(self.key_codes), _ptr(self.key_scales), _ptr(self.value_codes),
+                      _ptr(self.value_scales), self.capacity_clusters, self.capacity_coarse, self.n_clustered,
                       self.n_clusters, self.n_coarse, self.n_blocks)
 
     def _take(self, cs: CState) -> None:
@@ -247,7 +257,8 @@ def update_window_concurrent(p: Params, k: torch.Tensor, v: torch.Tensor, n_toke
     blocks added).  `view` is the state as it was before the update: the same
     device arrays with the old host counters.  Decodes on other streams may go
     on using it while the update runs, because the update writes only past the
-    old clusters (new centroids, sizes, member lists, sorted rows) and
+    old clusters (new centroids and their fp8 copies, sizes, member lists,
+    sorted rows) and
     rewrites the old clusters' end offset with its own value.  Once `event`
     has completed (e.g. after stream.wait_event(event) on the decode stream),
     `state` holds the new clusters.  Flat method only."""

@@ -35,7 +35,8 @@ def test_struct_layout_matches_header():
 int main(void) {
   printf("params %zu state %zu debug %zu\n", sizeof(mpattn_params), sizeof(mpattn_state), sizeof(mpattn_decode_debug));
   P(mpattn_params, seed) P(mpattn_params, splits) P(mpattn_state, parent) P(mpattn_state, capacity_clusters)
-  P(mpattn_state, n_blocks) P(mpattn_decode_debug, exact_tokens)
+  P(mpattn_state, n_blocks) P(mpattn_decode_debug, exact_tokens) P(mpattn_params, centroid_format)
+  P(mpattn_state, key_codes) P(mpattn_state, value_scales)
   return 0;
 }
 """
@@ -56,6 +57,9 @@ int main(void) {
     assert int(offs["mpattn_state.capacity_clusters"]) == M.CState.capacity_clusters.offset
     assert int(offs["mpattn_state.n_blocks"]) == M.CState.n_blocks.offset
     assert int(offs["mpattn_decode_debug.exact_tokens"]) == M.CDebug.exact_tokens.offset
+    assert int(offs["mpattn_params.centroid_format"]) == M.CParams.centroid_format.offset
+    assert int(offs["mpattn_state.key_codes"]) == M.CState.key_codes.offset
+    assert int(offs["mpattn_state.value_scales"]) == M.CState.value_scales.offset
 
 
 def test_status_strings():
@@ -82,7 +86,7 @@ def test_capacity_bounds():
 def _fake_state(p, C=None, **over):
     C = C or p.max_clusters()
     fake = ctypes.c_void_p(0x10000)
-    s = M.CState(*([fake] * 7 + [None, None] + [None] * 7), C, 0, 0, 0, 0, 0)
+    s = M.CState(*([fake] * 7 + [None, None] + [None] * 7 + [None] * 4), C, 0, 0, 0, 0, 0)
     if p.hierarchical:
         for f in ("coarse_key_centroids", "coarse_value_centroids", "coarse_key_centroids_f32", "coarse_sizes",
                   "coarse_offsets", "coarse_members", "parent"):
@@ -119,6 +123,9 @@ def _decode(p, st, n_total, budget=128, mode=0, ws=1 << 40, first=0, last=None, 
     (dict(build_iters=0), M.ERR_INVALID_ARG),
     (dict(splits=-1), M.ERR_INVALID_ARG),
     (dict(coarse_tokens_per_centroid=64, cluster_block=8192), M.ERR_UNSUPPORTED),  # 128 coarse per block
+    (dict(centroid_format=2), M.ERR_INVALID_ARG),
+    (dict(centroid_format=1, dtype=torch.float32), M.ERR_UNSUPPORTED),
+    (dict(centroid_format=1, coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096), M.ERR_UNSUPPORTED),
 ])
 def test_parameter_validation(kw, status):
     p = _params(**kw)
@@ -142,6 +149,25 @@ def test_build_validation():
     assert _build(p, 100, _fake_state(p, sizes=None)) == M.ERR_INVALID_ARG
     ph = _params(coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
     assert _build(ph, 100, _fake_state(p)) == M.ERR_INVALID_ARG  # coarse arrays missing
+
+
+def test_fp8_centroid_validation():
+    """fp8 centroid copies: the state must carry all four arrays, and the
+    decode runs on the one-launch path only."""
+    p = _params(centroid_format=M.CENTROIDS_FP8)
+    assert _build(p, 100, _fake_state(p)) == M.ERR_INVALID_ARG  # no code arrays
+    full = dict(key_codes=FAKE, key_scales=FAKE, value_codes=FAKE, value_scales=FAKE)
+    for missing in full:
+        st = _fake_state(p, **{k: v for k, v in full.items() if k != missing})
+        assert _build(p, 100, st) == M.ERR_INVALID_ARG
+    st = _fake_state(p, n_clustered=4096, n_clusters=256, n_blocks=1, **full)
+    assert p.decode_stages() != ["unit"]                       # 2 units: the split launches
+    assert _decode(p, st, 4096) == M.ERR_UNSUPPORTED
+    assert _decode(p, _fake_state(p, n_clustered=4096, n_clusters=256, n_blocks=1), 4096) == M.ERR_INVALID_ARG
+    many = M.Params(batch=16, n_q_heads=32, n_kv_heads=8, capacity_tokens=32768, centroid_format=M.CENTROIDS_FP8)
+    assert many.decode_stages() == ["unit"]
+    assert _decode(dataclasses.replace(many, splits=4), _fake_state(many, n_clustered=4096, n_clusters=256,
+                                                                    n_blocks=1, **full), 4096) == M.ERR_UNSUPPORTED
 
 
 def test_update_validation():

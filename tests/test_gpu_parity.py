@@ -246,12 +246,13 @@ def test_tiny_config_free_running():
 # reductions, determinism, split invariance
 # ---------------------------------------------------------------------------
 
-def _built(B=2, Hq=8, Hkv=2, N=4500, Bc=2048, splits=0, dt=torch.bfloat16, sorted_copy=True, iters=4, r=16):
+def _built(B=2, Hq=8, Hkv=2, N=4500, Bc=2048, splits=0, dt=torch.bfloat16, sorted_copy=True, iters=4, r=16,
+           fmt=0):
     mp = M()
     w = small_workload(B, Hq, Hkv, N, 200, dt, outliers=4)
     K, V, means = workloads.make_cache(w)
     p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=dt, cluster_block=Bc,
-                  build_iters=iters, splits=splits, seed=1, tokens_per_centroid=r)
+                  build_iters=iters, splits=splits, seed=1, tokens_per_centroid=r, centroid_format=fmt)
     state = mp.ClusterState(p, DEV, sorted_copy=sorted_copy)
     mp.build_clusters(p, K.to(DEV), V.to(DEV), N, state)
     return mp, w, K, V, means, p, state
@@ -513,3 +514,104 @@ def test_per_head_selection_on_gpu_state_with_tail_and_replicas():
             ref = O.decode_unit(q[b, hq:hq + 1], K[b, hq // G], V[b, hq // G], 4500, st, T)
             ok, ea, er = close(out[b, hq:hq + 1], ref.out)
             assert ok, (b, hq, T, ea, er, n_cl)
+
+
+# ---------------------------------------------------------------------------
+# fp8 centroid copies: codes bit-exact against the oracle's encoder of the
+# GPU's own stored centroids; the decode against the oracle's decode of the
+# decoded centroids
+# ---------------------------------------------------------------------------
+def _check_codes(state, b, h, lo, hi):
+    from oracle import centroid_codes as F
+    for src, codes, scales in ((state.key_centroids, state.key_codes, state.key_scales),
+                               (state.value_centroids, state.value_codes, state.value_scales)):
+        want_c, want_s = F.encode_rows(src[b, h, lo:hi].double().cpu().numpy())
+        assert np.array_equal(codes[b, h, lo:hi].cpu().numpy(), want_c), (b, h)
+        assert np.array_equal(scales[b, h, lo:hi].cpu().numpy(), want_s), (b, h)
+
+
+def _coded_unit(state, b, h, p):
+    from oracle import centroid_codes as F
+    return F.coded_state(oracle_state_from_gpu(state, b, h, p))
+
+
+def test_fp8_codes_match_oracle_encoder():
+    mp, w, K, V, means, p, state = _built(B=16, Hq=32, Hkv=8, N=3000, Bc=1024, fmt=1)
+    C = state.n_clusters
+    for u in (0, 1, 77, 127):
+        _check_codes(state, u // 8, u % 8, 0, C)
+    # scale bytes stay in 1 .. 254 and no code is NaN
+    for t in (state.key_codes, state.value_codes):
+        assert not torch.any((t[:, :, :C] & 0x7F) == 0x7F)
+    assert int(state.key_scales[:, :, :C].min()) >= 1 and int(state.key_scales[:, :, :C].max()) <= 254
+
+
+@pytest.mark.parametrize("mode", ["multipole", "omit", "per_head"])
+def test_fp8_decode_matches_oracle(mode):
+    mp, w, K, V, means, p, state = _built(B=16, Hq=32, Hkv=8, N=3000, Bc=1024, fmt=1)
+    ps = dataclasses.replace(p, centroid_format=0)
+    assert p.decode_stages() == ["unit"]
+    md = {"multipole": mp.MODE_MULTIPOLE, "omit": mp.MODE_OMIT, "per_head": mp.MODE_PER_HEAD}[mode]
+    G = p.group
+    n_tie = 0
+    for step, T in enumerate((64, 700)):
+        q = queries(w, means, 70 + step)
+        dbg = mp.DecodeDebug.allocate(p, state, DEV, per_head=md == mp.MODE_PER_HEAD)
+        out = mp.decode(p, q.to(DEV), K.to(DEV), V.to(DEV), 3000, state, T, mode=md, debug=dbg).cpu().numpy()
+        stored = mp.decode(ps, q.to(DEV), K.to(DEV), V.to(DEV), 3000, state, T, mode=md).cpu().numpy()
+        assert not np.array_equal(out, stored)  # the codes are what the decode read
+        sel = dbg.selected.cpu().numpy()
+        for u in (0, 37, 127):
+            b, h = divmod(u, p.n_kv_heads)
+            st = _coded_unit(state, b, h, p)
+            heads = [(hq, hq, hq + 1) for hq in (h * G, h * G + G - 1)] if md == mp.MODE_PER_HEAD \
+                else [(h, h * G, (h + 1) * G)]
+            for sidx, g0, g1 in heads:
+                qu = q[b, g0:g1]
+                ref = O.decode_unit(qu, K[b, h], V[b, h], 3000, st, T, mode=1 if mode == "omit" else 0)
+                C = st.n_clusters
+                got_sel = sel[b, sidx, :C]
+                if np.array_equal(got_sel, ref.selected):
+                    want = ref.out
+                else:
+                    n_tie += 1
+                    tol = rank_tolerance(O.f64(qu), st.kbar[:C])
+                    assert selection_is_valid(ref.r, tol, st.sizes[:C], T, got_sel), (u, sidx, T)
+                    want = O.decode_with_selection(qu, K[b, h], V[b, h], 3000, st, got_sel,
+                                                   mode=1 if mode == "omit" else 0)
+                ok, ea, er = close(out[b, g0:g1], want)
+                assert ok, (mode, u, sidx, T, ea, er)
+    assert n_tie <= 2
+
+
+def test_fp8_codes_follow_the_window_update():
+    """The update writes the codes of the new clusters only; the old ones
+    keep theirs (the decode may read them meanwhile)."""
+    mp = M()
+    B, Hq, Hkv, Bc = 16, 32, 8, 1024
+    w = dataclasses.replace(small_workload(B, Hq, Hkv, 3000, 150, outliers=4), generated_blocks=2, cluster_block=Bc,
+                            drift=0.2)
+    K, V, means = workloads.make_cache(w)
+    N = w.capacity
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, cluster_block=Bc, build_iters=3,
+                  update_iters=2, seed=2, centroid_format=mp.CENTROIDS_FP8)
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, 3000, state)
+    C0 = state.n_clusters
+    before = state.key_codes[:, :, :C0].clone(), state.value_scales[:, :, :C0].clone()
+    mp.update_window(p, Kd, Vd, N, state)
+    C1 = state.n_clusters
+    assert C1 > C0
+    assert torch.equal(state.key_codes[:, :, :C0], before[0]) and torch.equal(state.value_scales[:, :, :C0], before[1])
+    for u in (3, 100):
+        _check_codes(state, u // Hkv, u % Hkv, C0, C1)
+    q = queries(w, means, 80)
+    T = 300
+    out = mp.decode(p, q.to(DEV), Kd, Vd, N, state, T).cpu().numpy()
+    G = p.group
+    for u in (3, 100):
+        b, h = divmod(u, Hkv)
+        ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], N, _coded_unit(state, b, h, p), T)
+        ok, ea, er = close(out[b, h * G:(h + 1) * G], ref.out)
+        assert ok, (u, ea, er)
