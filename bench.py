@@ -40,11 +40,19 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # (FETCH_SIZE reads 131085 KiB there: x2.0; WRITE_SIZE 262144 KiB: x1.0).
 # Valid only for the kernel sources they were taken on (sha256 over unit.hip,
 # attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
-UNIT_TRAFFIC = {
-    "sources_sha256": "3e1a2e8d5f1e92ddbbac7ee57b3a4a4b69384d945e76fb23f153b5c7c73c793c",
-    "fetch_bytes": int(121485.77 * 2.0 * 1024),
-    "write_bytes": int(7146.96 * 1.0 * 1024),
-    "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
+UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
+    "stored": {
+        "sources_sha256": "f21b3dd9775d50822813b8bf560aeff4329518183a2bc45cd7e8c2bbd4c2388b",
+        "fetch_bytes": int(122667.73 * 2.0 * 1024),
+        "write_bytes": int(5003.92 * 1.0 * 1024),
+        "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
+    },
+    "fp8": {
+        "sources_sha256": "f21b3dd9775d50822813b8bf560aeff4329518183a2bc45cd7e8c2bbd4c2388b",
+        "fetch_bytes": int(89949.05 * 2.0 * 1024),
+        "write_bytes": int(5004.12 * 1.0 * 1024),
+        "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
+    },
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
@@ -64,7 +72,10 @@ def parse():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--gather", action="store_true", help="decode by token-id gather instead of the sorted copy")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the online-update and hierarchical-decode measurements")
+                    help="skip the dense reference, the ablation, the fp8 step and the other rows")
+    ap.add_argument("--centroids", choices=["stored", "fp8"], default="stored",
+                    help="centroids the timed decode reads: the stored bf16 ones (the method as the pages "
+                         "describe it) or their fp8 copies")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -107,7 +118,8 @@ def main():
     Kd, Vd = K.to(dev), V.to(dev)
     p = M.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=w.dtype,
                  tokens_per_centroid=w.tokens_per_centroid, cluster_block=w.cluster_block,
-                 build_iters=w.build_iters, update_iters=w.update_iters, splits=args.splits, seed=0)
+                 build_iters=w.build_iters, update_iters=w.update_iters, splits=args.splits, seed=0,
+                 centroid_format=M.CENTROIDS_FP8 if args.centroids == "fp8" else M.CENTROIDS_STORED)
     state = M.ClusterState(p, dev, sorted_copy=not args.gather)
 
     # ---- build (prefill time), reported separately -------------------------
@@ -139,10 +151,11 @@ def main():
 
     def bytes_of(step):
         e = exact_rows[step]
-        score = B * Hq * d * 2 + U * C * d * 2            # queries + key centroids
+        crow = d + d // 32 if args.centroids == "fp8" else d * 2  # bytes of a centroid row
+        score = B * Hq * d * 2 + U * C * crow             # queries + key centroids
         # exact K/V rows + their ids + every value centroid (the attend launch
         # streams the approximate term of all clusters and removes the selected)
-        attend = e * d * 2 * 2 + e * 4 + U * C * d * 2
+        attend = e * d * 2 * 2 + e * 4 + U * C * crow
         other = U * C * 4 + B * Hq * d * 4                 # sizes + output
         return score, attend, other
 
@@ -241,7 +254,7 @@ def main():
 
     # ---- dense split-K decode of the same step (the pages' comparison point) --
     dense = fp8 = None
-    if not args.no_rows:
+    if not args.no_rows and args.centroids == "stored":
         dws = torch.empty(int(M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 1, 0, M.OP_DENSE)), dtype=torch.uint8,
                           device=dev)
         dts = []
@@ -282,7 +295,9 @@ def main():
         fp8 = {"us_per_step": round(f8_us, 2), "algorithmic_MB": round(f8_bytes / 1e6, 2),
                "roofline": {"bound": "hbm", "achieved": round(f8_bytes / (f8_us * 1e-6) / 1e9, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(f8_bytes / (f8_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+                            "frac": round(f8_bytes / (f8_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "traffic": _unit_traffic_bytes("fp8") if args.workload == DEFAULT_WORKLOAD and
+                            not args.gather else None},
                "speedup_vs_stored_centroids": round(cold_us / f8_us, 3)}
         log(f"[bench] fp8 centroids {f8_us:.1f} us/step ({fp8['roofline']['achieved']:.0f} GB/s algorithmic)")
         del state8
@@ -340,6 +355,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic clustered-Gaussian KV cache (no dataset/weights)",
         "config": {"workload": w.name, "batch": B, "seq_len": N, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d,
+                   "centroids": "bf16" if args.centroids == "stored" else "fp8 e4m3, scale per 32",
                    "token_budget": T, "tokens_per_centroid": w.tokens_per_centroid,
                    "cluster_block": w.cluster_block, "exact_rows": "sorted copy" if not args.gather else "gather",
                    "splits": args.splits or "auto"},
@@ -357,7 +373,8 @@ def main():
         "build_assign_TFLOPs_lower_bound": round(assign_flop / (build_ms * 1e-3) / 1e12, 1),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": _unit_traffic_bytes() if dom == "unit" and args.workload == DEFAULT_WORKLOAD else None,
+                     "traffic": _unit_traffic_bytes(args.centroids)
+                     if dom == "unit" and args.workload == DEFAULT_WORKLOAD and not args.gather else None,
                      "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
@@ -562,18 +579,21 @@ def measure_rows(M, workloads, dev, evict):
     return rows
 
 
-def _unit_traffic_bytes():
+def _unit_traffic_bytes(fmt):
     """Counter-derived HBM bytes per launch of the per-unit kernel, or None
     when its sources differ from the ones the counters were taken on."""
+    t = UNIT_TRAFFIC.get(fmt)
+    if t is None:
+        return None
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_long_context_means_amd", "csrc")
     for fn in ("unit.hip", "attn.hpp", "device.hpp", "kernels.hpp"):
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(f.read())
-    if h.hexdigest() != UNIT_TRAFFIC["sources_sha256"]:
+    if h.hexdigest() != t["sources_sha256"]:
         return None
-    return UNIT_TRAFFIC["fetch_bytes"] + UNIT_TRAFFIC["write_bytes"]
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def _cpu_model():
