@@ -116,10 +116,8 @@ def main():
     K, V, means = workloads.make_cache(w)
     log(f"[bench] synthetic cache {tuple(K.shape)} {K.dtype} in {time.time() - t0:.1f}s")
     Kd, Vd = K.to(dev), V.to(dev)
-    p = M.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, dtype=w.dtype,
-                 tokens_per_centroid=w.tokens_per_centroid, cluster_block=w.cluster_block,
-                 build_iters=w.build_iters, update_iters=w.update_iters, splits=args.splits, seed=0,
-                 centroid_format=M.CENTROIDS_FP8 if args.centroids == "fp8" else M.CENTROIDS_STORED)
+    p = _params_for(M, w, capacity_tokens=N, splits=args.splits,
+                    centroid_format=M.CENTROIDS_FP8 if args.centroids == "fp8" else M.CENTROIDS_STORED)
     state = M.ClusterState(p, dev, sorted_copy=not args.gather)
 
     # ---- build (prefill time), reported separately -------------------------
@@ -307,7 +305,7 @@ def main():
 
     # ---- CPU baseline: the oracle on the machine's host cores --------------------
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not p.hierarchical:  # the oracle leg times the flat decode
         import oracle as O
         from concurrent.futures import ThreadPoolExecutor
 
@@ -371,7 +369,7 @@ def main():
         "timed_wall_ms_incl_cache_flush": round(wall_ms, 2),
         "build_ms": round(build_ms, 2),
         "build_assign_TFLOPs_lower_bound": round(assign_flop / (build_ms * 1e-3) / 1e12, 1),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
+        "roofline": None if p.hierarchical else {"bound": "hbm", "kernel": dom, "achieved": round(att_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": _unit_traffic_bytes(args.centroids)
                      if dom == "unit" and args.workload == DEFAULT_WORKLOAD and not args.gather else None,
@@ -519,18 +517,26 @@ def measure_rows(M, workloads, dev, evict):
     dec_alone = float(np.median([x.elapsed_time(y) * 1e3 for x, y in evs]))
     conc_st = M.ClusterState(p, dev)
     M.build_clusters(p, Kd, Vd, w.n_tokens, conc_st)
+    torch.cuda.synchronize()
+    # both streams start at `origin`, which follows ~4 ms of streaming reads on
+    # the main stream: by then the host has enqueued the update and all the
+    # decodes, so the two really overlap
+    for _ in range(20):
+        evict()
     origin = torch.cuda.Event(enable_timing=True)
     origin.record(main)
     side.wait_event(origin)
     view, done, _ = M.update_window_concurrent(p, Kd, Vd, n_total, conc_st, side)
-    evs = decodes(view)
     end = torch.cuda.Event(enable_timing=True)
-    end.record(side)
+    end.record(side)  # right behind the update's launches
+    evs = decodes(view)
     torch.cuda.synchronize()
     upd_conc = origin.elapsed_time(end)
     during = [x.elapsed_time(y) * 1e3 for x, y in evs if origin.elapsed_time(x) < upd_conc]
+    last_dec = max(origin.elapsed_time(y) for _, y in evs)
     rows["H3_concurrent_update"] = {
         "workload": w.name, "decodes_enqueued": len(dq),
+        "decodes_end_ms": round(last_dec, 3),
         "decode_us_alone": round(dec_alone, 2),
         "decode_us_during_update": round(float(np.median(during)), 2) if during else None,
         "decodes_during_update": len(during),
