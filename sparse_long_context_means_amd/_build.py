@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmpattn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "kmeans.hip", "codes.hip", "decode.hip", "unit.hip", "dense.hip", "probe.hip"]
+SOURCES = ["api.hip", "kmeans.hip", "codes.hip", "decode.hip", "unit.hip", "hier.hip", "dense.hip", "probe.hip"]
 ARCH = os.environ.get("MPATTN_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

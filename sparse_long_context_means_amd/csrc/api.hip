@@ -81,6 +81,7 @@ int32_t max_chunks(const mpattn_params* p, int32_t Cmax, int32_t Dmax) {
 }
 
 bool unit_path(const mpattn_params* p);
+bool hier_unit_path(const mpattn_params* p);
 
 // Decode workspace regions.
 struct DecodeWs {
@@ -90,6 +91,9 @@ struct DecodeWs {
     uint64_t* xpart;      // [U][Rx][G][d + 2] partials
     uint64_t* xcount;     // [U] arrival words
     int32_t Rx;           // most replicas a decode on this layout uses
+    uint64_t* hpart;      // hierarchy in one launch: [U][Rh][G][d + 2] partial words
+    uint64_t* hcount;     // [U] arrival words
+    int32_t Rh;
     int32_t Rxh;          // the same when each query head is its own unit
     float* s;             // [U][Cmax][G] scores by cluster id
     int4* rs;             // [U][Cmax] cut records by item
@@ -139,6 +143,11 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
             w.xpart = (uint64_t*)take(parts * (kD + 2) * 8);
             w.xcount = (uint64_t*)take(U * G * 8);
         }
+    }
+    if (hier_unit_path(p)) {
+        w.Rh = hier_replicas((int)U);
+        w.hpart = (uint64_t*)take(U * w.Rh * G * (kD + 2) * 8);
+        w.hcount = (uint64_t*)take(U * 8);
     }
     w.s = (float*)take(U * Cmax * G * 4);
     w.rs = (int4*)take(U * Cmax * 16);
@@ -256,6 +265,16 @@ bool unit_path(const mpattn_params* p) {
     return unit_path_fits(p->dtype, G, mpattn_max_clusters(p)) && p->batch * p->n_kv_heads >= kUnitPathMinUnits;
 }
 const char* kHierStages[] = {"coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"};
+const char* kHierUnitStages[] = {"hier_unit"};
+
+// The whole hierarchical decode step of a unit in one launch (hier.hip):
+// bf16 storage, automatic splits, groups of up to 4 query heads, at most
+// 2048 coarse clusters and a candidate budget of at most 4096 tokens.
+bool hier_unit_path(const mpattn_params* p) {
+    if (!is_hier(p) || p->splits > 0 || p->dtype != MPATTN_BF16) return false;
+    const int G = p->n_q_heads / p->n_kv_heads;
+    return hier_path_fits(p->dtype, G, mpattn_max_coarse(p), p->coarse_candidate_tokens);
+}
 
 }  // namespace
 
@@ -361,13 +380,14 @@ mpattn_status mpattn_update_window(const mpattn_params* p, const void* k, const 
 
 int32_t mpattn_decode_stage_count(const mpattn_params* p) {
     if (check_params(p) != MPATTN_OK) return 0;
-    return is_hier(p) ? 6 : unit_path(p) ? 1 : 4;
+    return is_hier(p) ? (hier_unit_path(p) ? 1 : 6) : unit_path(p) ? 1 : 4;
 }
 
 const char* mpattn_decode_stage_name(const mpattn_params* p, int32_t stage) {
     const int32_t n = mpattn_decode_stage_count(p);
     if (stage < 0 || stage >= n) return nullptr;
-    return is_hier(p) ? kHierStages[stage] : unit_path(p) ? kUnitStages[stage] : kFlatStages[stage];
+    if (is_hier(p)) return hier_unit_path(p) ? kHierUnitStages[stage] : kHierStages[stage];
+    return unit_path(p) ? kUnitStages[stage] : kFlatStages[stage];
 }
 
 mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void* k, const void* v,
@@ -411,6 +431,47 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
     const int32_t bound = C < p->coarse_candidate_tokens ? C : p->coarse_candidate_tokens;
     const int32_t P = S;  // partial slots: one per attend split
 
+    if (hier_unit_path(p)) {  // one stage
+        const int R = hier_replicas(U);
+        if (R != w.Rh) return MPATTN_ERR_WORKSPACE;
+        HierArgs a{};
+        a.q = q;
+        a.kbar = st->key_centroids;
+        a.vbar = st->value_centroids;
+        a.sizes = st->sizes;
+        a.offsets = st->offsets;
+        a.Kx = sorted ? st->sorted_keys : k;
+        a.Vx = sorted ? st->sorted_values : v;
+        a.token_ids = sorted ? nullptr : st->token_ids;
+        a.K = k;
+        a.V = v;
+        a.ckbar = st->coarse_key_centroids;
+        a.cvbar = st->coarse_value_centroids;
+        a.csizes = st->coarse_sizes;
+        a.coffsets = st->coarse_offsets;
+        a.cmembers = st->coarse_members;
+        a.Cmax = Cmax;
+        a.Dmax = Dmax;
+        a.C = C;
+        a.D = st->n_coarse;
+        a.Nmax = N;
+        a.n_clustered = st->n_clustered;
+        a.n_total = n_tokens_total;
+        a.budget = token_budget;
+        a.cand_budget = p->coarse_candidate_tokens;
+        a.pseudo = want_pseudo;
+        a.Hq = p->n_q_heads;
+        a.Hkv = p->n_kv_heads;
+        a.out = out;
+        a.xpart = w.hpart;
+        a.xcount = w.hcount;
+        a.tag = next_tag();
+        a.dbg_selected = debug ? debug->selected : nullptr;
+        a.dbg_candidates = debug ? debug->candidates : nullptr;
+        a.dbg_exact = debug ? debug->exact_tokens : nullptr;
+        MPA_TRY(launch_hier_decode(p->dtype, G, a, U, R, s));
+        return MPATTN_OK;
+    }
     if (unit_path(p)) {  // one stage
         // per-head selection: each query head is a unit of one head that
         // reads the clusters and cache of its KV head

@@ -1,0 +1,702 @@
+// hier.hip -- one decode step of the hierarchical method for a (sequence, KV
+// head) unit in one launch: R workgroups of 512 threads per unit.
+//
+// Pages: atlas.scime.ai summary, "Approach" (the hierarchical variant: coarse
+// centroids over the fine ones, lookup and approximation at two levels) and
+// opening sentence (exact attention on the top-scoring clusters, centroid
+// terms for the rest).
+//
+// Every workgroup of a unit takes the same two cuts with the same operations:
+//   1. scores of all coarse clusters on the matrix cores; the group-mean key;
+//   2. the coarse cut under the candidate budget (candidates);
+//   3. the candidates' non-empty fine clusters, listed by coarse id, then in
+//      member order;
+//   4. scores of those fine clusters; the fine cut under the token budget,
+//      in (key desc, fine id asc) order;
+// then takes its share of the work:
+//   5. approximate terms: its share of the coarse clusters that are not
+//      candidates, and of the candidates' fine clusters that were not
+//      selected (n exp(s) on the value centroid, per query head);
+//   6. exact rows: its share of the selected fine clusters' members followed
+//      by the unclustered tail;
+//   7. the partials of the workgroups are merged by the last one to finish,
+//      through tagged 64-bit words as in unit.hip.
+// The coarse scoring is repeated in every workgroup of a unit (the
+// workgroups of a unit share an XCD, so the repeats read from its L2).
+#include <math.h>
+
+#include "attn.hpp"
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace mpa {
+
+constexpr int kHThreads = 512;
+constexpr int kHWaves = kHThreads / kWave;  // 8
+constexpr int kHRowBatch = 1024;            // staged exact rows per pass
+constexpr int kHScoreDepth = 4;             // score steps in flight per wave
+constexpr int kHExactDepth = 2;             // exact-row steps (16 rows) in flight per wave
+constexpr uint64_t kHPartialWaitTicks = 100000;
+
+// Workgroup barrier ordering LDS only (global loads and stores in flight are
+// not waited for).
+__device__ __forceinline__ void hlds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exclusive scan of one counter over the workgroup in thread order (`lds`:
+// kHWaves ints); the total in tot.
+__device__ __forceinline__ int block_exclusive_sum(int v, int& tot, int* lds) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int inc = wave_inclusive_sum(v);
+    if (lane == kWave - 1) lds[wave] = inc;
+    hlds_barrier();
+    int base = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < kHWaves; ++w) {
+        const int x = lds[w];
+        if (w < wave) base += x;
+        t += x;
+    }
+    hlds_barrier();  // lds may be reused right after
+    tot = t;
+    return base + inc - v;
+}
+
+// Budget cut over n items by the whole workgroup: the longest prefix of the
+// non-empty items in (key desc, id asc) order whose sizes sum to at most
+// `budget` (four 8-bit radix passes over the order-preserving key bits,
+// weighted by size, find the cut value; items at it are taken in id order
+// while they fit).  Thread t owns items ITEMS t .. ITEMS t + ITEMS - 1; bit j
+// of the result is item ITEMS t + j.  key(i), size(i), id(i) read item i
+// (i < n); id orders items with equal keys.
+template <int ITEMS, typename KeyF, typename SizeF, typename IdF>
+__device__ __forceinline__ uint32_t block_cut(KeyF key_of, SizeF size_of, IdF id_of, int n, int budget,
+                                              int (*hist)[256], int* scan) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    uint32_t key[ITEMS];
+    int isz[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int i = tid * ITEMS + j;
+        key[j] = i < n ? order_key(key_of(i)) : 0u;
+        isz[j] = i < n ? size_of(i) : 0;
+    }
+    for (int k = tid; k < 4 * 256; k += kHThreads) reinterpret_cast<int*>(hist)[k] = 0;
+    hlds_barrier();
+    uint32_t prefix = 0, pmask = 0;
+    int Rb = budget;
+    bool done = false;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j)
+            if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
+        hlds_barrier();
+        int v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = hist[p][255 - (4 * lane + q)];
+        int total;
+        int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
+        if (total <= Rb) {  // the same in every wave: every candidate left fits
+            done = true;
+            break;
+        }
+        int found = -1, cum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (found < 0 && run <= Rb && Rb < run + v[q]) {
+                found = 255 - (4 * lane + q);
+                cum = run;
+            }
+            run += v[q];
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = __ffsll((long long)bal) - 1;
+        const int digit = lane_value(found, src);
+        Rb -= lane_value(cum, src);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xFFu << shift;
+    }
+    uint32_t bits = 0;
+    if (done) {
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) bits |= (uint32_t)(isz[j] > 0 && key[j] >= prefix) << j;
+        return bits;
+    }
+    // items at the cut value, in id order while they fit: an item's running
+    // sum is the sizes of the tied items with lower ids (ties are rare, so
+    // each tied item scans all items)
+    int ties = 0;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) ties += isz[j] > 0 && key[j] == prefix;
+    int tt;
+    block_exclusive_sum(ties, tt, scan);  // tt: tied items in the workgroup
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        bool sel = isz[j] > 0 && key[j] > prefix;
+        if (isz[j] > 0 && key[j] == prefix) {
+            int run = 0;
+            if (tt > 1) {
+                const int me = id_of(tid * ITEMS + j);
+                for (int i = 0; i < n; ++i) {
+                    const int s = size_of(i);
+                    if (s > 0 && id_of(i) < me && order_key(key_of(i)) == prefix) run += s;
+                }
+            }
+            sel = run + isz[j] <= Rb;
+        }
+        bits |= (uint32_t)sel << j;
+    }
+    return bits;
+}
+
+// LDS layout (bytes).  Regions reused once their phase is over are noted.
+template <int G>
+struct HierLds {
+    static constexpr int ckey = 0;                               // float [MaxD]: coarse keys; then int
+                                                                 // [MaxD] candidate prefix; then int
+                                                                 // [MaxF] selected list (spans csz too)
+    static constexpr int csz = ckey + kHierMaxD * 4;             // int [MaxD]: coarse sizes
+    static constexpr int cmask = csz + kHierMaxD * 4;            // uint32 [MaxD / 32]: candidates
+    static constexpr int fid = cmask + kHierMaxD / 8;            // int [MaxF]: candidates' fine ids
+    static constexpr int fkey = fid + kHierMaxF * 4;             // float [MaxF]: fine keys
+    static constexpr int fsz = fkey + kHierMaxF * 4;             // int [MaxF]: fine sizes
+    static constexpr int fmask = fsz + kHierMaxF * 4;            // uint32 [MaxF / 32]: selected
+    static constexpr int spre = fmask + kHierMaxF / 8;           // int [MaxF + 4]: candidate coarse
+                                                                 // ids; then selected-row prefix
+    static constexpr int lg = spre + (kHierMaxF + 4) * 4;        // float [MaxShare][G]
+    static constexpr int hist = lg + kHierMaxShare * G * 4;      // int [4][256]
+    static constexpr int scan = hist + 4 * 256 * 4;              // int [64]
+    static constexpr int misc = scan + 64 * 4;                   // int [16]
+    static constexpr int gmax = misc + 16 * 4;                   // float [waves][G]
+    static constexpr int pexp = gmax + kHWaves * G * 4;         // float [waves][16][G]
+    static constexpr int row = pexp + kHWaves * 16 * G * 4;     // int [RowBatch]
+    static constexpr int bytes = row + kHRowBatch * 4;
+    static constexpr int red = fid;                              // float [waves][G][d + 2], after the
+                                                                 // exact rows (spans fid, fkey)
+    static_assert(kHWaves * G * (kHeadDim + 2) * 4 <= 2 * kHierMaxF * 4, "reduction region");
+};
+
+template <int G>
+__global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
+    using L = HierLds<G>;
+    __shared__ __align__(16) char lds[L::bytes];
+    float* s_ckey = reinterpret_cast<float*>(lds + L::ckey);
+    int32_t* s_cpre = reinterpret_cast<int32_t*>(lds + L::ckey);  // after the coarse cut
+    int32_t* s_sid = reinterpret_cast<int32_t*>(lds + L::ckey);   // after the fine cut
+    int32_t* s_csz = reinterpret_cast<int32_t*>(lds + L::csz);
+    uint32_t* s_cmask = reinterpret_cast<uint32_t*>(lds + L::cmask);
+    int32_t* s_fid = reinterpret_cast<int32_t*>(lds + L::fid);
+    float* s_fkey = reinterpret_cast<float*>(lds + L::fkey);
+    int32_t* s_fsz = reinterpret_cast<int32_t*>(lds + L::fsz);
+    uint32_t* s_fmask = reinterpret_cast<uint32_t*>(lds + L::fmask);
+    int32_t* s_ccand = reinterpret_cast<int32_t*>(lds + L::spre);  // before the fine cut
+    int32_t* s_spre = reinterpret_cast<int32_t*>(lds + L::spre);
+    float(*s_lg)[G] = reinterpret_cast<float(*)[G]>(lds + L::lg);
+    int(*hist)[256] = reinterpret_cast<int(*)[256]>(lds + L::hist);
+    int* s_scan = reinterpret_cast<int*>(lds + L::scan);
+    int* s_misc = reinterpret_cast<int*>(lds + L::misc);
+    float(*s_gmax)[G] = reinterpret_cast<float(*)[G]>(lds + L::gmax);
+    float* s_p = reinterpret_cast<float*>(lds + L::pexp);
+    int32_t* s_row = reinterpret_cast<int32_t*>(lds + L::row);
+    float(*s_red)[G][kHeadDim + 2] = reinterpret_cast<float(*)[G][kHeadDim + 2]>(lds + L::red);
+
+    const int unit = blockIdx.x, rep = blockIdx.y, R = gridDim.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rg = lane >> 4, li = lane & 15;
+    const int b = unit / a.Hkv, h = unit % a.Hkv;
+    const int D = a.D, C = a.C;
+    const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
+    const bf16_t* ck = reinterpret_cast<const bf16_t*>(a.ckbar) + (size_t)unit * a.Dmax * kHeadDim;
+    const bf16_t* fk = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim;
+    const int32_t* csizes = a.csizes + (size_t)unit * a.Dmax;
+    const int32_t* coffs = a.coffsets + (size_t)unit * (a.Dmax + 1);
+    const int32_t* cmem = a.cmembers + (size_t)unit * a.Cmax;
+    const int32_t* fsizes = a.sizes + (size_t)unit * a.Cmax;
+    const int32_t* foffs = a.offsets + (size_t)unit * (a.Cmax + 1);
+    const bool dbg = rep == 0;
+
+    // optional inspection: zeros first (the cuts set their ones after a
+    // barrier that orders global memory)
+    if (dbg && a.dbg_selected)
+        for (int i = tid; i < C; i += kHThreads) a.dbg_selected[(size_t)unit * C + i] = 0;
+
+    QOperand qop;
+    load_qop<G>(qop, qg, lane);
+    float lgmax = -INFINITY;  // the lane's maximum share logit (head li)
+
+    // Scores of items [0, n): row(i) is the centroid row of item i; the
+    // ranking key of item i goes to keys[i] (if keys), the base-2 logit
+    // s log2(e) + log2(size) of items of [s0, s1) to s_lg[i - s0 + lg0].
+    // Lane l loads row l % 16 of its wave's 16; the waves interleave.
+    auto score_items = [&](int n, auto row_of, auto size_of, float* keys, int s0, int s1, int lg0) {
+        if (n == 0) return;  // (uniform) row 0 exists only for n >= 1
+        const int steps = (n + 16 * kHWaves - 1) / (16 * kHWaves);
+        auto base = [&](int step) { return step * 16 * kHWaves + wave * 16; };
+        Slice8<bf16_t> ring[kHScoreDepth][4];
+#pragma unroll
+        for (int j = 0; j < kHScoreDepth; ++j) {
+            const int i = base(j) + li;
+            load_row_blocks(ring[j], row_of(i < n ? i : 0), lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int it = 0; it < steps; it += kHScoreDepth) {
+#pragma unroll
+            for (int j = 0; j < kHScoreDepth; ++j) {
+                const f32x4v d = mfma_scores(ring[j], qop);
+                const int cb = base(it + j) + 4 * rg;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sv = d[e] * kInvSqrtD;
+                    const float key = head_mean<G>(sv);
+                    const int i = cb + e;
+                    if (i < n) {
+                        if (li == 0 && keys) keys[i] = key;
+                        if (li < G && i >= s0 && i < s1) {
+                            const int sz = size_of(i);
+                            const float lgv = sz > 0 ? fmaf(sv, kLog2e, log2_count(sz)) : -INFINITY;
+                            s_lg[i - s0 + lg0][li] = lgv;
+                            lgmax = fmaxf(lgmax, lgv);
+                        }
+                    }
+                }
+                const int i = base(it + j + kHScoreDepth) + li;
+                load_row_blocks(ring[j], row_of(i < n ? i : 0), lane);
+                __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+            }
+        }
+    };
+
+    // ---- 1. coarse scores (all of them; the share's logits kept) ---------
+    for (int i = tid; i < D; i += kHThreads) s_csz[i] = csizes[i];
+    for (int i = tid; i < kHierMaxD / 32; i += kHThreads) s_cmask[i] = 0u;
+    for (int i = tid; i < kHierMaxF / 32; i += kHThreads) s_fmask[i] = 0u;
+    hlds_barrier();
+    const int cs0 = (int)((int64_t)D * rep / R), cs1 = (int)((int64_t)D * (rep + 1) / R);
+    score_items(
+        D, [&](int i) { return ck + (size_t)i * kHeadDim; }, [&](int i) { return s_csz[i]; }, s_ckey, cs0, cs1, 0);
+    hlds_barrier();
+
+    // ---- 2. coarse cut under the candidate budget -----------------------
+    constexpr int kCItems = kHierMaxD / kHThreads;
+    const uint32_t cbits = block_cut<kCItems>(
+        [&](int i) { return s_ckey[i]; }, [&](int i) { return s_csz[i]; }, [&](int i) { return i; }, D,
+        a.cand_budget, hist, s_scan);
+    // candidate flags; then the candidates in id order with their member
+    // counts (prefix), and the fine candidate count F
+    int nmem = 0;
+#pragma unroll
+    for (int j = 0; j < kCItems; ++j) {
+        const int i = tid * kCItems + j;
+        if ((cbits >> j) & 1u) nmem += coffs[i + 1] - coffs[i];
+    }
+    {
+        // kCItems <= 32: one word of flags per thread (bits of consecutive items)
+        static_assert(kCItems <= 32 && 32 % kCItems == 0, "flag packing");
+        const uint32_t shifted = cbits << ((tid * kCItems) & 31);
+        atomicOr(&s_cmask[(tid * kCItems) >> 5], shifted);
+    }
+    int ncand_t = __popc(cbits), ncand;
+    const int k0 = block_exclusive_sum(ncand_t, ncand, s_scan);
+    int F;
+    int m0 = block_exclusive_sum(nmem, F, s_scan + 16);
+    // F <= candidate budget <= kHierMaxF for any state the build wrote: every
+    // candidate fine cluster holds at least one of the candidates' tokens
+    F = min(F, kHierMaxF);
+    {
+        int k = k0;
+#pragma unroll
+        for (int j = 0; j < kCItems; ++j) {
+            const int i = tid * kCItems + j;
+            if ((cbits >> j) & 1u) {
+                s_ccand[k] = i;
+                s_cpre[k] = m0;
+                m0 += coffs[i + 1] - coffs[i];
+                ++k;
+            }
+        }
+    }
+    if (tid == 0) s_cpre[ncand] = F;
+    if (dbg && a.dbg_candidates)
+#pragma unroll
+        for (int j = 0; j < kCItems; ++j) {
+            const int i = tid * kCItems + j;
+            if (i < D) a.dbg_candidates[(size_t)unit * D + i] = (cbits >> j) & 1u;
+        }
+    hlds_barrier();
+    for (int p = tid; p < F; p += kHThreads) {
+        const int k = upper_index(s_cpre, ncand, p);
+        const int c = s_ccand[k];
+        const int f = cmem[coffs[c] + p - s_cpre[k]];
+        s_fid[p] = f;
+        s_fsz[p] = fsizes[f];
+    }
+    hlds_barrier();
+
+    // ---- 3. fine scores of the candidates ---------------------------------
+    const int dsh = cs1 - cs0;  // coarse share logits at s_lg[0 .. dsh)
+    const int fs0 = (int)((int64_t)F * rep / R), fs1 = (int)((int64_t)F * (rep + 1) / R);
+    score_items(
+        F, [&](int i) { return fk + (size_t)s_fid[i] * kHeadDim; }, [&](int i) { return s_fsz[i]; }, s_fkey, fs0, fs1,
+        dsh);
+    lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 16));
+    lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 32));
+    if (lane < G) s_gmax[wave][lane] = lgmax;
+    hlds_barrier();
+
+    // ---- 4. fine cut under the token budget, in fine-id order for ties ----
+    constexpr int kFItems = kHierMaxF / kHThreads;
+    const uint32_t fbits = block_cut<kFItems>(
+        [&](int i) { return s_fkey[i]; }, [&](int i) { return s_fsz[i]; }, [&](int i) { return s_fid[i]; }, F,
+        a.budget, hist, s_scan);
+    {
+        static_assert(kFItems <= 32 && 32 % kFItems == 0, "flag packing");
+        atomicOr(&s_fmask[(tid * kFItems) >> 5], fbits << ((tid * kFItems) & 31));
+    }
+    // the selected candidates in candidate order with their row prefix
+    int rows_t = 0;
+#pragma unroll
+    for (int j = 0; j < kFItems; ++j)
+        if ((fbits >> j) & 1u) rows_t += s_fsz[tid * kFItems + j];
+    int nsel, E;
+    const int sk0 = block_exclusive_sum(__popc(fbits), nsel, s_scan);
+    int ro = block_exclusive_sum(rows_t, E, s_scan + 16);
+    {
+        int k = sk0;
+#pragma unroll
+        for (int j = 0; j < kFItems; ++j) {
+            const int i = tid * kFItems + j;
+            if ((fbits >> j) & 1u) {
+                s_sid[k] = i;
+                s_spre[k] = ro;
+                ro += s_fsz[i];
+                ++k;
+            }
+        }
+    }
+    if (tid == 0) s_spre[nsel] = E;
+    if (dbg) {
+        if (a.dbg_selected) {
+            __syncthreads();  // the zeros above are written
+#pragma unroll
+            for (int j = 0; j < kFItems; ++j)
+                if ((fbits >> j) & 1u) a.dbg_selected[(size_t)unit * C + s_fid[tid * kFItems + j]] = 1;
+        }
+        if (tid == 0 && a.dbg_exact) a.dbg_exact[unit] = E;
+    }
+
+    // ---- 5. approximate terms of the share: coarse clusters that are not
+    //      candidates, fine candidates not selected.  Weights 2^(lg - M),
+    //      M the share's largest logit per head (every weight <= 1). -----------
+    SoftState<G> st;
+    st.init();
+    float Mref[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float m = s_gmax[0][g];
+#pragma unroll
+        for (int w = 1; w < kHWaves; ++w) m = fmaxf(m, s_gmax[w][g]);
+        Mref[g] = m;
+    }
+    const int fsh = fs1 - fs0, nsh = dsh + fsh;
+    for (int t = tid; t < nsh; t += kHThreads) {
+        bool keep;
+        if (t < dsh) {
+            const int c = cs0 + t;
+            keep = !((s_cmask[c >> 5] >> (c & 31)) & 1u);
+        } else {
+            const int i = fs0 + t - dsh;
+            keep = !((s_fmask[i >> 5] >> (i & 31)) & 1u);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float lgv = s_lg[t][g];
+            s_lg[t][g] = keep && lgv != -INFINITY ? __builtin_amdgcn_exp2f(lgv - Mref[g]) : 0.f;
+        }
+    }
+    hlds_barrier();
+    if (a.pseudo && nsh > 0) {  // (uniform) item 0 of the share exists
+#pragma unroll
+        for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
+        const bf16_t* cv = reinterpret_cast<const bf16_t*>(a.cvbar) + (size_t)unit * a.Dmax * kHeadDim + li * 8;
+        const bf16_t* fv = reinterpret_cast<const bf16_t*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+        auto vrow = [&](int t) {
+            return t < dsh ? cv + (size_t)(cs0 + t) * kHeadDim : fv + (size_t)s_fid[fs0 + t - dsh] * kHeadDim;
+        };
+        // 32 row groups, one row each per pass, two passes in flight
+        const int rgi = wave * 4 + rg;
+        constexpr int kPass = 4 * kHWaves;
+        Slice8<bf16_t> v[2];
+        v[0].load(vrow(rgi < nsh ? rgi : 0));
+        v[1].load(vrow(rgi + kPass < nsh ? rgi + kPass : 0));
+        for (int t0 = 0; t0 < nsh; t0 += 2 * kPass) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int t = t0 + u * kPass + rgi;
+                float x[8];
+                v[u].unpack(x);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float w = t < nsh ? s_lg[t][g] : 0.f;
+                    st.l[g] += w;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+                }
+                const int tn = t + 2 * kPass;
+                v[u].load(vrow(tn < nsh ? tn : 0));
+            }
+        }
+    }
+
+    // ---- 6. exact rows of the share: selected members [0, E), then the
+    //      unclustered tail [E, E + Tn) (staged as -1 - token, read from K, V)
+    const float qscale = kInvSqrtD * kLog2e;
+    const size_t ubase = (size_t)unit * a.Nmax * kHeadDim;
+    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)unit * a.Nmax : nullptr;
+    const int Tn = a.n_total - a.n_clustered;
+    const int Et = E + Tn;
+    const int e0 = (int)((int64_t)Et * rep / R), e1 = (int)((int64_t)Et * (rep + 1) / R);
+    {
+        const bf16_t* Kx = reinterpret_cast<const bf16_t*>(a.Kx) + ubase;
+        const bf16_t* Vx = reinterpret_cast<const bf16_t*>(a.Vx) + ubase + li * 8;
+        const bf16_t* Kt = reinterpret_cast<const bf16_t*>(a.K) + ubase;
+        const bf16_t* Vt = reinterpret_cast<const bf16_t*>(a.V) + ubase + li * 8;
+        float mv = exact16_enter<G>(st);
+        float lp = 0.f;
+        float* sp = s_p + wave * 16 * G;
+        for (int c0 = e0; c0 < e1; c0 += kHRowBatch) {
+            const int cnt = min(kHRowBatch, e1 - c0);
+            hlds_barrier();  // the previous batch is consumed
+            for (int i = tid; i < cnt; i += kHThreads) {
+                const int r = c0 + i;
+                int v;
+                if (r < E) {  // member r - pre[k] of selected candidate k
+                    const int k = upper_index(s_spre, nsel, r);
+                    const int pos = foffs[s_fid[s_sid[k]]] + r - s_spre[k];
+                    v = tids ? tids[pos] : pos;
+                } else {
+                    v = -1 - (a.n_clustered + r - E);
+                }
+                s_row[i] = v;
+            }
+            hlds_barrier();
+            const int nb = (cnt + 15) / 16;
+            auto blk = [&](int step) {
+                const int q = step * kHWaves + wave;
+                return q < nb ? q : nb;  // nb: past the end, masked
+            };
+            auto load_step = [&](ExactRows16& rr, int step) {
+                const int ib = blk(step) * 16;
+                const int ik = ib + li;
+                const int rk = s_row[ik < cnt ? ik : 0];
+                load_row_blocks(rr.k, rk >= 0 ? Kx + (size_t)rk * kHeadDim : Kt + (size_t)(-1 - rk) * kHeadDim, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int iv = ib + 4 * rg + e;
+                    const int rv = s_row[iv < cnt ? iv : 0];
+                    rr.v[e].load(rv >= 0 ? Vx + (size_t)rv * kHeadDim : Vt + (size_t)(-1 - rv) * kHeadDim);
+                }
+            };
+            ExactRows16 ring[kHExactDepth];
+#pragma unroll
+            for (int j = 0; j < kHExactDepth; ++j) {
+                load_step(ring[j], j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int steps = (nb + kHWaves - 1) / kHWaves;
+            for (int it = 0; it < steps; it += kHExactDepth) {
+#pragma unroll
+                for (int j = 0; j < kHExactDepth; ++j) {
+                    exact16_step<G>(st, mv, lp, sp, qop, ring[j], blk(it + j) * 16 + 4 * rg, cnt, qscale);
+                    load_step(ring[j], it + j + kHExactDepth);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        exact16_leave<G>(st, mv, lp);
+    }
+
+    // ---- 7. combine the row groups (shuffles), then the waves (LDS) --------
+#pragma unroll
+    for (int step = 16; step <= 32; step <<= 1) {
+        float om[G], ol[G], oacc[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            om[g] = shfl_xor_f(st.m[g], step);
+            ol[g] = shfl_xor_f(st.l[g], step);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
+        }
+        merge_state<G>(st, om, ol, oacc);
+    }
+    hlds_barrier();  // the candidate lists are dead: the reduction region is free
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
+            if (li == 0) {
+                s_red[wave][g][kHeadDim] = st.m[g];
+                s_red[wave][g][kHeadDim + 1] = st.l[g];
+            }
+        }
+    }
+    hlds_barrier();
+    constexpr int kOut = (G * kHeadDim + kHThreads - 1) / kHThreads;
+    float oM[kOut], oL[kOut], oA[kOut];
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kHThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kHWaves; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kHWaves; ++w) {
+                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
+                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
+                acc = fmaf(s_red[w][g][dd], wt, acc);
+            }
+        }
+        oM[k] = M;
+        oL[k] = l;
+        oA[k] = acc;
+    }
+    float* outu = a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
+    if (R == 1) {
+#pragma unroll
+        for (int k = 0; k < kOut; ++k) {
+            const int e = tid + k * kHThreads;
+            if (e < G * kHeadDim) outu[e] = oL[k] > 0.f ? oA[k] / oL[k] : 0.f;
+        }
+        return;
+    }
+
+    // ---- several workgroups: each posts its partial as tagged words and
+    //      counts itself in on the unit's arrival word; the last one to
+    //      arrive merges in workgroup order (waiting only for words that are
+    //      already stored) and writes the output. -------------------------------
+    const uint64_t tagw = (uint64_t)a.tag << 32;
+    constexpr int kPart = G * (kHeadDim + 2);
+    uint64_t* xp = a.xpart + (size_t)unit * R * kPart;
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kHThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
+        __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (dd == 0) {
+            __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    hlds_barrier();
+    if (tid == 0) {
+        uint64_t* cntw = a.xcount + unit;
+        uint64_t old = __hip_atomic_load(cntw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t arrived;
+        for (;;) {
+            arrived = ((uint32_t)(old >> 32) == a.tag ? (uint32_t)old : 0u) + 1u;
+            if (__hip_atomic_compare_exchange_strong(cntw, &old, tagw | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+        s_misc[0] = arrived == (uint32_t)R;
+    }
+    hlds_barrier();
+    if (!s_misc[0]) return;
+    const uint64_t t0 = wall_clock64();
+    bool late = false;
+    auto fresh = [&](uint64_t v, const uint64_t* p) {
+        while ((uint32_t)(v >> 32) != a.tag && !late) {
+            if (wall_clock64() - t0 > kHPartialWaitTicks) late = true;
+            __builtin_amdgcn_s_sleep(1);
+            v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return (uint32_t)(v >> 32) == a.tag ? __uint_as_float((uint32_t)v) : NAN;
+    };
+    constexpr int kMaxR = kHierMaxReplicas;
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kHThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        uint64_t wm[kMaxR], wl[kMaxR], wa[kMaxR];
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R && r2 != rep) {
+                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                wm[r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wl[r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wa[r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        float pm[kMaxR], pl[kMaxR], pa[kMaxR];
+        float M = -INFINITY;
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R) {
+                if (r2 == rep) {
+                    pm[r2] = oM[k];
+                    pl[r2] = oL[k];
+                    pa[r2] = oA[k];
+                } else {
+                    const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                    pm[r2] = fresh(wm[r2], pg + kHeadDim);
+                    pl[r2] = fresh(wl[r2], pg + kHeadDim + 1);
+                    pa[r2] = fresh(wa[r2], pg + dd);
+                }
+                M = fmaxf(M, pm[r2]);
+            }
+        }
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int r2 = 0; r2 < kMaxR; ++r2) {
+                if (r2 < R) {
+                    const float wt = __builtin_amdgcn_exp2f(pm[r2] - M);
+                    l = fmaf(pl[r2], wt, l);
+                    acc = fmaf(pa[r2], wt, acc);
+                }
+            }
+        }
+        outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
+    }
+}
+
+int hier_replicas(int units) {
+    constexpr int kWorkgroups = 256;
+    int r = kHierMinReplicas;
+    while (units * r < kWorkgroups && r < kHierMaxReplicas) ++r;
+    return r;
+}
+
+bool hier_path_fits(int dtype, int G, int max_coarse, int cand_budget) {
+    return dtype == 1 && (G == 1 || G == 2 || G == 4) && max_coarse >= 1 && max_coarse <= kHierMaxD &&
+           cand_budget >= 0 && cand_budget <= kHierMaxF;
+}
+
+hipError_t launch_hier_decode(int dtype, int G, const HierArgs& a, int units, int replicas, hipStream_t st) {
+    if (!hier_path_fits(dtype, G, a.D, a.cand_budget) || a.D > a.Dmax || replicas < kHierMinReplicas ||
+        replicas > kHierMaxReplicas || !a.out || !a.xpart || !a.xcount || a.tag == 0u)
+        return hipErrorInvalidValue;
+    dim3 grid(units, replicas);
+    switch (G) {
+        case 1: hipLaunchKernelGGL(hier_decode_kernel<1>, grid, dim3(kHThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(hier_decode_kernel<2>, grid, dim3(kHThreads), 0, st, a); break;
+        case 4: hipLaunchKernelGGL(hier_decode_kernel<4>, grid, dim3(kHThreads), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mpa

@@ -37,6 +37,45 @@ hipError_t launch_kmeans_csr(const int32_t* assign, UnitGeom g, BlockRange br, i
 hipError_t launch_segmented_mean(int dtype, const void* X, UnitGeom g, int c_begin, int c_count,
                                  const int32_t* sizes, const int32_t* offsets, const int32_t* token_ids,
                                  float* master, void* store, bool empty_zero, hipStream_t st);
+// ---- hierarchical decode in one launch (hier.hip) ------------------------
+constexpr int kHierMaxD = 2048;          // coarse clusters per unit
+constexpr int kHierMaxF = 4096;          // candidate fine clusters (bounded by the candidate budget)
+constexpr int kHierMinReplicas = 3;      // workgroups per unit: at least 3, so a share fits ...
+constexpr int kHierMaxReplicas = 8;
+constexpr int kHierMaxShare = (kHierMaxD + kHierMinReplicas - 1) / kHierMinReplicas +
+                              (kHierMaxF + kHierMinReplicas - 1) / kHierMinReplicas + 16;  // ... in LDS
+
+struct HierArgs {
+    const void* q;               // [B][Hq][d]
+    const void* kbar;            // fine [U][Cmax][d]
+    const void* vbar;
+    const int32_t* sizes;        // fine [U][Cmax]
+    const int32_t* offsets;      // fine [U][Cmax + 1]
+    const void* Kx;              // exact rows: sorted copy, or K, V gathered through token_ids
+    const void* Vx;
+    const int32_t* token_ids;    // null when Kx, Vx are the sorted copy
+    const void* K;               // tail rows
+    const void* V;
+    const void* ckbar;           // coarse [U][Dmax][d]
+    const void* cvbar;
+    const int32_t* csizes;       // coarse [U][Dmax]
+    const int32_t* coffsets;     // coarse [U][Dmax + 1]: start in cmembers
+    const int32_t* cmembers;     // [U][Cmax]
+    int32_t Cmax, Dmax, C, D, Nmax, n_clustered, n_total, budget, cand_budget;
+    int32_t pseudo;
+    int32_t Hq, Hkv;
+    float* out;                  // [B][Hq][d]
+    uint64_t* xpart;             // [U][R][G][d + 2] tagged partial words
+    uint64_t* xcount;            // [U] tagged arrival words
+    uint32_t tag;
+    int32_t* dbg_selected;       // optional [U][C]
+    int32_t* dbg_candidates;     // optional [U][D]
+    int32_t* dbg_exact;          // optional [U]
+};
+int hier_replicas(int units);
+bool hier_path_fits(int dtype, int G, int max_coarse, int cand_budget);
+hipError_t launch_hier_decode(int dtype, int G, const HierArgs& a, int units, int replicas, hipStream_t st);
+
 // fp8 copies of centroid rows [c_begin, c_begin + c_count) of every unit (codes.hip)
 hipError_t launch_encode_codes(UnitGeom g, int c_begin, int c_count, const void* kbar, const void* vbar,
                                uint8_t* kcodes, uint8_t* kscales, uint8_t* vcodes, uint8_t* vscales, hipStream_t st);

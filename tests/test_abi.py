@@ -214,7 +214,15 @@ def test_workspace_and_stages():
     assert M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 100, 0, 9) == ctypes.c_size_t(-1).value
     assert p.decode_stages() == ["score", "select", "attend", "merge"]
     ph = _params(coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096)
-    assert ph.decode_stages() == ["coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"]
+    # the hierarchy in one launch (bf16, automatic splits, G <= 4, up to 2048
+    # coarse clusters and 4096 candidate tokens), else six launches
+    assert ph.decode_stages() == ["hier_unit"]
+    six = ["coarse_score", "coarse_select", "fine_score", "fine_select", "attend", "merge"]
+    assert dataclasses.replace(ph, splits=4).decode_stages() == six
+    assert dataclasses.replace(ph, coarse_candidate_tokens=4097).decode_stages() == six
+    assert dataclasses.replace(ph, n_q_heads=16).decode_stages() == six                   # G = 8
+    assert dataclasses.replace(ph, capacity_tokens=1 << 18).decode_stages() == six        # 2048 + 33 coarse
+    assert dataclasses.replace(ph, dtype=torch.float32).decode_stages() == six
     # many units, automatic splits, bf16: the whole step of a unit in one workgroup
     many = M.Params(batch=16, n_q_heads=32, n_kv_heads=8, capacity_tokens=32768)
     assert many.decode_stages() == ["unit"]

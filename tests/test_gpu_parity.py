@@ -615,3 +615,64 @@ def test_fp8_codes_follow_the_window_update():
         ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], N, _coded_unit(state, b, h, p), T)
         ok, ea, er = close(out[b, h * G:(h + 1) * G], ref.out)
         assert ok, (u, ea, er)
+
+
+# ---------------------------------------------------------------------------
+# the hierarchical decode in one launch, against the six launches and the
+# oracle
+# ---------------------------------------------------------------------------
+HIER_CASES = [
+    # B, Hq, Hkv, n_clustered, n_total, block, coarse tokens per centroid, T_cand, budgets, sorted copy
+    (4, 32, 8, 16384, 16384, 4096, 128, 2048, (256, 1000), True),
+    (2, 8, 2, 12000, 13000, 4096, 64, 4096, (0, 300), False),
+    (1, 4, 4, 9000, 9000, 2048, 128, 512, (100, 2000), True),
+]
+
+
+@pytest.mark.parametrize("case", HIER_CASES, ids=lambda c: f"B{c[0]}-G{c[1] // c[2]}-N{c[4]}-cand{c[7]}")
+def test_hier_one_launch_matches_six_launches_and_oracle(case):
+    mp = M()
+    B, Hq, Hkv, n_cl, n_tot, Bc, ctpc, Tc, budgets, sorted_copy = case
+    w = small_workload(B, Hq, Hkv, n_tot, max(8, n_tot // 16), outliers=4, index=92)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=n_tot, cluster_block=Bc, build_iters=3,
+                  coarse_tokens_per_centroid=ctpc, coarse_candidate_tokens=Tc, seed=3)
+    assert p.decode_stages() == ["hier_unit"]
+    ps = dataclasses.replace(p, splits=4)
+    state = mp.ClusterState(p, DEV, sorted_copy=sorted_copy)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, n_cl, state)
+    G = p.group
+    for step, T in enumerate(budgets):
+        q = queries(w, means, 90 + step)
+        d1, d6 = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+        o1 = mp.decode(p, q.to(DEV), Kd, Vd, n_tot, state, T, debug=d1).cpu().numpy()
+        o6 = mp.decode(ps, q.to(DEV), Kd, Vd, n_tot, state, T, debug=d6).cpu().numpy()
+        # the same keys and cuts from the same operations: identical decisions
+        assert torch.equal(d1.candidates.cpu(), d6.candidates.cpu()), T
+        assert torch.equal(d1.selected.cpu(), d6.selected.cpu()), T
+        assert torch.equal(d1.exact_tokens.cpu(), d6.exact_tokens.cpu()), T
+        np.testing.assert_allclose(o1, o6, rtol=1e-4, atol=1e-5)
+        cand, sel = d1.candidates.cpu().numpy(), d1.selected.cpu().numpy()
+        for u in sorted({0, p.units // 2, p.units - 1}):
+            b, h = divmod(u, Hkv)
+            st = oracle_state_from_gpu(state, b, h, p)
+            qu = q[b, h * G:(h + 1) * G]
+            q64 = O.f64(qu)
+            ref = O.decode_unit_hier(qu, K[b, h], V[b, h], n_tot, st, T, Tc)
+            want = ref.out
+            D, C = st.n_coarse, st.n_clusters
+            if not np.array_equal(cand[b, h], ref.candidates):
+                cr = (q64 @ st.ckbar[:D].T).mean(0) / np.sqrt(128)
+                assert selection_is_valid(cr, rank_tolerance(q64, st.ckbar[:D]), st.csizes[:D], Tc, cand[b, h])
+            if not (np.array_equal(cand[b, h], ref.candidates) and np.array_equal(sel[b, h], ref.selected)):
+                forced = O.decode_unit_hier(qu, K[b, h], V[b, h], n_tot, st, T, Tc, candidates=cand[b, h])
+                inside = st.sizes[:C] * (cand[b, h][np.maximum(st.parent[:C], 0)] > 0) * (st.parent[:C] >= 0)
+                assert selection_is_valid(forced.r, rank_tolerance(q64, st.kbar[:C]), inside.astype(np.int32), T,
+                                          sel[b, h]), (u, T)
+                want = O.decode_unit_hier(qu, K[b, h], V[b, h], n_tot, st, T, Tc, candidates=cand[b, h],
+                                          selected=sel[b, h]).out
+            ok, ea, er = close(o1[b, h * G:(h + 1) * G], want)
+            assert ok, (u, T, ea, er)
+            assert st.sizes[:C][sel[b, h].astype(bool)].sum() <= T
+            assert d1.exact_tokens.cpu().numpy()[b, h] == st.sizes[:C][sel[b, h].astype(bool)].sum()
