@@ -152,11 +152,12 @@ typedef struct mpattn_decode_debug {
     int32_t* selected;      /* device [B][Hkv][n_clusters]: 1 for clusters attended exactly      */
     int32_t* candidates;    /* device [B][Hkv][n_coarse]: 1 for coarse candidates (hierarchical) */
     int32_t* exact_tokens;  /* device [B][Hkv]: tokens of the selected clusters                   */
-    int32_t rescore;        /* one-launch flat decode only; 0: normal.  1: every workgroup of a
-                               unit scores all of its clusters instead of taking the other
-                               workgroups' keys.  2: as if those keys never arrived (the path taken
-                               when a workgroup is late: one wave scores them).  The result is the
-                               same bits in all three cases. */
+    int32_t rescore;        /* one-launch decodes only (flat: all clusters; hierarchical: the
+                               coarse clusters); 0: normal.  1: every workgroup of a unit scores
+                               all of them instead of taking the other workgroups' keys.  2: as if
+                               those keys never arrived (the path taken when a workgroup is late:
+                               it scores them itself).  The result is the same bits in all three
+                               cases. */
 } mpattn_decode_debug;
 
 /* Human-readable text of a status code (static storage). */
@@ -263,12 +264,15 @@ mpattn_status mpattn_dense_decode(const mpattn_params* params, const void* q, co
                                   void* stream);
 
 /* Number of kernel stages one decode enqueues (for timing stage by stage):
- * 6 for the hierarchical method (coarse_score, coarse_select, fine_score,
- * fine_select, attend, merge); for the flat method 1 (unit) when the whole
- * step of a unit runs in one launch -- bf16 storage, splits = 0, at least 16
- * units and at most 4096 clusters per unit -- else 4 (score, select, attend,
- * merge).  Both forms compute the same cut and, up to fp32 summation order,
- * the same output. */
+ * for the hierarchical method 1 (hier_unit) when the whole step of a unit
+ * runs in one launch -- bf16 storage, splits = 0, groups of 1, 2 or 4 query
+ * heads, mpattn_max_coarse <= 2048 and coarse_candidate_tokens <= 4096 --
+ * else 6 (coarse_score, coarse_select, fine_score, fine_select, attend,
+ * merge); for the flat method 1 (unit) when the whole step of a unit runs in
+ * one launch -- bf16 storage, splits = 0, at least 16 units and at most 4096
+ * clusters per unit -- else 4 (score, select, attend, merge).  The forms of a
+ * method compute the same cuts and, up to fp32 summation order, the same
+ * output. */
 int32_t mpattn_decode_stage_count(const mpattn_params* params);
 
 /* Name of decode stage i (static storage), NULL if out of range. */

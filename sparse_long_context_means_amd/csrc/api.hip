@@ -91,7 +91,8 @@ struct DecodeWs {
     uint64_t* xpart;      // [U][Rx][G][d + 2] partials
     uint64_t* xcount;     // [U] arrival words
     int32_t Rx;           // most replicas a decode on this layout uses
-    uint64_t* hpart;      // hierarchy in one launch: [U][Rh][G][d + 2] partial words
+    uint64_t* hch;        // hierarchy in one launch: [U][Rh][Dmax] coarse-key words
+    uint64_t* hpart;      // [U][Rh][G][d + 2] partial words
     uint64_t* hcount;     // [U] arrival words
     int32_t Rh;
     int32_t Rxh;          // the same when each query head is its own unit
@@ -146,6 +147,7 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
     }
     if (hier_unit_path(p)) {
         w.Rh = hier_replicas((int)U);
+        w.hch = (uint64_t*)take(U * w.Rh * (size_t)Dmax * 8);
         w.hpart = (uint64_t*)take(U * w.Rh * G * (kD + 2) * 8);
         w.hcount = (uint64_t*)take(U * 8);
     }
@@ -463,12 +465,14 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         a.Hq = p->n_q_heads;
         a.Hkv = p->n_kv_heads;
         a.out = out;
+        a.xch = w.hch;
         a.xpart = w.hpart;
         a.xcount = w.hcount;
         a.tag = next_tag();
         a.dbg_selected = debug ? debug->selected : nullptr;
         a.dbg_candidates = debug ? debug->candidates : nullptr;
         a.dbg_exact = debug ? debug->exact_tokens : nullptr;
+        a.rescore = debug ? debug->rescore : 0;
         MPA_TRY(launch_hier_decode(p->dtype, G, a, U, R, s));
         return MPATTN_OK;
     }

@@ -36,6 +36,10 @@ constexpr int kHWaves = kHThreads / kWave;  // 8
 constexpr int kHRowBatch = 1024;            // staged exact rows per pass
 constexpr int kHScoreDepth = 4;             // score steps in flight per wave
 constexpr int kHExactDepth = 2;             // exact-row steps (16 rows) in flight per wave
+// Waits on the other workgroups of a unit, in ticks of the 100 MHz constant
+// clock: for their coarse keys (then the workgroup scores them itself) and
+// for the partial words of workgroups that have already counted in.
+constexpr uint64_t kHExchangeWaitTicks = 2000;
 constexpr uint64_t kHPartialWaitTicks = 100000;
 
 // Workgroup barrier ordering LDS only (global loads and stores in flight are
@@ -229,21 +233,28 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     load_qop<G>(qop, qg, lane);
     float lgmax = -INFINITY;  // the lane's maximum share logit (head li)
 
-    // Scores of items [0, n): row(i) is the centroid row of item i; the
+    // Scores of items [lo, hi): row(i) is the centroid row of item i; the
     // ranking key of item i goes to keys[i] (if keys), the base-2 logit
     // s log2(e) + log2(size) of items of [s0, s1) to s_lg[i - s0 + lg0].
-    // Lane l loads row l % 16 of its wave's 16; the waves interleave.
-    auto score_items = [&](int n, auto row_of, auto size_of, float* keys, int s0, int s1, int lg0) {
-        if (n == 0) return;  // (uniform) row 0 exists only for n >= 1
-        const int steps = (n + 16 * kHWaves - 1) / (16 * kHWaves);
-        auto base = [&](int step) { return step * 16 * kHWaves + wave * 16; };
+    // Lane l loads row l % 16 of its wave's 16; the waves interleave.  pre()
+    // runs once the first rows are in flight (it may end with a barrier).
+    // The same item gets the same bits whichever pass scores it.
+    auto score_items = [&](int lo, int hi, auto row_of, auto size_of, float* keys, int s0, int s1, int lg0,
+                           auto pre) {
+        if (hi <= lo) {  // (uniform) row lo exists only for hi > lo
+            pre();
+            return;
+        }
+        const int steps = (hi - lo + 16 * kHWaves - 1) / (16 * kHWaves);
+        auto base = [&](int step) { return lo + step * 16 * kHWaves + wave * 16; };
         Slice8<bf16_t> ring[kHScoreDepth][4];
 #pragma unroll
         for (int j = 0; j < kHScoreDepth; ++j) {
             const int i = base(j) + li;
-            load_row_blocks(ring[j], row_of(i < n ? i : 0), lane);
+            load_row_blocks(ring[j], row_of(i < hi ? i : lo), lane);
             __builtin_amdgcn_sched_barrier(0);
         }
+        pre();
         for (int it = 0; it < steps; it += kHScoreDepth) {
 #pragma unroll
             for (int j = 0; j < kHScoreDepth; ++j) {
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                     const float sv = d[e] * kInvSqrtD;
                     const float key = head_mean<G>(sv);
                     const int i = cb + e;
-                    if (i < n) {
+                    if (i < hi) {
                         if (li == 0 && keys) keys[i] = key;
                         if (li < G && i >= s0 && i < s1) {
                             const int sz = size_of(i);
@@ -265,24 +276,82 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                     }
                 }
                 const int i = base(it + j + kHScoreDepth) + li;
-                load_row_blocks(ring[j], row_of(i < n ? i : 0), lane);
+                load_row_blocks(ring[j], row_of(i < hi ? i : lo), lane);
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
     };
 
-    // ---- 1. coarse scores (all of them; the share's logits kept) ---------
-    for (int i = tid; i < D; i += kHThreads) s_csz[i] = csizes[i];
-    for (int i = tid; i < kHierMaxD / 32; i += kHThreads) s_cmask[i] = 0u;
-    for (int i = tid; i < kHierMaxF / 32; i += kHThreads) s_fmask[i] = 0u;
-    hlds_barrier();
+    // ---- 1. coarse scores.  With several workgroups each scores its share
+    //      [cs0, cs1) and takes the others' keys as 64-bit words (call tag
+    //      << 32 | key bits) that every workgroup stores into each other's
+    //      slot; a word counts once it carries this call's tag, so no fence
+    //      orders the words and words of earlier calls need no clearing.  If
+    //      a word is still missing after kHExchangeWaitTicks (a partner not
+    //      yet running), the workgroup scores every coarse cluster itself,
+    //      which gives the same keys.  The coarse sizes go out ahead of the
+    //      rows, as unconditional loads (clamped index), and reach LDS while
+    //      the first rows are in flight.
+    constexpr int kCItems = kHierMaxD / kHThreads;
+    int csz_r[kCItems];
+#pragma unroll
+    for (int j = 0; j < kCItems; ++j) csz_r[j] = csizes[min(tid + j * kHThreads, D - 1)];
     const int cs0 = (int)((int64_t)D * rep / R), cs1 = (int)((int64_t)D * (rep + 1) / R);
-    score_items(
-        D, [&](int i) { return ck + (size_t)i * kHeadDim; }, [&](int i) { return s_csz[i]; }, s_ckey, cs0, cs1, 0);
+    const bool xchg = R > 1 && a.rescore != 1;
+    auto crow = [&](int i) { return ck + (size_t)i * kHeadDim; };
+    auto csize = [&](int i) { return s_csz[i]; };
+    score_items(xchg ? cs0 : 0, xchg ? cs1 : D, crow, csize, s_ckey, cs0, cs1, 0, [&]() {
+#pragma unroll
+        for (int j = 0; j < kCItems; ++j)
+            if (tid + j * kHThreads < D) s_csz[tid + j * kHThreads] = csz_r[j];
+        for (int i = tid; i < kHierMaxD / 32; i += kHThreads) s_cmask[i] = 0u;
+        for (int i = tid; i < kHierMaxF / 32; i += kHThreads) s_fmask[i] = 0u;
+        if (tid == 0) s_misc[1] = 0;
+        hlds_barrier();
+    });
     hlds_barrier();
+    if (xchg) {
+        const uint64_t tagw = (uint64_t)a.tag << 32;
+        uint64_t* xu = a.xch + (size_t)unit * R * a.Dmax;
+        for (int i = cs0 + tid; i < cs1; i += kHThreads) {
+            const uint64_t w = tagw | __float_as_uint(s_ckey[i]);
+            for (int r2 = 0; r2 < R; ++r2)
+                if (r2 != rep)
+                    __hip_atomic_store(xu + (size_t)r2 * a.Dmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        bool miss = a.rescore == 2;  // 2: as if the other keys never came
+        if (!miss) {
+            const uint64_t* slot = xu + (size_t)rep * a.Dmax;
+            uint64_t w[kCItems];
+#pragma unroll
+            for (int q = 0; q < kCItems; ++q)  // unconditional (clamped): exact wait counts
+                w[q] = __hip_atomic_load(slot + min(tid + q * kHThreads, D - 1), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t t0 = wall_clock64();
+#pragma unroll
+            for (int q = 0; q < kCItems; ++q) {
+                const int i = tid + q * kHThreads;
+                const bool need = i < D && (i < cs0 || i >= cs1);
+                while (need && !miss && (uint32_t)(w[q] >> 32) != a.tag) {
+                    if (wall_clock64() - t0 > kHExchangeWaitTicks) {
+                        miss = true;
+                    } else {
+                        __builtin_amdgcn_s_sleep(2);
+                        w[q] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                if (need && (uint32_t)(w[q] >> 32) == a.tag) s_ckey[i] = __uint_as_float((uint32_t)w[q]);
+            }
+        }
+        if (miss) s_misc[1] = 1;
+        hlds_barrier();
+        if (s_misc[1]) {  // (uniform) score them here: keys only
+            score_items(0, D, crow, csize, s_ckey, 0, 0, 0, []() {});
+            hlds_barrier();
+        }
+    }
 
     // ---- 2. coarse cut under the candidate budget -----------------------
-    constexpr int kCItems = kHierMaxD / kHThreads;
     const uint32_t cbits = block_cut<kCItems>(
         [&](int i) { return s_ckey[i]; }, [&](int i) { return s_csz[i]; }, [&](int i) { return i; }, D,
         a.cand_budget, hist, s_scan);
@@ -341,8 +410,8 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     const int dsh = cs1 - cs0;  // coarse share logits at s_lg[0 .. dsh)
     const int fs0 = (int)((int64_t)F * rep / R), fs1 = (int)((int64_t)F * (rep + 1) / R);
     score_items(
-        F, [&](int i) { return fk + (size_t)s_fid[i] * kHeadDim; }, [&](int i) { return s_fsz[i]; }, s_fkey, fs0, fs1,
-        dsh);
+        0, F, [&](int i) { return fk + (size_t)s_fid[i] * kHeadDim; }, [&](int i) { return s_fsz[i]; }, s_fkey, fs0,
+        fs1, dsh, []() {});
     lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 16));
     lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 32));
     if (lane < G) s_gmax[wave][lane] = lgmax;
@@ -687,7 +756,7 @@ bool hier_path_fits(int dtype, int G, int max_coarse, int cand_budget) {
 
 hipError_t launch_hier_decode(int dtype, int G, const HierArgs& a, int units, int replicas, hipStream_t st) {
     if (!hier_path_fits(dtype, G, a.D, a.cand_budget) || a.D > a.Dmax || replicas < kHierMinReplicas ||
-        replicas > kHierMaxReplicas || !a.out || !a.xpart || !a.xcount || a.tag == 0u)
+        replicas > kHierMaxReplicas || !a.out || !a.xch || !a.xpart || !a.xcount || a.tag == 0u)
         return hipErrorInvalidValue;
     dim3 grid(units, replicas);
     switch (G) {

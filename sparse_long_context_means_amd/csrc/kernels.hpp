@@ -65,12 +65,14 @@ struct HierArgs {
     int32_t pseudo;
     int32_t Hq, Hkv;
     float* out;                  // [B][Hq][d]
+    uint64_t* xch;               // [U][R][Dmax] tagged coarse-key words, slot r read by workgroup r
     uint64_t* xpart;             // [U][R][G][d + 2] tagged partial words
     uint64_t* xcount;            // [U] tagged arrival words
     uint32_t tag;
     int32_t* dbg_selected;       // optional [U][C]
     int32_t* dbg_candidates;     // optional [U][D]
     int32_t* dbg_exact;          // optional [U]
+    int32_t rescore;             // 0; 1: every workgroup scores all coarse clusters; 2: as if no key came
 };
 int hier_replicas(int units);
 bool hier_path_fits(int dtype, int G, int max_coarse, int cand_budget);

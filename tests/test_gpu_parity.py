@@ -676,3 +676,32 @@ def test_hier_one_launch_matches_six_launches_and_oracle(case):
             assert ok, (u, T, ea, er)
             assert st.sizes[:C][sel[b, h].astype(bool)].sum() <= T
             assert d1.exact_tokens.cpu().numpy()[b, h] == st.sizes[:C][sel[b, h].astype(bool)].sum()
+
+
+def test_hier_one_launch_rescore_gives_the_same_result():
+    """The workgroups of a unit score a share of the coarse clusters each and
+    exchange the keys; scoring all of them locally (rescore 1) or falling back
+    as when a partner is late (rescore 2) must give the same bits."""
+    mp = M()
+    B, Hq, Hkv, N = 4, 32, 8, 16384
+    w = small_workload(B, Hq, Hkv, N, N // 16, outliers=4, index=93)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, cluster_block=4096, build_iters=3,
+                  coarse_tokens_per_centroid=128, coarse_candidate_tokens=2048, seed=4)
+    assert p.decode_stages() == ["hier_unit"]
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, N, state)
+    for step, T in enumerate((128, 900)):
+        q = queries(w, means, 100 + step).to(DEV)
+        outs, dbgs = [], []
+        for rescore in (0, 1, 2, 0):
+            d = mp.DecodeDebug.allocate(p, state, DEV)
+            d.rescore = rescore
+            outs.append(mp.decode(p, q, Kd, Vd, N, state, T, debug=d).cpu())
+            dbgs.append(d)
+        for o, d in zip(outs[1:], dbgs[1:]):
+            assert torch.equal(o, outs[0]), T
+            assert torch.equal(d.candidates.cpu(), dbgs[0].candidates.cpu())
+            assert torch.equal(d.selected.cpu(), dbgs[0].selected.cpu())
+            assert torch.equal(d.exact_tokens.cpu(), dbgs[0].exact_tokens.cpu())
