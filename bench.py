@@ -42,17 +42,24 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
 UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
     "stored": {
-        "sources_sha256": "f21b3dd9775d50822813b8bf560aeff4329518183a2bc45cd7e8c2bbd4c2388b",
-        "fetch_bytes": int(122667.73 * 2.0 * 1024),
-        "write_bytes": int(5003.92 * 1.0 * 1024),
+        "sources_sha256": "362de5b1506d1a997feebd94a7e85954e59672ce64d287ace309153c15f4b25d",
+        "fetch_bytes": int(122695.08 * 2.0 * 1024),
+        "write_bytes": int(5004.18 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "f21b3dd9775d50822813b8bf560aeff4329518183a2bc45cd7e8c2bbd4c2388b",
-        "fetch_bytes": int(89949.05 * 2.0 * 1024),
-        "write_bytes": int(5004.12 * 1.0 * 1024),
+        "sources_sha256": "362de5b1506d1a997feebd94a7e85954e59672ce64d287ace309153c15f4b25d",
+        "fetch_bytes": int(89964.04 * 2.0 * 1024),
+        "write_bytes": int(5004.11 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
+}
+HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
+    "sources_sha256": "66fdc93e2a751189237a9b850e01740a03d6881153169f3da73784be1621275d",
+    "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
+    "fetch_bytes": int(18120.66 * 2.0 * 1024),
+    "write_bytes": int(3484.05 * 1.0 * 1024),
+    "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
@@ -236,8 +243,8 @@ def main():
     byts = np.array([sum(bytes_of(s)) for s in steps_idx], dtype=np.float64)
     # dominant kernel: the per-unit kernel (the whole step) or the split
     # attend kernel
-    if "unit" in stage_names:
-        dom = "unit"
+    if len(stage_names) == 1:  # one launch: the whole step
+        dom = stage_names[0]
         att_bytes = byts.copy()
     else:
         dom = "attend"
@@ -499,22 +506,22 @@ def measure_rows(M, workloads, dev, evict):
     main, side = torch.cuda.current_stream(dev), torch.cuda.Stream(dev)
     n_total = w.n_tokens + w.cluster_block  # the new block is the tail until clustered
     dq = qs[:8] * 4
+    dout = torch.empty(p.batch, p.n_q_heads, d, dtype=torch.float32, device=dev)
+    dev_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in dq]
 
-    def decodes(view):
-        evs = []
-        for q in dq:
-            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def decodes(view):  # nothing allocated inside: the loop only enqueues
+        for q, (e_a, e_b) in zip(dq, dev_evs):
             e_a.record(main)
-            M.decode(p, q, Kd, Vd, n_total, view, T, workspace=ws)
+            M.decode(p, q, Kd, Vd, n_total, view, T, out=dout, workspace=ws)
             e_b.record(main)
-            evs.append((e_a, e_b))
-        return evs
+        return dev_evs
 
     alone_st = M.ClusterState(p, dev)
     M.build_clusters(p, Kd, Vd, w.n_tokens, alone_st)
     evs = decodes(alone_st)
     torch.cuda.synchronize()
     dec_alone = float(np.median([x.elapsed_time(y) * 1e3 for x, y in evs]))
+    torch.cuda.empty_cache()
     conc_st = M.ClusterState(p, dev)
     M.build_clusters(p, Kd, Vd, w.n_tokens, conc_st)
     torch.cuda.synchronize()
@@ -578,28 +585,33 @@ def measure_rows(M, workloads, dev, evict):
         "workload": w.name, "token_budget": T, "coarse_candidate_tokens": w.coarse_candidate_tokens,
         "build_ms": round(build_ms, 2), "us_per_step": round(us, 2), "algorithmic_MB": round(byts / 1e6, 2),
         "roofline": {"bound": "hbm", "achieved": round(byts / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+                     "unit": "GB/s", "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": _counter_traffic(HIER_TRAFFIC) if p.decode_stages() == ["hier_unit"] else None}}
     log(f"[bench] H8 build {build_ms:.1f} ms, hierarchical decode {us:.1f} us ({byts / 1e6:.1f} MB)")
     del K, V, Kd, Vd, st, ws
     torch.cuda.empty_cache()
     return rows
 
 
-def _unit_traffic_bytes(fmt):
-    """Counter-derived HBM bytes per launch of the per-unit kernel, or None
-    when its sources differ from the ones the counters were taken on."""
-    t = UNIT_TRAFFIC.get(fmt)
-    if t is None:
-        return None
+def _counter_traffic(t, files=("unit.hip", "attn.hpp", "device.hpp", "kernels.hpp")):
+    """Counter-derived HBM bytes per launch recorded in t, or None when the
+    kernel sources differ from the ones the counters were taken on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_long_context_means_amd", "csrc")
-    for fn in ("unit.hip", "attn.hpp", "device.hpp", "kernels.hpp"):
+    for fn in t.get("files", files):
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(f.read())
     if h.hexdigest() != t["sources_sha256"]:
         return None
     return t["fetch_bytes"] + t["write_bytes"]
+
+
+def _unit_traffic_bytes(fmt):
+    """Counter-derived HBM bytes per launch of the per-unit kernel for a
+    centroid format, or None (no record, or the sources changed)."""
+    t = UNIT_TRAFFIC.get(fmt)
+    return None if t is None else _counter_traffic(t)
 
 
 def _cpu_model():
