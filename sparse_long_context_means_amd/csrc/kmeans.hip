@@ -410,6 +410,9 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
     __shared__ int32_t loc[kCoarseMaxFine];       // coarse assignment of each point
     __shared__ uint16_t perm[kCoarseMaxFine];
     __shared__ uint16_t pick[kCoarseMaxD];
+    __shared__ uint16_t order[kCoarseMaxFine];    // points by (coarse cluster, point index)
+    __shared__ int32_t bstart[kCoarseMaxD + 1];   // start of each coarse cluster in order
+    __shared__ float wt[kCoarseMaxFine];          // size of each point (its weight)
     __shared__ int scan_lds[16];
     __shared__ int s_m;
     const int j = blockIdx.x, unit = blockIdx.y;
@@ -460,7 +463,10 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
     for (int gg = D + threadIdx.x; gg < Dfull; gg += 256) csizes[(size_t)unit * cr.Dmax + g0 + gg] = 0;
 
     // seeded init among the m points
-    for (int i = threadIdx.x; i < m; i += 256) perm[i] = (uint16_t)i;
+    for (int i = threadIdx.x; i < m; i += 256) {
+        perm[i] = (uint16_t)i;
+        wt[i] = (float)su[ids[i]];
+    }
     const uint64_t s0 =
         seed ^ sm64_mix(((uint64_t)unit << 32) + (uint64_t)(cr.fine.j_base + j) + (1ull << 62));
     for (int t = threadIdx.x; t < D; t += 256) {
@@ -486,6 +492,41 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
     }
     __syncthreads();
 
+    // points of each coarse cluster in increasing point index (a stable
+    // counting sort of loc), so the weighted means below visit exactly the
+    // members, in point order
+    auto bucket = [&]() {
+        if (threadIdx.x < D) {
+            int n = 0;
+            for (int i = 0; i < m; ++i) n += loc[i] == threadIdx.x;
+            bstart[threadIdx.x + 1] = n;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            bstart[0] = 0;
+            for (int gg = 0; gg < D; ++gg) bstart[gg + 1] += bstart[gg];
+        }
+        __syncthreads();
+        if (threadIdx.x < D) {
+            int k = bstart[threadIdx.x];
+            for (int i = 0; i < m; ++i)
+                if (loc[i] == threadIdx.x) order[k++] = (uint16_t)i;
+        }
+        __syncthreads();
+    };
+    // weighted mean of column cc of coarse cluster gg over its members (point
+    // order); den = 0 for an empty cluster
+    auto wmean = [&](const T* src, int gg, int cc, float& num, float& den) {
+        num = 0.f;
+        den = 0.f;
+        for (int k = bstart[gg]; k < bstart[gg + 1]; ++k) {
+            const int i = order[k];
+            const float w = wt[i];
+            num = fmaf(w, (float)src[(size_t)ids[i] * kHeadDim + cc], num);
+            den += w;
+        }
+    };
+
     for (int it = 0; it < iters; ++it) {
         if (threadIdx.x < D) {
             float ss = 0.f;
@@ -493,14 +534,20 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
             hn[threadIdx.x] = 0.5f * ss;
         }
         __syncthreads();
-        // assign each point to the best stored centroid (lowest id on ties)
+        // assign each point to the best stored centroid (lowest id on ties);
+        // the point's row is held in registers, the centroids are LDS
+        // broadcasts
         for (int i = threadIdx.x; i < m; i += 256) {
             const T* x = kb_u + (size_t)ids[i] * kHeadDim;
+            float xr[kHeadDim];
+#pragma unroll
+            for (int e = 0; e < kHeadDim; ++e) xr[e] = (float)x[e];
             float best = -INFINITY;
             int bi = 0;
             for (int gg = 0; gg < D; ++gg) {
                 float v = -hn[gg];
-                for (int e = 0; e < kHeadDim; ++e) v = fmaf((float)x[e], cen[gg][e], v);
+#pragma unroll
+                for (int e = 0; e < kHeadDim; ++e) v = fmaf(xr[e], cen[gg][e], v);
                 if (v > best) {
                     best = v;
                     bi = gg;
@@ -509,16 +556,12 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
             loc[i] = bi;
         }
         __syncthreads();
+        bucket();
         // weighted means in point order; empty clusters keep their centroid
         for (int e = threadIdx.x; e < D * kHeadDim; e += 256) {
             const int gg = e / kHeadDim, cc = e % kHeadDim;
-            float num = 0.f, den = 0.f;
-            for (int i = 0; i < m; ++i) {
-                if (loc[i] != gg) continue;
-                const float w = (float)su[ids[i]];
-                num = fmaf(w, (float)kb_u[(size_t)ids[i] * kHeadDim + cc], num);
-                den += w;
-            }
+            float num, den;
+            wmean(kb_u, gg, cc, num, den);
             if (den > 0.f) {
                 const float mean = num / den;
                 cmu_u[(size_t)(g0 + gg) * kHeadDim + cc] = mean;
@@ -531,13 +574,8 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
     for (int e = threadIdx.x; e < D * kHeadDim; e += 256) {
         const int gg = e / kHeadDim, cc = e % kHeadDim;
         ck_u[(size_t)(g0 + gg) * kHeadDim + cc] = (T)cen[gg][cc];
-        float num = 0.f, den = 0.f;
-        for (int i = 0; i < m; ++i) {
-            if (loc[i] != gg) continue;
-            const float w = (float)su[ids[i]];
-            num = fmaf(w, (float)vb_u[(size_t)ids[i] * kHeadDim + cc], num);
-            den += w;
-        }
+        float num, den;
+        wmean(vb_u, gg, cc, num, den);
         cv_u[(size_t)(g0 + gg) * kHeadDim + cc] = den > 0.f ? (T)(num / den) : (T)0;
     }
     // parents (-1 for empty fine clusters)
@@ -548,21 +586,15 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
     // member lists by (coarse, fine), one thread for the block
     int32_t* ou = coffsets + (size_t)unit * (cr.Dmax + 1);
     int32_t* mu_ = cmembers + (size_t)unit * g.Cmax;
-    if (threadIdx.x == 0) {
-        int pos = before;
-        for (int gg = 0; gg < Dfull; ++gg) {
-            ou[g0 + gg] = pos;
-            int tot = 0;
-            if (gg < D) {
-                for (int i = 0; i < m; ++i) {
-                    if (loc[i] != gg) continue;
-                    mu_[pos++] = ids[i];
-                    tot += su[ids[i]];
-                }
-            }
-            if (gg < D) csizes[(size_t)unit * cr.Dmax + g0 + gg] = tot;
+    for (int gg = threadIdx.x; gg <= Dfull; gg += 256) ou[g0 + gg] = before + (gg < D ? bstart[gg] : m);
+    for (int gg = threadIdx.x; gg < D; gg += 256) {
+        int tot = 0;
+        for (int k = bstart[gg]; k < bstart[gg + 1]; ++k) {
+            const int i = order[k];
+            mu_[before + k] = ids[i];
+            tot += su[ids[i]];
         }
-        ou[g0 + Dfull] = pos;
+        csizes[(size_t)unit * cr.Dmax + g0 + gg] = tot;
     }
 }
 
