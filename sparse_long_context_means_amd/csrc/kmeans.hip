@@ -88,8 +88,11 @@ constexpr int kAsgPad = 17;    // uint4 per staged row (16 + 1 to spread LDS ban
 __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* __restrict__ K, UnitGeom g,
                                                                  BlockRange br, const bf16_t* __restrict__ kbar,
                                                                  int32_t* __restrict__ assign, int tiles) {
-    __shared__ uint4 cs[kAsgChunk * kAsgPad];
-    __shared__ __align__(16) float hn[kAsgChunk];
+    // two LDS buffers of staged centroids: chunk ch + 1 is loaded into
+    // registers while chunk ch is on the matrix cores, then written to the
+    // other buffer (one barrier per chunk)
+    __shared__ uint4 cs[2][kAsgChunk * kAsgPad];
+    __shared__ __align__(16) float hn[2][kAsgChunk];
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int group = lid / tiles, tile = lid % tiles;
     if (group >= g.units * br.nb) return;
@@ -114,30 +117,48 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
     int bidx[2] = {0x7fffffff, 0x7fffffff};
     const bf16_t* Cu = kbar + ((size_t)unit * g.Cmax + c0) * kHeadDim;
 
-    for (int ch = 0; ch < C; ch += kAsgChunk) {
+    // thread t stages parts t + 256 m (m < 4) of a chunk: row (t + 256 m) / 16
+    auto fetch = [&](int ch, uint4 (&v)[4]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = threadIdx.x + m * 256;
+            const int c = ch + (e >> 4);
+            v[m] = c < C ? reinterpret_cast<const uint4*>(Cu + (size_t)c * kHeadDim)[e & 15] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto stage = [&](int ch, const uint4 (&v)[4], int buf) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int e = threadIdx.x + m * 256;
             const int row = e >> 4, part = e & 15;
             const int c = ch + row;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < C) v = reinterpret_cast<const uint4*>(Cu + (size_t)c * kHeadDim)[part];
-            cs[row * kAsgPad + part] = v;
-            const float x0 = bf16_lo(v.x), x1 = bf16_hi(v.x), x2 = bf16_lo(v.y), x3 = bf16_hi(v.y);
-            const float x4 = bf16_lo(v.z), x5 = bf16_hi(v.z), x6 = bf16_lo(v.w), x7 = bf16_hi(v.w);
+            cs[buf][row * kAsgPad + part] = v[m];
+            const float x0 = bf16_lo(v[m].x), x1 = bf16_hi(v[m].x), x2 = bf16_lo(v[m].y), x3 = bf16_hi(v[m].y);
+            const float x4 = bf16_lo(v[m].z), x5 = bf16_hi(v[m].z), x6 = bf16_lo(v[m].w), x7 = bf16_hi(v[m].w);
             float ss = x0 * x0;
             ss = fmaf(x1, x1, ss); ss = fmaf(x2, x2, ss); ss = fmaf(x3, x3, ss);
             ss = fmaf(x4, x4, ss); ss = fmaf(x5, x5, ss); ss = fmaf(x6, x6, ss); ss = fmaf(x7, x7, ss);
             ss = row16_sum(ss);  // the 16 lanes of a row hold its 16 parts
-            if (part == 0) hn[row] = c < C ? 0.5f * ss : INFINITY;
+            if (part == 0) hn[buf][row] = c < C ? 0.5f * ss : INFINITY;
         }
-        __syncthreads();
+    };
+    {
+        uint4 v[4];
+        fetch(0, v);
+        stage(0, v, 0);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int ch = 0; ch < C; ch += kAsgChunk) {
+        const bool more = ch + kAsgChunk < C;  // (uniform)
+        uint4 nv[4];
+        if (more) fetch(ch + kAsgChunk, nv);
         f32x16_t acc[2][2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 h = *reinterpret_cast<const float4*>(&hn[cb * 32 + 8 * q4 + 4 * half]);
+                const float4 h = *reinterpret_cast<const float4*>(&hn[buf][cb * 32 + 8 * q4 + 4 * half]);
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
                     acc[cb][tb][4 * q4 + 0] = -h.x;
@@ -151,7 +172,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const uint4 a = cs[(cb * 32 + col) * kAsgPad + 2 * s + half];
+                const uint4 a = cs[buf][(cb * 32 + col) * kAsgPad + 2 * s + half];
                 const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
@@ -174,7 +195,9 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
                         bidx[tb] = c;
                     }
                 }
+        if (more) stage(ch + kAsgChunk, nv, buf ^ 1);  // the other buffer: read by no wave now
         __syncthreads();
+        buf ^= 1;
     }
     int32_t* au = assign + (size_t)unit * g.Nmax + p;
 #pragma unroll
