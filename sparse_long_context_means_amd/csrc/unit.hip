@@ -422,7 +422,9 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             v.load(vb + (size_t)c * kHeadDim);
     };
     constexpr int kCutWaves = 4, kStreamWaves = kUnitWaves - kCutWaves;
-    constexpr int kSteps = (kUnitShare + 16 * kStreamWaves - 1) / (16 * kStreamWaves);
+    constexpr int kSteps = kUnitShare / (16 * kStreamWaves);
+    // every step of the stream lies inside the share
+    static_assert(kUnitShare % (16 * kStreamWaves) == 0 && kSteps % kPseudoDepth == 0, "stream steps");
     const int sw = wave - kCutWaves;  // stream wave index (waves 4-7)
     auto item = [&](int step, int u) { return step * 16 * kStreamWaves + sw * 16 + u * 4 + rg; };
     struct VRows4 {
@@ -548,21 +550,31 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 }
                 k_hi = lo;
             }
-            const int rgi = wave * 4 + rg;  // 16 row groups, one row each per pass
-            for (int k0 = k_lo; k0 < k_hi; k0 += 4 * kCutWaves) {
-                const int k = k0 + rgi;
-                const bool ok = k < k_hi;
-                const int c = ok ? s_sid[k] : cs;
-                VRow v;
-                vload(v, c);
-                float x[8];
-                v.unpack(x);
+            // 16 row groups take kRemoveBatch rows each per pass, the loads
+            // of a pass in flight together (one memory latency per pass)
+            constexpr int kRemoveBatch = 4;
+            const int rgi = wave * 4 + rg;
+            for (int k0 = k_lo; k0 < k_hi; k0 += 16 * kRemoveBatch) {
+                VRow v[kRemoveBatch];
+                int c[kRemoveBatch];
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float p = ok ? s_lg[c - cs][g] : 0.f;  // every state's reference is still Mref
-                    st.l[g] -= p;
+                for (int j = 0; j < kRemoveBatch; ++j) {
+                    const int k = k0 + 16 * j + rgi;
+                    c[j] = k < k_hi ? s_sid[k] : -1;
+                    vload(v[j], c[j] >= 0 ? c[j] : cs);
+                }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(-p, x[e], st.acc[g][e]);
+                for (int j = 0; j < kRemoveBatch; ++j) {
+                    float x[8];
+                    v[j].unpack(x);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        // every state's reference is still Mref
+                        const float p = c[j] >= 0 ? s_lg[c[j] - cs][g] : 0.f;
+                        st.l[g] -= p;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(-p, x[e], st.acc[g][e]);
+                    }
                 }
             }
         }
@@ -578,14 +590,28 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // the weights, once per cluster and head, replace the logits in LDS (0
-        // for clusters outside the share or empty), while the first rows fly
+        // for clusters outside the share or empty), while the first rows fly;
+        // their sum per head goes to the weight sum of lane 0 (the lane whose
+        // sum the combine keeps), so the stream below only accumulates values
+        float wsum[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) wsum[g] = 0.f;
         for (int t = tid - kCutWaves * kWave; t < kUnitShare; t += kStreamWaves * kWave) {
             const int c = cs + t;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float lgv = c < ce ? s_lg[t][g] : -INFINITY;
-                s_lg[t][g] = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - Mref[g]);
+                const float w = lgv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lgv - Mref[g]);
+                s_lg[t][g] = w;
+                wsum[g] += w;
             }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float v = row16_sum(wsum[g]);
+            v += shfl_xor_f(v, 16);
+            v += shfl_xor_f(v, 32);
+            if (lane == 0) st.l[g] += v;
         }
         int sgen = 0;
         group_barrier<kStreamWaves>(sctr, sgen);
@@ -596,13 +622,11 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int r = item(it + j, u);
-                    const int rr = r < kUnitShare ? r : kUnitShare - 1;  // past the share: weight 0
                     float x[8];
                     pring[j].r[u].unpack(x);
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        const float w = r < kUnitShare ? s_lg[rr][g] : 0.f;
-                        st.l[g] += w;
+                        const float w = s_lg[r][g];  // 0 past the share's clusters
 #pragma unroll
                         for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
                     }
