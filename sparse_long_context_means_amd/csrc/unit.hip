@@ -433,6 +433,15 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     VRows4 pring[kPseudoDepth];
     SoftState<G> st;
     st.init();
+    // the first batch of the removal (below): rows in flight through the exact
+    // rows, weights relative to Mref (0: no row), applied after them
+    constexpr int kRemoveBatch = 4;
+    VRow rem_v[kRemoveBatch];
+    float rem_p[kRemoveBatch][G];
+#pragma unroll
+    for (int j = 0; j < kRemoveBatch; ++j)
+#pragma unroll
+        for (int g = 0; g < G; ++g) rem_p[j][g] = 0.f;
     float Mref[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -551,10 +560,20 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 k_hi = lo;
             }
             // 16 row groups take kRemoveBatch rows each per pass, the loads
-            // of a pass in flight together (one memory latency per pass)
-            constexpr int kRemoveBatch = 4;
+            // of a pass in flight together.  The first pass is only issued
+            // here: its rows are taken out after the exact rows, so their
+            // latency hides behind them; further passes (more than 64
+            // selected clusters in the share) run now.
             const int rgi = wave * 4 + rg;
-            for (int k0 = k_lo; k0 < k_hi; k0 += 16 * kRemoveBatch) {
+#pragma unroll
+            for (int j = 0; j < kRemoveBatch; ++j) {
+                const int k = k_lo + 16 * j + rgi;
+                const int c = k < k_hi ? s_sid[k] : -1;
+                vload(rem_v[j], c >= 0 ? c : cs);
+#pragma unroll
+                for (int g = 0; g < G; ++g) rem_p[j][g] = c >= 0 ? s_lg[c - cs][g] : 0.f;
+            }
+            for (int k0 = k_lo + 16 * kRemoveBatch; k0 < k_hi; k0 += 16 * kRemoveBatch) {
                 VRow v[kRemoveBatch];
                 int c[kRemoveBatch];
 #pragma unroll
@@ -729,6 +748,26 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
         }
         exact16_leave<G>(st, mv, lp);
+    }
+    if (wave < kCutWaves && a.pseudo) {  // the deferred first pass of the removal
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            // the weights are relative to Mref; the reference may have risen since
+            const float sc = Mref[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mref[g] - st.m[g]);
+#pragma unroll
+            for (int j = 0; j < kRemoveBatch; ++j) rem_p[j][g] *= sc;
+        }
+#pragma unroll
+        for (int j = 0; j < kRemoveBatch; ++j) {
+            float x[8];
+            rem_v[j].unpack(x);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                st.l[g] -= rem_p[j][g];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(-rem_p[j][g], x[e], st.acc[g][e]);
+            }
+        }
     }
     // ---- combine the row groups: 4 per wave by shuffles, then the waves
     //      through LDS (in wave order) ---------------------------------------
