@@ -42,15 +42,15 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
 UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
     "stored": {
-        "sources_sha256": "362de5b1506d1a997feebd94a7e85954e59672ce64d287ace309153c15f4b25d",
-        "fetch_bytes": int(122695.08 * 2.0 * 1024),
-        "write_bytes": int(5004.18 * 1.0 * 1024),
+        "sources_sha256": "912af47fefd3adc5dc8b533d7a4cafa12b6c5d34be3e0353e3672d93d8243943",
+        "fetch_bytes": int(122772.52 * 2.0 * 1024),
+        "write_bytes": int(5003.71 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "362de5b1506d1a997feebd94a7e85954e59672ce64d287ace309153c15f4b25d",
-        "fetch_bytes": int(89964.04 * 2.0 * 1024),
-        "write_bytes": int(5004.11 * 1.0 * 1024),
+        "sources_sha256": "912af47fefd3adc5dc8b533d7a4cafa12b6c5d34be3e0353e3672d93d8243943",
+        "fetch_bytes": int(90086.23 * 2.0 * 1024),
+        "write_bytes": int(5003.81 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
 }
