@@ -312,6 +312,195 @@ __device__ __forceinline__ void exact16_leave(SoftState<G>& st, float mv, float 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Workgroup barrier ordering LDS only: global loads and stores in flight are
+// not waited for (every barrier of the one-launch kernels publishes LDS data;
+// a plain __syncthreads() after a global store would also drain the load
+// rings).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// End of a unit's step in a workgroup of NW waves (one-launch kernels): the
+// row groups' states are combined (shuffles), then the waves' (through
+// s_red, which may alias LDS data that is dead once every wave got here).
+// With one workgroup per unit (R = 1) it writes the normalised output outu
+// [G][d].  Otherwise each of the R workgroups posts its partial (per head the
+// state m, l and the 128 sums) as words (tag << 32 | value) into its slot of
+// xp [R][G][d + 2] and counts itself in on the unit's arrival word *xcount
+// (compare-and-swap; a stale tag counts as zero).  The workgroup that arrives
+// last reads the others' partials -- waiting only for words already stored,
+// for at most wait_ticks of the 100 MHz constant clock -- and merges them in
+// workgroup order.  s_flag: one int of LDS.
+template <int G, int NW>
+__device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][kHeadDim + 2], int* s_flag,
+                                            float* outu, uint64_t* xp, uint64_t* xcount, uint32_t tag, int R,
+                                            int rep, uint64_t wait_ticks) {
+    constexpr int kThreads = NW * kWave;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int rg = lane >> 4, li = lane & 15;
+    const uint64_t tagw = (uint64_t)tag << 32;
+    // ---- combine the row groups: 4 per wave by shuffles, then the waves
+    //      through LDS (in wave order) ---------------------------------------
+#pragma unroll
+    for (int step = 16; step <= 32; step <<= 1) {
+        float om[G], ol[G], oacc[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            om[g] = shfl_xor_f(st.m[g], step);
+            ol[g] = shfl_xor_f(st.l[g], step);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
+        }
+        merge_state<G>(st, om, ol, oacc);
+    }
+    lds_barrier();  // the big region is free
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
+            if (li == 0) {
+                s_red[wave][g][kHeadDim] = st.m[g];
+                s_red[wave][g][kHeadDim + 1] = st.l[g];
+            }
+        }
+    }
+    lds_barrier();
+    // thread tid owns outputs e = tid + kThreads k of the unit's G heads
+    constexpr int kOut = (G * kHeadDim + kThreads - 1) / kThreads;
+    float oM[kOut], oL[kOut], oA[kOut];
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
+                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
+                acc = fmaf(s_red[w][g][dd], wt, acc);
+            }
+        }
+        oM[k] = M;
+        oL[k] = l;
+        oA[k] = acc;
+    }
+    if (R == 1) {
+#pragma unroll
+        for (int k = 0; k < kOut; ++k) {
+            const int e = tid + k * kThreads;
+            if (e < G * kHeadDim) outu[e] = oL[k] > 0.f ? oA[k] / oL[k] : 0.f;
+        }
+        return;
+    }
+
+    // ---- several replicas: each posts its partial (per head: the state m, l
+    //      and the 128 sums) as tagged words, then counts itself in on the
+    //      unit's arrival word (call tag << 32 | count, compare-and-swap; a
+    //      stale tag counts as zero).  The replica that arrives last reads the
+    //      others' partials (waiting only for words already stored) and writes
+    //      the normalised output, merging in replica order. -------------------
+    constexpr int kPart = G * (kHeadDim + 2);
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
+        __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (dd == 0) {
+            __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    lds_barrier();
+    if (tid == 0) {
+        uint64_t* cnt = xcount;
+        uint64_t old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t arrived;
+        for (;;) {
+            arrived = ((uint32_t)(old >> 32) == tag ? (uint32_t)old : 0u) + 1u;
+            if (__hip_atomic_compare_exchange_strong(cnt, &old, tagw | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT))
+                break;
+        }
+        *s_flag = arrived == (uint32_t)R;
+    }
+    lds_barrier();
+    if (!*s_flag) return;
+    const uint64_t t0 = wall_clock64();
+    bool late = false;
+    // a partner word of this call (all of them are issued before the first
+    // is checked, so the reads take one round trip)
+    auto fresh = [&](uint64_t v, const uint64_t* p) {
+        while ((uint32_t)(v >> 32) != tag && !late) {
+            if (wall_clock64() - t0 > wait_ticks) late = true;
+            __builtin_amdgcn_s_sleep(1);
+            v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return (uint32_t)(v >> 32) == tag ? __uint_as_float((uint32_t)v) : NAN;
+    };
+    constexpr int kMaxR = 8;
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+        uint64_t wm[kMaxR], wl[kMaxR], wa[kMaxR];
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R && r2 != rep) {
+                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                wm[r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wl[r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wa[r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        float pm[kMaxR], pl[kMaxR], pa[kMaxR];
+        float M = -INFINITY;
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R) {
+                if (r2 == rep) {
+                    pm[r2] = oM[k];
+                    pl[r2] = oL[k];
+                    pa[r2] = oA[k];
+                } else {
+                    const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                    pm[r2] = fresh(wm[r2], pg + kHeadDim);
+                    pl[r2] = fresh(wl[r2], pg + kHeadDim + 1);
+                    pa[r2] = fresh(wa[r2], pg + dd);
+                }
+                M = fmaxf(M, pm[r2]);
+            }
+        }
+        float l = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int r2 = 0; r2 < kMaxR; ++r2) {
+                if (r2 < R) {
+                    const float wt = __builtin_amdgcn_exp2f(pm[r2] - M);
+                    l = fmaf(pl[r2], wt, l);
+                    acc = fmaf(pa[r2], wt, acc);
+                }
+            }
+        }
+        // a partial that never arrived (cannot happen once its replica has
+        // counted in) poisons the output instead of hanging
+        outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
+    }
+}
+
 template <typename T>
 struct RowBuf {
     Slice8<T> k[2], v[2];

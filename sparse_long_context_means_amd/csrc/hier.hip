@@ -42,21 +42,13 @@ constexpr int kHExactDepth = 2;             // exact-row steps (16 rows) in flig
 constexpr uint64_t kHExchangeWaitTicks = 2000;
 constexpr uint64_t kHPartialWaitTicks = 100000;
 
-// Workgroup barrier ordering LDS only (global loads and stores in flight are
-// not waited for).
-__device__ __forceinline__ void hlds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Exclusive scan of one counter over the workgroup in thread order (`lds`:
 // kHWaves ints); the total in tot.
 __device__ __forceinline__ int block_exclusive_sum(int v, int& tot, int* lds) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int inc = wave_inclusive_sum(v);
     if (lane == kWave - 1) lds[wave] = inc;
-    hlds_barrier();
+    lds_barrier();
     int base = 0, t = 0;
 #pragma unroll
     for (int w = 0; w < kHWaves; ++w) {
@@ -64,7 +56,7 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int& tot, int* lds) {
         if (w < wave) base += x;
         t += x;
     }
-    hlds_barrier();  // lds may be reused right after
+    lds_barrier();  // lds may be reused right after
     tot = t;
     return base + inc - v;
 }
@@ -89,7 +81,7 @@ __device__ __forceinline__ uint32_t block_cut(KeyF key_of, SizeF size_of, IdF id
         isz[j] = i < n ? size_of(i) : 0;
     }
     for (int k = tid; k < 4 * 256; k += kHThreads) reinterpret_cast<int*>(hist)[k] = 0;
-    hlds_barrier();
+    lds_barrier();
     uint32_t prefix = 0, pmask = 0;
     int Rb = budget;
     bool done = false;
@@ -99,7 +91,7 @@ __device__ __forceinline__ uint32_t block_cut(KeyF key_of, SizeF size_of, IdF id
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j)
             if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
-        hlds_barrier();
+        lds_barrier();
         int v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = hist[p][255 - (4 * lane + q)];
@@ -307,9 +299,9 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         for (int i = tid; i < kHierMaxD / 32; i += kHThreads) s_cmask[i] = 0u;
         for (int i = tid; i < kHierMaxF / 32; i += kHThreads) s_fmask[i] = 0u;
         if (tid == 0) s_misc[1] = 0;
-        hlds_barrier();
+        lds_barrier();
     });
-    hlds_barrier();
+    lds_barrier();
     if (xchg) {
         const uint64_t tagw = (uint64_t)a.tag << 32;
         uint64_t* xu = a.xch + (size_t)unit * R * a.Dmax;
@@ -344,10 +336,10 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
             }
         }
         if (miss) s_misc[1] = 1;
-        hlds_barrier();
+        lds_barrier();
         if (s_misc[1]) {  // (uniform) score them here: keys only
             score_items(0, D, crow, csize, s_ckey, 0, 0, 0, []() {});
-            hlds_barrier();
+            lds_barrier();
         }
     }
 
@@ -396,7 +388,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
             const int i = tid * kCItems + j;
             if (i < D) a.dbg_candidates[(size_t)unit * D + i] = (cbits >> j) & 1u;
         }
-    hlds_barrier();
+    lds_barrier();
     for (int p = tid; p < F; p += kHThreads) {
         const int k = upper_index(s_cpre, ncand, p);
         const int c = s_ccand[k];
@@ -404,7 +396,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         s_fid[p] = f;
         s_fsz[p] = fsizes[f];
     }
-    hlds_barrier();
+    lds_barrier();
 
     // ---- 3. fine scores of the candidates ---------------------------------
     const int dsh = cs1 - cs0;  // coarse share logits at s_lg[0 .. dsh)
@@ -415,7 +407,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 16));
     lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 32));
     if (lane < G) s_gmax[wave][lane] = lgmax;
-    hlds_barrier();
+    lds_barrier();
 
     // ---- 4. fine cut under the token budget, in fine-id order for ties ----
     constexpr int kFItems = kHierMaxF / kHThreads;
@@ -487,7 +479,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
             s_lg[t][g] = keep && lgv != -INFINITY ? __builtin_amdgcn_exp2f(lgv - Mref[g]) : 0.f;
         }
     }
-    hlds_barrier();
+    lds_barrier();
     if (a.pseudo && nsh > 0) {  // (uniform) item 0 of the share exists
 #pragma unroll
         for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
@@ -539,7 +531,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         float* sp = s_p + wave * 16 * G;
         for (int c0 = e0; c0 < e1; c0 += kHRowBatch) {
             const int cnt = min(kHRowBatch, e1 - c0);
-            hlds_barrier();  // the previous batch is consumed
+            lds_barrier();  // the previous batch is consumed
             for (int i = tid; i < cnt; i += kHThreads) {
                 const int r = c0 + i;
                 int v;
@@ -552,7 +544,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                 }
                 s_row[i] = v;
             }
-            hlds_barrier();
+            lds_barrier();
             const int nb = (cnt + 15) / 16;
             auto blk = [&](int step) {
                 const int q = step * kHWaves + wave;
@@ -589,157 +581,11 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         exact16_leave<G>(st, mv, lp);
     }
 
-    // ---- 7. combine the row groups (shuffles), then the waves (LDS) --------
-#pragma unroll
-    for (int step = 16; step <= 32; step <<= 1) {
-        float om[G], ol[G], oacc[G][8];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            om[g] = shfl_xor_f(st.m[g], step);
-            ol[g] = shfl_xor_f(st.l[g], step);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
-        }
-        merge_state<G>(st, om, ol, oacc);
-    }
-    hlds_barrier();  // the candidate lists are dead: the reduction region is free
-    if (rg == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
-            if (li == 0) {
-                s_red[wave][g][kHeadDim] = st.m[g];
-                s_red[wave][g][kHeadDim + 1] = st.l[g];
-            }
-        }
-    }
-    hlds_barrier();
-    constexpr int kOut = (G * kHeadDim + kHThreads - 1) / kHThreads;
-    float oM[kOut], oL[kOut], oA[kOut];
-#pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kHThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kHWaves; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
-        float l = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < kHWaves; ++w) {
-                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
-                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
-                acc = fmaf(s_red[w][g][dd], wt, acc);
-            }
-        }
-        oM[k] = M;
-        oL[k] = l;
-        oA[k] = acc;
-    }
-    float* outu = a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
-    if (R == 1) {
-#pragma unroll
-        for (int k = 0; k < kOut; ++k) {
-            const int e = tid + k * kHThreads;
-            if (e < G * kHeadDim) outu[e] = oL[k] > 0.f ? oA[k] / oL[k] : 0.f;
-        }
-        return;
-    }
-
-    // ---- several workgroups: each posts its partial as tagged words and
-    //      counts itself in on the unit's arrival word; the last one to
-    //      arrive merges in workgroup order (waiting only for words that are
-    //      already stored) and writes the output. -------------------------------
-    const uint64_t tagw = (uint64_t)a.tag << 32;
-    constexpr int kPart = G * (kHeadDim + 2);
-    uint64_t* xp = a.xpart + (size_t)unit * R * kPart;
-#pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kHThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
-        __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (dd == 0) {
-            __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    hlds_barrier();
-    if (tid == 0) {
-        uint64_t* cntw = a.xcount + unit;
-        uint64_t old = __hip_atomic_load(cntw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t arrived;
-        for (;;) {
-            arrived = ((uint32_t)(old >> 32) == a.tag ? (uint32_t)old : 0u) + 1u;
-            if (__hip_atomic_compare_exchange_strong(cntw, &old, tagw | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-                break;
-        }
-        s_misc[0] = arrived == (uint32_t)R;
-    }
-    hlds_barrier();
-    if (!s_misc[0]) return;
-    const uint64_t t0 = wall_clock64();
-    bool late = false;
-    auto fresh = [&](uint64_t v, const uint64_t* p) {
-        while ((uint32_t)(v >> 32) != a.tag && !late) {
-            if (wall_clock64() - t0 > kHPartialWaitTicks) late = true;
-            __builtin_amdgcn_s_sleep(1);
-            v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        return (uint32_t)(v >> 32) == a.tag ? __uint_as_float((uint32_t)v) : NAN;
-    };
-    constexpr int kMaxR = kHierMaxReplicas;
-#pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kHThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        uint64_t wm[kMaxR], wl[kMaxR], wa[kMaxR];
-#pragma unroll
-        for (int r2 = 0; r2 < kMaxR; ++r2) {
-            if (r2 < R && r2 != rep) {
-                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                wm[r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wl[r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wa[r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        float pm[kMaxR], pl[kMaxR], pa[kMaxR];
-        float M = -INFINITY;
-#pragma unroll
-        for (int r2 = 0; r2 < kMaxR; ++r2) {
-            if (r2 < R) {
-                if (r2 == rep) {
-                    pm[r2] = oM[k];
-                    pl[r2] = oL[k];
-                    pa[r2] = oA[k];
-                } else {
-                    const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                    pm[r2] = fresh(wm[r2], pg + kHeadDim);
-                    pl[r2] = fresh(wl[r2], pg + kHeadDim + 1);
-                    pa[r2] = fresh(wa[r2], pg + dd);
-                }
-                M = fmaxf(M, pm[r2]);
-            }
-        }
-        float l = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int r2 = 0; r2 < kMaxR; ++r2) {
-                if (r2 < R) {
-                    const float wt = __builtin_amdgcn_exp2f(pm[r2] - M);
-                    l = fmaf(pl[r2], wt, l);
-                    acc = fmaf(pa[r2], wt, acc);
-                }
-            }
-        }
-        outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
-    }
+    // ---- 7. combine the workgroup's states; the last workgroup of the unit
+    //      merges the partials and writes the output -------------------------
+    finish_step<G, kHWaves>(st, s_red, s_misc, a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim,
+                            a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, a.tag, R, rep,
+                            kHPartialWaitTicks);
 }
 
 int hier_replicas(int units) {

@@ -1,22 +1,28 @@
 // unit.hip -- one Multipole Attention decode step of a (sequence, KV head)
-// unit in ONE 1024-thread workgroup (or R replicas of it).
+// unit in one launch: R workgroups of 512 threads per unit (R = 1 when the
+// batch has 256 units or more and at most 2048 clusters per unit).
 //
 // Pages: atlas.scime.ai summary, opening sentence (exact attention on the
 // top-scoring clusters, centroid attention for the rest) and "Approach"
 // (value centroids stand in for the unselected clusters); mlsanity.com paper
 // page, "Abstract (arXiv)" (centroids pick the important keys).
 //
-// Each replica scores every cluster of its unit and takes the budget cut in
-// LDS (the replicas compute the same keys with the same operations, so they
-// reach the same cut); replica r then attends its share of the work: the
-// approximate terms of clusters [C r / R, C (r + 1) / R) (selected clusters
-// skipped through the LDS bitmask) and exact rows [E r / R, E (r + 1) / R) of
-// the selected clusters, plus its share of the unclustered tail.  With R = 1
-// the workgroup writes the normalised output; otherwise one partial per
-// replica goes to the merge launch.  No cut record, score or selection list
-// leaves the workgroup, and there is no launch boundary between the steps.
-// This path is meant for batches with many units (one workgroup per CU);
-// the split launches in decode.hip serve the rest.
+// Workgroup r of a unit:
+//   1. scores its share [C r / R, C (r + 1) / R) of the clusters on the
+//      matrix cores and takes the other shares' ranking keys from the other
+//      workgroups as tagged 64-bit words (or scores them itself when a
+//      partner is late: the same bits);
+//   2. splits its waves: waves 0-3 take the budget cut (radix passes over
+//      size-weighted LDS histograms) while waves 4-7 stream the approximate
+//      term n exp(s) Vbar of every cluster of the share; the selected
+//      clusters' terms are taken back out afterwards;
+//   3. attends its share of the exact rows (the selected clusters' members,
+//      then the unclustered tail) on the matrix cores;
+//   4. combines its waves; the last workgroup of the unit to finish merges the
+//      partials and writes the output (finish_step).
+// No score, cut record or selection list leaves the workgroup, and there is
+// no launch boundary between the steps.  The split launches in decode.hip
+// serve the configurations this path does not take.
 #include <math.h>
 
 #include <type_traits>
@@ -35,15 +41,6 @@ constexpr int kUnitRowBatch = 1024;               // staged exact rows per pass
 // shares of up to 1024 per replica.
 constexpr int kUnitMaxCSmall = 2048, kUnitShareSmall = 2048;
 constexpr int kUnitMaxCLarge = 4096, kUnitShareLarge = 1024;
-
-// Workgroup barrier ordering LDS only: global loads and stores in flight are
-// not waited for (every barrier here publishes LDS data; a plain
-// __syncthreads() after a global store would also drain the load rings).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Barrier of waves 0 .. NW-1 of the workgroup through an LDS counter, the
 // other waves running on.  Each of those waves passes the same sequence of
@@ -769,164 +766,9 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
         }
     }
-    // ---- combine the row groups: 4 per wave by shuffles, then the waves
-    //      through LDS (in wave order) ---------------------------------------
-#pragma unroll
-    for (int step = 16; step <= 32; step <<= 1) {
-        float om[G], ol[G], oacc[G][8];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            om[g] = shfl_xor_f(st.m[g], step);
-            ol[g] = shfl_xor_f(st.l[g], step);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
-        }
-        merge_state<G>(st, om, ol, oacc);
-    }
-    lds_barrier();  // the big region is free
-    if (rg == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_red[wave][g][li * 8 + e] = st.acc[g][e];
-            if (li == 0) {
-                s_red[wave][g][kHeadDim] = st.m[g];
-                s_red[wave][g][kHeadDim + 1] = st.l[g];
-            }
-        }
-    }
-    lds_barrier();
-    // thread tid owns outputs e = tid + kUnitThreads k of the unit's G heads
-    constexpr int kOut = (G * kHeadDim + kUnitThreads - 1) / kUnitThreads;
-    float oM[kOut], oL[kOut], oA[kOut];
-#pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kUnitThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kUnitWaves; ++w) M = fmaxf(M, s_red[w][g][kHeadDim]);
-        float l = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < kUnitWaves; ++w) {
-                const float wt = __builtin_amdgcn_exp2f(s_red[w][g][kHeadDim] - M);
-                l = fmaf(s_red[w][g][kHeadDim + 1], wt, l);
-                acc = fmaf(s_red[w][g][dd], wt, acc);
-            }
-        }
-        oM[k] = M;
-        oL[k] = l;
-        oA[k] = acc;
-    }
-    float* outu = a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
-    if (R == 1) {
-#pragma unroll
-        for (int k = 0; k < kOut; ++k) {
-            const int e = tid + k * kUnitThreads;
-            if (e < G * kHeadDim) outu[e] = oL[k] > 0.f ? oA[k] / oL[k] : 0.f;
-        }
-        return;
-    }
-
-    // ---- several replicas: each posts its partial (per head: the state m, l
-    //      and the 128 sums) as tagged words, then counts itself in on the
-    //      unit's arrival word (call tag << 32 | count, compare-and-swap; a
-    //      stale tag counts as zero).  The replica that arrives last reads the
-    //      others' partials (waiting only for words already stored) and writes
-    //      the normalised output, merging in replica order. -------------------
-    constexpr int kPart = G * (kHeadDim + 2);
-    uint64_t* xp = a.xpart + (size_t)unit * R * kPart;
-#pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kUnitThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
-        __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (dd == 0) {
-            __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    lds_barrier();
-    if (tid == 0) {
-        uint64_t* cnt = a.xcount + unit;
-        uint64_t old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t arrived;
-        for (;;) {
-            arrived = ((uint32_t)(old >> 32) == a.tag ? (uint32_t)old : 0u) + 1u;
-            if (__hip_atomic_compare_exchange_strong(cnt, &old, tagw | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-                break;
-        }
-        s_misc[0] = arrived == (uint32_t)R;
-    }
-    lds_barrier();
-    if (!s_misc[0]) return;
-    const uint64_t t0 = wall_clock64();
-    bool late = false;
-    // a partner word of this call (all of them are issued before the first
-    // is checked, so the reads take one round trip)
-    auto fresh = [&](uint64_t v, const uint64_t* p) {
-        while ((uint32_t)(v >> 32) != a.tag && !late) {
-            if (wall_clock64() - t0 > kPartialWaitTicks) late = true;
-            __builtin_amdgcn_s_sleep(1);
-            v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        return (uint32_t)(v >> 32) == a.tag ? __uint_as_float((uint32_t)v) : NAN;
-    };
-    constexpr int kMaxR = 8;
-#pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kUnitThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        uint64_t wm[kMaxR], wl[kMaxR], wa[kMaxR];
-#pragma unroll
-        for (int r2 = 0; r2 < kMaxR; ++r2) {
-            if (r2 < R && r2 != rep) {
-                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                wm[r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wl[r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wa[r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        float pm[kMaxR], pl[kMaxR], pa[kMaxR];
-        float M = -INFINITY;
-#pragma unroll
-        for (int r2 = 0; r2 < kMaxR; ++r2) {
-            if (r2 < R) {
-                if (r2 == rep) {
-                    pm[r2] = oM[k];
-                    pl[r2] = oL[k];
-                    pa[r2] = oA[k];
-                } else {
-                    const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                    pm[r2] = fresh(wm[r2], pg + kHeadDim);
-                    pl[r2] = fresh(wl[r2], pg + kHeadDim + 1);
-                    pa[r2] = fresh(wa[r2], pg + dd);
-                }
-                M = fmaxf(M, pm[r2]);
-            }
-        }
-        float l = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int r2 = 0; r2 < kMaxR; ++r2) {
-                if (r2 < R) {
-                    const float wt = __builtin_amdgcn_exp2f(pm[r2] - M);
-                    l = fmaf(pl[r2], wt, l);
-                    acc = fmaf(pa[r2], wt, acc);
-                }
-            }
-        }
-        // a partial that never arrived (cannot happen once its replica has
-        // counted in) poisons the output instead of hanging
-        outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
-    }
+    finish_step<G, kUnitWaves>(st, s_red, s_misc, a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim,
+                               a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, a.tag, R, rep,
+                               kPartialWaitTicks);
 }
 
 // One replica per unit only once the units alone give a workgroup to every CU
