@@ -42,23 +42,23 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
 UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
     "stored": {
-        "sources_sha256": "912af47fefd3adc5dc8b533d7a4cafa12b6c5d34be3e0353e3672d93d8243943",
-        "fetch_bytes": int(122772.52 * 2.0 * 1024),
-        "write_bytes": int(5003.71 * 1.0 * 1024),
+        "sources_sha256": "e19b73f55844ffbc827ffc582db5401e0a2d6f18d3bdeff443bef4a09b65a684",
+        "fetch_bytes": int(122781.90 * 2.0 * 1024),
+        "write_bytes": int(5003.52 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "912af47fefd3adc5dc8b533d7a4cafa12b6c5d34be3e0353e3672d93d8243943",
-        "fetch_bytes": int(90086.23 * 2.0 * 1024),
-        "write_bytes": int(5003.81 * 1.0 * 1024),
+        "sources_sha256": "e19b73f55844ffbc827ffc582db5401e0a2d6f18d3bdeff443bef4a09b65a684",
+        "fetch_bytes": int(90107.95 * 2.0 * 1024),
+        "write_bytes": int(5003.43 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
 }
 HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
-    "sources_sha256": "66fdc93e2a751189237a9b850e01740a03d6881153169f3da73784be1621275d",
+    "sources_sha256": "5d3ba480db50b7bfda78cc5999abbcc1f151f6afcb49ef323d80570aee74d608",
     "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
-    "fetch_bytes": int(18120.66 * 2.0 * 1024),
-    "write_bytes": int(3484.05 * 1.0 * 1024),
+    "fetch_bytes": int(18111.49 * 2.0 * 1024),
+    "write_bytes": int(3482.15 * 1.0 * 1024),
     "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
