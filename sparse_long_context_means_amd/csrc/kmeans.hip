@@ -278,35 +278,85 @@ __device__ __forceinline__ int lds_lower_bound(const uint32_t* a, int n, uint32_
     return lo;
 }
 
-__global__ __launch_bounds__(1024) void kmeans_csr_kernel(const int32_t* __restrict__ assign, UnitGeom g,
-                                                          BlockRange br, int32_t* __restrict__ sizes,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ token_ids) {
+constexpr int kCsrThreads = 1024;
+
+// A bitonic sort of P2 = K * kCsrThreads keys, thread t holding keys
+// t K .. t K + K - 1 in v: exchanges at distance jj < K stay in the thread,
+// jj < 64 K cross lanes of a wave (shuffles), larger ones go through LDS
+// (`keys`).  Sorted, the keys are back in `keys`.
+template <int K>
+__device__ __forceinline__ void csr_sort(uint32_t* keys, const int32_t* au, int L, int c0) {
+    constexpr int P2 = K * kCsrThreads;
+    const int t = threadIdx.x;
+    uint32_t v[K];
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+        const int i = t * K + q;
+        v[q] = i < L ? ((uint32_t)(au[i] - c0) << 14) | (uint32_t)i : 0xFFFFFFFFu;
+    }
+    for (int k = 2; k <= P2; k <<= 1) {
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            if (jj >= kWave * K) {  // (uniform) partner in another wave
+#pragma unroll
+                for (int q = 0; q < K; ++q) keys[t * K + q] = v[q];
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < K; ++q) {
+                    const int i = t * K + q;
+                    const uint32_t b = keys[i ^ jj];
+                    const bool keep_min = ((i & jj) == 0) == ((i & k) == 0);
+                    v[q] = keep_min ? min(v[q], b) : max(v[q], b);
+                }
+                __syncthreads();  // before the keys are written again
+            } else if (jj >= K) {  // (uniform) partner in another lane of the wave
+                const int lj = jj / K;
+                uint32_t b[K];
+#pragma unroll
+                for (int q = 0; q < K; ++q) b[q] = (uint32_t)__shfl_xor((int)v[q], lj, kWave);
+#pragma unroll
+                for (int q = 0; q < K; ++q) {
+                    const int i = t * K + q;
+                    const bool keep_min = ((i & jj) == 0) == ((i & k) == 0);
+                    v[q] = keep_min ? min(v[q], b[q]) : max(v[q], b[q]);
+                }
+            } else {  // partner in the same thread
+#pragma unroll
+                for (int q = 0; q < K; ++q) {
+                    if ((q & jj) == 0) {
+                        const int i = t * K + q;
+                        const uint32_t a = v[q], b = v[q ^ jj];
+                        const bool asc = (i & k) == 0;
+                        v[q] = asc ? min(a, b) : max(a, b);
+                        v[q ^ jj] = asc ? max(a, b) : min(a, b);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < K; ++q) keys[t * K + q] = v[q];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kCsrThreads) void kmeans_csr_kernel(const int32_t* __restrict__ assign, UnitGeom g,
+                                                                 BlockRange br, int32_t* __restrict__ sizes,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ token_ids) {
     __shared__ uint32_t keys[kMaxBlock];
     const int j = blockIdx.x, unit = blockIdx.y;
     int p, L, c0, C;
     block_info(br, j, p, L, c0, C);
-    int P2 = 2;
+    // keys cluster << 14 | token, sorted (distinct keys: the (cluster, token)
+    // order); the keys past L sort last
+    int P2 = kCsrThreads;
     while (P2 < L) P2 <<= 1;
     const int32_t* au = assign + (size_t)unit * g.Nmax + p;
-    for (int i = threadIdx.x; i < P2; i += blockDim.x)
-        keys[i] = i < L ? ((uint32_t)(au[i] - c0) << 14) | (uint32_t)i : 0xFFFFFFFFu;
-    __syncthreads();
-    for (int k = 2; k <= P2; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = threadIdx.x; i < P2; i += blockDim.x) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const uint32_t a = keys[i], b = keys[ixj];
-                    const bool asc = (i & k) == 0;
-                    if ((a > b) == asc) {
-                        keys[i] = b;
-                        keys[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    switch (P2 / kCsrThreads) {  // (uniform)
+        case 1: csr_sort<1>(keys, au, L, c0); break;
+        case 2: csr_sort<2>(keys, au, L, c0); break;
+        case 4: csr_sort<4>(keys, au, L, c0); break;
+        case 8: csr_sort<8>(keys, au, L, c0); break;
+        default: csr_sort<16>(keys, au, L, c0); break;
     }
     int32_t* tu = token_ids + (size_t)unit * g.Nmax;
     for (int pos = threadIdx.x; pos < L; pos += blockDim.x) tu[p + pos] = p + (int)(keys[pos] & 0x3FFFu);
@@ -654,8 +704,8 @@ hipError_t launch_kmeans_assign(int dtype, const void* K, UnitGeom g, BlockRange
 
 hipError_t launch_kmeans_csr(const int32_t* assign, UnitGeom g, BlockRange br, int32_t* sizes, int32_t* offsets,
                              int32_t* token_ids, hipStream_t st) {
-    hipLaunchKernelGGL(kmeans_csr_kernel, dim3(br.nb, g.units), dim3(1024), 0, st, assign, g, br, sizes, offsets,
-                       token_ids);
+    hipLaunchKernelGGL(kmeans_csr_kernel, dim3(br.nb, g.units), dim3(kCsrThreads), 0, st, assign, g, br, sizes,
+                       offsets, token_ids);
     return hipGetLastError();
 }
 
