@@ -91,7 +91,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(every (sequence, KV head) unit is independent; see the sharding notes).", file=sys.stderr)
         sys.exit(2)
 

@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
         carry += tot.x;
     }
     // the lists of the blocks follow each other: this block's starts after
-    // the non-empty fine clusters of the earlier blocks (of this build or
+    // the non-empty fine clusters of the earlier blocks (of the same build or
     // update alike), so a block's end offset is the next block's start
     int before = 0;
     for (int base = 0; base < c0; base += 256) {
