@@ -626,6 +626,9 @@ HIER_CASES = [
     (4, 32, 8, 16384, 16384, 4096, 128, 2048, (256, 1000), True),
     (2, 8, 2, 12000, 13000, 4096, 64, 4096, (0, 300), False),
     (1, 4, 4, 9000, 9000, 2048, 128, 512, (100, 2000), True),
+    # no candidates (every coarse cluster approximated); every token a candidate
+    (2, 8, 8, 6000, 6500, 2048, 128, 0, (0, 300), True),
+    (2, 16, 8, 3000, 3000, 1024, 128, 4096, (0, 3000), False),
 ]
 
 
