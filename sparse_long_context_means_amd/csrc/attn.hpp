@@ -35,6 +35,142 @@ __device__ __forceinline__ int upper_index(const int32_t* pre, int n, int x) {
     return lo;
 }
 
+// ---------------------------------------------------------------------------
+// First pass of the budget cut, by value.  The cut keeps the longest prefix
+// of the non-empty items in (key desc, id asc) order whose sizes fit the
+// budget.  The open items' key range [min, max] is split into 256 bins of
+// equal width; the bin index is a non-decreasing function of the key, so all
+// items of a higher bin come before all items of a lower one.  A histogram
+// of sizes (and counts) finds the bin where the budget runs out: items above
+// it are taken, items below it dropped.  When at most kRankCap items share
+// that bin (clustered keys put a handful there) each of them adds up the
+// sizes of the bin's items ahead of it, by order key and id, and is taken if
+// it still fits: the same decisions as an exact radix cut, in three barriers
+// instead of six or more.  Otherwise, or when the key range is degenerate,
+// it returns false with `act` holding the items still open and `budget` what
+// is left of it, for an exact radix pass that starts with a barrier.
+//
+// Thread t holds ITEMS items (bit j of act / sel for its item j); id_of(j)
+// is the id of its item j.  The NW waves 0 .. NW-1 take part, `bar` is their
+// barrier.  h64: 256 64-bit words of histogram followed by kRankCap 16-byte
+// list entries (LDS, 16-byte aligned); mm: 2 NW + 1 words (LDS).  Both are
+// free again after the next barrier of the caller.
+constexpr int kRankCap = 128;
+
+template <int NW, int ITEMS, typename IdF, typename Bar>
+__device__ __forceinline__ bool range_cut(const float (&kf)[ITEMS], const uint32_t (&key)[ITEMS],
+                                          const int (&isz)[ITEMS], IdF id_of, int& budget, uint32_t& act,
+                                          uint32_t& sel, unsigned long long* h64, float* mm, Bar bar) {
+    static_assert(ITEMS <= 32, "one bit per item");
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    uint4* s_list = reinterpret_cast<uint4*>(h64 + 256);
+    int* s_cnt = reinterpret_cast<int*>(mm + 2 * NW);
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+        if ((act >> j) & 1u) {
+            lo = fminf(lo, kf[j]);
+            hi = fmaxf(hi, kf[j]);
+        }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+        lo = fminf(lo, shfl_xor_f(lo, o));
+        hi = fmaxf(hi, shfl_xor_f(hi, o));
+    }
+    if (lane == 0) {
+        mm[2 * wave] = lo;
+        mm[2 * wave + 1] = hi;
+    }
+    for (int k = tid; k < 256; k += NW * kWave) h64[k] = 0ull;
+    if (tid == 0) *s_cnt = 0;
+    bar();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        lo = fminf(lo, mm[2 * w]);
+        hi = fmaxf(hi, mm[2 * w + 1]);
+    }
+    const float width = hi - lo;
+    if (!(width > 0.f) || !(width < INFINITY)) return false;  // the same in every thread
+    const float inv = 256.f / width;
+    int bin[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        bin[j] = (int)fminf(fmaxf((kf[j] - lo) * inv, 0.f), 255.f);
+        if ((act >> j) & 1u) atomicAdd(&h64[bin[j]], (1ull << 40) | (unsigned long long)isz[j]);
+    }
+    bar();
+    int vs[4], vc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const unsigned long long v = h64[255 - (4 * lane + q)];
+        vs[q] = (int)(v & ((1ull << 40) - 1));
+        vc[q] = (int)(v >> 40);
+    }
+    int total;
+    int run = wave_exclusive_sum(vs[0] + vs[1] + vs[2] + vs[3], total);
+    if (total <= budget) {  // every open item fits
+        sel |= act;
+        act = 0;
+        return true;
+    }
+    int found = -1, cum = 0, cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (found < 0 && run <= budget && budget < run + vs[q]) {
+            found = 255 - (4 * lane + q);
+            cum = run;
+            cnt = vc[q];
+        }
+        run += vs[q];
+    }
+    const uint64_t bal = __ballot(found >= 0);
+    const int src = __ffsll((long long)bal) - 1;
+    const int c = lane_value(found, src), m = lane_value(cnt, src);
+    budget -= lane_value(cum, src);
+    uint32_t inbin = 0;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+        if ((act >> j) & 1u) {
+            if (bin[j] > c) sel |= 1u << j;
+            else if (bin[j] == c) inbin |= 1u << j;
+        }
+    act = inbin;
+    if (m > kRankCap) return false;
+    // The bin's m items in a list (m counted them: the slots stay below m) as
+    // 64-bit ranks (order key above, inverted id below: a larger rank comes
+    // first) with their sizes.  Every wave then ranks the whole list, lane l
+    // taking entries l and l + 64 against a broadcast of each entry; the
+    // ballots of the two results give every owner its items' decisions.
+    int slot[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        slot[j] = -1;
+        if ((inbin >> j) & 1u) {
+            slot[j] = atomicAdd(s_cnt, 1);
+            s_list[slot[j]] = make_uint4(~(uint32_t)id_of(j), key[j], (uint32_t)isz[j], 0u);
+        }
+    }
+    bar();
+    const uint4 e0 = lane < m ? s_list[lane] : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 e1 = lane + kWave < m ? s_list[lane + kWave] : make_uint4(0u, 0u, 0u, 0u);
+    const uint64_t r0 = ((uint64_t)e0.y << 32) | e0.x, r1 = ((uint64_t)e1.y << 32) | e1.x;
+    int b0 = 0, b1 = 0;
+#pragma unroll 4
+    for (int t = 0; t < m; ++t) {
+        const uint4 e = s_list[t];
+        const uint64_t r = ((uint64_t)e.y << 32) | e.x;
+        b0 += r > r0 ? (int)e.z : 0;
+        b1 += r > r1 ? (int)e.z : 0;
+    }
+    const uint64_t f0 = __ballot(lane < m && b0 + (int)e0.z <= budget);
+    const uint64_t f1 = __ballot(lane + kWave < m && b1 + (int)e1.z <= budget);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+        if (slot[j] >= 0 && (((slot[j] < kWave ? f0 : f1) >> (slot[j] & (kWave - 1))) & 1ull)) sel |= 1u << j;
+    act = 0;
+    return true;
+}
+
 // log2 of a positive count, as both the adding and the removing side take it.
 __device__ __forceinline__ float log2_count(int n) { return __builtin_amdgcn_logf((float)n); }
 

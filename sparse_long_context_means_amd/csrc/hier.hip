@@ -63,27 +63,40 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int& tot, int* lds) {
 
 // Budget cut over n items by the whole workgroup: the longest prefix of the
 // non-empty items in (key desc, id asc) order whose sizes sum to at most
-// `budget` (four 8-bit radix passes over the order-preserving key bits,
-// weighted by size, find the cut value; items at it are taken in id order
-// while they fit).  Thread t owns items ITEMS t .. ITEMS t + ITEMS - 1; bit j
-// of the result is item ITEMS t + j.  key(i), size(i), id(i) read item i
-// (i < n); id orders items with equal keys.
+// `budget`.  A pass over equal-width value bins usually settles it; else four
+// 8-bit radix passes over the order-preserving key bits of the items still
+// open, weighted by size, find the cut value, and items at it are taken in id
+// order while they fit.  Thread t owns items ITEMS t .. ITEMS t + ITEMS - 1;
+// bit j of the result is item ITEMS t + j.  key(i), size(i), id(i) read item
+// i (i < n); id orders items with equal keys.
 template <int ITEMS, typename KeyF, typename SizeF, typename IdF>
 __device__ __forceinline__ uint32_t block_cut(KeyF key_of, SizeF size_of, IdF id_of, int n, int budget,
                                               int (*hist)[256], int* scan) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     uint32_t key[ITEMS];
+    float kf[ITEMS];
     int isz[ITEMS];
+    uint32_t act = 0, bits = 0;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const int i = tid * ITEMS + j;
-        key[j] = i < n ? order_key(key_of(i)) : 0u;
+        kf[j] = i < n ? key_of(i) : 0.f;
+        key[j] = order_key(kf[j]);
         isz[j] = i < n ? size_of(i) : 0;
+        act |= (uint32_t)(isz[j] > 0) << j;
     }
+    int Rb = budget;
+    if (range_cut<kHWaves, ITEMS>(kf, key, isz, [&](int j) { return id_of(tid * ITEMS + j); }, Rb, act, bits,
+                                  reinterpret_cast<unsigned long long*>(&hist[0][0]), reinterpret_cast<float*>(scan),
+                                  []() { lds_barrier(); }))
+        return bits;
+    // (uniform, rare) exact radix passes over the open items
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) isz[j] = ((act >> j) & 1u) ? isz[j] : 0;
+    lds_barrier();  // the first pass's histogram is read
     for (int k = tid; k < 4 * 256; k += kHThreads) reinterpret_cast<int*>(hist)[k] = 0;
     lds_barrier();
     uint32_t prefix = 0, pmask = 0;
-    int Rb = budget;
     bool done = false;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -117,7 +130,6 @@ __device__ __forceinline__ uint32_t block_cut(KeyF key_of, SizeF size_of, IdF id
         prefix |= (uint32_t)digit << shift;
         pmask |= 0xFFu << shift;
     }
-    uint32_t bits = 0;
     if (done) {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) bits |= (uint32_t)(isz[j] > 0 && key[j] >= prefix) << j;
@@ -125,7 +137,9 @@ __device__ __forceinline__ uint32_t block_cut(KeyF key_of, SizeF size_of, IdF id
     }
     // items at the cut value, in id order while they fit: an item's running
     // sum is the sizes of the tied items with lower ids (ties are rare, so
-    // each tied item scans all items)
+    // each tied item scans all items; an item at the cut value is open, as
+    // the taken items' keys lie above every open key and the dropped ones'
+    // below)
     int ties = 0;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) ties += isz[j] > 0 && key[j] == prefix;
@@ -165,7 +179,7 @@ struct HierLds {
     static constexpr int spre = fmask + kHierMaxF / 8;           // int [MaxF + 4]: candidate coarse
                                                                  // ids; then selected-row prefix
     static constexpr int lg = spre + (kHierMaxF + 4) * 4;        // float [MaxShare][G]
-    static constexpr int hist = lg + kHierMaxShare * G * 4;      // int [4][256]
+    static constexpr int hist = (lg + kHierMaxShare * G * 4 + 15) / 16 * 16;  // int [4][256]
     static constexpr int scan = hist + 4 * 256 * 4;              // int [64]
     static constexpr int misc = scan + 64 * 4;                   // int [16]
     static constexpr int gmax = misc + 16 * 4;                   // float [waves][G]
@@ -175,6 +189,8 @@ struct HierLds {
     static constexpr int red = fid;                              // float [waves][G][d + 2], after the
                                                                  // exact rows (spans fid, fkey)
     static_assert(kHWaves * G * (kHeadDim + 2) * 4 <= 2 * kHierMaxF * 4, "reduction region");
+    static_assert(hist % 16 == 0 && 256 * 8 + kRankCap * 16 <= 4 * 256 * 4, "value-bin pass in the histogram");
+    static_assert(2 * kHWaves + 1 <= 64, "value-bin pass in the scan words");
 };
 
 template <int G>

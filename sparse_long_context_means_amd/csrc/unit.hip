@@ -12,10 +12,11 @@
 //      matrix cores and takes the other shares' ranking keys from the other
 //      workgroups as tagged 64-bit words (or scores them itself when a
 //      partner is late: the same bits);
-//   2. splits its waves: waves 0-3 take the budget cut (radix passes over
-//      size-weighted LDS histograms) while waves 4-7 stream the approximate
-//      term n exp(s) Vbar of every cluster of the share; the selected
-//      clusters' terms are taken back out afterwards;
+//   2. splits its waves: waves 0-3 take the budget cut (a size-weighted LDS
+//      histogram over value bins, radix passes when that does not settle
+//      it) while waves 4-7 stream the approximate term n exp(s) Vbar of
+//      every cluster of the share; the selected clusters' terms are taken
+//      back out afterwards;
 //   3. attends its share of the exact rows (the selected clusters' members,
 //      then the unclustered tail) on the matrix cores;
 //   4. combines its waves; the last workgroup of the unit to finish merges the
@@ -98,13 +99,14 @@ __device__ __forceinline__ int2 group_exclusive_sum2(int2 v, int2& tot, int* lds
 
 // Budget cut taken by waves 0 .. NW-1 (the others run on): the longest prefix
 // of the non-empty clusters in (key desc, id asc) order whose sizes sum to at
-// most `budget`.  Thread t owns clusters ITEMS t .. ITEMS t + ITEMS - 1.  Four
-// 8-bit radix passes over the order-preserving key bits, weighted by size,
-// into LDS histograms find the cut value (every wave scans the histogram and
-// reaches the same digit); clusters above it are selected, clusters equal to
-// it in id order while they fit.  One group scan places the selected clusters
-// in id order: ids, first members, member-row prefix (s_spre[nsel] = E), and
-// nsel, E in out[0], out[1].
+// most `budget`.  Thread t owns clusters ITEMS t .. ITEMS t + ITEMS - 1.  A
+// pass over equal-width value bins (range_cut) usually settles it.  Else four
+// 8-bit radix passes over the order-preserving key bits of the clusters still
+// open, weighted by size, into LDS histograms find the cut value (every wave
+// scans the histogram and reaches the same digit); clusters above it are
+// selected, clusters equal to it in id order while they fit.  One group scan
+// places the selected clusters in id order: ids, first members, member-row
+// prefix (s_spre[nsel] = E), and nsel, E in out[0], out[1].
 template <int NW, int ITEMS>
 __device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_sz, const int32_t* s_off,
                                           const int32_t* s_rows, int C, int budget, int (*hist)[256], int* s_scan,
@@ -112,58 +114,67 @@ __device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_s
                                           int* out, int32_t* dbg_sel) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     uint32_t key[ITEMS];
+    float kf[ITEMS];
     int isz[ITEMS];
+    uint32_t act = 0, selbits = 0;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const int i = tid * ITEMS + j;
-        key[j] = i < C ? order_key(s_key[i]) : 0u;
+        kf[j] = i < C ? s_key[i] : 0.f;
+        key[j] = order_key(kf[j]);
         isz[j] = i < C ? s_sz[i] : 0;
+        act |= (uint32_t)(isz[j] > 0) << j;
     }
-    for (int k = tid; k < 4 * 256; k += NW * kWave) reinterpret_cast<int*>(hist)[k] = 0;
-    group_barrier<NW>(ctr, gen);
-    uint32_t prefix = 0, pmask = 0;
     int Rb = budget;
-    bool done = false;
+    auto bar = [&]() { group_barrier<NW>(ctr, gen); };
+    if (!range_cut<NW, ITEMS>(kf, key, isz, [&](int j) { return tid * ITEMS + j; }, Rb, act, selbits,
+                              reinterpret_cast<unsigned long long*>(&hist[0][0]), reinterpret_cast<float*>(s_scan),
+                              bar)) {  // (uniform, rare) exact radix passes over the open items
+        int rsz[ITEMS];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int shift = 24 - 8 * p;
+        for (int j = 0; j < ITEMS; ++j) rsz[j] = ((act >> j) & 1u) ? isz[j] : 0;
+        bar();  // the first pass's histogram is read
+        for (int k = tid; k < 4 * 256; k += NW * kWave) reinterpret_cast<int*>(hist)[k] = 0;
+        bar();
+        uint32_t prefix = 0, pmask = 0;
+        bool done = false;
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j)
-            if (isz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], isz[j]);
-        group_barrier<NW>(ctr, gen);
-        int v[4];
+        for (int p = 0; p < 4; ++p) {
+            const int shift = 24 - 8 * p;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = hist[p][255 - (4 * lane + q)];
-        int total;
-        int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
-        if (total <= Rb) {  // the same in every wave: every candidate left fits
-            done = true;
-            break;
-        }
-        int found = -1, cum = 0;
+            for (int j = 0; j < ITEMS; ++j)
+                if (rsz[j] > 0 && (key[j] & pmask) == prefix) atomicAdd(&hist[p][(key[j] >> shift) & 255u], rsz[j]);
+            bar();
+            int v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (found < 0 && run <= Rb && Rb < run + v[q]) {
-                found = 255 - (4 * lane + q);
-                cum = run;
+            for (int q = 0; q < 4; ++q) v[q] = hist[p][255 - (4 * lane + q)];
+            int total;
+            int run = wave_exclusive_sum(v[0] + v[1] + v[2] + v[3], total);
+            if (total <= Rb) {  // the same in every wave: every candidate left fits
+                done = true;
+                break;
             }
-            run += v[q];
+            int found = -1, cum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (found < 0 && run <= Rb && Rb < run + v[q]) {
+                    found = 255 - (4 * lane + q);
+                    cum = run;
+                }
+                run += v[q];
+            }
+            const uint64_t bal = __ballot(found >= 0);
+            const int src = __ffsll((long long)bal) - 1;
+            const int digit = lane_value(found, src);
+            Rb -= lane_value(cum, src);
+            prefix |= (uint32_t)digit << shift;
+            pmask |= 0xFFu << shift;
         }
-        const uint64_t bal = __ballot(found >= 0);
-        const int src = __ffsll((long long)bal) - 1;
-        const int digit = lane_value(found, src);
-        Rb -= lane_value(cum, src);
-        prefix |= (uint32_t)digit << shift;
-        pmask |= 0xFFu << shift;
-    }
-    uint32_t selbits = 0;
-    int s_local = 0, rows_local = 0;
-    {
         int tie_local = 0;
         if (!done) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j)
-                if (isz[j] > 0 && key[j] == prefix) tie_local += isz[j];
+                if (rsz[j] > 0 && key[j] == prefix) tie_local += rsz[j];
         }
         int run_tie = 0;
         if (!done && group_count<NW>(tie_local > 0, s_scan + 32, ctr, gen) > 1) {  // uniform
@@ -177,14 +188,18 @@ __device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_s
                 sel = key[j] >= prefix;  // prefix: the digits fixed so far, low bits zero
             } else {
                 const bool tie = key[j] == prefix;
-                sel = key[j] > prefix || (tie && run_tie + isz[j] <= Rb);
-                if (tie) run_tie += isz[j];
+                sel = key[j] > prefix || (tie && run_tie + rsz[j] <= Rb);
+                if (tie) run_tie += rsz[j];
             }
-            sel = sel && isz[j] > 0;
-            selbits |= (uint32_t)sel << j;
-            s_local += sel;
-            rows_local += sel ? s_rows[tid * ITEMS + j] : 0;
+            selbits |= (uint32_t)(sel && rsz[j] > 0) << j;
         }
+    }
+    int s_local = 0, rows_local = 0;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const bool sel = (selbits >> j) & 1u;
+        s_local += sel;
+        rows_local += sel ? s_rows[tid * ITEMS + j] : 0;
     }
     int2 tot;
     const int2 ex = group_exclusive_sum2<NW>(make_int2(s_local, rows_local), tot, s_scan, ctr, gen);
@@ -230,6 +245,7 @@ struct UnitLds {
     static constexpr int big_end = row + kUnitRowBatch * 4;
     static constexpr int red_bytes = kUnitWaves * G * (kHeadDim + 2) * 4;
     static constexpr int bytes = (big_end > big + red_bytes ? big_end : big + red_bytes);
+    static_assert(hist % 16 == 0 && 256 * 8 + kRankCap * 16 <= 4 * 256 * 4, "value-bin pass in the histogram");
 };
 
 constexpr int kScoreDepth = 4;                           // score steps in flight per wave
