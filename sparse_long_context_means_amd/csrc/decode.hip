@@ -349,6 +349,25 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int unit) {
     int32_t* spre = a.sel_rowpre + (size_t)unit * (a.sel_stride + 1);
     int32_t* dbg = a.dbg_selected ? a.dbg_selected + (size_t)unit * a.dbg_stride : nullptr;
     int carry_rows = 0, carry_sel = 0, carry_tie = 0;
+    // With an id list (the candidates' fine clusters, listed by coarse id)
+    // the item order is not the id order: when several items carry the cut
+    // value, each of them sums the tied sizes of lower ids over all items
+    // (ties are rare).  The count of tied items comes first.
+    bool by_id = false;
+    if (!done && gids) {
+        int tied = 0;
+        for (int base = 0; base < n; base += kSelTileN) {
+            if (!resident) load_items(a, unit, n, base, it);
+            int h = 0;
+#pragma unroll
+            for (int j = 0; j < kSelItems; ++j) h += it.sz[j] > 0 && it.key[j] == tau;
+            int4 tt;
+            block256_exclusive_sum4(make_int4(h, 0, 0, 0), tt, scan_lds);
+            tied += tt.x;
+        }
+        by_id = tied > 1;
+    }
+    const int4* rsu = a.rs + (size_t)unit * a.rs_stride;
     for (int base = 0; base < n; base += kSelTileN) {
         if (!resident) load_items(a, unit, n, base, it);
         const int t0 = base + tid * kSelItems;
@@ -359,7 +378,7 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int unit) {
                 if (it.sz[j] > 0 && it.key[j] == tau) tie_local += it.sz[j];
         }
         int run_tie = carry_tie;
-        if (!done) {
+        if (!done && !by_id) {
             // usually a single item carries the cut value: then no scan is needed
             const int holders = __syncthreads_count(tie_local > 0);
             if (holders > 1 || !resident) {
@@ -378,8 +397,17 @@ __device__ __forceinline__ void select_unit(const SelectArgs& a, int unit) {
             if (done) {
                 sel = u >= prefix;
             } else {
-                const bool tie = u == tau;
-                sel = u > tau || (tie && run_tie + sz <= R);
+                const bool tie = u == tau && sz > 0;
+                int before = run_tie;
+                if (tie && by_id) {
+                    before = 0;
+                    const int me = gids[t0 + j];
+                    for (int i = 0; i < n; ++i) {
+                        const int4 v = rsu[i];
+                        if (v.y > 0 && order_key(__int_as_float(v.x)) == tau && gids[i] < me) before += v.y;
+                    }
+                }
+                sel = u > tau || (tie && before + sz <= R);
                 if (tie) run_tie += sz;
             }
             sel = sel && sz > 0;

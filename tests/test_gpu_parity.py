@@ -406,6 +406,53 @@ def test_unit_path_over_2048_clusters_matches_split_path_and_oracle():
             assert ok, (u, T, ea, er)
 
 
+@pytest.mark.parametrize("recipe", ["zero_queries", "outlier_cluster", "plain"])
+def test_unit_path_cut_paths_match_split_path(recipe):
+    """The one-launch cut settles most units with one pass over value bins
+    and a ranking of the cut bin's clusters; a degenerate key range (zero
+    queries: every key 0, ties broken by id) and a crowded cut bin (one
+    cluster of huge keys stretches the range, so the bulk shares a bin) take
+    the exact radix passes instead.  All three must pick exactly the clusters
+    of the split launches' radix cut; at zero queries the result is also the
+    oracle's (every key is exactly 0 on both sides)."""
+    mp = M()
+    B, Hq, Hkv, N, Bc = 16, 32, 8, 6000, 2048
+    w = small_workload(B, Hq, Hkv, N, 200, torch.bfloat16, outliers=4)
+    K, V, means = workloads.make_cache(w)
+    q = queries(w, means, 50)
+    if recipe == "outlier_cluster":
+        v = torch.randn(128, generator=torch.Generator().manual_seed(5))
+        v = v / v.norm()
+        K[:, :, :64] = (20000.0 * v).to(K.dtype)  # 64 tokens far along v: keys in the thousands
+        q = (q.float() + 3.0 * v).to(q.dtype)
+    elif recipe == "zero_queries":
+        q = torch.zeros_like(q)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, cluster_block=Bc, build_iters=3,
+                  seed=1)
+    assert p.decode_stages() == ["unit"]
+    ps = dataclasses.replace(p, splits=8)
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, N, state)
+    G = p.group
+    for T in (0, 100, 700, 5990):
+        du, ds = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+        ou = mp.decode(p, q.to(DEV), Kd, Vd, N, state, T, debug=du).cpu().numpy()
+        os_ = mp.decode(ps, q.to(DEV), Kd, Vd, N, state, T, debug=ds).cpu().numpy()
+        assert torch.equal(du.scores.cpu(), ds.scores.cpu()), (recipe, T)
+        assert torch.equal(du.selected.cpu(), ds.selected.cpu()), (recipe, T)
+        assert torch.equal(du.exact_tokens.cpu(), ds.exact_tokens.cpu()), (recipe, T)
+        np.testing.assert_allclose(ou, os_, rtol=1e-4, atol=1e-5)
+        if recipe == "zero_queries":
+            for u in (0, 77):
+                b, h = divmod(u, Hkv)
+                st = oracle_state_from_gpu(state, b, h, p)
+                ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], N, st, T)
+                assert np.array_equal(du.selected.cpu().numpy()[b, h, :st.n_clusters], ref.selected), (u, T)
+                ok, ea, er = close(ou[b, h * G:(h + 1) * G], ref.out)
+                assert ok, (u, T, ea, er)
+
+
 def test_unit_path_rescore_gives_the_same_result():
     """The one-launch decode splits a unit over several workgroups that take
     each other's cluster keys; the paths that score the other shares locally
@@ -679,6 +726,40 @@ def test_hier_one_launch_matches_six_launches_and_oracle(case):
             assert ok, (u, T, ea, er)
             assert st.sizes[:C][sel[b, h].astype(bool)].sum() <= T
             assert d1.exact_tokens.cpu().numpy()[b, h] == st.sizes[:C][sel[b, h].astype(bool)].sum()
+
+
+def test_hier_one_launch_zero_queries_take_clusters_in_id_order():
+    """Zero queries make every coarse and fine key exactly 0: both cuts of
+    the one-launch kernel take their exact radix passes (a degenerate key
+    range) and break the ties by id, as the six launches and the oracle do."""
+    mp = M()
+    B, Hq, Hkv, N = 2, 16, 8, 9000
+    w = small_workload(B, Hq, Hkv, N, N // 16, outliers=4, index=94)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, cluster_block=2048, build_iters=3,
+                  coarse_tokens_per_centroid=128, coarse_candidate_tokens=1000, seed=6)
+    assert p.decode_stages() == ["hier_unit"]
+    ps = dataclasses.replace(p, splits=4)
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, N, state)
+    q = torch.zeros(B, Hq, 128, dtype=torch.bfloat16)
+    G = p.group
+    for T in (100, 700):
+        d1, d6 = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+        o1 = mp.decode(p, q.to(DEV), Kd, Vd, N, state, T, debug=d1).cpu().numpy()
+        o6 = mp.decode(ps, q.to(DEV), Kd, Vd, N, state, T, debug=d6).cpu().numpy()
+        assert torch.equal(d1.candidates.cpu(), d6.candidates.cpu()), T
+        assert torch.equal(d1.selected.cpu(), d6.selected.cpu()), T
+        np.testing.assert_allclose(o1, o6, rtol=1e-4, atol=1e-5)
+        for u in (0, p.units - 1):
+            b, h = divmod(u, Hkv)
+            st = oracle_state_from_gpu(state, b, h, p)
+            ref = O.decode_unit_hier(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], N, st, T, 1000)
+            assert np.array_equal(d1.candidates.cpu().numpy()[b, h, :st.n_coarse], ref.candidates), (u, T)
+            assert np.array_equal(d1.selected.cpu().numpy()[b, h, :st.n_clusters], ref.selected), (u, T)
+            ok, ea, er = close(o1[b, h * G:(h + 1) * G], ref.out)
+            assert ok, (u, T, ea, er)
 
 
 def test_hier_one_launch_rescore_gives_the_same_result():
