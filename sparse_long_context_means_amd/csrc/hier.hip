@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     float* s_fkey = reinterpret_cast<float*>(lds + L::fkey);
     int32_t* s_fsz = reinterpret_cast<int32_t*>(lds + L::fsz);
     uint32_t* s_fmask = reinterpret_cast<uint32_t*>(lds + L::fmask);
-    int32_t* s_ccand = reinterpret_cast<int32_t*>(lds + L::spre);  // before the fine cut
+    int32_t* s_ccand = reinterpret_cast<int32_t*>(lds + L::spre);  // candidates' member starts, before the fine cut
     int32_t* s_spre = reinterpret_cast<int32_t*>(lds + L::spre);
     float(*s_lg)[G] = reinterpret_cast<float(*)[G]>(lds + L::lg);
     int(*hist)[256] = reinterpret_cast<int(*)[256]>(lds + L::hist);
@@ -304,6 +304,11 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     int csz_r[kCItems];
 #pragma unroll
     for (int j = 0; j < kCItems; ++j) csz_r[j] = csizes[min(tid + j * kHThreads, D - 1)];
+    // member ranges of the thread's coarse clusters in the cut's item order
+    // (items kCItems t .. kCItems t + kCItems - 1), in flight with the rows
+    int cof_r[kCItems + 1];
+#pragma unroll
+    for (int j = 0; j <= kCItems; ++j) cof_r[j] = coffs[min(tid * kCItems + j, D)];
     const int cs0 = (int)((int64_t)D * rep / R), cs1 = (int)((int64_t)D * (rep + 1) / R);
     const bool xchg = R > 1 && a.rescore != 1;
     auto crow = [&](int i) { return ck + (size_t)i * kHeadDim; };
@@ -367,10 +372,8 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     // counts (prefix), and the fine candidate count F
     int nmem = 0;
 #pragma unroll
-    for (int j = 0; j < kCItems; ++j) {
-        const int i = tid * kCItems + j;
-        if ((cbits >> j) & 1u) nmem += coffs[i + 1] - coffs[i];
-    }
+    for (int j = 0; j < kCItems; ++j)
+        if ((cbits >> j) & 1u) nmem += cof_r[j + 1] - cof_r[j];
     {
         // kCItems <= 32: one word of flags per thread (bits of consecutive items)
         static_assert(kCItems <= 32 && 32 % kCItems == 0, "flag packing");
@@ -388,11 +391,10 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         int k = k0;
 #pragma unroll
         for (int j = 0; j < kCItems; ++j) {
-            const int i = tid * kCItems + j;
             if ((cbits >> j) & 1u) {
-                s_ccand[k] = i;
+                s_ccand[k] = cof_r[j];
                 s_cpre[k] = m0;
-                m0 += coffs[i + 1] - coffs[i];
+                m0 += cof_r[j + 1] - cof_r[j];
                 ++k;
             }
         }
@@ -407,8 +409,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     lds_barrier();
     for (int p = tid; p < F; p += kHThreads) {
         const int k = upper_index(s_cpre, ncand, p);
-        const int c = s_ccand[k];
-        const int f = cmem[coffs[c] + p - s_cpre[k]];
+        const int f = cmem[s_ccand[k] + p - s_cpre[k]];
         s_fid[p] = f;
         s_fsz[p] = fsizes[f];
     }
