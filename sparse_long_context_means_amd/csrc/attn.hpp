@@ -562,7 +562,10 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     lds_barrier();
     if (tid == 0) {
         uint64_t* cnt = xcount;
-        uint64_t old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // first guess: all the others are in (then the exchange succeeds at
+        // once and the merging replica, the one on the critical path, spends
+        // a single round trip); a failed exchange returns the word as it is
+        uint64_t old = tagw | (uint32_t)(R - 1);
         uint32_t arrived;
         for (;;) {
             arrived = ((uint32_t)(old >> 32) == tag ? (uint32_t)old : 0u) + 1u;
