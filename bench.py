@@ -42,23 +42,23 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
 UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
     "stored": {
-        "sources_sha256": "e19b73f55844ffbc827ffc582db5401e0a2d6f18d3bdeff443bef4a09b65a684",
-        "fetch_bytes": int(122781.90 * 2.0 * 1024),
-        "write_bytes": int(5003.52 * 1.0 * 1024),
+        "sources_sha256": "00167dfe3867a0a5be795f09f95b8c655320532b89cafe789c79f102175f30b3",
+        "fetch_bytes": int(122781.22 * 2.0 * 1024),
+        "write_bytes": int(5014.24 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "e19b73f55844ffbc827ffc582db5401e0a2d6f18d3bdeff443bef4a09b65a684",
-        "fetch_bytes": int(90107.95 * 2.0 * 1024),
-        "write_bytes": int(5003.43 * 1.0 * 1024),
+        "sources_sha256": "00167dfe3867a0a5be795f09f95b8c655320532b89cafe789c79f102175f30b3",
+        "fetch_bytes": int(90105.32 * 2.0 * 1024),
+        "write_bytes": int(5014.93 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
 }
 HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
-    "sources_sha256": "5d3ba480db50b7bfda78cc5999abbcc1f151f6afcb49ef323d80570aee74d608",
+    "sources_sha256": "37a745f763d39faa642b38dfb97907c26931599aaafd22cc68a505ec51e503d4",
     "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
-    "fetch_bytes": int(18111.49 * 2.0 * 1024),
-    "write_bytes": int(3482.15 * 1.0 * 1024),
+    "fetch_bytes": int(18098.56 * 2.0 * 1024),
+    "write_bytes": int(3494.59 * 1.0 * 1024),
     "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
