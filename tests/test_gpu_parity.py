@@ -762,6 +762,39 @@ def test_hier_one_launch_zero_queries_take_clusters_in_id_order():
             assert ok, (u, T, ea, er)
 
 
+def test_hier_one_launch_outlier_keys_match_six_launches():
+    """64 tokens far along one direction that the queries share give one
+    coarse and a few fine clusters keys in the thousands: the rest of each
+    level then shares one value bin, so both cuts of the one-launch kernel
+    take their exact radix passes over a crowded bin (192 coarse clusters,
+    about 270 fine candidates per unit).  Decisions must equal the six
+    launches' radix cuts."""
+    mp = M()
+    B, Hq, Hkv, N = 2, 16, 8, 24576
+    w = small_workload(B, Hq, Hkv, N, N // 16, outliers=4, index=95)
+    K, V, means = workloads.make_cache(w)
+    v = torch.randn(128, generator=torch.Generator().manual_seed(5))
+    v = v / v.norm()
+    K[:, :, :64] = (20000.0 * v).to(K.dtype)
+    q = (queries(w, means, 7).float() + 3.0 * v).to(torch.bfloat16)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, cluster_block=8192, build_iters=3,
+                  coarse_tokens_per_centroid=128, coarse_candidate_tokens=4096, seed=7)
+    assert p.decode_stages() == ["hier_unit"]
+    ps = dataclasses.replace(p, splits=4)
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, N, state)
+    assert state.n_coarse > 128
+    for T in (100, 700):
+        d1, d6 = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+        o1 = mp.decode(p, q.to(DEV), Kd, Vd, N, state, T, debug=d1).cpu().numpy()
+        o6 = mp.decode(ps, q.to(DEV), Kd, Vd, N, state, T, debug=d6).cpu().numpy()
+        assert torch.equal(d1.candidates.cpu(), d6.candidates.cpu()), T
+        assert torch.equal(d1.selected.cpu(), d6.selected.cpu()), T
+        assert torch.equal(d1.exact_tokens.cpu(), d6.exact_tokens.cpu()), T
+        np.testing.assert_allclose(o1, o6, rtol=1e-4, atol=1e-5)
+
+
 def test_hier_one_launch_rescore_gives_the_same_result():
     """The workgroups of a unit score a share of the coarse clusters each and
     exchange the keys; scoring all of them locally (rescore 1) or falling back
