@@ -235,7 +235,9 @@ mpattn_status mpattn_update_window(const mpattn_params* params, const void* k, c
  * exact_tokens, [B][Hq][C] scores).  The hierarchical method (coarse level present) first
  * selects coarse candidates under coarse_candidate_tokens, then selects fine
  * clusters inside them; unselected fine clusters of candidates and all
- * non-candidate coarse clusters give the approximate terms.
+ * non-candidate coarse clusters give the approximate terms.  Both cuts break
+ * equal keys by the lower cluster id (coarse id, then fine id), whatever
+ * order the candidates' fine clusters are listed in.
  *   q   : device [B][Hq][d] dtype.      k, v: device K, V (tail rows, and all
  *   exact rows when the state has no sorted copy).   out: device [B][Hq][d] fp32.
  *   token_budget >= 0 tokens per unit.
