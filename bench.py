@@ -55,10 +55,10 @@ UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
     },
 }
 HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
-    "sources_sha256": "37a745f763d39faa642b38dfb97907c26931599aaafd22cc68a505ec51e503d4",
+    "sources_sha256": "ed726fbb3793bd4f512cf18626a6c30bd169731e98b94a9b6f8e221774e23f06",
     "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
-    "fetch_bytes": int(18098.56 * 2.0 * 1024),
-    "write_bytes": int(3494.59 * 1.0 * 1024),
+    "fetch_bytes": int(16755.88 * 2.0 * 1024),
+    "write_bytes": int(1807.69 * 1.0 * 1024),
     "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16

@@ -7,7 +7,10 @@
 // terms for the rest).
 //
 // Every workgroup of a unit takes the same two cuts with the same operations:
-//   1. scores of all coarse clusters on the matrix cores; the group-mean key;
+//   1. keys of all coarse clusters: it scores its share on the matrix cores
+//      and takes the other shares' keys from the other workgroups as tagged
+//      64-bit words (or scores them itself when a partner is late: the same
+//      bits); the key is the group mean;
 //   2. the coarse cut under the candidate budget (candidates);
 //   3. the candidates' non-empty fine clusters, listed by coarse id, then in
 //      member order;
@@ -21,8 +24,6 @@
 //      by the unclustered tail;
 //   7. the partials of the workgroups are merged by the last one to finish,
 //      through tagged 64-bit words as in unit.hip.
-// The coarse scoring is repeated in every workgroup of a unit (the
-// workgroups of a unit share an XCD, so the repeats read from its L2).
 #include <math.h>
 
 #include "attn.hpp"
@@ -34,7 +35,7 @@ namespace mpa {
 constexpr int kHThreads = 512;
 constexpr int kHWaves = kHThreads / kWave;  // 8
 constexpr int kHRowBatch = 1024;            // staged exact rows per pass
-constexpr int kHScoreDepth = 4;             // score steps in flight per wave
+constexpr int kHScoreDepth = 2;             // score steps in flight per wave (4 measured slower)
 constexpr int kHExactDepth = 2;             // exact-row steps (16 rows) in flight per wave
 // Waits on the other workgroups of a unit, in ticks of the 100 MHz constant
 // clock: for their coarse keys (then the workgroup scores them itself) and
@@ -605,8 +606,12 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                             kHPartialWaitTicks);
 }
 
+// Workgroups per unit: enough for about 128 workgroups in all, at least 3.
+// Each phase is short and latency-bound, so fewer partners to exchange keys
+// and partials with beat filling every CU (4 per unit at 32 units measured
+// 3 us faster than 8).
 int hier_replicas(int units) {
-    constexpr int kWorkgroups = 256;
+    constexpr int kWorkgroups = 128;
     int r = kHierMinReplicas;
     while (units * r < kWorkgroups && r < kHierMaxReplicas) ++r;
     return r;
