@@ -42,13 +42,13 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
 UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
     "stored": {
-        "sources_sha256": "00167dfe3867a0a5be795f09f95b8c655320532b89cafe789c79f102175f30b3",
+        "sources_sha256": "cc7bca4410d6c9ef705ba529aab0b8c946df39ddbd0f2090ce262c91b94ef5ad",
         "fetch_bytes": int(122781.22 * 2.0 * 1024),
         "write_bytes": int(5014.24 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "00167dfe3867a0a5be795f09f95b8c655320532b89cafe789c79f102175f30b3",
+        "sources_sha256": "cc7bca4410d6c9ef705ba529aab0b8c946df39ddbd0f2090ce262c91b94ef5ad",
         "fetch_bytes": int(90105.32 * 2.0 * 1024),
         "write_bytes": int(5014.93 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",

@@ -268,7 +268,6 @@ struct Rows4 {
 template <typename T, int G, int kUnitMaxC, int kUnitShare, bool F8>
 __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     constexpr int kUnitRecItems = kUnitMaxC / kUnitThreads;        // cluster records per thread
-    constexpr int kUnitSharePerWave = kUnitShare / kUnitWaves;     // approximate-term clusters per wave
     using L = UnitLds<G, kUnitMaxC, kUnitShare>;
     __shared__ __align__(16) char lds[L::bytes];
     float* s_key = reinterpret_cast<float*>(lds + L::key);
