@@ -257,8 +257,31 @@ def main():
     log(f"[bench] cold {cold_us:.1f} us/step  warm {warm_us:.1f} us/step  "
         f"stages(us) " + " ".join(f"{n}={stage_ms[:, k].mean() * 1e3:.1f}" for k, n in enumerate(stage_names)))
 
+    # every timed step must have completed normally: the workspace counters of
+    # the one-launch decode (key-exchange fallbacks, outputs poisoned because a
+    # partial did not arrive) and a finite output
+    fallbacks, poisoned = M.decode_status(ws)
+    finite = bool(torch.isfinite(out).all())
+    if poisoned or not finite:
+        raise RuntimeError(f"decode failed: {poisoned} poisoned outputs, finite output {finite}")
+    status = {"key_exchange_fallbacks": fallbacks, "poisoned_outputs": poisoned, "output_finite": finite}
+
+    # ---- memory: what the method keeps beside the KV cache -------------------
+    Cm = state.capacity_clusters
+    kv_bytes = 2 * U * N * d * 2
+    memory = {
+        "kv_cache_bytes": kv_bytes,
+        "centroids_read_by_decode_bytes": 2 * U * Cm * d * 2 + U * Cm * 4 * 2,   # Kbar, Vbar, sizes, offsets
+        "cluster_state_bytes": U * Cm * d * (2 + 2 + 4) + U * (2 * Cm + 1) * 4 + 2 * U * N * 4,
+        "sorted_copy_bytes": 0 if args.gather else kv_bytes,
+    }
+    for k in ("centroids_read_by_decode_bytes", "cluster_state_bytes", "sorted_copy_bytes"):
+        memory[k.replace("_bytes", "_frac_of_kv")] = round(memory[k] / kv_bytes, 4)
+    log(f"[bench] memory beside the KV cache: centroids {memory['centroids_read_by_decode_frac_of_kv']:.3f}, "
+        f"whole cluster state {memory['cluster_state_frac_of_kv']:.3f}, sorted copy {memory['sorted_copy_frac_of_kv']:.3f}")
+
     # ---- dense split-K decode of the same step (the pages' comparison point) --
-    dense = fp8 = None
+    dense = fp8 = gather = None
     if not args.no_rows and args.centroids == "stored":
         dws = torch.empty(int(M.lib.mpattn_workspace_bytes(ctypes.byref(cp), 1, 0, M.OP_DENSE)), dtype=torch.uint8,
                           device=dev)
@@ -307,6 +330,23 @@ def main():
         log(f"[bench] fp8 centroids {f8_us:.1f} us/step ({fp8['roofline']['achieved']:.0f} GB/s algorithmic)")
         del state8
         del dws
+        if not args.gather:
+            # the same clusters without the sorted copy: exact rows gathered
+            # from K, V through the token ids (no duplicate of the cache)
+            stg = M.ClusterState(p, dev, sorted_copy=False)
+            M.build_clusters(p, Kd, Vd, N, stg)
+            torch.cuda.synchronize()
+            wsg = M.Workspace().get(p, stg, dev)
+            g_us = _cold_decode_us(M, p, [qs[args.warmup + i] for i in range(min(40, args.steps))], Kd, Vd, N, stg, T,
+                                   wsg, evict)
+            g_bytes = float(byts.mean())
+            gather = {"us_per_step": round(g_us, 2), "algorithmic_MB": round(g_bytes / 1e6, 2),
+                      "roofline": {"bound": "hbm", "achieved": round(g_bytes / (g_us * 1e-6) / 1e9, 1),
+                                   "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(g_bytes / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+                      "extra_memory_bytes": 0, "sorted_copy_speedup": round(g_us / cold_us, 3)}
+            log(f"[bench] gathered exact rows (no sorted copy) {g_us:.1f} us/step")
+            del stg, wsg
 
     rows = None if args.no_rows else measure_rows(M, workloads, dev, evict)
 
@@ -340,11 +380,34 @@ def main():
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(one, jobs))
         cpu_s = time.perf_counter() - c0
-        cpu = {"value": cpu_s / args.cpu_steps * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+        # one host thread: the median of single full steps
+        one_thread = []
+        for i in range(min(3, args.cpu_steps)):
+            c1 = time.perf_counter()
+            for u in range(U):
+                one((i, u))
+            one_thread.append(time.perf_counter() - c1)
+        # clustering: one (unit, block) of the workload, every Lloyd round,
+        # on one thread; the build covers U units x nb blocks
+        Kb, Vb = O.f64(K[0, 0]), O.f64(V[0, 0])
+        st1 = O.empty_state(d, N, state.capacity_clusters, O.BF16)
+        c2 = time.perf_counter()
+        O.cluster_block(st1, Kb, Vb, 0, w.cluster_block, w.build_iters, w.tokens_per_centroid, 0, 0, 0)
+        blk_s = time.perf_counter() - c2
+        cpu = {"value": cpu_s / args.cpu_steps * 1e6, "unit": "us/step", "cores": threads,
+               "host_cpu_count": os.cpu_count(), "kind": "oracle",
                "sample": f"{args.cpu_steps} full decode steps ({U} units each) of the same workload, fp64 oracle, "
-                         f"one host thread per unit",
+                         f"units spread over {threads} host threads",
+               "one_thread_us_per_step_median": round(float(np.median(one_thread)) * 1e6, 1),
+               "one_thread_sample": f"{len(one_thread)} full decode steps, one host thread",
+               "build_one_unit_block_s": round(blk_s, 3),
+               "build_extrapolated_s": {"one_thread": round(blk_s * U * nb, 1),
+                                        f"{threads}_threads": round(blk_s * U * nb / threads, 2),
+                                        "basis": f"one (unit, block) of {w.cluster_block} tokens, {w.build_iters} "
+                                                 f"rounds, timed; x {U * nb} (unit, block) pairs"},
                "cpu_model": _cpu_model()}
-        log(f"[bench] oracle {cpu['value'] / 1e3:.1f} ms/step on {threads} threads")
+        log(f"[bench] oracle {cpu['value'] / 1e3:.1f} ms/step on {threads} threads, "
+            f"{cpu['one_thread_us_per_step_median'] / 1e3:.1f} ms/step on one; one (unit, block) build {blk_s:.2f} s")
 
     res = {
         "metric": "decode attn µs/step + effective HBM GB/s, 32K ctx, bs16, 95% sparsity",
@@ -383,6 +446,9 @@ def main():
                      "algorithmic_MB_per_launch": round(float(att_bytes.mean()) / 1e6, 2),
                      "avg_launch_us": round(float(att_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
+        "decode_status": status,
+        "memory": memory,
+        "gather_exact_rows": gather,
         "dense_reference": dense,
         "fp8_centroids": fp8,
         "rows": rows,
@@ -463,6 +529,32 @@ def measure_rows(M, workloads, dev, evict):
     import torch
     rows = {}
     d = 128
+    # ---- the small workloads: the tiny fp32 case and the batch-1 layer -------
+    for name in ("tiny-fp32", "qwen3-8b-layer-b1-32k"):
+        w = workloads.WORKLOADS[name]
+        K, V, means = workloads.make_cache(w)
+        Kd, Vd = K.to(dev), V.to(dev)
+        p = _params_for(M, w)
+        st = M.ClusterState(p, dev)
+        M.build_clusters(p, Kd, Vd, w.n_tokens, st)
+        ws = M.Workspace().get(p, st, dev)
+        qs = [workloads.make_queries(w, means, s).to(dev) for s in range(12)]
+        C, U = st.n_clusters, p.units
+        esz = 2 if w.dtype == torch.bfloat16 else 4
+        for T in w.budgets:
+            dbg = M.DecodeDebug.allocate(p, st, dev)
+            M.decode(p, qs[0], Kd, Vd, w.n_tokens, st, T, workspace=ws, debug=dbg)
+            E = int(dbg.exact_tokens.sum())
+            byts = p.batch * p.n_q_heads * d * (esz + 4) + U * C * (2 * d * esz + 4) + E * (2 * d * esz + 4)
+            us = _cold_decode_us(M, p, qs[2:], Kd, Vd, w.n_tokens, st, T, ws, evict)
+            rows[f"{name}_T{T}"] = {
+                "workload": name, "token_budget": T, "dtype": "f32" if esz == 4 else "bf16",
+                "decode_stages": p.decode_stages(), "us_per_step": round(us, 2), "algorithmic_MB": round(byts / 1e6, 3),
+                "roofline": {"bound": "hbm", "achieved": round(byts / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                             "unit": "GB/s", "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+            log(f"[bench] {name} T={T}: {us:.1f} us/step ({byts / 1e6:.2f} MB)")
+        del K, V, Kd, Vd, st, ws
+    torch.cuda.empty_cache()
     # ---- online update (H3) and decode with a tail ----------------------------
     w = workloads.WORKLOADS["qwen3-8b-layer-b4-online"]
     K, V, means = workloads.make_cache(w)

@@ -21,8 +21,8 @@
  * Conventions shared by every entry point
  *   - Pointers marked "device" are HIP device addresses; all other pointers
  *     are host addresses.  Every buffer is allocated and owned by the caller;
- *     the library allocates nothing, keeps no global state and is re-entrant
- *     on distinct states and workspaces.
+ *     the library allocates nothing and is re-entrant on distinct states and
+ *     workspaces.
  *   - Layouts are dense and row-major.  K and V are [B][Hkv][capacity_tokens][d]
  *     (capacity_tokens rows per (sequence, KV head) "unit"), q is [B][Hq][d],
  *     out is [B][Hq][d] float32.  Query head hq belongs to KV head hq / G with
@@ -34,6 +34,8 @@
  *     nothing is enqueued and a negative status is returned.  A launch failure
  *     reported by the HIP runtime after enqueueing maps to MPATTN_ERR_HIP.
  *   - Results are deterministic: the same inputs give the same bits.
+ *   - The library keeps no global state: a decode's per-call tags live in
+ *     its workspace.
  */
 #ifndef MPATTN_H
 #define MPATTN_H
@@ -175,9 +177,17 @@ int32_t mpattn_max_coarse(const mpattn_params* params);
  * clusters (and `capacity_coarse` coarse clusters).  0 means no workspace.
  * Returns (size_t)-1 when the parameters are invalid.  Decodes that share a
  * workspace must not overlap in time.  A decode workspace must hold zeros
- * before its first decode and must not be written by anything else between
- * decodes (the workgroups of a unit exchange tagged words through it; a
- * decode leaves it valid for the next one). */
+ * before its first decode, and again before it serves other parameters or
+ * capacities, and must not be written by anything else between decodes: the
+ * workgroups of a unit exchange tagged words through it, and it keeps the tag
+ * of each unit's last decode (a decode leaves it valid for the next one).
+ * Its first 8 bytes are two uint32 counters that the one-launch decodes add
+ * to and never reset:
+ *   [0] workgroups that scored the other workgroups' clusters themselves
+ *       because those ranking keys had not arrived within a bounded wait
+ *       (the same bits result, later; debug rescore 2 forces this path);
+ *   [1] output values written as NaN because another workgroup's partial sum
+ *       had not arrived within a bounded wait (a failure to check for). */
 size_t mpattn_workspace_bytes(const mpattn_params* params, int32_t capacity_clusters, int32_t capacity_coarse,
                               int32_t op);
 

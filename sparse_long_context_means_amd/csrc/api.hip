@@ -5,8 +5,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "../../include/mpattn.h"
 #include "kernels.hpp"
 
@@ -22,6 +20,7 @@ constexpr int kMaxFinePerBlockHier = 2048;
 constexpr int kMaxCoarsePerBlock = 64;
 constexpr int kMaxDecodeClusters = 32768;  // selection bitmask held in LDS
 constexpr int kUnitPathMinUnits = 16;      // fewer units: the split launches
+constexpr size_t kStatusBytes = 8;         // two uint32 counters at the start of a decode workspace
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -85,15 +84,18 @@ bool hier_unit_path(const mpattn_params* p);
 
 // Decode workspace regions.
 struct DecodeWs {
+    uint32_t* status;     // [2] counters the one-launch decodes add to (first bytes of the workspace)
     // per-unit path with several replicas: exchange words (tag << 32 | value);
     // they rely on the workspace holding zeros before its first decode
     uint64_t* xch;        // [U][Rx][Cmax] keys
     uint64_t* xpart;      // [U][Rx][G][d + 2] partials
     uint64_t* xcount;     // [U] arrival words
+    uint32_t* xepoch;     // [U] tag of each unit's last decode
     int32_t Rx;           // most replicas a decode on this layout uses
     uint64_t* hch;        // hierarchy in one launch: [U][Rh][Dmax] coarse-key words
     uint64_t* hpart;      // [U][Rh][G][d + 2] partial words
     uint64_t* hcount;     // [U] arrival words
+    uint32_t* hepoch;     // [U]
     int32_t Rh;
     int32_t Rxh;          // the same when each query head is its own unit
     float* s;             // [U][Cmax][G] scores by cluster id
@@ -131,6 +133,7 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
         off += align_up(bytes);
         return ptr;
     };
+    w.status = (uint32_t*)take(kStatusBytes);
     if (unit_path(p)) {
         // sized for both unit layouts: one unit per KV head (G heads each),
         // or one per query head (per-head selection)
@@ -143,6 +146,7 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
             w.xch = (uint64_t*)take(words * Cmax * 8);
             w.xpart = (uint64_t*)take(parts * (kD + 2) * 8);
             w.xcount = (uint64_t*)take(U * G * 8);
+            w.xepoch = (uint32_t*)take(U * G * 4);
         }
     }
     if (hier_unit_path(p)) {
@@ -150,6 +154,7 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
         w.hch = (uint64_t*)take(U * w.Rh * (size_t)Dmax * 8);
         w.hpart = (uint64_t*)take(U * w.Rh * G * (kD + 2) * 8);
         w.hcount = (uint64_t*)take(U * 8);
+        w.hepoch = (uint32_t*)take(U * 4);
     }
     w.s = (float*)take(U * Cmax * G * 4);
     w.rs = (int4*)take(U * Cmax * 16);
@@ -172,22 +177,6 @@ DecodeWs layout_decode(const mpattn_params* p, int32_t Cmax, int32_t Dmax, char*
     }
     w.bytes = off;
     return w;
-}
-
-// Tag of one decode call: a bijective 32-bit mix (the MurmurHash3 finalizer)
-// of a per-process call counter, never zero, so no two calls of the last 2^32
-// share one and a zeroed word never matches.
-uint32_t next_tag() {
-    static std::atomic<uint32_t> counter{0};
-    for (;;) {
-        uint32_t h = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-        h ^= h >> 16;
-        h *= 0x85ebca6bu;
-        h ^= h >> 13;
-        h *= 0xc2b2ae35u;
-        h ^= h >> 16;
-        if (h != 0u) return h;
-    }
 }
 
 // Dense decode workspace: partials [U][G][S][2] and [U][G][S][d].
@@ -468,7 +457,8 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         a.xch = w.hch;
         a.xpart = w.hpart;
         a.xcount = w.hcount;
-        a.tag = next_tag();
+        a.xepoch = w.hepoch;
+        a.status = w.status;
         a.dbg_selected = debug ? debug->selected : nullptr;
         a.dbg_candidates = debug ? debug->candidates : nullptr;
         a.dbg_exact = debug ? debug->exact_tokens : nullptr;
@@ -514,7 +504,8 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
         a.xch = w.xch;
         a.xpart = w.xpart;
         a.xcount = w.xcount;
-        a.tag = next_tag();
+        a.xepoch = w.xepoch;
+        a.status = w.status;
         a.dbg_scores = debug ? debug->scores : nullptr;
         a.dbg_selected = debug ? debug->selected : nullptr;
         a.dbg_exact = debug ? debug->exact_tokens : nullptr;

@@ -469,12 +469,15 @@ __device__ __forceinline__ void lds_barrier() {
 // xp [R][G][d + 2] and counts itself in on the unit's arrival word *xcount
 // (compare-and-swap; a stale tag counts as zero).  The workgroup that arrives
 // last reads the others' partials -- waiting only for words already stored,
-// for at most wait_ticks of the 100 MHz constant clock -- and merges them in
-// workgroup order.  s_flag: one int of LDS.
+// for at most wait_ticks of the 100 MHz constant clock (a word given up on
+// is counted in status[1], status may be null) -- merges them in workgroup
+// order and stores the call's tag in the unit's *epoch.  s_flag: one int of
+// LDS.
 template <int G, int NW>
 __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][kHeadDim + 2], int* s_flag,
-                                            float* outu, uint64_t* xp, uint64_t* xcount, uint32_t tag, int R,
-                                            int rep, uint64_t wait_ticks) {
+                                            float* outu, uint64_t* xp, uint64_t* xcount, uint32_t tag,
+                                            uint32_t* epoch, uint32_t* status, int R, int rep,
+                                            uint64_t wait_ticks) {
     constexpr int kThreads = NW * kWave;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int rg = lane >> 4, li = lane & 15;
@@ -559,6 +562,26 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    // every thread reads the other replicas' words of its outputs now, beside
+    // the arrival count: the merging replica then usually finds them there
+    // after that one trip (the others drop them)
+    constexpr int kMaxR = 8;
+    uint64_t wm[kOut][kMaxR], wl[kOut][kMaxR], wa[kOut][kMaxR];
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+        const int e = tid + k * kThreads;
+        if (e >= G * kHeadDim) break;
+        const int g = e / kHeadDim, dd = e % kHeadDim;
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxR; ++r2) {
+            if (r2 < R && r2 != rep) {
+                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
+                wm[k][r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wl[k][r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wa[k][r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
     lds_barrier();
     if (tid == 0) {
         uint64_t* cnt = xcount;
@@ -579,8 +602,8 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     if (!*s_flag) return;
     const uint64_t t0 = wall_clock64();
     bool late = false;
-    // a partner word of this call (all of them are issued before the first
-    // is checked, so the reads take one round trip)
+    // a partner word of this call (polled again, for a bounded time, while it
+    // still carries another call's tag)
     auto fresh = [&](uint64_t v, const uint64_t* p) {
         while ((uint32_t)(v >> 32) != tag && !late) {
             if (wall_clock64() - t0 > wait_ticks) late = true;
@@ -589,22 +612,11 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
         }
         return (uint32_t)(v >> 32) == tag ? __uint_as_float((uint32_t)v) : NAN;
     };
-    constexpr int kMaxR = 8;
 #pragma unroll
     for (int k = 0; k < kOut; ++k) {
         const int e = tid + k * kThreads;
         if (e >= G * kHeadDim) break;
         const int g = e / kHeadDim, dd = e % kHeadDim;
-        uint64_t wm[kMaxR], wl[kMaxR], wa[kMaxR];
-#pragma unroll
-        for (int r2 = 0; r2 < kMaxR; ++r2) {
-            if (r2 < R && r2 != rep) {
-                const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                wm[r2] = __hip_atomic_load(pg + kHeadDim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wl[r2] = __hip_atomic_load(pg + kHeadDim + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wa[r2] = __hip_atomic_load(pg + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
         float pm[kMaxR], pl[kMaxR], pa[kMaxR];
         float M = -INFINITY;
 #pragma unroll
@@ -616,9 +628,9 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
                     pa[r2] = oA[k];
                 } else {
                     const uint64_t* pg = xp + (size_t)r2 * kPart + g * (kHeadDim + 2);
-                    pm[r2] = fresh(wm[r2], pg + kHeadDim);
-                    pl[r2] = fresh(wl[r2], pg + kHeadDim + 1);
-                    pa[r2] = fresh(wa[r2], pg + dd);
+                    pm[r2] = fresh(wm[k][r2], pg + kHeadDim);
+                    pl[r2] = fresh(wl[k][r2], pg + kHeadDim + 1);
+                    pa[r2] = fresh(wa[k][r2], pg + dd);
                 }
                 M = fmaxf(M, pm[r2]);
             }
@@ -634,10 +646,14 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
                 }
             }
         }
-        // a partial that never arrived (cannot happen once its replica has
-        // counted in) poisons the output instead of hanging
+        // a partial that has not arrived within the bounded wait poisons the
+        // output instead of hanging, and is counted in status[1]
         outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
+        if (late && status) __hip_atomic_fetch_add(status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // the merging replica is the last of the unit: every replica has read the
+    // unit's epoch, so the next decode may take the following tag
+    if (tid == 0) *epoch = tag;
 }
 
 template <typename T>

@@ -223,6 +223,10 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     const int rg = lane >> 4, li = lane & 15;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
     const int D = a.D, C = a.C;
+    // the call's tag of the unit's exchange words: one more than the tag of
+    // its last decode (0 is never a tag: a zeroed word matches no call)
+    uint32_t tag = a.xepoch[unit] + 1u;
+    if (tag == 0u) tag = 1u;
     const bf16_t* qg = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim;
     const bf16_t* ck = reinterpret_cast<const bf16_t*>(a.ckbar) + (size_t)unit * a.Dmax * kHeadDim;
     const bf16_t* fk = reinterpret_cast<const bf16_t*>(a.kbar) + (size_t)unit * a.Cmax * kHeadDim;
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     });
     lds_barrier();
     if (xchg) {
-        const uint64_t tagw = (uint64_t)a.tag << 32;
+        const uint64_t tagw = (uint64_t)tag << 32;
         uint64_t* xu = a.xch + (size_t)unit * R * a.Dmax;
         for (int i = cs0 + tid; i < cs1; i += kHThreads) {
             const uint64_t w = tagw | __float_as_uint(s_ckey[i]);
@@ -341,25 +345,39 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
             for (int q = 0; q < kCItems; ++q)  // unconditional (clamped): exact wait counts
                 w[q] = __hip_atomic_load(slot + min(tid + q * kHThreads, D - 1), __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
+            // stale words are read again in one batch per round (one trip to
+            // memory a round), for a bounded time
             const uint64_t t0 = wall_clock64();
+            for (;;) {
+                bool stale = false;
+#pragma unroll
+                for (int q = 0; q < kCItems; ++q) {
+                    const int i = tid + q * kHThreads;
+                    stale = stale || (i < D && (i < cs0 || i >= cs1) && (uint32_t)(w[q] >> 32) != tag);
+                }
+                if (!stale) break;
+                if (wall_clock64() - t0 > kHExchangeWaitTicks) {
+                    miss = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                for (int q = 0; q < kCItems; ++q) {
+                    const int i = tid + q * kHThreads;
+                    if (i < D && (i < cs0 || i >= cs1) && (uint32_t)(w[q] >> 32) != tag)
+                        w[q] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
 #pragma unroll
             for (int q = 0; q < kCItems; ++q) {
                 const int i = tid + q * kHThreads;
-                const bool need = i < D && (i < cs0 || i >= cs1);
-                while (need && !miss && (uint32_t)(w[q] >> 32) != a.tag) {
-                    if (wall_clock64() - t0 > kHExchangeWaitTicks) {
-                        miss = true;
-                    } else {
-                        __builtin_amdgcn_s_sleep(2);
-                        w[q] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-                if (need && (uint32_t)(w[q] >> 32) == a.tag) s_ckey[i] = __uint_as_float((uint32_t)w[q]);
+                if (i < D && (i < cs0 || i >= cs1) && (uint32_t)(w[q] >> 32) == tag) s_ckey[i] = __uint_as_float((uint32_t)w[q]);
             }
         }
         if (miss) s_misc[1] = 1;
         lds_barrier();
         if (s_misc[1]) {  // (uniform) score them here: keys only
+            if (tid == 0 && a.status) __hip_atomic_fetch_add(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             score_items(0, D, crow, csize, s_ckey, 0, 0, 0, []() {});
             lds_barrier();
         }
@@ -602,8 +620,8 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     // ---- 7. combine the workgroup's states; the last workgroup of the unit
     //      merges the partials and writes the output -------------------------
     finish_step<G, kHWaves>(st, s_red, s_misc, a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim,
-                            a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, a.tag, R, rep,
-                            kHPartialWaitTicks);
+                            a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, tag, a.xepoch + unit,
+                            a.status, R, rep, kHPartialWaitTicks);
 }
 
 // Workgroups per unit: enough for about 128 workgroups in all, at least 3.
@@ -624,7 +642,7 @@ bool hier_path_fits(int dtype, int G, int max_coarse, int cand_budget) {
 
 hipError_t launch_hier_decode(int dtype, int G, const HierArgs& a, int units, int replicas, hipStream_t st) {
     if (!hier_path_fits(dtype, G, a.D, a.cand_budget) || a.D > a.Dmax || replicas < kHierMinReplicas ||
-        replicas > kHierMaxReplicas || !a.out || !a.xch || !a.xpart || !a.xcount || a.tag == 0u)
+        replicas > kHierMaxReplicas || !a.out || !a.xch || !a.xpart || !a.xcount || !a.xepoch)
         return hipErrorInvalidValue;
     dim3 grid(units, replicas);
     switch (G) {

@@ -106,12 +106,14 @@ __device__ __forceinline__ int2 group_exclusive_sum2(int2 v, int2& tot, int* lds
 // scans the histogram and reaches the same digit); clusters above it are
 // selected, clusters equal to it in id order while they fit.  One group scan
 // places the selected clusters in id order: ids, first members, member-row
-// prefix (s_spre[nsel] = E), and nsel, E in out[0], out[1].
+// prefix (s_spre[nsel] = E), and nsel, E in out[0], out[1]; marks[0] and
+// marks[1] receive the number of selected clusters with an id below mark_lo
+// and mark_hi.
 template <int NW, int ITEMS>
 __device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_sz, const int32_t* s_off,
                                           const int32_t* s_rows, int C, int budget, int (*hist)[256], int* s_scan,
                                           int* ctr, int& gen, int32_t* s_sid, int32_t* s_soff, int32_t* s_spre,
-                                          int* out, int32_t* dbg_sel) {
+                                          int* out, int32_t* dbg_sel, int mark_lo, int mark_hi, int* marks) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     uint32_t key[ITEMS];
     float kf[ITEMS];
@@ -207,6 +209,8 @@ __device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_s
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
         const int i = tid * ITEMS + j;
+        if (i == mark_lo) marks[0] = k;
+        if (i == mark_hi) marks[1] = k;
         if ((selbits >> j) & 1u) {
             s_sid[k] = i;
             s_soff[k] = s_off[i];
@@ -220,6 +224,7 @@ __device__ __forceinline__ void group_cut(const float* s_key, const int32_t* s_s
         s_spre[tot.x] = tot.y;
         out[0] = tot.x;
         out[1] = tot.y;
+        if (mark_hi >= NW * kWave * ITEMS) marks[1] = tot.x;
     }
 }
 
@@ -251,6 +256,9 @@ struct UnitLds {
 constexpr int kScoreDepth = 4;                           // score steps in flight per wave
 constexpr int kPseudoDepth = 2;                          // value-centroid steps in flight per wave
 constexpr int kExactDepth = 2;                           // exact-row steps (16 rows) in flight per wave
+// sixteenths of the first batch of exact rows that waves 0-3 take (they
+// start on it while waves 4-7 finish the approximate term)
+constexpr int kFirstBatchEarly = 10;
 // Waits on the other replicas of a unit, in ticks of the 100 MHz constant
 // clock: for their keys (then the workgroup scores them itself) and for the
 // partial words of replicas that have already counted in.
@@ -294,6 +302,13 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     const int rg = lane >> 4, li = lane & 15;
     const int C = a.C;
     const int b = unit / a.Hkv, h = unit % a.Hkv;
+    // the call's tag of the unit's exchange words: one more than the tag of
+    // its last decode (0 is never a tag: a zeroed word matches no call)
+    uint32_t tag = 0;
+    if (R > 1) {
+        tag = a.xepoch[unit] + 1u;
+        if (tag == 0u) tag = 1u;
+    }
     const int su = unit / a.ugroup;  // the unit's clusters and cache (shared by a group when per head)
     const int32_t* szu = a.sizes + (size_t)su * a.Cmax;
     const int32_t* ofu = a.offsets + (size_t)su * (a.Cmax + 1);
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
         for (int j = 0; j < kScoreDepth; ++j) {
             const int i = base(j) + li;
-            kload(ring[j], i < hi ? i : 0);
+            kload(ring[j], i < hi ? i : hi - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (first) {
@@ -394,8 +409,11 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                         }
                     }
                 }
+                // past the end: every lane reads the share's last row, which
+                // the last real step loads (one cached row, not a trip to
+                // HBM that the end of the pass would wait for)
                 const int i = base(it + j + kScoreDepth) + li;
-                kload(ring[j], i < hi ? i : 0);
+                kload(ring[j], i < hi ? i : hi - 1);
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
@@ -472,7 +490,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     //      missing after kExchangeWaitTicks (a replica not yet running) makes
     //      waves 0-3 score every cluster themselves with the same operations,
     //      which gives the same keys. ------------------------------------------
-    const uint64_t tagw = (uint64_t)a.tag << 32;
+    const uint64_t tagw = (uint64_t)tag << 32;
     uint64_t* xu = a.xch + (size_t)unit * R * a.Cmax;
     if (R > 1 && !a.rescore) {
         for (int i = cs + tid; i < ce; i += kUnitThreads) {
@@ -491,11 +509,42 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     }
     int* gctr = s_misc + 5;  // group barrier counters: waves 0-3, waves 4-7
     int* sctr = s_misc + 4;
+    int* rflag = s_misc + 3;  // set once waves 0-3 have staged the first batch of exact rows
     if (tid == 0) {
         *gctr = 0;
         *sctr = 0;
+        *rflag = 0;
     }
     lds_barrier();
+    // exact rows of the replica: the selected clusters' members [0, E), then
+    // the unclustered tail [E, E + Tn); this replica takes [e0, e1) of them,
+    // in batches of kUnitRowBatch staged in s_row (a member position, or -1 -
+    // token for a tail row, read from K, V)
+    const int Tn = a.n_total - a.n_clustered;
+    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)su * a.Nmax : nullptr;
+    // threads t0, t0 + nt, ... take the selected clusters in turn and write
+    // the positions of their members that fall in the batch (no search: a
+    // cluster's rows are [pre[k], pre[k + 1]) at first member off[k]), then
+    // the tail rows of the batch
+    auto stage = [&](int c0, int cnt, int nsel, int E, int t0, int nt) {
+        const int c1 = c0 + cnt;
+        for (int k = t0; k < nsel; k += nt) {
+            const int p0 = s_spre[k], p1 = s_spre[k + 1];
+            const int lo = max(p0, c0), hi = min(p1, c1);
+            const int off = s_soff[k] - p0;
+            if (tids) {
+                for (int r = lo; r < hi; ++r) s_row[r - c0] = tids[off + r];
+            } else {
+                for (int r = lo; r < hi; ++r) s_row[r - c0] = off + r;
+            }
+        }
+        for (int i = max(E - c0, 0) + t0; i < cnt; i += nt) s_row[i] = -1 - (a.n_clustered + c0 + i - E);
+    };
+    auto row_range = [&](int E, int& e0, int& e1) {
+        const int Et = E + Tn;
+        e0 = (int)((int64_t)Et * rep / R);
+        e1 = (int)((int64_t)Et * (rep + 1) / R);
+    };
 
     if (wave < kCutWaves) {
         // ---- waves 0-3: the other replicas' keys, then the budget cut -------
@@ -514,63 +563,69 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
                 for (int q = 0; q < kPoll; ++q) {
                     const int i = tid + q * kCutWaves * kWave;
-                    fresh = fresh && (!(i < C && (i < cs || i >= ce)) || (uint32_t)(w[q] >> 32) == a.tag);
+                    fresh = fresh && (!(i < C && (i < cs || i >= ce)) || (uint32_t)(w[q] >> 32) == tag);
                 }
                 if (!fresh) {  // a partner is behind: poll its words, for a bounded time
+                    // every stale word of the thread is read again in one
+                    // batch per round, so a round costs one trip to L2
                     const uint64_t t0 = wall_clock64();
+                    for (;;) {
+                        bool stale = false;
 #pragma unroll
-                    for (int q = 0; q < kPoll; ++q) {
-                        const int i = tid + q * kCutWaves * kWave;
-                        const bool need = i < C && (i < cs || i >= ce);
-                        while (need && !miss && (uint32_t)(w[q] >> 32) != a.tag) {
-                            if (wall_clock64() - t0 > kExchangeWaitTicks) {
-                                miss = true;
-                            } else {
-                                __builtin_amdgcn_s_sleep(2);
+                        for (int q = 0; q < kPoll; ++q) {
+                            const int i = tid + q * kCutWaves * kWave;
+                            stale = stale || (i < C && (i < cs || i >= ce) && (uint32_t)(w[q] >> 32) != tag);
+                        }
+                        if (!stale) break;
+                        if (wall_clock64() - t0 > kExchangeWaitTicks) {
+                            miss = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                        for (int q = 0; q < kPoll; ++q) {
+                            const int i = tid + q * kCutWaves * kWave;
+                            if (i < C && (i < cs || i >= ce) && (uint32_t)(w[q] >> 32) != tag)
                                 w[q] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            }
                         }
                     }
                 }
 #pragma unroll
                 for (int q = 0; q < kPoll; ++q) {
                     const int i = tid + q * kCutWaves * kWave;
-                    if (i < C && (i < cs || i >= ce) && (uint32_t)(w[q] >> 32) == a.tag)
+                    if (i < C && (i < cs || i >= ce) && (uint32_t)(w[q] >> 32) == tag)
                         s_key[i] = __uint_as_float((uint32_t)w[q]);
                 }
             }
             if (group_count<kCutWaves>(miss, s_scan + 32, gctr, gen) > 0) {
+                if (tid == 0 && a.status)
+                    __hip_atomic_fetch_add(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 score_pass(0, C, false, kCutWaves, wave);  // these four waves
             }
             group_barrier<kCutWaves>(gctr, gen);
         }
         group_cut<kCutWaves, kUnitMaxC / (kCutWaves * kWave)>(
             s_key, s_sz, s_off, s_rows, C, a.budget, hist, s_scan, gctr, gen, s_sid, s_soff, s_spre, s_misc + 6,
-            a.dbg_selected && rep == 0 ? a.dbg_selected + (size_t)unit * C : nullptr);
+            a.dbg_selected && rep == 0 ? a.dbg_selected + (size_t)unit * C : nullptr, cs, ce, s_misc + 1);
+        group_barrier<kCutWaves>(gctr, gen);  // the whole list is written
+        {
+            // the first batch of exact rows, staged while waves 4-7 still
+            // stream the approximate term; the flag lets them in after it
+            int e0, e1;
+            row_range(s_misc[7], e0, e1);
+            stage(e0, min(kUnitRowBatch, e1 - e0), s_misc[6], s_misc[7], tid, kCutWaves * kWave);
+            group_barrier<kCutWaves>(gctr, gen);
+            if (tid == 0) __hip_atomic_store(rflag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         if (a.pseudo) {
             // take the selected clusters of the share [cs, ce) (a contiguous
             // run of the ascending selected list) back out of the approximate
             // term, with the weights waves 4-7 computed (their first barrier)
-            group_barrier<kCutWaves>(gctr, gen);  // the whole list is written
             while (__hip_atomic_load(sctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kStreamWaves)
                 __builtin_amdgcn_s_sleep(1);
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-            const int nsel = s_misc[6];
-            int k_lo = 0, k_hi = nsel;
-            {
-                int lo = 0, hi = nsel;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_sid[mid] < cs) lo = mid + 1; else hi = mid;
-                }
-                k_lo = lo;
-                hi = nsel;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_sid[mid] < ce) lo = mid + 1; else hi = mid;
-                }
-                k_hi = lo;
-            }
+            // the share's run of the selected list, counted by the cut
+            const int k_lo = s_misc[1], k_hi = s_misc[2];
             // 16 row groups take kRemoveBatch rows each per pass, the loads
             // of a pass in flight together.  The first pass is only issued
             // here: its rows are taken out after the exact rows, so their
@@ -616,7 +671,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = cs + item(j, u);
-                vload(pring[j].r[u], c < ce ? c : cs);
+                vload(pring[j].r[u], c < ce ? c : ce - 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -664,34 +719,38 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
+                    // past the share: its last row, loaded by the last real
+                    // step (one cached row)
                     const int c = cs + item(it + j + kPseudoDepth, u);
-                    vload(pring[j].r[u], c < ce && it + j + kPseudoDepth < kSteps ? c : cs);
+                    vload(pring[j].r[u], c < ce && it + j + kPseudoDepth < kSteps ? c : ce - 1);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
     }
-    lds_barrier();
+    if (wave >= kCutWaves) {  // waves 4-7 join the exact rows once the first batch is staged
+        while (__hip_atomic_load(rflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
     const int nsel = s_misc[6], E = s_misc[7];
     if (tid == 0 && a.dbg_exact && rep == 0) a.dbg_exact[unit] = E;
 
-    // ---- exact rows of the replica's share, staged in batches, 16 rows per
-    //      wave step through a ring of kExactDepth steps (branch-free body:
-    //      exact wait counts; rows past the end load staged row 0 and are
-    //      masked).  The scores of a step come from the matrix cores (lane
-    //      (rg, li) receives rows 4 rg + e for head li); the wave keeps one
-    //      reference exponent per head, raised lazily as in SoftState; the
-    //      weights go through a per-wave LDS tile to the row groups, which
-    //      accumulate rows 4 rg + e of the step into their value sums.  The
-    //      rows are the selected clusters' members [0, E) followed by the
-    //      unclustered tail [E, E + Tn); a staged tail row holds -1 - token
-    //      and is read from K, V instead of the exact-row source. ------------
+    // ---- exact rows of the replica's share, 16 rows per wave step through a
+    //      ring of kExactDepth steps (branch-free body: exact wait counts; rows
+    //      past the wave's range re-load cached rows and are masked).  The
+    //      scores of a step come from the matrix cores (lane (rg, li)
+    //      receives rows 4 rg + e for head li); the wave keeps one reference
+    //      exponent per head, raised lazily as in SoftState; the weights go
+    //      through a per-wave LDS tile to the row groups, which accumulate
+    //      rows 4 rg + e of the step into their value sums.  The first batch
+    //      starts on waves 0-3 as soon as they have staged it, while waves 4-7
+    //      finish the approximate term, so waves 0-3 take the larger part of
+    //      it; later batches (more than kUnitRowBatch rows per replica) are
+    //      staged by all waves between workgroup barriers. -----------------
     const float qscale = kInvSqrtD * kLog2e;
     const size_t ubase = (size_t)su * a.Nmax * kHeadDim;
-    const int32_t* tids = a.token_ids ? a.token_ids + (size_t)su * a.Nmax : nullptr;
-    const int Tn = a.n_total - a.n_clustered;
-    const int Et = E + Tn;
-    const int e0 = (int)((int64_t)Et * rep / R), e1 = (int)((int64_t)Et * (rep + 1) / R);
+    int e0, e1;
+    row_range(E, e0, e1);
     {
         const bf16_t* Kx = reinterpret_cast<const bf16_t*>(a.Kx) + ubase;
         const bf16_t* Vx = reinterpret_cast<const bf16_t*>(a.Vx) + ubase + li * 8;
@@ -704,42 +763,19 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         float mv = exact16_enter<G>(st);
         float lp = 0.f;
         float* sp = s_p + wave * 16 * G;  // [16][G] weights of the step
-        for (int c0 = e0; c0 < e1; c0 += kUnitRowBatch) {
-            const int cnt = min(kUnitRowBatch, e1 - c0);
-            lds_barrier();  // the previous batch is consumed
-            for (int i = tid; i < cnt; i += kUnitThreads) {
-                const int r = c0 + i;
-                int v;
-                if (r < E) {  // member r - pre[k] of selected cluster k
-                    const int k = upper_index(s_spre, nsel, r);
-                    const int pos = s_soff[k] + r - s_spre[k];
-                    v = tids ? tids[pos] : pos;
-                } else {
-                    v = -1 - (a.n_clustered + r - E);
-                }
-                s_row[i] = v;
-            }
-            lds_barrier();
-            // 16-row blocks: the older waves 0-3 (first in issue order on
-            // their SIMDs, measured to finish their share ~25% sooner) take
-            // the first 9/16 of the blocks, waves 4-7 the rest; each half
-            // interleaves its blocks over its four waves
-            const int nb = (cnt + 15) / 16;
-            const int na = (nb * 9 + 8) / 16;
-            const int hb = wave < 4 ? 0 : na, hn = wave < 4 ? na : nb - na, hw = wave & 3;
-            auto blk = [&](int step) {
-                const int q = step * 4 + hw;
-                return q < hn ? hb + q : nb;  // nb: past the end, masked
-            };
+        // rows [w0, w1) of the staged batch, in order (the sums keep a fixed
+        // order); rows past w1 re-load row w1 - 1 (a cache hit) and weigh
+        // nothing
+        auto run_rows = [&](int w0, int w1) {
+            const int steps = (w1 - w0 + 15) / 16;
+            auto row_at = [&](int i) { return s_row[max(min(i, w1 - 1), 0)]; };
             auto load_step = [&](ExactRows16& rr, int step) {
-                const int ib = blk(step) * 16;
-                const int ik = ib + li;
-                const int rk = s_row[ik < cnt ? ik : 0];
+                const int ib = w0 + step * 16;
+                const int rk = row_at(ib + li);
                 load_row_blocks(rr.k, rk >= 0 ? Kx + (size_t)rk * kHeadDim : Kt + (size_t)(-1 - rk) * kHeadDim, lane);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int iv = ib + 4 * rg + e;
-                    const int rv = s_row[iv < cnt ? iv : 0];
+                    const int rv = row_at(ib + 4 * rg + e);
                     rr.v[e].load(rv >= 0 ? Vx + (size_t)rv * kHeadDim : Vt + (size_t)(-1 - rv) * kHeadDim);
                 }
             };
@@ -749,15 +785,43 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 load_step(ring[j], j);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const int steps = (hn + 3) / 4;  // per wave
             for (int it = 0; it < steps; it += kExactDepth) {
 #pragma unroll
                 for (int j = 0; j < kExactDepth; ++j) {
-                    exact16_step<G>(st, mv, lp, sp, qop, ring[j], blk(it + j) * 16 + 4 * rg, cnt, qscale);
+                    exact16_step<G>(st, mv, lp, sp, qop, ring[j], w0 + (it + j) * 16 + 4 * rg, w1, qscale);
                     load_step(ring[j], it + j + kExactDepth);
                     __builtin_amdgcn_sched_barrier(0);  // keep the ring order
                 }
             }
+        };
+        // wave's contiguous part of `part` rows starting at `base`, shared by
+        // the 4 waves of its half
+        auto quarter = [&](int base, int part, int& w0, int& w1) {
+            const int hw = wave & 3;
+            w0 = base + part * hw / 4;
+            w1 = base + part * (hw + 1) / 4;
+        };
+        {
+            const int cnt = min(kUnitRowBatch, e1 - e0);
+            const int na = (cnt * kFirstBatchEarly + 8) / 16;
+            int w0, w1;
+            if (wave < kCutWaves) quarter(0, na, w0, w1);
+            else quarter(na, cnt - na, w0, w1);
+            if (cnt > 0) run_rows(w0, w1);
+        }
+        for (int c0 = e0 + kUnitRowBatch; c0 < e1; c0 += kUnitRowBatch) {
+            const int cnt = min(kUnitRowBatch, e1 - c0);
+            lds_barrier();  // the previous batch is consumed
+            stage(c0, cnt, nsel, E, tid, kUnitThreads);
+            lds_barrier();
+            // waves 0-3, which issue first on their SIMDs and were measured
+            // to stream about a quarter faster than waves 4-7 beside them,
+            // share the first 9/16 of the rows
+            const int na = (cnt * 9 + 8) / 16;
+            int w0, w1;
+            if (wave < kCutWaves) quarter(0, na, w0, w1);
+            else quarter(na, cnt - na, w0, w1);
+            run_rows(w0, w1);
         }
         exact16_leave<G>(st, mv, lp);
     }
@@ -782,8 +846,8 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
     }
     finish_step<G, kUnitWaves>(st, s_red, s_misc, a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim,
-                               a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, a.tag, R, rep,
-                               kPartialWaitTicks);
+                               a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, tag,
+                               R > 1 ? a.xepoch + unit : nullptr, a.status, R, rep, kPartialWaitTicks);
 }
 
 // One replica per unit only once the units alone give a workgroup to every CU
@@ -821,7 +885,7 @@ static hipError_t unit_dispatch(int G, const UnitArgs& a, dim3 grid, hipStream_t
 
 hipError_t launch_unit_decode(int dtype, int G, const UnitArgs& a, int units, int replicas, hipStream_t st) {
     if (!unit_path_fits(dtype, G, a.C) || a.C > a.Cmax || replicas < 1 || a.ugroup < 1 ||
-        !a.out || (replicas > 1 && (!a.xch || !a.xpart || !a.xcount || a.tag == 0u)) ||
+        !a.out || (replicas > 1 && (!a.xch || !a.xpart || !a.xcount || !a.xepoch)) ||
         (a.kcodes && (!a.kscales || !a.vcodes || !a.vscales)))
         return hipErrorInvalidValue;
     dim3 grid(units, replicas);

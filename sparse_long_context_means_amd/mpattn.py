@@ -273,22 +273,37 @@ def update_window_concurrent(p: Params, k: torch.Tensor, v: torch.Tensor, n_toke
 
 
 class Workspace:
-    """A reusable device workspace sized by mpattn_workspace_bytes."""
+    """A reusable device workspace sized by mpattn_workspace_bytes, one per
+    (device, stream, workspace layout): a decode workspace keeps per-unit
+    call tags, so a buffer that served another layout is zeroed again."""
 
     def __init__(self):
-        self._buf: Dict[str, torch.Tensor] = {}
+        self._buf: Dict[tuple, torch.Tensor] = {}
 
-    def get(self, p: Params, state: ClusterState, device) -> torch.Tensor:
+    def get(self, p: Params, state: ClusterState, device, stream: Optional[int] = None) -> torch.Tensor:
         cp = p.c()
         n = lib.mpattn_workspace_bytes(ctypes.byref(cp), state.capacity_clusters, state.capacity_coarse, OP_DECODE)
         if n == ctypes.c_size_t(-1).value:
             raise MpattnError(ERR_INVALID_ARG, "mpattn_workspace_bytes")
-        key = str(device)
+        if stream is None:
+            stream = torch.cuda.current_stream(device).cuda_stream
+        layout = (p.batch, p.n_q_heads, p.n_kv_heads, p.capacity_tokens, p.tokens_per_centroid, p.cluster_block,
+                  p.coarse_tokens_per_centroid, p.coarse_candidate_tokens, p.splits, _DTYPES[p.dtype],
+                  state.capacity_clusters, state.capacity_coarse, n)
+        key = (str(device), int(stream), layout)
         buf = self._buf.get(key)
-        if buf is None or buf.numel() < max(n, 1):
-            buf = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # counters start at zero
+        if buf is None:
+            buf = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # tags and counters start at zero
             self._buf[key] = buf
         return buf
+
+
+def decode_status(workspace: torch.Tensor) -> Tuple[int, int]:
+    """The two counters at the start of a decode workspace (see
+    mpattn_workspace_bytes): (key-exchange fallbacks, output values poisoned
+    because a partial sum did not arrive in time).  Synchronises."""
+    v = workspace[:8].view(torch.int32).cpu()
+    return int(v[0]), int(v[1])
 
 
 _default_ws = Workspace()

@@ -144,3 +144,94 @@ def close(gpu, ref, atol=2e-3, rtol=1e-2):
     ok = bool(np.all(err <= atol + rtol * np.abs(ref)))
     rel = float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0
     return ok, float(err.max()) if err.size else 0.0, rel
+
+
+# ---------------------------------------------------------------------------
+# coarse level of the hierarchy (size-weighted Lloyd over each block's
+# non-empty fine key centroids), teacher forced
+# ---------------------------------------------------------------------------
+
+def _rne_bracket(lo, hi, storage):
+    """Storage values a correctly rounded result of any x in [lo, hi] can take."""
+    return O.round_storage(lo, storage), O.round_storage(hi, storage)
+
+
+def check_coarse_round(p, prev, cur, b, h, seed=0, from_init=False):
+    """One teacher-forced weighted Lloyd round of the coarse level of unit
+    (b, h), block by block.  `cur` holds the GPU state after k rounds; the
+    round starts from `prev` (the GPU state after k - 1 rounds) or, with
+    from_init, from the seeded init the oracle draws itself (cur after one
+    round).  Checks, against the oracle's steps on the GPU's fine state:
+    parents (nearest stored coarse centroid, ties to the lower id) outside
+    the fp32 tie window; weighted means (fp32 master within the rounding
+    bound of the fp64 size-weighted mean, stored copy = master rounded to
+    nearest even); coarse sizes, member lists and offsets exactly; coarse
+    value centroids within the bound of the size-weighted mean of the fine
+    value centroids.  Returns the number of tie-window assignment
+    differences."""
+    storage = storage_of(p.dtype)
+    unit = b * p.n_kv_heads + h
+    c = oracle_state_from_gpu(cur, b, h, p)
+    q = None if from_init else oracle_state_from_gpu(prev, b, h, p)
+    C = c.n_clusters
+    if q is not None:  # the fine level does not depend on the coarse rounds
+        np.testing.assert_array_equal(q.kbar[:C], c.kbar[:C])
+        np.testing.assert_array_equal(q.sizes[:C], c.sizes[:C])
+    dfull = -(-p.cluster_block // p.coarse_tokens_per_centroid)
+    n_diff, pos = 0, 0
+    want_members = np.zeros(C, np.int32)
+    for blk in c.blocks:
+        g0 = blk.index * dfull
+        ids = np.nonzero(c.sizes[blk.c0:blk.c0 + blk.C] > 0)[0].astype(np.int32) + blk.c0
+        m = len(ids)
+        D = min(-(-blk.L // p.coarse_tokens_per_centroid), m)
+        x, wts = c.kbar[ids], c.sizes[ids].astype(np.float64)
+        if from_init:
+            idx = O.init_indices(O.block_stream(seed, unit, blk.index, 1), m, D)
+            mu_prev = x[idx].copy()
+            mus_prev = x[idx].copy()
+        else:
+            mu_prev, mus_prev = q.cmu[g0:g0 + D], q.ckbar[g0:g0 + D]
+        a_ref, _, _ = O.assign_step(x, mus_prev)
+        a_gpu = c.parent[ids] - g0
+        assert np.all((a_gpu >= 0) & (a_gpu < D)), "parent outside the block's coarse clusters"
+        nd, bad = assign_tie_violations(x, mus_prev, a_gpu, a_ref)
+        assert not bad, f"unit {unit} block {blk.index}: {len(bad)} coarse assignments outside the tie window"
+        n_diff += nd
+        mu, _, counts = O.update_step(x, a_gpu, mu_prev, mus_prev, storage, w=wts)
+        live = counts > 0
+        gm = c.cmu[g0:g0 + D]
+        absmean = np.zeros_like(mu)
+        wsum = np.zeros(D)
+        np.add.at(absmean, a_gpu, wts[:, None] * np.abs(x))
+        np.add.at(wsum, a_gpu, wts)
+        absmean[live] /= wsum[live, None]
+        bound = gamma(counts[:, None] + 1) * absmean + U32 * np.abs(mu)
+        assert np.all(np.abs(gm - mu)[live] <= bound[live] + 1e-30), f"unit {unit} block {blk.index}: coarse means"
+        np.testing.assert_array_equal(c.ckbar[g0:g0 + D][live], O.round_storage(gm[live], storage))
+        # empty coarse clusters keep their centroid
+        np.testing.assert_array_equal(c.ckbar[g0:g0 + D][~live], mus_prev[~live])
+        # sizes, member lists (non-empty fine ids by coarse id, then fine id) and offsets
+        np.testing.assert_array_equal(c.csizes[g0:g0 + D], np.bincount(a_gpu, weights=wts, minlength=D).astype(np.int64))
+        for g in range(D):
+            mem = ids[a_gpu == g]
+            assert c.coffsets[g0 + g] == pos, f"unit {unit} block {blk.index}: offset of coarse cluster {g}"
+            want_members[pos:pos + len(mem)] = mem
+            pos += len(mem)
+        # value centroids: the size-weighted mean of the members' fine value
+        # centroids, rounded once to storage (the fp32 sum's rounding bound)
+        v = c.vbar[ids]
+        v64 = np.zeros((D, v.shape[1]))
+        vabs = np.zeros((D, v.shape[1]))
+        np.add.at(v64, a_gpu, wts[:, None] * v)
+        np.add.at(vabs, a_gpu, wts[:, None] * np.abs(v))
+        v64[live] /= wsum[live, None]
+        vabs[live] /= wsum[live, None]
+        vb = gamma(counts[:, None] + 1) * vabs + U32 * np.abs(v64)
+        lo, hi = _rne_bracket(v64 - vb, v64 + vb, storage)
+        gv = c.cvbar[g0:g0 + D]
+        assert np.all((gv[live] >= lo[live]) & (gv[live] <= hi[live])), f"unit {unit} block {blk.index}: coarse values"
+        assert np.all(gv[~live] == 0)
+    np.testing.assert_array_equal(c.cmembers[:pos], want_members[:pos])
+    assert c.coffsets[c.n_coarse] == pos
+    return n_diff

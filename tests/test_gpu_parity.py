@@ -16,8 +16,8 @@ import torch
 
 import oracle as O
 import workloads
-from gpu_util import (assign_tie_violations, close, gamma, load_oracle_states, oracle_state_from_gpu,
-                      rank_tolerance, selection_is_valid, storage_of, U32)
+from gpu_util import (assign_tie_violations, check_coarse_round, close, gamma, load_oracle_states,
+                      oracle_state_from_gpu, rank_tolerance, selection_is_valid, storage_of, U32)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -380,6 +380,47 @@ def test_unit_path_matches_split_path_and_oracle(mode):
             assert ok, (u, T, ea, er)
 
 
+def test_unit_path_exact_rows_in_several_batches():
+    """More exact rows per workgroup than one staged batch holds (the first
+    batch starts early on the cut waves, later batches are staged by all
+    waves): a budget of every clustered token with an unclustered tail is
+    dense attention over all tokens, and a partial budget matches the split
+    launches and the oracle."""
+    mp = M()
+    B, Hq, Hkv, n_cl, n_tot = 8, 16, 2, 10000, 12000
+    w = small_workload(B, Hq, Hkv, n_tot, 600, outliers=4, index=96)
+    K, V, means = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=n_tot, cluster_block=2048, build_iters=3,
+                  seed=9)
+    assert p.decode_stages() == ["unit"]
+    ps = dataclasses.replace(p, splits=4)
+    state = mp.ClusterState(p, DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    mp.build_clusters(p, Kd, Vd, n_cl, state)
+    G = p.group
+    q = queries(w, means, 41)
+    out = mp.decode(p, q.to(DEV), Kd, Vd, n_tot, state, n_cl).cpu().numpy()
+    for u in (0, 7, p.units - 1):
+        b, h = divmod(u, Hkv)
+        ok, ea, er = close(out[b, h * G:(h + 1) * G], O.dense(q[b, h * G:(h + 1) * G], K[b, h, :n_tot], V[b, h, :n_tot]))
+        assert ok, (u, ea, er)
+    T = 4000
+    d1, d4 = mp.DecodeDebug.allocate(p, state, DEV), mp.DecodeDebug.allocate(ps, state, DEV)
+    o1 = mp.decode(p, q.to(DEV), Kd, Vd, n_tot, state, T, debug=d1).cpu().numpy()
+    o4 = mp.decode(ps, q.to(DEV), Kd, Vd, n_tot, state, T, debug=d4).cpu().numpy()
+    assert torch.equal(d1.selected.cpu(), d4.selected.cpu())
+    np.testing.assert_allclose(o1, o4, rtol=1e-4, atol=1e-5)
+    sel = d1.selected.cpu().numpy()
+    for u in (1, 10):
+        b, h = divmod(u, Hkv)
+        st = oracle_state_from_gpu(state, b, h, p)
+        ref = O.decode_unit(q[b, h * G:(h + 1) * G], K[b, h], V[b, h], n_tot, st, T)
+        want = ref.out if np.array_equal(sel[b, h], ref.selected) else O.decode_with_selection(
+            q[b, h * G:(h + 1) * G], K[b, h], V[b, h], n_tot, st, sel[b, h])
+        ok, ea, er = close(o1[b, h * G:(h + 1) * G], want)
+        assert ok, (u, ea, er)
+
+
 def test_unit_path_over_2048_clusters_matches_split_path_and_oracle():
     """The one-launch decode at more than 2048 clusters per unit (the
     4096-cluster shape, four workgroups per unit at 64 units): same keys, cut
@@ -462,13 +503,21 @@ def test_unit_path_rescore_gives_the_same_result():
     for B, Hkv in ((16, 8), (8, 8)):
         mp, w, K, V, means, p, state = _built(B=B, Hq=4 * Hkv, Hkv=Hkv, N=3000, Bc=1024)
         assert p.decode_stages() == ["unit"]
+        ws = mp.Workspace().get(p, state, DEV)
         for step, T in enumerate((64, 700)):
             q = queries(w, means, 20 + step).to(DEV)
             outs, dbgs = [], []
             for rescore in (0, 1, 2, 0):
                 d = mp.DecodeDebug.allocate(p, state, DEV)
                 d.rescore = rescore
-                outs.append(mp.decode(p, q, K.to(DEV), V.to(DEV), 3000, state, T, debug=d).cpu())
+                before = mp.decode_status(ws)
+                outs.append(mp.decode(p, q, K.to(DEV), V.to(DEV), 3000, state, T, debug=d, workspace=ws).cpu())
+                after = mp.decode_status(ws)
+                # the workspace counters: every workgroup of the forced
+                # late-partner path counts one fallback; nothing is poisoned
+                assert after[1] == 0
+                if rescore == 2:
+                    assert after[0] - before[0] >= 2 * p.units
                 dbgs.append(d)
             for o, d in zip(outs[1:], dbgs[1:]):
                 assert torch.equal(o, outs[0]), (B, T)
@@ -728,6 +777,33 @@ def test_hier_one_launch_matches_six_launches_and_oracle(case):
             assert d1.exact_tokens.cpu().numpy()[b, h] == st.sizes[:C][sel[b, h].astype(bool)].sum()
 
 
+def test_hier_coarse_build_rounds_match_oracle():
+    """The GPU's coarse level on a hierarchical shape (4 blocks of 4096
+    tokens, 32 coarse clusters each), teacher forced on three units: the
+    last weighted round from the GPU's state one round earlier, the first
+    round from the oracle's seeded init (parents outside tie windows,
+    weighted means, exact sizes, member lists and offsets, size-weighted
+    value centroids)."""
+    mp = M()
+    B, Hq, Hkv, N = 4, 32, 8, 16384
+    w = small_workload(B, Hq, Hkv, N, N // 16, outliers=4, index=92)
+    K, V, _ = workloads.make_cache(w)
+    base = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, cluster_block=4096, build_iters=3,
+                coarse_tokens_per_centroid=128, coarse_candidate_tokens=2048, seed=3)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    states = {}
+    for it in (1, 9, 10):
+        p = mp.Params(coarse_iters=it, **base)
+        states[it] = mp.ClusterState(p, DEV, sorted_copy=False)
+        mp.build_clusters(p, Kd, Vd, N, states[it])
+    torch.cuda.synchronize()
+    p = states[10].params
+    for u in (0, 13, p.units - 1):
+        b, h = divmod(u, Hkv)
+        check_coarse_round(p, states[9], states[10], b, h, seed=3)
+        check_coarse_round(p, None, states[1], b, h, seed=3, from_init=True)
+
+
 def test_hier_one_launch_zero_queries_take_clusters_in_id_order():
     """Zero queries make every coarse and fine key exactly 0: both cuts of
     the one-launch kernel take their exact radix passes (a degenerate key
@@ -809,13 +885,19 @@ def test_hier_one_launch_rescore_gives_the_same_result():
     state = mp.ClusterState(p, DEV)
     Kd, Vd = K.to(DEV), V.to(DEV)
     mp.build_clusters(p, Kd, Vd, N, state)
+    ws = mp.Workspace().get(p, state, DEV)
     for step, T in enumerate((128, 900)):
         q = queries(w, means, 100 + step).to(DEV)
         outs, dbgs = [], []
         for rescore in (0, 1, 2, 0):
             d = mp.DecodeDebug.allocate(p, state, DEV)
             d.rescore = rescore
-            outs.append(mp.decode(p, q, Kd, Vd, N, state, T, debug=d).cpu())
+            before = mp.decode_status(ws)
+            outs.append(mp.decode(p, q, Kd, Vd, N, state, T, debug=d, workspace=ws).cpu())
+            after = mp.decode_status(ws)
+            assert after[1] == 0
+            if rescore == 2:
+                assert after[0] - before[0] >= 3 * p.units
             dbgs.append(d)
         for o, d in zip(outs[1:], dbgs[1:]):
             assert torch.equal(o, outs[0]), T

@@ -14,8 +14,8 @@ import torch
 
 import oracle as O
 import workloads
-from gpu_util import (assign_tie_violations, close, gamma, oracle_state_from_gpu, rank_tolerance,
-                      selection_is_valid, U32)
+from gpu_util import (assign_tie_violations, check_coarse_round, close, gamma, oracle_state_from_gpu,
+                      rank_tolerance, selection_is_valid, U32)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -231,15 +231,26 @@ def test_concurrent_update_leaves_the_old_state_usable():
     view, done, added = mp.update_window_concurrent(p, Kd, Vd, n_total, state, side)
     assert added == 1 and view.n_clustered == n_prompt and state.n_clustered == n_total
     ws = mp.Workspace().get(p, view, DEV)
-    outs = [mp.decode(p, q, Kd, Vd, n_total, view, T, workspace=ws).clone() for _ in range(12)]
+    dbg_view = mp.DecodeDebug.allocate(p, view, DEV)
+    outs = [mp.decode(p, q, Kd, Vd, n_total, view, T, workspace=ws, debug=dbg_view if i == 0 else None).clone()
+            for i in range(12)]
     overlapped = not done.query()  # the update was still running after the decodes were enqueued
     torch.cuda.current_stream().wait_event(done)
-    new = mp.decode(p, q, Kd, Vd, n_total, state, T, workspace=ws)
+    dbg_new = mp.DecodeDebug.allocate(p, state, DEV)
+    new = mp.decode(p, q, Kd, Vd, n_total, state, T, workspace=ws, debug=dbg_new)
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, before)
     assert torch.equal(new, after)
     print("update still running while the decodes were enqueued:", overlapped)
+    # the oracle on sampled units: during the update, the old clusters with
+    # the new block as an unclustered tail attended exactly; after it, the
+    # new block's clusters
+    sample = [0, 9, 18, 31]
+    qc = q.cpu()
+    check_decode_units(p, view, qc, K, V, n_total, T, outs[0].cpu().numpy(), dbg_view.selected.cpu().numpy(), sample)
+    assert view.n_clustered == n_prompt
+    check_decode_units(p, state, qc, K, V, n_total, T, new.cpu().numpy(), dbg_new.selected.cpu().numpy(), sample)
 
 
 def test_update_equals_build_on_gpu():
@@ -276,20 +287,21 @@ def test_hierarchical_128k_sampled():
     T, Tc = w.budgets[0], w.coarse_candidate_tokens
     rng = np.random.default_rng(1)
     sample = sorted(rng.choice(p.units, 4, replace=False).tolist())
+    # coarse level, teacher forced: the last weighted round from the GPU's
+    # state one round earlier, and the first round from the oracle's own
+    # seeded init, on every block of two sampled units
+    prev = mp.ClusterState(dataclasses.replace(p, coarse_iters=p.coarse_iters - 1), DEV, sorted_copy=False)
+    mp.build_clusters(prev.params, Kd, Vd, w.n_tokens, prev)
+    one = mp.ClusterState(dataclasses.replace(p, coarse_iters=1), DEV, sorted_copy=False)
+    mp.build_clusters(one.params, Kd, Vd, w.n_tokens, one)
+    torch.cuda.synchronize()
+    nd = 0
     for u in sample[:2]:
         b, h = divmod(u, p.n_kv_heads)
-        gst = oracle_state_from_gpu(state, b, h, p)
-        ref = oracle_state_from_gpu(state, b, h, p)
-        O.build_coarse(ref, coarse_tokens_per_centroid=128, iters=p.coarse_iters, seed=0, unit=u)
-        C, D = gst.n_clusters, gst.n_coarse
-        agree = np.mean(gst.parent[:C] == ref.parent[:C])
-        assert agree > 0.99, f"unit {u}: coarse parents agree on {agree:.4f}"
-        if agree == 1.0:
-            np.testing.assert_array_equal(gst.csizes[:D], ref.csizes[:D])
-            np.testing.assert_array_equal(gst.cmembers[:C], ref.cmembers[:C])
-            np.testing.assert_array_equal(gst.coffsets[:D + 1], ref.coffsets[:D + 1])
-            rel = np.abs(gst.ckbar[:D] - ref.ckbar[:D]) / np.maximum(np.abs(ref.ckbar[:D]), 1e-3)
-            assert np.mean(rel <= 2 ** -8) > 0.999
+        nd += check_coarse_round(p, prev, state, b, h)
+        nd += check_coarse_round(p, None, one, b, h, from_init=True)
+    print(f"coarse tie-window assignment differences: {nd}")
+    del prev, one
     for step in range(2):
         q = workloads.make_queries(w, means, step)
         dbg = mp.DecodeDebug.allocate(p, state, DEV)
