@@ -259,6 +259,32 @@ mpattn_status mpattn_decode(const mpattn_params* params, const void* q, const vo
                             int32_t mode, float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mpattn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same decode, with the library's own workspace -- a file-scope device
+ * array of mpattn_decode_noalloc_max_bytes() bytes that every GPU the library
+ * runs on holds until the process ends.  It allocates nothing.  The array is
+ * cleared on its first use on a device and whenever the decode layout
+ * (parameters and capacities) differs from the previous call's on that
+ * device; otherwise it keeps the previous call's contents (call tags, and
+ * the two counters described under mpattn_workspace_bytes, which this entry
+ * point gives no access to).  All calls on one GPU share the array: calls
+ * that overlap in time on one GPU race, so the caller serialises them (one
+ * stream, or events).
+ *   Arguments as mpattn_decode without the workspace.
+ * Errors: as mpattn_decode; MPATTN_ERR_WORKSPACE when the layout needs more
+ * than mpattn_decode_noalloc_max_bytes() (checked, with every other argument,
+ * before anything is enqueued); MPATTN_ERR_UNSUPPORTED for a device index of
+ * 64 or more.
+ */
+mpattn_status mpattn_decode_noalloc(const mpattn_params* params, const void* q, const void* k, const void* v,
+                                    int32_t n_tokens_total, const mpattn_state* state, int32_t token_budget,
+                                    int32_t mode, float* out, void* stream);
+
+/* Size of the device array mpattn_decode_noalloc uses as its workspace. */
+size_t mpattn_decode_noalloc_max_bytes(void);
+
+/*
  * Dense decode: exact attention of every query head over all tokens
  * [0, n_tokens) of its KV head, the comparison point of the sparse decode
  * (pages: atlas summary, "Key results": the speedups are quoted against a

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mpattn.h"
 #include "kernels.hpp"
 
@@ -267,6 +269,94 @@ bool hier_unit_path(const mpattn_params* p) {
     return hier_path_fits(p->dtype, G, mpattn_max_coarse(p), p->coarse_candidate_tokens);
 }
 
+// Every argument of a decode but the workspace.
+mpattn_status check_decode(const mpattn_params* p, const void* q, const void* k, const void* v,
+                           int32_t n_tokens_total, const mpattn_state* st, int32_t token_budget, int32_t mode,
+                           const float* out, int32_t first_stage, int32_t last_stage) {
+    mpattn_status rc = check_params(p);
+    if (rc != MPATTN_OK) return rc;
+    if (!q || !k || !v || !out) return MPATTN_ERR_INVALID_ARG;
+    if ((rc = check_state(p, st)) != MPATTN_OK) return rc;
+    if (st->n_clusters < 1 || st->n_clusters > st->capacity_clusters) return MPATTN_ERR_INVALID_ARG;
+    if (n_tokens_total < st->n_clustered || n_tokens_total > p->capacity_tokens) return MPATTN_ERR_INVALID_ARG;
+    if (token_budget < 0) return MPATTN_ERR_INVALID_ARG;
+    if (mode != MPATTN_MODE_MULTIPOLE && mode != MPATTN_MODE_OMIT && mode != MPATTN_MODE_PER_HEAD)
+        return MPATTN_ERR_INVALID_ARG;
+    const bool hier = is_hier(p);
+    if (hier && mode != MPATTN_MODE_MULTIPOLE) return MPATTN_ERR_UNSUPPORTED;
+    if ((mode == MPATTN_MODE_PER_HEAD || p->centroid_format == MPATTN_CENTROIDS_FP8) && !unit_path(p))
+        return MPATTN_ERR_UNSUPPORTED;
+    if (st->capacity_clusters > kMaxDecodeClusters || st->capacity_coarse > kMaxDecodeClusters)
+        return MPATTN_ERR_UNSUPPORTED;
+    if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
+    const int32_t n_stages = mpattn_decode_stage_count(p);
+    if (first_stage < 0 || last_stage >= n_stages || first_stage > last_stage) return MPATTN_ERR_INVALID_ARG;
+    return MPATTN_OK;
+}
+
+// ---- the decode entry point that allocates nothing: its workspace is this
+//      file-scope device array (each GPU the library runs on holds its own
+//      copy until the process ends).  In host code the array's name is only
+//      a stand-in: its device address comes from hipGetSymbolAddress, once per
+//      device, and only that address reaches kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchSlot {
+    void* ptr;        // device address of `scratch` on this device
+    uint64_t layout;  // layout of the decode that used it last
+    bool used;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kScratchDevices];
+
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// FNV-1a over the fields that fix the decode workspace layout.
+uint64_t layout_key(const mpattn_params* p, const mpattn_state* st) {
+    const int64_t f[] = {p->batch, p->n_q_heads, p->n_kv_heads, p->dtype, p->capacity_tokens, p->tokens_per_centroid,
+                         p->cluster_block, p->coarse_tokens_per_centroid, p->coarse_candidate_tokens, p->splits,
+                         p->centroid_format, st->capacity_clusters, st->capacity_coarse};
+    uint64_t h = 1469598103934665603ull;
+    for (int64_t x : f) {
+        for (int b = 0; b < 8; ++b) {
+            h ^= (uint64_t)((x >> (8 * b)) & 0xff);
+            h *= 1099511628211ull;
+        }
+    }
+    return h;
+}
+
+// The device address of this device's scratch array, cleared (with a fill
+// kernel on the caller's stream) on its first use and whenever the decode
+// layout differs from the last call's: the array then holds no tag of
+// another layout.
+mpattn_status scratch_for(const mpattn_params* p, const mpattn_state* st, void** out, hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MPATTN_ERR_HIP;
+    if (dev < 0 || dev >= kScratchDevices) return MPATTN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchSlot& slot = g_scratch[dev];
+    if (!slot.ptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MPATTN_ERR_HIP;
+        slot.ptr = ptr;
+    }
+    const uint64_t key = layout_key(p, st);
+    if (!slot.used || slot.layout != key) {
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, s, (uint4*)slot.ptr, kScratchBytes / 16);
+        if (hipGetLastError() != hipSuccess) return MPATTN_ERR_HIP;
+        slot.layout = key;
+        slot.used = true;
+    }
+    *out = slot.ptr;
+    return MPATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -385,24 +475,9 @@ mpattn_status mpattn_decode_ex(const mpattn_params* p, const void* q, const void
                                int32_t n_tokens_total, const mpattn_state* st, int32_t token_budget, int32_t mode,
                                float* out, void* workspace, size_t workspace_bytes, void* stream,
                                const mpattn_decode_debug* debug, int32_t first_stage, int32_t last_stage) {
-    mpattn_status rc = check_params(p);
+    mpattn_status rc = check_decode(p, q, k, v, n_tokens_total, st, token_budget, mode, out, first_stage, last_stage);
     if (rc != MPATTN_OK) return rc;
-    if (!q || !k || !v || !out) return MPATTN_ERR_INVALID_ARG;
-    if ((rc = check_state(p, st)) != MPATTN_OK) return rc;
-    if (st->n_clusters < 1 || st->n_clusters > st->capacity_clusters) return MPATTN_ERR_INVALID_ARG;
-    if (n_tokens_total < st->n_clustered || n_tokens_total > p->capacity_tokens) return MPATTN_ERR_INVALID_ARG;
-    if (token_budget < 0) return MPATTN_ERR_INVALID_ARG;
-    if (mode != MPATTN_MODE_MULTIPOLE && mode != MPATTN_MODE_OMIT && mode != MPATTN_MODE_PER_HEAD)
-        return MPATTN_ERR_INVALID_ARG;
     const bool hier = is_hier(p);
-    if (hier && mode != MPATTN_MODE_MULTIPOLE) return MPATTN_ERR_UNSUPPORTED;
-    if ((mode == MPATTN_MODE_PER_HEAD || p->centroid_format == MPATTN_CENTROIDS_FP8) && !unit_path(p))
-        return MPATTN_ERR_UNSUPPORTED;
-    if (st->capacity_clusters > kMaxDecodeClusters || st->capacity_coarse > kMaxDecodeClusters)
-        return MPATTN_ERR_UNSUPPORTED;
-    if (hier && (st->n_coarse < 1 || st->n_coarse > st->capacity_coarse)) return MPATTN_ERR_INVALID_ARG;
-    const int32_t n_stages = mpattn_decode_stage_count(p);
-    if (first_stage < 0 || last_stage >= n_stages || first_stage > last_stage) return MPATTN_ERR_INVALID_ARG;
     const DecodeWs need = layout_decode(p, st->capacity_clusters, st->capacity_coarse, nullptr);
     if (!workspace || workspace_bytes < need.bytes) return MPATTN_ERR_WORKSPACE;
     const DecodeWs w = layout_decode(p, st->capacity_clusters, st->capacity_coarse, (char*)workspace);
@@ -606,6 +681,24 @@ mpattn_status mpattn_decode(const mpattn_params* p, const void* q, const void* k
     return mpattn_decode_ex(p, q, k, v, n_tokens_total, st, token_budget, mode, out, workspace, workspace_bytes,
                             stream, nullptr, 0, n - 1);
 }
+
+mpattn_status mpattn_decode_noalloc(const mpattn_params* p, const void* q, const void* k, const void* v,
+                                    int32_t n_tokens_total, const mpattn_state* st, int32_t token_budget,
+                                    int32_t mode, float* out, void* stream) {
+    const int32_t n = mpattn_decode_stage_count(p);
+    if (n == 0) return check_params(p) == MPATTN_OK ? MPATTN_ERR_INVALID_ARG : check_params(p);
+    // everything is checked before the first enqueue (the scratch clear)
+    mpattn_status rc = check_decode(p, q, k, v, n_tokens_total, st, token_budget, mode, out, 0, n - 1);
+    if (rc != MPATTN_OK) return rc;
+    if (layout_decode(p, st->capacity_clusters, st->capacity_coarse, nullptr).bytes > kScratchBytes)
+        return MPATTN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((rc = scratch_for(p, st, &ws, (hipStream_t)stream)) != MPATTN_OK) return rc;
+    return mpattn_decode_ex(p, q, k, v, n_tokens_total, st, token_budget, mode, out, ws, kScratchBytes, stream,
+                            nullptr, 0, n - 1);
+}
+
+size_t mpattn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 mpattn_status mpattn_dense_decode(const mpattn_params* p, const void* q, const void* k, const void* v,
                                   int32_t n_tokens, float* out, void* workspace, size_t workspace_bytes,

@@ -86,6 +86,10 @@ def _load() -> ctypes.CDLL:
     lib.mpattn_dense_decode.argtypes = [P, _VP, _VP, _VP, i32, _VP, _VP, sz, _VP]
     lib.mpattn_read_probe.restype = ctypes.c_int
     lib.mpattn_read_probe.argtypes = [_VP, sz, _VP, _VP]
+    lib.mpattn_decode_noalloc.restype = ctypes.c_int
+    lib.mpattn_decode_noalloc.argtypes = [P, _VP, _VP, _VP, i32, S, i32, i32, _VP, _VP]
+    lib.mpattn_decode_noalloc_max_bytes.restype = sz
+    lib.mpattn_decode_noalloc_max_bytes.argtypes = []
     return lib
 
 
@@ -368,6 +372,23 @@ def decode(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_token
                               token_budget, mode, _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(q.device), ctypes.byref(dbg) if dbg is not None else None, first, last)
     _raise(st, "mpattn_decode")
+    return out
+
+
+def decode_noalloc(p: Params, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_tokens_total: int,
+                   state: ClusterState, token_budget: int, out: torch.Tensor, mode: int = MODE_MULTIPOLE) -> torch.Tensor:
+    """mpattn_decode_noalloc: the decode with the library's own device
+    workspace; `out` [B][Hq][d] float32 must be given (nothing is allocated)."""
+    _check_cache(p, k, v)
+    qshape = (p.batch, p.n_q_heads, p.head_dim)
+    if tuple(q.shape) != qshape or q.dtype != p.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError(f"q must be a contiguous {p.dtype} CUDA tensor of shape {qshape}")
+    if tuple(out.shape) != qshape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of shape [B][Hq][d]")
+    cp, cs = p.c(), state.c()
+    st = lib.mpattn_decode_noalloc(ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), n_tokens_total, ctypes.byref(cs),
+                                   token_budget, mode, _ptr(out), _stream(q.device))
+    _raise(st, "mpattn_decode_noalloc")
     return out
 
 

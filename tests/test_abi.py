@@ -207,6 +207,34 @@ def test_decode_validation():
     assert _decode(p, st, 4096, mode=M.MODE_PER_HEAD) == M.ERR_UNSUPPORTED
 
 
+def test_noalloc_decode_validation():
+    """The allocation-free decode checks every argument, and that the
+    layout fits its device array, before anything is enqueued (every case
+    below returns before the device is touched)."""
+    assert M.lib.mpattn_decode_noalloc_max_bytes() == 32 << 20
+    p = _params()
+    st = _fake_state(p, n_clustered=4096, n_clusters=256, n_blocks=1)
+    cp = p.c()
+    na = lambda n, budget=128, mode=0, q=FAKE, par=ctypes.byref(cp), s=st: M.lib.mpattn_decode_noalloc(
+        par, q, FAKE, FAKE, n, ctypes.byref(s), budget, mode, FAKE, None)
+    assert na(4096, budget=-1) == M.ERR_INVALID_ARG
+    assert na(4000) == M.ERR_INVALID_ARG
+    assert na(40000) == M.ERR_INVALID_ARG
+    assert na(4096, mode=7) == M.ERR_INVALID_ARG
+    assert na(4096, q=None) == M.ERR_INVALID_ARG
+    assert na(4096, par=None) == M.ERR_INVALID_ARG
+    assert na(0, s=_fake_state(p)) == M.ERR_INVALID_ARG
+    assert na(4096, mode=M.MODE_PER_HEAD) == M.ERR_UNSUPPORTED
+    # 512 units of 2053 clusters need more than the 32 MiB array
+    big = _params(batch=64, n_q_heads=32, n_kv_heads=8)
+    need = M.lib.mpattn_workspace_bytes(ctypes.byref(big.c()), big.max_clusters(), 0, M.OP_DECODE)
+    assert need > 32 << 20
+    sb = _fake_state(big, n_clustered=4096, n_clusters=256, n_blocks=1)
+    cb = big.c()
+    assert M.lib.mpattn_decode_noalloc(ctypes.byref(cb), FAKE, FAKE, FAKE, 4096, ctypes.byref(sb), 128, 0, FAKE,
+                                       None) == M.ERR_WORKSPACE
+
+
 def test_workspace_and_stages():
     p = _params()
     cp = p.c()
