@@ -162,8 +162,9 @@ typedef struct mpattn_decode_debug {
                                cases. */
 } mpattn_decode_debug;
 
-/* Human-readable text of a status code (static storage). */
-const char* mpattn_status_string(mpattn_status status);
+/* Human-readable text of a status code (static storage); any int is accepted
+ * ("unknown status" for a value that is not an mpattn_status). */
+const char* mpattn_status_string(int32_t status);
 
 /* Clusters per unit that any build/update sequence within capacity_tokens can
  * need: ceil(N / r) + ceil(N / cluster_block) + 1 for N = capacity_tokens.

@@ -39,9 +39,12 @@ def build_library(out: str = _LIB) -> str:
 
 
 def _load():
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build_library()
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("MPATTN_ORACLE_LIB")  # another build of the same source (a sanitizer build)
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build_library()
+    lib = ctypes.CDLL(path)
     sig = {
         "orc_round_storage": (ctypes.c_double, [ctypes.c_double, ctypes.c_int]),
         "orc_round_array": (None, [_D, _i64, ctypes.c_int, _D]),

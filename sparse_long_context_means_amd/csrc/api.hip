@@ -361,7 +361,7 @@ mpattn_status scratch_for(const mpattn_params* p, const mpattn_state* st, void**
 
 extern "C" {
 
-const char* mpattn_status_string(mpattn_status status) {
+const char* mpattn_status_string(int32_t status) {
     switch (status) {
         case MPATTN_OK: return "ok";
         case MPATTN_ERR_INVALID_ARG: return "invalid argument";

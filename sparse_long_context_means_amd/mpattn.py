@@ -16,7 +16,8 @@ from typing import Dict, Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmpattn.so")
+# another build of the same sources may be named (a host-sanitizer build)
+LIB_PATH = os.environ.get("MPATTN_LIB") or os.path.join(_HERE, "libmpattn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
