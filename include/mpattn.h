@@ -180,8 +180,9 @@ int32_t mpattn_max_coarse(const mpattn_params* params);
  * workspace must not overlap in time.  A decode workspace must hold zeros
  * before its first decode, and again before it serves other parameters or
  * capacities, and must not be written by anything else between decodes: the
- * workgroups of a unit exchange tagged words through it, and it keeps the tag
- * of each unit's last decode (a decode leaves it valid for the next one).
+ * workgroups of a unit exchange tagged words and count themselves in on a
+ * counter through it; it keeps the tag of each unit's last decode and every
+ * counter back at zero (a decode leaves it valid for the next one).
  * Its first 8 bytes are two uint32 counters that the one-launch decodes add
  * to and never reset:
  *   [0] workgroups that scored the other workgroups' clusters themselves

@@ -91,7 +91,7 @@ struct DecodeWs {
     // they rely on the workspace holding zeros before its first decode
     uint64_t* xch;        // [U][Rx][Cmax] keys
     uint64_t* xpart;      // [U][Rx][G][d + 2] partials
-    uint64_t* xcount;     // [U] arrival words
+    uint64_t* xcount;     // [U] arrival counters (the merging replica sets them back to 0)
     uint32_t* xepoch;     // [U] tag of each unit's last decode
     int32_t Rx;           // most replicas a decode on this layout uses
     uint64_t* hch;        // hierarchy in one launch: [U][Rh][Dmax] coarse-key words

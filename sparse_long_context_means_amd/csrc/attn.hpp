@@ -464,15 +464,15 @@ __device__ __forceinline__ void lds_barrier() {
 // row groups' states are combined (shuffles), then the waves' (through
 // s_red, which may alias LDS data that is dead once every wave got here).
 // With one workgroup per unit (R = 1) it writes the normalised output outu
-// [G][d].  Otherwise each of the R workgroups posts its partial (per head the
-// state m, l and the 128 sums) as words (tag << 32 | value) into its slot of
-// xp [R][G][d + 2] and counts itself in on the unit's arrival word *xcount
-// (compare-and-swap; a stale tag counts as zero).  The workgroup that arrives
-// last reads the others' partials -- waiting only for words already stored,
-// for at most wait_ticks of the 100 MHz constant clock (a word given up on
-// is counted in status[1], status may be null) -- merges them in workgroup
-// order and stores the call's tag in the unit's *epoch.  s_flag: one int of
-// LDS.
+// [G][d].  Otherwise each of the R workgroups counts itself in on the unit's
+// arrival counter *xcount as it enters (the last to arrive merges) and posts
+// its partial (per head the state m, l and the 128 sums) as words (tag << 32
+// | value) into its slot of xp [R][G][d + 2].  The workgroup that arrived
+// last reads the others' partials -- polling a word that still carries
+// another call's tag for at most wait_ticks of the 100 MHz constant clock (a
+// word given up on is counted in status[1], status may be null) -- merges
+// them in workgroup order, sets the counter back to zero and stores the
+// call's tag in the unit's *epoch.  s_flag: one int of LDS.
 template <int G, int NW>
 __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][kHeadDim + 2], int* s_flag,
                                             float* outu, uint64_t* xp, uint64_t* xcount, uint32_t tag,
@@ -482,19 +482,57 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int rg = lane >> 4, li = lane & 15;
     const uint64_t tagw = (uint64_t)tag << 32;
-    // ---- combine the row groups: 4 per wave by shuffles, then the waves
-    //      through LDS (in wave order) ---------------------------------------
+    // several replicas: count in on the unit's arrival counter now, so the
+    // round trip runs beside the combine below (the replica that sees R - 1
+    // arrivals before its own merges; it finds the others' partials by their
+    // tags, polling while a partner still stores them)
+    uint64_t arrivals = 0;
+    if (R > 1 && tid == 0) arrivals = __hip_atomic_fetch_add(xcount, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- combine the row groups, 4 per wave, then the waves through LDS (in
+    //      wave order).  When the row groups of the wave share each head's
+    //      reference exponent (the exact-row steps keep one per wave) their
+    //      sums just add: pairs of rows by v_permlane16_swap, then pairs of
+    //      halves by v_permlane32_swap, the same additions in the same order
+    //      as the general merge below, which shuffles through LDS. ----------
+    bool uniform = true;
 #pragma unroll
-    for (int step = 16; step <= 32; step <<= 1) {
-        float om[G], ol[G], oacc[G][8];
+    for (int g = 0; g < G; ++g)
+        uniform = uniform && __builtin_amdgcn_ballot_w64(st.m[g] != __int_as_float(__builtin_amdgcn_readlane(
+                                                             __float_as_int(st.m[g]), 0))) == 0;
+    if (uniform) {  // (wave-uniform)
+        auto add16 = [](float& x) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        };
+        auto add32 = [](float& x) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        };
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            om[g] = shfl_xor_f(st.m[g], step);
-            ol[g] = shfl_xor_f(st.l[g], step);
+            add16(st.l[g]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
+            for (int e = 0; e < 8; ++e) add16(st.acc[g][e]);
         }
-        merge_state<G>(st, om, ol, oacc);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            add32(st.l[g]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) add32(st.acc[g][e]);
+        }
+    } else {
+#pragma unroll
+        for (int step = 16; step <= 32; step <<= 1) {
+            float om[G], ol[G], oacc[G][8];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                om[g] = shfl_xor_f(st.m[g], step);
+                ol[g] = shfl_xor_f(st.l[g], step);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) oacc[g][e] = shfl_xor_f(st.acc[g][e], step);
+            }
+            merge_state<G>(st, om, ol, oacc);
+        }
     }
     lds_barrier();  // the big region is free
     if (rg == 0) {
@@ -543,11 +581,9 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     }
 
     // ---- several replicas: each posts its partial (per head: the state m, l
-    //      and the 128 sums) as tagged words, then counts itself in on the
-    //      unit's arrival word (call tag << 32 | count, compare-and-swap; a
-    //      stale tag counts as zero).  The replica that arrives last reads the
-    //      others' partials (waiting only for words already stored) and writes
-    //      the normalised output, merging in replica order. -------------------
+    //      and the 128 sums) as tagged words.  The replica that counted in
+    //      last reads the others' partials and writes the normalised output,
+    //      merging in replica order. ------------------------------------------
     constexpr int kPart = G * (kHeadDim + 2);
 #pragma unroll
     for (int k = 0; k < kOut; ++k) {
@@ -582,22 +618,7 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
             }
         }
     }
-    lds_barrier();
-    if (tid == 0) {
-        uint64_t* cnt = xcount;
-        // first guess: all the others are in (then the exchange succeeds at
-        // once and the merging replica, the one on the critical path, spends
-        // a single round trip); a failed exchange returns the word as it is
-        uint64_t old = tagw | (uint32_t)(R - 1);
-        uint32_t arrived;
-        for (;;) {
-            arrived = ((uint32_t)(old >> 32) == tag ? (uint32_t)old : 0u) + 1u;
-            if (__hip_atomic_compare_exchange_strong(cnt, &old, tagw | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT))
-                break;
-        }
-        *s_flag = arrived == (uint32_t)R;
-    }
+    if (tid == 0) *s_flag = arrivals + 1 == (uint64_t)R;
     lds_barrier();
     if (!*s_flag) return;
     const uint64_t t0 = wall_clock64();
@@ -651,9 +672,13 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
         outu[e] = late ? NAN : (l > 0.f ? acc / l : 0.f);
         if (late && status) __hip_atomic_fetch_add(status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // the merging replica is the last of the unit: every replica has read the
-    // unit's epoch, so the next decode may take the following tag
-    if (tid == 0) *epoch = tag;
+    // the merging replica is the last of the unit: every replica has counted
+    // in and read the unit's epoch, so the counter starts again from zero and
+    // the next decode takes the following tag
+    if (tid == 0) {
+        __hip_atomic_store(xcount, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *epoch = tag;
+    }
 }
 
 template <typename T>

@@ -67,7 +67,7 @@ struct HierArgs {
     float* out;                  // [B][Hq][d]
     uint64_t* xch;               // [U][R][Dmax] tagged coarse-key words, slot r read by workgroup r
     uint64_t* xpart;             // [U][R][G][d + 2] tagged partial words
-    uint64_t* xcount;            // [U] tagged arrival words
+    uint64_t* xcount;            // [U] arrival counters, 0 between decodes (the merging workgroup resets)
     uint32_t* xepoch;            // [U] tag of the unit's last decode (the merging workgroup writes it)
     uint32_t* status;            // [2] counters: key-exchange fallbacks, partial words given up on
     int32_t* dbg_selected;       // optional [U][C]
@@ -224,7 +224,7 @@ struct UnitArgs {
     // replica exchange (several replicas): words are (tag << 32 | 32-bit value)
     uint64_t* xch;               // [U][R][Cmax]: keys, slot r read by replica r
     uint64_t* xpart;             // [U][R][G][d + 2]: partial sums, m, l of each replica
-    uint64_t* xcount;            // [U]: arrival word (tag << 32 | replicas counted in)
+    uint64_t* xcount;            // [U]: replicas counted in, 0 between decodes (the merging replica resets)
     uint32_t* xepoch;            // [U]: tag of the unit's last decode; this call's is one more (never 0)
     uint32_t* status;            // [2]: key-exchange fallbacks, partial words given up on
     int32_t rescore;             // 1: every workgroup scores every cluster; 2: one wave does, as after a timeout
