@@ -258,7 +258,7 @@ constexpr int kPseudoDepth = 2;                          // value-centroid steps
 constexpr int kExactDepth = 2;                           // exact-row steps (16 rows) in flight per wave
 // sixteenths of the first batch of exact rows that waves 0-3 take (they
 // start on it while waves 4-7 finish the approximate term)
-constexpr int kFirstBatchEarly = 10;
+constexpr int kFirstBatchEarly = 11;
 // Waits on the other replicas of a unit, in ticks of the 100 MHz constant
 // clock: for their keys (then the workgroup scores them itself) and for the
 // partial words of replicas that have already counted in.
