@@ -37,6 +37,8 @@ constexpr int kHWaves = kHThreads / kWave;  // 8
 constexpr int kHRowBatch = 1024;            // staged exact rows per pass
 constexpr int kHScoreDepth = 2;             // score steps in flight per wave (4 measured slower)
 constexpr int kHExactDepth = 2;             // exact-row steps (16 rows) in flight per wave
+constexpr int kHCoarseAhead = 1;            // coarse value rows per row group loaded during the key exchange
+constexpr int kHFineAhead = 1;              // fine value rows per row group loaded with the fine scores
 // Waits on the other workgroups of a unit, in ticks of the 100 MHz constant
 // clock: for their coarse keys (then the workgroup scores them itself) and
 // for the partial words of workgroups that have already counted in.
@@ -186,7 +188,8 @@ struct HierLds {
     static constexpr int gmax = misc + 16 * 4;                   // float [waves][G]
     static constexpr int pexp = gmax + kHWaves * G * 4;         // float [waves][16][G]
     static constexpr int row = pexp + kHWaves * 16 * G * 4;     // int [RowBatch]
-    static constexpr int bytes = row + kHRowBatch * 4;
+    static constexpr int foff = row + kHRowBatch * 4;            // int [MaxF]: candidates' member starts
+    static constexpr int bytes = foff + kHierMaxF * 4;
     static constexpr int red = fid;                              // float [waves][G][d + 2], after the
                                                                  // exact rows (spans fid, fkey)
     static_assert(kHWaves * G * (kHeadDim + 2) * 4 <= 2 * kHierMaxF * 4, "reduction region");
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     float(*s_gmax)[G] = reinterpret_cast<float(*)[G]>(lds + L::gmax);
     float* s_p = reinterpret_cast<float*>(lds + L::pexp);
     int32_t* s_row = reinterpret_cast<int32_t*>(lds + L::row);
+    int32_t* s_foff = reinterpret_cast<int32_t*>(lds + L::foff);
     float(*s_red)[G][kHeadDim + 2] = reinterpret_cast<float(*)[G][kHeadDim + 2]>(lds + L::red);
 
     const int unit = blockIdx.x, rep = blockIdx.y, R = gridDim.y;
@@ -328,6 +332,21 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         lds_barrier();
     });
     lds_barrier();
+    // the share's first coarse value rows (row group rgi takes items rgi +
+    // 32 j of the share, the order of the approximate-term pass below) go out
+    // now, the candidates among them too (their weight is 0), and are added
+    // after the fine cut: they arrive while the partners' keys are awaited
+    // (a wave's loads complete in issue order, so a later load's wait covers
+    // them too) and the lookup in between reads little
+    const int dsh = cs1 - cs0;  // coarse share logits at s_lg[0 .. dsh)
+    const int rgi = wave * 4 + rg;
+    constexpr int kPass = 4 * kHWaves;
+    const bf16_t* cv = reinterpret_cast<const bf16_t*>(a.cvbar) + (size_t)unit * a.Dmax * kHeadDim + li * 8;
+    Slice8<bf16_t> pv[kHCoarseAhead];
+    if (a.pseudo && dsh > 0) {  // (uniform)
+#pragma unroll
+        for (int j = 0; j < kHCoarseAhead; ++j) pv[j].load(cv + (size_t)(cs0 + min(rgi + j * kPass, dsh - 1)) * kHeadDim);
+    }
     if (xchg) {
         const uint64_t tagw = (uint64_t)tag << 32;
         uint64_t* xu = a.xch + (size_t)unit * R * a.Dmax;
@@ -383,6 +402,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         }
     }
 
+
     // ---- 2. coarse cut under the candidate budget -----------------------
     const uint32_t cbits = block_cut<kCItems>(
         [&](int i) { return s_ckey[i]; }, [&](int i) { return s_csz[i]; }, [&](int i) { return i; }, D,
@@ -431,12 +451,23 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         const int f = cmem[s_ccand[k] + p - s_cpre[k]];
         s_fid[p] = f;
         s_fsz[p] = fsizes[f];
+        s_foff[p] = foffs[f];  // for the exact rows, fetched with the size
     }
     lds_barrier();
 
     // ---- 3. fine scores of the candidates ---------------------------------
-    const int dsh = cs1 - cs0;  // coarse share logits at s_lg[0 .. dsh)
     const int fs0 = (int)((int64_t)F * rep / R), fs1 = (int)((int64_t)F * (rep + 1) / R);
+    const int fsh = fs1 - fs0;  // fine share logits at s_lg[dsh .. dsh + fsh)
+    // the share's first fine value rows go out now as well (row group rgi
+    // takes candidates fs0 + rgi + 32 j), added after the fine cut like the
+    // coarse ones: the selected among them weigh 0
+    const bf16_t* fv = reinterpret_cast<const bf16_t*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
+    Slice8<bf16_t> pf[kHFineAhead];
+    if (a.pseudo && fsh > 0) {  // (uniform)
+#pragma unroll
+        for (int j = 0; j < kHFineAhead; ++j)
+            pf[j].load(fv + (size_t)s_fid[fs0 + min(rgi + j * kPass, fsh - 1)] * kHeadDim);
+    }
     score_items(
         0, F, [&](int i) { return fk + (size_t)s_fid[i] * kHeadDim; }, [&](int i) { return s_fsz[i]; }, s_fkey, fs0,
         fs1, dsh, []() {});
@@ -444,6 +475,19 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
     lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 32));
     if (lane < G) s_gmax[wave][lane] = lgmax;
     lds_barrier();
+
+    // reference exponent of the share's approximate terms: its largest logit
+    // per head (every weight <= 1)
+    SoftState<G> st;
+    st.init();
+    float Mref[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float m = s_gmax[0][g];
+#pragma unroll
+        for (int w = 1; w < kHWaves; ++w) m = fmaxf(m, s_gmax[w][g]);
+        Mref[g] = m;
+    }
 
     // ---- 4. fine cut under the token budget, in fine-id order for ties ----
     constexpr int kFItems = kHierMaxF / kHThreads;
@@ -488,19 +532,47 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
 
     // ---- 5. approximate terms of the share: coarse clusters that are not
     //      candidates, fine candidates not selected.  Weights 2^(lg - M),
-    //      M the share's largest logit per head (every weight <= 1). -----------
-    SoftState<G> st;
-    st.init();
-    float Mref[G];
+    //      M the share's largest logit per head (every weight <= 1).  Row
+    //      group rgi adds coarse items rgi + 32 j and fine items rgi + 32 j
+    //      of the share for j below kHCoarseAhead and kHFineAhead (loaded
+    //      ahead), then items rgi + 32 k of the rest, coarse before fine. ----
+    if (a.pseudo) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float m = s_gmax[0][g];
+        for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
+        auto add_row = [&](const Slice8<bf16_t>& v, bool keep, int lgi) {
+            float x[8];
+            v.unpack(x);
 #pragma unroll
-        for (int w = 1; w < kHWaves; ++w) m = fmaxf(m, s_gmax[w][g]);
-        Mref[g] = m;
+            for (int g = 0; g < G; ++g) {
+                const float lgv = keep ? s_lg[lgi][g] : -INFINITY;
+                const float w = lgv != -INFINITY ? __builtin_amdgcn_exp2f(lgv - Mref[g]) : 0.f;
+                st.l[g] += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+            }
+        };
+        if (dsh > 0) {
+#pragma unroll
+            for (int j = 0; j < kHCoarseAhead; ++j) {
+                const int t = rgi + j * kPass, c = cs0 + t;
+                add_row(pv[j], t < dsh && !((s_cmask[c >> 5] >> (c & 31)) & 1u), min(t, dsh - 1));
+            }
+        }
+        if (fsh > 0) {
+#pragma unroll
+            for (int j = 0; j < kHFineAhead; ++j) {
+                const int i = rgi + j * kPass, fi = fs0 + i;
+                add_row(pf[j], i < fsh && !((s_fmask[fi >> 5] >> (fi & 31)) & 1u), dsh + min(i, fsh - 1));
+            }
+        }
     }
-    const int fsh = fs1 - fs0, nsh = dsh + fsh;
-    for (int t = tid; t < nsh; t += kHThreads) {
+    // the rest: coarse items [ca, dsh), then fine items [fa, fsh), as one
+    // list u = 0 .. nrest - 1; lg_index(u) is the item's row of s_lg
+    const int ca = min(kHCoarseAhead * kPass, dsh), fa = min(kHFineAhead * kPass, fsh);
+    const int nrc = dsh - ca, nrest = nrc + fsh - fa;
+    auto lg_index = [&](int u) { return u < nrc ? ca + u : dsh + fa + (u - nrc); };
+    for (int u = tid; u < nrest; u += kHThreads) {
+        const int t = lg_index(u);
         bool keep;
         if (t < dsh) {
             const int c = cs0 + t;
@@ -515,36 +587,32 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
             s_lg[t][g] = keep && lgv != -INFINITY ? __builtin_amdgcn_exp2f(lgv - Mref[g]) : 0.f;
         }
     }
-    lds_barrier();
-    if (a.pseudo && nsh > 0) {  // (uniform) item 0 of the share exists
-#pragma unroll
-        for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
-        const bf16_t* cv = reinterpret_cast<const bf16_t*>(a.cvbar) + (size_t)unit * a.Dmax * kHeadDim + li * 8;
-        const bf16_t* fv = reinterpret_cast<const bf16_t*>(a.vbar) + (size_t)unit * a.Cmax * kHeadDim + li * 8;
-        auto vrow = [&](int t) {
+    if (a.pseudo && nrest > 0) {  // (uniform)
+        lds_barrier();
+        auto vrow = [&](int u) {
+            const int t = lg_index(u);
             return t < dsh ? cv + (size_t)(cs0 + t) * kHeadDim : fv + (size_t)s_fid[fs0 + t - dsh] * kHeadDim;
         };
         // 32 row groups, one row each per pass, two passes in flight
-        const int rgi = wave * 4 + rg;
-        constexpr int kPass = 4 * kHWaves;
         Slice8<bf16_t> v[2];
-        v[0].load(vrow(rgi < nsh ? rgi : 0));
-        v[1].load(vrow(rgi + kPass < nsh ? rgi + kPass : 0));
-        for (int t0 = 0; t0 < nsh; t0 += 2 * kPass) {
+        v[0].load(vrow(rgi < nrest ? rgi : 0));
+        v[1].load(vrow(rgi + kPass < nrest ? rgi + kPass : 0));
+        for (int u0 = 0; u0 < nrest; u0 += 2 * kPass) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int t = t0 + u * kPass + rgi;
+            for (int k = 0; k < 2; ++k) {
+                const int u = u0 + k * kPass + rgi;
                 float x[8];
-                v[u].unpack(x);
+                v[k].unpack(x);
+                const int t = lg_index(u < nrest ? u : 0);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float w = t < nsh ? s_lg[t][g] : 0.f;
+                    const float w = u < nrest ? s_lg[t][g] : 0.f;
                     st.l[g] += w;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
                 }
-                const int tn = t + 2 * kPass;
-                v[u].load(vrow(tn < nsh ? tn : 0));
+                const int un = u + 2 * kPass;
+                v[k].load(vrow(un < nrest ? un : 0));
             }
         }
     }
@@ -573,7 +641,7 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                 int v;
                 if (r < E) {  // member r - pre[k] of selected candidate k
                     const int k = upper_index(s_spre, nsel, r);
-                    const int pos = foffs[s_fid[s_sid[k]]] + r - s_spre[k];
+                    const int pos = s_foff[s_sid[k]] + r - s_spre[k];
                     v = tids ? tids[pos] : pos;
                 } else {
                     v = -1 - (a.n_clustered + r - E);
@@ -624,12 +692,13 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                             a.status, R, rep, kHPartialWaitTicks);
 }
 
-// Workgroups per unit: enough for about 128 workgroups in all, at least 3.
-// Each phase is short and latency-bound, so fewer partners to exchange keys
-// and partials with beat filling every CU (4 per unit at 32 units measured
-// 3 us faster than 8).
+// Workgroups per unit: enough for about 256 workgroups in all (one per
+// compute unit), at least 3.  Every phase reads a few tens of KB per
+// workgroup and a compute unit streams some 30 GB/s, so smaller shares
+// shorten each phase more than the extra partners lengthen the key exchange
+// (8 per unit at 32 units measured 1 us faster than 4).
 int hier_replicas(int units) {
-    constexpr int kWorkgroups = 128;
+    constexpr int kWorkgroups = 256;
     int r = kHierMinReplicas;
     while (units * r < kWorkgroups && r < kHierMaxReplicas) ++r;
     return r;
