@@ -20,9 +20,19 @@ FLAGS = [
 ]
 
 
+# per-source additions: the k-means assignment keeps its matrix-core
+# accumulators in ordinary vector registers, which its argmax reads directly
+# (no copies out of the accumulator registers)
+EXTRA_FLAGS = {"kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def flags_for(src: str) -> list:
+    return [*FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), [])]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *flags_for(src), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void kmeans_init_kernel(const T* __restrict__ 
 // MFMA 32x32x16 with A = 32 centroids (from LDS), B = 32 tokens (registers);
 // lane l holds token l % 32 and 16 centroid rows of the tile, so the running
 // argmax needs no cross-lane traffic until the end.  The accumulator starts at
-// -|mu|^2 / 2 so the MFMA result is the score itself.
+// -|mu|^2 / 2 (kept negated in LDS) so the MFMA result is the score itself.
 // ---------------------------------------------------------------------------
 constexpr int kAsgChunk = 64;  // centroids staged per LDS round
 constexpr int kAsgPad = 17;    // uint4 per staged row (16 + 1 to spread LDS banks)
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
             ss = fmaf(x1, x1, ss); ss = fmaf(x2, x2, ss); ss = fmaf(x3, x3, ss);
             ss = fmaf(x4, x4, ss); ss = fmaf(x5, x5, ss); ss = fmaf(x6, x6, ss); ss = fmaf(x7, x7, ss);
             ss = row16_sum(ss);  // the 16 lanes of a row hold its 16 parts
-            if (part == 0) hn[buf][row] = c < C ? 0.5f * ss : INFINITY;
+            if (part == 0) hn[buf][row] = c < C ? -0.5f * ss : -INFINITY;
         }
     };
     {
@@ -153,21 +153,20 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
         const bool more = ch + kAsgChunk < C;  // (uniform)
         uint4 nv[4];
         if (more) fetch(ch + kAsgChunk, nv);
-        f32x16_t acc[2][2];
+        // accumulators start at -|mu|^2 / 2 of their centroid rows (the
+        // first product takes them as its addend)
+        f32x16_t init[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 h = *reinterpret_cast<const float4*>(&hn[buf][cb * 32 + 8 * q4 + 4 * half]);
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    acc[cb][tb][4 * q4 + 0] = -h.x;
-                    acc[cb][tb][4 * q4 + 1] = -h.y;
-                    acc[cb][tb][4 * q4 + 2] = -h.z;
-                    acc[cb][tb][4 * q4 + 3] = -h.w;
-                }
+                init[cb][4 * q4 + 0] = h.x;
+                init[cb][4 * q4 + 1] = h.y;
+                init[cb][4 * q4 + 2] = h.z;
+                init[cb][4 * q4 + 3] = h.w;
             }
-        }
+        f32x16_t acc[2][2];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -177,24 +176,36 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
                     acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        av, __builtin_bit_cast(bf16x8_t, kb[tb][s]), acc[cb][tb], 0, 0, 0);
+                        av, __builtin_bit_cast(bf16x8_t, kb[tb][s]), s == 0 ? init[cb] : acc[cb][tb], 0, 0, 0);
             }
         }
-        // rows held by this lane increase with the register index, and tiles
-        // are visited in increasing id order: '>' keeps the lowest id on ties
+        // the rows this lane holds increase with the register index, and
+        // tiles are visited in increasing id order: a tile replaces the
+        // running best only when its maximum is strictly larger, taking the
+        // lowest row that reaches it (ties keep the lowest id).  The maximum
+        // takes 8 three-way max instructions; the row search runs only in
+        // waves where some lane improved.
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb) {
+                const f32x16_t v = acc[cb][tb];
+                float m = fmaxf(fmaxf(v[0], v[1]), v[2]);
+                m = fmaxf(fmaxf(m, v[3]), v[4]);
+                m = fmaxf(fmaxf(m, v[5]), v[6]);
+                m = fmaxf(fmaxf(m, v[7]), v[8]);
+                m = fmaxf(fmaxf(m, v[9]), v[10]);
+                m = fmaxf(fmaxf(m, v[11]), v[12]);
+                m = fmaxf(fmaxf(m, v[13]), v[14]);
+                m = fmaxf(m, v[15]);
+                if (m > best[tb]) {
+                    int r = 15;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = ch + cb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const float v = acc[cb][tb][r];
-                    if (v > best[tb]) {
-                        best[tb] = v;
-                        bidx[tb] = c;
-                    }
+                    for (int k = 14; k >= 0; --k) r = v[k] == m ? k : r;
+                    best[tb] = m;
+                    bidx[tb] = ch + cb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 }
+            }
         if (more) stage(ch + kAsgChunk, nv, buf ^ 1);  // the other buffer: read by no wave now
         __syncthreads();
         buf ^= 1;
