@@ -13,7 +13,7 @@ and reported separately.  Headline timing is cold: before every step a 1 GiB
 streaming read (the library's read probe) evicts the 256 MB Infinity Cache and
 the L2s with clean lines, so the centroids and rows come from HBM.  The steps
 run back to back, each behind its flush, inside one event pair; the same
-number of flushes timed alone is subtracted (median of 5 alternating rounds).
+number of flushes timed alone is subtracted (median of 9 alternating rounds).
 Cold steps each bracketed by their own event pair are reported too: that
 figure also holds the event records and the dispatch of a launch that waits
 for its start event (an empty kernel reads about 6 us that way, reported as
@@ -91,6 +91,8 @@ def parse():
                          "describe it) or their fp8 copies")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--read-probe-mb", type=int, default=0,
+                    help="only run the library's streaming read of this many MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -119,6 +121,15 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         log(f"copy probe: 3 copies of {args.copy_probe_mb} MiB")
+        return
+    if args.read_probe_mb:
+        x = torch.ones(args.read_probe_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            M.read_probe(x, sink)
+        torch.cuda.synchronize()
+        log(f"read probe: 3 reads of {args.read_probe_mb} MiB")
         return
 
     w = workloads.WORKLOADS[args.workload]
@@ -236,7 +247,7 @@ def main():
                          for i in range(args.steps)])
 
     # cold, back to back (headline): K x (cache flush + step) inside one event
-    # pair, less K flushes timed alone the same way, in alternating rounds
+    # pair, less K flushes timed alone the same way, in 9 alternating rounds
     # (median).  The per-step pairs above also time the two event records and
     # a dispatch that cannot begin before its start event; an empty kernel
     # reads about 6 us there (floor below).  Here every launch is queued
@@ -255,7 +266,7 @@ def main():
         return a_.elapsed_time(b_) * 1e3
 
     b2b_rounds = []
-    for _ in range(5):
+    for _ in range(9):
         both = loop_us(True)
         b2b_rounds.append((both - loop_us(False)) / args.steps)
     b2b_us = float(np.median(b2b_rounds))

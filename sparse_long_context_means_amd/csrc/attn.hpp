@@ -465,14 +465,15 @@ __device__ __forceinline__ void lds_barrier() {
 // s_red, which may alias LDS data that is dead once every wave got here).
 // With one workgroup per unit (R = 1) it writes the normalised output outu
 // [G][d].  Otherwise each of the R workgroups counts itself in on the unit's
-// arrival counter *xcount as it enters (the last to arrive merges) and posts
-// its partial (per head the state m, l and the 128 sums) as words (tag << 32
-// | value) into its slot of xp [R][G][d + 2].  The workgroup that arrived
-// last reads the others' partials -- polling a word that still carries
+// arrival counter *xcount as it enters; all but the last to arrive post
+// their partial (per head the state m, l and the 128 sums) as words (tag <<
+// 32 | value) into their slot of xp [R][G][d + 2] and are done.  The last
+// one reads the others' partials -- polling a word that still carries
 // another call's tag for at most wait_ticks of the 100 MHz constant clock (a
 // word given up on is counted in status[1], status may be null) -- merges
 // them in workgroup order, sets the counter back to zero and stores the
-// call's tag in the unit's *epoch.  s_flag: one int of LDS.
+// call's tag in the unit's *epoch.  s_flag: one int of LDS that nothing else
+// uses during the call.
 template <int G, int NW>
 __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][kHeadDim + 2], int* s_flag,
                                             float* outu, uint64_t* xp, uint64_t* xcount, uint32_t tag,
@@ -486,8 +487,10 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     // round trip runs beside the combine below (the replica that sees R - 1
     // arrivals before its own merges; it finds the others' partials by their
     // tags, polling while a partner still stores them)
-    uint64_t arrivals = 0;
-    if (R > 1 && tid == 0) arrivals = __hip_atomic_fetch_add(xcount, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (R > 1 && tid == 0) {
+        const uint64_t arrivals = __hip_atomic_fetch_add(xcount, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = arrivals + 1 == (uint64_t)R;  // read after the barriers below
+    }
     // ---- combine the row groups, 4 per wave, then the waves through LDS (in
     //      wave order).  When the row groups of the wave share each head's
     //      reference exponent (the exact-row steps keep one per wave) their
@@ -580,27 +583,30 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
         return;
     }
 
-    // ---- several replicas: each posts its partial (per head: the state m, l
-    //      and the 128 sums) as tagged words.  The replica that counted in
-    //      last reads the others' partials and writes the normalised output,
-    //      merging in replica order. ------------------------------------------
+    // ---- several replicas: the others each post their partial (per head:
+    //      the state m, l and the 128 sums) as tagged words and are done; the
+    //      replica that counted in last stores nothing (its own stores would
+    //      hold up its loads, which complete after them) and reads the others'
+    //      partials, then writes the normalised output, merging in replica
+    //      order. ------------------------------------------------------------
     constexpr int kPart = G * (kHeadDim + 2);
+    if (!*s_flag) {
 #pragma unroll
-    for (int k = 0; k < kOut; ++k) {
-        const int e = tid + k * kThreads;
-        if (e >= G * kHeadDim) break;
-        const int g = e / kHeadDim, dd = e % kHeadDim;
-        uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
-        __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (dd == 0) {
-            __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < kOut; ++k) {
+            const int e = tid + k * kThreads;
+            if (e >= G * kHeadDim) break;
+            const int g = e / kHeadDim, dd = e % kHeadDim;
+            uint64_t* pg = xp + (size_t)rep * kPart + g * (kHeadDim + 2);
+            __hip_atomic_store(pg + dd, tagw | __float_as_uint(oA[k]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (dd == 0) {
+                __hip_atomic_store(pg + kHeadDim, tagw | __float_as_uint(oM[k]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(pg + kHeadDim + 1, tagw | __float_as_uint(oL[k]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
+        return;
     }
-    // every thread reads the other replicas' words of its outputs now, beside
-    // the arrival count: the merging replica then usually finds them there
-    // after that one trip (the others drop them)
     constexpr int kMaxR = 8;
     uint64_t wm[kOut][kMaxR], wl[kOut][kMaxR], wa[kOut][kMaxR];
 #pragma unroll
@@ -618,9 +624,6 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
             }
         }
     }
-    if (tid == 0) *s_flag = arrivals + 1 == (uint64_t)R;
-    lds_barrier();
-    if (!*s_flag) return;
     const uint64_t t0 = wall_clock64();
     bool late = false;
     // a partner word of this call (polled again, for a bounded time, while it
