@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
         for (int j = 0; j < kScoreDepth; ++j) {
             const int i = base(j) + li;
-            kload(ring[j], i < hi ? i : hi - 1);
+            kload(ring[j], i < hi ? i : max(hi - 1, 0));
             __builtin_amdgcn_sched_barrier(0);
         }
         if (first) {
@@ -378,45 +378,54 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             for (int k = tid; k < 4 * 256; k += kUnitThreads) reinterpret_cast<int*>(hist)[k] = 0;
             lds_barrier();
         }
-        for (int it = 0; it < steps; it += kScoreDepth) {
+        // step s from ring slot r: lane (rg, li) receives rows 4 rg + e of
+        // the 16 for head li; rows past the end store nothing
+        auto consume = [&](const KRow& r, int s) {
+            f32x4v d;
+            if constexpr (F8) {
+                Slice8<bf16_t> op[4];
+                r.operands(op);
+                d = mfma_scores(op, qop);
+            } else {
+                d = mfma_scores(r.r, qop);
+            }
+            const int cb = base(s) + 4 * rg;
 #pragma unroll
-            for (int j = 0; j < kScoreDepth; ++j) {
-                // lane (rg, li) receives rows 4 rg + e of the 16 for head li
-                f32x4v d;
-                if constexpr (F8) {
-                    Slice8<bf16_t> op[4];
-                    ring[j].operands(op);
-                    d = mfma_scores(op, qop);
-                } else {
-                    d = mfma_scores(ring[j].r, qop);
-                }
-                const int cb = base(it + j) + 4 * rg;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float sv = d[e] * kInvSqrtD;
-                    const float key = head_mean<G>(sv);
-                    const int i = cb + e;
-                    if (i < hi) {
-                        if (li == 0) s_key[i] = key;
-                        if (li < G) {
-                            if (a.dbg_scores) a.dbg_scores[((size_t)unit * C + i) * G + li] = sv;
-                            if (first && i >= cs && i < ce) {  // later passes keep them
-                                const int n = s_sz[i];
-                                const float lgv = n > 0 ? fmaf(sv, kLog2e, log2_count(n)) : -INFINITY;
-                                s_lg[i - cs][li] = lgv;
-                                lgmax = fmaxf(lgmax, lgv);
-                            }
+            for (int e = 0; e < 4; ++e) {
+                const float sv = d[e] * kInvSqrtD;
+                const float key = head_mean<G>(sv);
+                const int i = cb + e;
+                if (i < hi) {
+                    if (li == 0) s_key[i] = key;
+                    if (li < G) {
+                        if (a.dbg_scores) a.dbg_scores[((size_t)unit * C + i) * G + li] = sv;
+                        if (first && i >= cs && i < ce) {  // later passes keep them
+                            const int n = s_sz[i];
+                            const float lgv = n > 0 ? fmaf(sv, kLog2e, log2_count(n)) : -INFINITY;
+                            s_lg[i - cs][li] = lgv;
+                            lgmax = fmaxf(lgmax, lgv);
                         }
                     }
                 }
-                // past the end: every lane reads the share's last row, which
-                // the last real step loads (one cached row, not a trip to
-                // HBM that the end of the pass would wait for)
+            }
+        };
+        // the ring's last group is consumed without loading further rows, so
+        // nothing is left in flight when the pass ends (a later wait would
+        // include it); rows past the end of a partial step read the range's
+        // last row, or row 0 when the range is empty (fewer clusters than
+        // replicas): a cached row
+        int it = 0;
+        for (; it + kScoreDepth < steps; it += kScoreDepth) {
+#pragma unroll
+            for (int j = 0; j < kScoreDepth; ++j) {
+                consume(ring[j], it + j);
                 const int i = base(it + j + kScoreDepth) + li;
-                kload(ring[j], i < hi ? i : hi - 1);
+                kload(ring[j], i < hi ? i : max(hi - 1, 0));
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
+#pragma unroll
+        for (int j = 0; j < kScoreDepth; ++j) consume(ring[j], it + j);
         if (first) {  // the wave's maximum logit of head li over the share
             lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 16));
             lgmax = fmaxf(lgmax, shfl_xor_f(lgmax, 32));
@@ -499,6 +508,17 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 if (r2 != rep)
                     __hip_atomic_store(xu + (size_t)r2 * a.Cmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+    }
+    // The replica counts itself in on the unit's arrival counter now, behind
+    // its key words: the round trip runs beside the value stream and the
+    // exact rows instead of at the end of the step.  The replica that sees
+    // R - 1 arrivals before its own merges the partials (finish_step); every
+    // replica it waits for there has started.  Wave 4 counts in: its value
+    // rows go out behind its key stores anyway.
+    if (R > 1 && tid == kCutWaves * kWave) {
+        const uint64_t arrivals =
+            __hip_atomic_fetch_add(a.xcount + unit, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_misc[0] = arrivals + 1 == (uint64_t)R;  // read after the barriers of finish_step
     }
     if (a.pseudo) {
 #pragma unroll
@@ -671,7 +691,7 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = cs + item(j, u);
-                vload(pring[j].r[u], c < ce ? c : ce - 1);
+                vload(pring[j].r[u], c < ce ? c : max(ce - 1, 0));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -701,32 +721,38 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
         }
         int sgen = 0;
         group_barrier<kStreamWaves>(sctr, sgen);
+        auto vconsume = [&](const VRows4& rr, int step) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = item(step, u);
+                float x[8];
+                rr.r[u].unpack(x);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float w = s_lg[r][g];  // 0 past the share's clusters
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+                }
+            }
+        };
+        // the last group is consumed without loading further rows (nothing
+        // left in flight for the exact rows' first wait)
 #pragma unroll 1
-        for (int it = 0; it < kSteps; it += kPseudoDepth) {
+        for (int it = 0; it + kPseudoDepth < kSteps; it += kPseudoDepth) {
 #pragma unroll
             for (int j = 0; j < kPseudoDepth; ++j) {
+                vconsume(pring[j], it + j);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int r = item(it + j, u);
-                    float x[8];
-                    pring[j].r[u].unpack(x);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float w = s_lg[r][g];  // 0 past the share's clusters
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    // past the share: its last row, loaded by the last real
-                    // step (one cached row)
+                    // rows past the share: its last row, or row 0 (cached)
                     const int c = cs + item(it + j + kPseudoDepth, u);
-                    vload(pring[j].r[u], c < ce && it + j + kPseudoDepth < kSteps ? c : ce - 1);
+                    vload(pring[j].r[u], c < ce ? c : max(ce - 1, 0));
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
+#pragma unroll
+        for (int j = 0; j < kPseudoDepth; ++j) vconsume(pring[j], kSteps - kPseudoDepth + j);
     }
     if (wave >= kCutWaves) {  // waves 4-7 join the exact rows once the first batch is staged
         while (__hip_atomic_load(rflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) __builtin_amdgcn_s_sleep(2);
@@ -785,7 +811,12 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                 load_step(ring[j], j);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            for (int it = 0; it < steps; it += kExactDepth) {
+            // the last group is consumed without loading further rows, so
+            // nothing is in flight when the rows end (the combine that
+            // follows would wait for it); with no rows at all its steps are
+            // masked and weigh nothing
+            int it = 0;
+            for (; it + kExactDepth < steps; it += kExactDepth) {
 #pragma unroll
                 for (int j = 0; j < kExactDepth; ++j) {
                     exact16_step<G>(st, mv, lp, sp, qop, ring[j], w0 + (it + j) * 16 + 4 * rg, w1, qscale);
@@ -793,6 +824,9 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                     __builtin_amdgcn_sched_barrier(0);  // keep the ring order
                 }
             }
+#pragma unroll
+            for (int j = 0; j < kExactDepth; ++j)
+                exact16_step<G>(st, mv, lp, sp, qop, ring[j], w0 + (it + j) * 16 + 4 * rg, w1, qscale);
         };
         // wave's contiguous part of `part` rows starting at `base`, shared by
         // the 4 waves of its half
@@ -847,7 +881,8 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
     }
     finish_step<G, kUnitWaves>(st, s_red, s_misc, a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim,
                                a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, tag,
-                               R > 1 ? a.xepoch + unit : nullptr, a.status, R, rep, kPartialWaitTicks);
+                               R > 1 ? a.xepoch + unit : nullptr, a.status, R, rep, kPartialWaitTicks,
+                               /*counted_in=*/true);
 }
 
 // One replica per unit only once the units alone give a workgroup to every CU
