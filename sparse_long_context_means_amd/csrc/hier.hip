@@ -272,31 +272,39 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         pre();
-        for (int it = 0; it < steps; it += kHScoreDepth) {
+        auto consume = [&](const Slice8<bf16_t> (&r)[4], int s) {
+            const f32x4v d = mfma_scores(r, qop);
+            const int cb = base(s) + 4 * rg;
 #pragma unroll
-            for (int j = 0; j < kHScoreDepth; ++j) {
-                const f32x4v d = mfma_scores(ring[j], qop);
-                const int cb = base(it + j) + 4 * rg;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float sv = d[e] * kInvSqrtD;
-                    const float key = head_mean<G>(sv);
-                    const int i = cb + e;
-                    if (i < hi) {
-                        if (li == 0 && keys) keys[i] = key;
-                        if (li < G && i >= s0 && i < s1) {
-                            const int sz = size_of(i);
-                            const float lgv = sz > 0 ? fmaf(sv, kLog2e, log2_count(sz)) : -INFINITY;
-                            s_lg[i - s0 + lg0][li] = lgv;
-                            lgmax = fmaxf(lgmax, lgv);
-                        }
+            for (int e = 0; e < 4; ++e) {
+                const float sv = d[e] * kInvSqrtD;
+                const float key = head_mean<G>(sv);
+                const int i = cb + e;
+                if (i < hi) {
+                    if (li == 0 && keys) keys[i] = key;
+                    if (li < G && i >= s0 && i < s1) {
+                        const int sz = size_of(i);
+                        const float lgv = sz > 0 ? fmaf(sv, kLog2e, log2_count(sz)) : -INFINITY;
+                        s_lg[i - s0 + lg0][li] = lgv;
+                        lgmax = fmaxf(lgmax, lgv);
                     }
                 }
+            }
+        };
+        // the last group is consumed without loading rows past the end, so
+        // nothing is left in flight for the next phase's first wait
+        int it = 0;
+        for (; it + kHScoreDepth < steps; it += kHScoreDepth) {
+#pragma unroll
+            for (int j = 0; j < kHScoreDepth; ++j) {
+                consume(ring[j], it + j);
                 const int i = base(it + j + kHScoreDepth) + li;
                 load_row_blocks(ring[j], row_of(i < hi ? i : lo), lane);
                 __builtin_amdgcn_sched_barrier(0);  // keep the ring order
             }
         }
+#pragma unroll
+        for (int j = 0; j < kHScoreDepth; ++j) consume(ring[j], it + j);
     };
 
     // ---- 1. coarse scores.  With several workgroups each scores its share
@@ -597,24 +605,31 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         Slice8<bf16_t> v[2];
         v[0].load(vrow(rgi < nrest ? rgi : 0));
         v[1].load(vrow(rgi + kPass < nrest ? rgi + kPass : 0));
-        for (int u0 = 0; u0 < nrest; u0 += 2 * kPass) {
+        auto absorb = [&](const Slice8<bf16_t>& vr, int u) {
+            float x[8];
+            vr.unpack(x);
+            const int t = lg_index(u < nrest ? u : 0);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float w = u < nrest ? s_lg[t][g] : 0.f;
+                st.l[g] += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
+            }
+        };
+        // the last two passes are taken without loading rows past the end
+        int u0 = 0;
+        for (; u0 + 2 * kPass < nrest; u0 += 2 * kPass) {
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int u = u0 + k * kPass + rgi;
-                float x[8];
-                v[k].unpack(x);
-                const int t = lg_index(u < nrest ? u : 0);
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float w = u < nrest ? s_lg[t][g] : 0.f;
-                    st.l[g] += w;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) st.acc[g][e] = fmaf(w, x[e], st.acc[g][e]);
-                }
+                absorb(v[k], u);
                 const int un = u + 2 * kPass;
                 v[k].load(vrow(un < nrest ? un : 0));
             }
         }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) absorb(v[k], u0 + k * kPass + rgi);
     }
 
     // ---- 6. exact rows of the share: selected members [0, E), then the
@@ -673,7 +688,9 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int steps = (nb + kHWaves - 1) / kHWaves;
-            for (int it = 0; it < steps; it += kHExactDepth) {
+            // the last group is consumed without loading further rows
+            int it = 0;
+            for (; it + kHExactDepth < steps; it += kHExactDepth) {
 #pragma unroll
                 for (int j = 0; j < kHExactDepth; ++j) {
                     exact16_step<G>(st, mv, lp, sp, qop, ring[j], blk(it + j) * 16 + 4 * rg, cnt, qscale);
@@ -681,6 +698,9 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+#pragma unroll
+            for (int j = 0; j < kHExactDepth; ++j)
+                exact16_step<G>(st, mv, lp, sp, qop, ring[j], blk(it + j) * 16 + 4 * rg, cnt, qscale);
         }
         exact16_leave<G>(st, mv, lp);
     }
