@@ -40,31 +40,32 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 
-# HBM bytes per launch of the per-unit decode kernel on this workload, from
-# two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
-# each scaled by what the same counter reads for a 256 MiB device copy
-# (FETCH_SIZE reads 131085 KiB there: x2.0; WRITE_SIZE 262144 KiB: x1.0).
-# Valid only for the kernel sources they were taken on (sha256 over unit.hip,
-# attn.hpp, device.hpp, kernels.hpp in that order); otherwise reported null.
-UNIT_TRAFFIC = {  # per centroid format; null once the kernel sources differ
+# HBM bytes per launch of the one-launch decode kernels, from two rocprofv3
+# --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean over the
+# run's dispatches), each scaled by what the same counter reads for data of
+# known size: a 256 MiB device copy and the library's 256 MiB streaming read
+# both give FETCH_SIZE 131085 KiB (x2.0); the copy's WRITE_SIZE is 262144 KiB
+# (x1.0).  Valid only for the kernel sources they were taken on (sha256 over
+# the listed files, in that order); otherwise reported null.
+UNIT_TRAFFIC = {  # per centroid format
     "stored": {
-        "sources_sha256": "cc7bca4410d6c9ef705ba529aab0b8c946df39ddbd0f2090ce262c91b94ef5ad",
-        "fetch_bytes": int(122781.22 * 2.0 * 1024),
-        "write_bytes": int(5014.24 * 1.0 * 1024),
+        "sources_sha256": "4588d2f6a5dd3d6e17f4bf81bf80ab20f174e047ea857eb91b6b62974cc1039f",
+        "fetch_bytes": int(122981.8 * 2.0 * 1024),
+        "write_bytes": int(3476.0 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "cc7bca4410d6c9ef705ba529aab0b8c946df39ddbd0f2090ce262c91b94ef5ad",
-        "fetch_bytes": int(90105.32 * 2.0 * 1024),
-        "write_bytes": int(5014.93 * 1.0 * 1024),
+        "sources_sha256": "4588d2f6a5dd3d6e17f4bf81bf80ab20f174e047ea857eb91b6b62974cc1039f",
+        "fetch_bytes": int(90302.9 * 2.0 * 1024),
+        "write_bytes": int(3475.9 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
 }
 HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
-    "sources_sha256": "ed726fbb3793bd4f512cf18626a6c30bd169731e98b94a9b6f8e221774e23f06",
+    "sources_sha256": "0dff542046adb6d2b8cb1b501aac83b8e443025ad0d0c4c6e361068e1cd84c79",
     "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
-    "fetch_bytes": int(16755.88 * 2.0 * 1024),
-    "write_bytes": int(1807.69 * 1.0 * 1024),
+    "fetch_bytes": int(18474.0 * 2.0 * 1024),
+    "write_bytes": int(3053.9 * 1.0 * 1024),
     "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
