@@ -10,8 +10,10 @@
 //   assign  -- keys x centroids contraction on bf16 MFMA (fp32 accumulate);
 //              the nearest centroid is the argmax of k.mu - |mu|^2 / 2, folded
 //              into the accumulator initial value, ties to the lowest id;
-//   csr     -- per block, an LDS bitonic sort of (cluster, token) keys gives
-//              the membership lists, sizes and offsets (deterministic);
+//   csr     -- per block, the membership lists in (cluster, token) order,
+//              sizes and offsets: a stable counting sort in LDS for blocks of
+//              up to 1024 clusters, an LDS bitonic sort of (cluster, token)
+//              keys beyond (the same result, deterministic);
 //   mean    -- segmented mean of member rows, fixed summation order.
 #include <math.h>
 
@@ -76,18 +78,26 @@ __global__ __launch_bounds__(256) void kmeans_init_kernel(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Assignment, bf16: one workgroup = 256 tokens of one block (4 waves x 64).
-// MFMA 32x32x16 with A = 32 centroids (from LDS), B = 32 tokens (registers);
-// lane l holds token l % 32 and 16 centroid rows of the tile, so the running
-// argmax needs no cross-lane traffic until the end.  The accumulator starts at
-// -|mu|^2 / 2 (kept negated in LDS) so the MFMA result is the score itself.
+// Assignment, bf16: one workgroup = 64 kAsgWaves tokens of one block (64 per
+// wave).  MFMA 32x32x16 with A = 32 centroids (from LDS), B = 32 tokens
+// (registers); lane l holds token l % 32 and 16 centroid rows of the tile, so
+// the running argmax needs no cross-lane traffic until the end.  The
+// accumulator starts at -|mu|^2 / 2 (kept negated in LDS) so the MFMA result
+// is the score itself.
 // ---------------------------------------------------------------------------
-constexpr int kAsgChunk = 64;  // centroids staged per LDS round
+constexpr int kAsgWaves = 4;                     // waves per workgroup
+constexpr int kAsgThreads = kAsgWaves * kWave;
+constexpr int kAsgTokens = kAsgThreads;          // tokens per workgroup
+constexpr int kAsgChunk = 64;                    // centroids staged per LDS round
+constexpr int kAsgTiles = kAsgChunk / 32;        // centroid tiles per chunk
+constexpr int kAsgStage = kAsgChunk * 16 / kAsgThreads;  // 16-byte parts each thread stages
 constexpr int kAsgPad = 17;    // uint4 per staged row (16 + 1 to spread LDS banks)
+static_assert(kAsgChunk % 32 == 0 && (kAsgChunk * 16) % kAsgThreads == 0, "chunk staging");
 
-__global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* __restrict__ K, UnitGeom g,
-                                                                 BlockRange br, const bf16_t* __restrict__ kbar,
-                                                                 int32_t* __restrict__ assign, int tiles) {
+__global__ __launch_bounds__(kAsgThreads) void kmeans_assign_bf16_kernel(const bf16_t* __restrict__ K, UnitGeom g,
+                                                                         BlockRange br,
+                                                                         const bf16_t* __restrict__ kbar,
+                                                                         int32_t* __restrict__ assign, int tiles) {
     // two LDS buffers of staged centroids: chunk ch + 1 is loaded into
     // registers while chunk ch is on the matrix cores, then written to the
     // other buffer (one barrier per chunk)
@@ -99,7 +109,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
     const int unit = group / br.nb, j = group % br.nb;
     int p, L, c0, C;
     block_info(br, j, p, L, c0, C);
-    const int t0 = tile * 256;
+    const int t0 = tile * kAsgTokens;
     if (t0 >= L) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = lane >> 5, col = lane & 31;
@@ -117,19 +127,20 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
     int bidx[2] = {0x7fffffff, 0x7fffffff};
     const bf16_t* Cu = kbar + ((size_t)unit * g.Cmax + c0) * kHeadDim;
 
-    // thread t stages parts t + 256 m (m < 4) of a chunk: row (t + 256 m) / 16
-    auto fetch = [&](int ch, uint4 (&v)[4]) {
+    // thread t stages parts t + T m (m < kAsgStage, T threads) of a chunk:
+    // row (t + T m) / 16
+    auto fetch = [&](int ch, uint4 (&v)[kAsgStage]) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = threadIdx.x + m * 256;
+        for (int m = 0; m < kAsgStage; ++m) {
+            const int e = threadIdx.x + m * kAsgThreads;
             const int c = ch + (e >> 4);
             v[m] = c < C ? reinterpret_cast<const uint4*>(Cu + (size_t)c * kHeadDim)[e & 15] : make_uint4(0, 0, 0, 0);
         }
     };
-    auto stage = [&](int ch, const uint4 (&v)[4], int buf) {
+    auto stage = [&](int ch, const uint4 (&v)[kAsgStage], int buf) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = threadIdx.x + m * 256;
+        for (int m = 0; m < kAsgStage; ++m) {
+            const int e = threadIdx.x + m * kAsgThreads;
             const int row = e >> 4, part = e & 15;
             const int c = ch + row;
             cs[buf][row * kAsgPad + part] = v[m];
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
         }
     };
     {
-        uint4 v[4];
+        uint4 v[kAsgStage];
         fetch(0, v);
         stage(0, v, 0);
     }
@@ -151,13 +162,13 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
     int buf = 0;
     for (int ch = 0; ch < C; ch += kAsgChunk) {
         const bool more = ch + kAsgChunk < C;  // (uniform)
-        uint4 nv[4];
+        uint4 nv[kAsgStage];
         if (more) fetch(ch + kAsgChunk, nv);
         // accumulators start at -|mu|^2 / 2 of their centroid rows (the
         // first product takes them as its addend)
-        f32x16_t init[2];
+        f32x16_t init[kAsgTiles];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < kAsgTiles; ++cb)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 h = *reinterpret_cast<const float4*>(&hn[buf][cb * 32 + 8 * q4 + 4 * half]);
@@ -166,11 +177,11 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
                 init[cb][4 * q4 + 2] = h.z;
                 init[cb][4 * q4 + 3] = h.w;
             }
-        f32x16_t acc[2][2];
+        f32x16_t acc[kAsgTiles][2];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < kAsgTiles; ++cb) {
                 const uint4 a = cs[buf][(cb * 32 + col) * kAsgPad + 2 * s + half];
                 const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
@@ -186,7 +197,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_bf16_kernel(const bf16_t* _
         // takes 8 three-way max instructions; the row search runs only in
         // waves where some lane improved.
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < kAsgTiles; ++cb)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 const f32x16_t v = acc[cb][tb];
@@ -380,6 +391,109 @@ __global__ __launch_bounds__(kCsrThreads) void kmeans_csr_kernel(const int32_t* 
         su[c0 + c] = hi - lo;
     }
     if (threadIdx.x == 0) ou[c0 + C] = p + L;
+}
+
+
+// Membership lists by a stable counting sort, for blocks of at most
+// kCountMaxC clusters: the same (cluster, token) order, sizes and offsets as
+// the sort above, in three LDS passes.  Wave w owns tokens [w R 64, (w + 1)
+// R 64) of the block (R rounds of 64); it counts its tokens per cluster;
+// per cluster the counts are turned into bases (clusters in order, then
+// waves in order); then each wave places its rounds in order.  Inside a
+// round the 64 (cluster, lane) keys are sorted across the lanes (a bitonic
+// network over lane shuffles), so the lanes of one cluster are placed in
+// lane, that is token, order: rank = sorted position - first position of the
+// cluster, and the cluster's last lane moves its base on.
+constexpr int kCountMaxC = 1024;
+
+// Inclusive maximum over the 64 lanes of non-negative values (DPP as in
+// wave_inclusive_sum; lanes without a source take 0).
+__device__ __forceinline__ int wave_inclusive_max(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 -> rows 1, 3
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+__global__ __launch_bounds__(kCsrThreads) void kmeans_csr_count_kernel(const int32_t* __restrict__ assign,
+                                                                       UnitGeom g, BlockRange br,
+                                                                       int32_t* __restrict__ sizes,
+                                                                       int32_t* __restrict__ offsets,
+                                                                       int32_t* __restrict__ token_ids) {
+    constexpr int kWaves = kCsrThreads / kWave;
+    __shared__ uint32_t base[kWaves][kCountMaxC];  // counts, then bases
+    __shared__ int32_t placed[kMaxBlock];          // token ids in member order
+    __shared__ int wsum[kWaves];
+    const int j = blockIdx.x, unit = blockIdx.y;
+    int p, L, c0, C;
+    block_info(br, j, p, L, c0, C);
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int rounds = (L + kCsrThreads - 1) / kCsrThreads;
+    const int w0 = wave * kWave * rounds;  // the wave's first token
+    const int32_t* au = assign + (size_t)unit * g.Nmax + p;
+    // a token's local cluster; an id outside the block (no finite score won
+    // its argmax) counts as the last cluster, so every token is placed once
+    auto local = [&](int i) { return min((uint32_t)(au[i] - c0), (uint32_t)(C - 1)); };
+    for (int e = tid; e < kWaves * kCountMaxC; e += kCsrThreads) (&base[0][0])[e] = 0u;
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+        const int i = w0 + r * kWave + lane;
+        if (i < L) atomicAdd(&base[wave][local(i)], 1u);
+    }
+    __syncthreads();
+    // cluster tid: bases over the waves, then over the clusters
+    int total = 0;
+    if (tid < C) {
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t t = base[w][tid];
+            base[w][tid] = (uint32_t)total;
+            total += (int)t;
+        }
+    }
+    const int inc = wave_inclusive_sum(total);
+    if (lane == kWave - 1) wsum[wave] = inc;
+    __syncthreads();
+    int off = inc - total;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    int32_t* su = sizes + (size_t)unit * g.Cmax;
+    int32_t* ou = offsets + (size_t)unit * (g.Cmax + 1);
+    if (tid < C) {
+        for (int w = 0; w < kWaves; ++w) base[w][tid] += (uint32_t)off;
+        ou[c0 + tid] = p + off;
+        su[c0 + tid] = total;
+    }
+    if (tid == 0) ou[c0 + C] = p + L;
+    __syncthreads();
+    for (int r = 0; r < rounds; ++r) {
+        const int i = w0 + r * kWave + lane;
+        uint32_t key = i < L ? (local(i) << 6) | (uint32_t)lane : 0xFFFFFFFFu;
+#pragma unroll
+        for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+            for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                const uint32_t o = (uint32_t)__shfl_xor((int)key, jj, kWave);
+                const bool lower = ((lane & k) == 0) == ((lane & jj) == 0);
+                key = lower ? min(key, o) : max(key, o);
+            }
+        // keys past L (all ones) sort last and are not placed
+        const uint32_t c = key >> 6;
+        const uint32_t prev = (uint32_t)__shfl_up((int)key, 1, kWave);
+        const uint32_t next = (uint32_t)__shfl_down((int)key, 1, kWave);
+        const bool first = lane == 0 || (prev >> 6) != c;
+        const bool last = lane == kWave - 1 || (next >> 6) != c;
+        const int rank = lane - wave_inclusive_max(first ? lane : 0);
+        if (key != 0xFFFFFFFFu) {
+            const uint32_t b = base[wave][c];
+            placed[b + rank] = p + w0 + r * kWave + (int)(key & 63u);
+            if (last) base[wave][c] = b + (uint32_t)rank + 1u;
+        }
+    }
+    __syncthreads();
+    int32_t* tu = token_ids + (size_t)unit * g.Nmax;
+    for (int pos = tid; pos < L; pos += kCsrThreads) tu[p + pos] = placed[pos];
 }
 
 // ---------------------------------------------------------------------------
@@ -701,22 +815,29 @@ hipError_t launch_kmeans_init(int dtype, const void* K, UnitGeom g, BlockRange b
 
 hipError_t launch_kmeans_assign(int dtype, const void* K, UnitGeom g, BlockRange br, const void* kbar,
                                 int32_t* assign, hipStream_t st) {
-    const int tiles = (br.block_len + 255) / 256;
     const int groups = g.units * br.nb;
-    const int grid = pad_to_xcds(groups * tiles);
-    if (dtype == 1)
-        hipLaunchKernelGGL(kmeans_assign_bf16_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)K, g, br,
+    if (dtype == 1) {
+        const int tiles = (br.block_len + kAsgTokens - 1) / kAsgTokens;
+        const int grid = pad_to_xcds(groups * tiles);
+        hipLaunchKernelGGL(kmeans_assign_bf16_kernel, dim3(grid), dim3(kAsgThreads), 0, st, (const bf16_t*)K, g, br,
                            (const bf16_t*)kbar, assign, tiles);
-    else
+    } else {
+        const int tiles = (br.block_len + 255) / 256;
+        const int grid = pad_to_xcds(groups * tiles);
         hipLaunchKernelGGL(kmeans_assign_f32_kernel, dim3(grid), dim3(256), 0, st, (const float*)K, g, br,
                            (const float*)kbar, assign, tiles);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_kmeans_csr(const int32_t* assign, UnitGeom g, BlockRange br, int32_t* sizes, int32_t* offsets,
                              int32_t* token_ids, hipStream_t st) {
-    hipLaunchKernelGGL(kmeans_csr_kernel, dim3(br.nb, g.units), dim3(kCsrThreads), 0, st, assign, g, br, sizes,
-                       offsets, token_ids);
+    if (br.cfull <= kCountMaxC)
+        hipLaunchKernelGGL(kmeans_csr_count_kernel, dim3(br.nb, g.units), dim3(kCsrThreads), 0, st, assign, g, br,
+                           sizes, offsets, token_ids);
+    else
+        hipLaunchKernelGGL(kmeans_csr_kernel, dim3(br.nb, g.units), dim3(kCsrThreads), 0, st, assign, g, br, sizes,
+                           offsets, token_ids);
     return hipGetLastError();
 }
 
