@@ -17,6 +17,8 @@
 //   mean    -- segmented mean of member rows, fixed summation order.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -588,7 +590,10 @@ __global__ __launch_bounds__(256) void sorted_copy_kernel(const T* __restrict__ 
 // size-weighted Lloyd k-means over the block's non-empty fine key centroids
 // (weights = fine sizes), seeded like the token level with stream level 1;
 // then parents, member lists by (coarse, fine), sizes and value centroids
-// (size-weighted means of the stored fine value centroids).
+// (size-weighted means of the stored fine value centroids).  With bf16
+// storage the assignment runs on the matrix cores (32-point tiles against
+// the stored centroids, as the token level does); the weighted means take
+// one 16-lane row group per coarse cluster, members in point order.
 // ---------------------------------------------------------------------------
 constexpr int kCoarseMaxFine = 2048;  // fine clusters per block
 constexpr int kCoarseMaxD = 64;       // coarse clusters per block
@@ -604,6 +609,11 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
                                                            int32_t* __restrict__ cmembers) {
     __shared__ float cen[kCoarseMaxD][kHeadDim];  // stored (rounded) coarse centroids
     __shared__ float hn[kCoarseMaxD];
+    // bf16 storage: the stored centroids as matrix-core operands (rows padded
+    // as in the token-level assignment) and their negated half norms (-inf
+    // past the D centroids)
+    __shared__ uint4 cenb[std::is_same<T, float>::value ? 1 : kCoarseMaxD * kAsgPad];
+    __shared__ __align__(16) float hnn[kCoarseMaxD];
     __shared__ int32_t ids[kCoarseMaxFine];       // non-empty fine ids, increasing
     __shared__ int32_t loc[kCoarseMaxFine];       // coarse assignment of each point
     __shared__ uint16_t perm[kCoarseMaxFine];
@@ -712,16 +722,35 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
         }
         __syncthreads();
     };
-    // weighted mean of column cc of coarse cluster gg over its members (point
-    // order); den = 0 for an empty cluster
-    auto wmean = [&](const T* src, int gg, int cc, float& num, float& den) {
-        num = 0.f;
+    // weighted mean of coarse cluster gg over its members, in point order, by
+    // a 16-lane row group: lane li sums columns 8 li .. 8 li + 7 (num), every
+    // lane the weights (den; 0 for an empty cluster).  The members' rows load
+    // four at a time, so a round trip serves four members.
+    const int rgi = threadIdx.x >> 4, li = threadIdx.x & 15;
+    constexpr int kGroups = 256 / 16;
+    auto wmean8 = [&](const T* src, int gg, float (&num)[8], float& den) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] = 0.f;
         den = 0.f;
-        for (int k = bstart[gg]; k < bstart[gg + 1]; ++k) {
-            const int i = order[k];
-            const float w = wt[i];
-            num = fmaf(w, (float)src[(size_t)ids[i] * kHeadDim + cc], num);
-            den += w;
+        const int k0 = bstart[gg], k1 = bstart[gg + 1];
+        for (int kb = k0; kb < k1; kb += 4) {
+            float x[4][8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = order[min(kb + q, k1 - 1)];
+                const T* r = src + (size_t)ids[i] * kHeadDim + li * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[q][e] = (float)r[e];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (kb + q < k1) {
+                    const float w = wt[order[kb + q]];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) num[e] = fmaf(w, x[q][e], num[e]);
+                    den += w;
+                }
+            }
         }
     };
 
@@ -731,7 +760,72 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
             for (int e = 0; e < kHeadDim; ++e) ss = fmaf(cen[threadIdx.x][e], cen[threadIdx.x][e], ss);
             hn[threadIdx.x] = 0.5f * ss;
         }
+        if constexpr (!std::is_same<T, float>::value) {
+            // the stored centroids are bf16 values: their bits are the operand
+            for (int e = threadIdx.x; e < kCoarseMaxD * 16; e += 256) {
+                const int row = e >> 4, part = e & 15;
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                if (row < D) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        w[q] = (__float_as_uint(cen[row][part * 8 + 2 * q]) >> 16) |
+                               (__float_as_uint(cen[row][part * 8 + 2 * q + 1]) & 0xFFFF0000u);
+                }
+                cenb[row * kAsgPad + part] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
         __syncthreads();
+        if constexpr (!std::is_same<T, float>::value) {
+            if (threadIdx.x < kCoarseMaxD) hnn[threadIdx.x] = threadIdx.x < D ? -hn[threadIdx.x] : -INFINITY;
+            __syncthreads();
+            // assign each point to the best stored centroid (lowest id on
+            // ties) on the matrix cores, as the token-level assignment does:
+            // 32-point tiles per wave, the accumulator starts at -|mu|^2 / 2
+            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+            const int half = lane >> 5, col = lane & 31;
+            for (int t0 = wave * 32; t0 < m; t0 += 4 * 32) {
+                const int pt = t0 + col;
+                const uint4* row = reinterpret_cast<const uint4*>(kb_u + (size_t)ids[min(pt, m - 1)] * kHeadDim);
+                uint4 kr[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) kr[s] = row[2 * s + half];
+                f32x16_t acc[2];
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const float4 h = *reinterpret_cast<const float4*>(&hnn[cb * 32 + 8 * q4 + 4 * half]);
+                        acc[cb][4 * q4 + 0] = h.x;
+                        acc[cb][4 * q4 + 1] = h.y;
+                        acc[cb][4 * q4 + 2] = h.z;
+                        acc[cb][4 * q4 + 3] = h.w;
+                    }
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, cenb[(cb * 32 + col) * kAsgPad + 2 * s + half]),
+                            __builtin_bit_cast(bf16x8_t, kr[s]), acc[cb], 0, 0, 0);
+                // value r of tile cb is centroid cb 32 + 8 (r / 4) + 4 half + r % 4:
+                // increasing with (cb, r), so a strict comparison keeps the
+                // lowest id among equal maxima
+                float best = -INFINITY;
+                int bidx = 0x7fffffff;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (acc[cb][r] > best) {
+                            best = acc[cb][r];
+                            bidx = cb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        }
+                const float ov = shfl_xor_f(best, 32);
+                const int oi = shfl_xor_i(bidx, 32);
+                if (ov > best || (ov == best && oi < bidx)) bidx = oi;
+                if (half == 0 && pt < m) loc[pt] = bidx;
+            }
+        } else {
         // assign each point to the best stored centroid (lowest id on ties);
         // the point's row is held in registers, the centroids are LDS
         // broadcasts
@@ -753,28 +847,33 @@ __global__ __launch_bounds__(256) void coarse_build_kernel(UnitGeom g, CoarseRan
             }
             loc[i] = bi;
         }
+        }
         __syncthreads();
         bucket();
         // weighted means in point order; empty clusters keep their centroid
-        for (int e = threadIdx.x; e < D * kHeadDim; e += 256) {
-            const int gg = e / kHeadDim, cc = e % kHeadDim;
-            float num, den;
-            wmean(kb_u, gg, cc, num, den);
+        for (int gg = rgi; gg < D; gg += kGroups) {
+            float num[8], den;
+            wmean8(kb_u, gg, num, den);
             if (den > 0.f) {
-                const float mean = num / den;
-                cmu_u[(size_t)(g0 + gg) * kHeadDim + cc] = mean;
-                cen[gg][cc] = (float)(T)mean;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float mean = num[e] / den;
+                    cmu_u[(size_t)(g0 + gg) * kHeadDim + li * 8 + e] = mean;
+                    cen[gg][li * 8 + e] = (float)(T)mean;
+                }
             }
         }
         __syncthreads();
     }
     // stored coarse key centroids, sizes, value centroids
-    for (int e = threadIdx.x; e < D * kHeadDim; e += 256) {
-        const int gg = e / kHeadDim, cc = e % kHeadDim;
-        ck_u[(size_t)(g0 + gg) * kHeadDim + cc] = (T)cen[gg][cc];
-        float num, den;
-        wmean(vb_u, gg, cc, num, den);
-        cv_u[(size_t)(g0 + gg) * kHeadDim + cc] = den > 0.f ? (T)(num / den) : (T)0;
+    for (int gg = rgi; gg < D; gg += kGroups) {
+        float num[8], den;
+        wmean8(vb_u, gg, num, den);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ck_u[(size_t)(g0 + gg) * kHeadDim + li * 8 + e] = (T)cen[gg][li * 8 + e];
+            cv_u[(size_t)(g0 + gg) * kHeadDim + li * 8 + e] = den > 0.f ? (T)(num[e] / den) : (T)0;
+        }
     }
     // parents (-1 for empty fine clusters)
     int32_t* pu = parent + (size_t)unit * g.Cmax;
