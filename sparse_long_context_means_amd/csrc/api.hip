@@ -299,7 +299,7 @@ mpattn_status check_decode(const mpattn_params* p, const void* q, const void* k,
 //      copy until the process ends).  In host code the array's name is only
 //      a stand-in: its device address comes from hipGetSymbolAddress, once per
 //      device, and only that address reaches kernels.
-constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchBytes = size_t(64) << 20;
 constexpr int kScratchDevices = 64;
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
 

@@ -211,7 +211,7 @@ def test_noalloc_decode_validation():
     """The allocation-free decode checks every argument, and that the
     layout fits its device array, before anything is enqueued (every case
     below returns before the device is touched)."""
-    assert M.lib.mpattn_decode_noalloc_max_bytes() == 32 << 20
+    assert M.lib.mpattn_decode_noalloc_max_bytes() == 64 << 20
     p = _params()
     st = _fake_state(p, n_clustered=4096, n_clusters=256, n_blocks=1)
     cp = p.c()
@@ -225,10 +225,10 @@ def test_noalloc_decode_validation():
     assert na(4096, par=None) == M.ERR_INVALID_ARG
     assert na(0, s=_fake_state(p)) == M.ERR_INVALID_ARG
     assert na(4096, mode=M.MODE_PER_HEAD) == M.ERR_UNSUPPORTED
-    # 512 units of 2053 clusters need more than the 32 MiB array
+    # 512 units of 2053 clusters need more than the library's array
     big = _params(batch=64, n_q_heads=32, n_kv_heads=8)
     need = M.lib.mpattn_workspace_bytes(ctypes.byref(big.c()), big.max_clusters(), 0, M.OP_DECODE)
-    assert need > 32 << 20
+    assert need > M.lib.mpattn_decode_noalloc_max_bytes()
     sb = _fake_state(big, n_clustered=4096, n_clusters=256, n_blocks=1)
     cb = big.c()
     assert M.lib.mpattn_decode_noalloc(ctypes.byref(cb), FAKE, FAKE, FAKE, 4096, ctypes.byref(sb), 128, 0, FAKE,

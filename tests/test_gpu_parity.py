@@ -149,6 +149,39 @@ def test_hand_derived_example_on_gpu(golden_dir):
 # clustering, teacher-forced round by round
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("block,tpc", [(16384, 16), (16384, 8), (12000, 12)])
+def test_membership_lists_follow_the_assignment(block, tpc):
+    """Member lists, sizes and offsets against their definition on the GPU's
+    own assignment: each block's tokens in (cluster, token) order.  The
+    shapes take both list kernels: a counting sort up to 1024 clusters per
+    block (16384 / 16, and 12000 / 12 = 1000), the bitonic sort beyond
+    (16384 / 8 = 2048); the cache ends in a ragged block."""
+    mp = M()
+    B, Hq, Hkv, N = 1, 4, 2, 20000
+    w = small_workload(B, Hq, Hkv, N, N // 16, outliers=4, index=77)
+    K, V, _ = workloads.make_cache(w)
+    p = mp.Params(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, capacity_tokens=N, tokens_per_centroid=tpc,
+                  cluster_block=block, build_iters=2, seed=5)
+    st = mp.ClusterState(p, DEV, sorted_copy=False)
+    mp.build_clusters(p, K.to(DEV), V.to(DEV), N, st)
+    torch.cuda.synchronize()
+    cfull = -(-block // tpc)
+    for h in range(Hkv):
+        a = st.assign[0, h, :N].cpu().numpy()
+        tids = st.token_ids[0, h, :N].cpu().numpy()
+        sizes = st.sizes[0, h].cpu().numpy()
+        offs = st.offsets[0, h].cpu().numpy()
+        for j, p0 in enumerate(range(0, N, block)):
+            L = min(block, N - p0)
+            c0, C = j * cfull, -(-L // tpc)
+            loc = a[p0:p0 + L] - c0
+            assert loc.min() >= 0 and loc.max() < C, (h, j)
+            counts = np.bincount(loc, minlength=C)
+            np.testing.assert_array_equal(sizes[c0:c0 + C], counts)
+            np.testing.assert_array_equal(offs[c0:c0 + C], p0 + np.concatenate([[0], np.cumsum(counts)[:-1]]))
+            np.testing.assert_array_equal(tids[p0:p0 + L], p0 + np.lexsort((np.arange(L), loc)))
+
+
 @pytest.mark.parametrize("dt_name", ["bf16", "fp32"])
 def test_build_rounds_match_oracle(dt_name):
     mp = M()

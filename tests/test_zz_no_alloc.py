@@ -73,3 +73,17 @@ def test_noalloc_split_and_hierarchical_paths():
     _check(mph, wh, meansh, ph, sth, Kdh, Vdh, 1, 512)
     _check(mph, wh, meansh, ph, sth, Kdh, Vdh, 2, 300)
     _check(mp, w, means, p, st, Kd, Vd, 3, 100)
+
+
+def test_noalloc_serves_the_batch16_32k_layout():
+    """The layout of a Qwen3-8B-shaped layer at batch 16 and 32768 tokens
+    (128 units of 2048 clusters, about 39 MiB of decode workspace) fits the
+    library's array: the same bits as mpattn_decode on two steps."""
+    mp, w, means, p, st, Kd, Vd = _case(16, 32, 8, 32768)
+    assert p.decode_stages() == ["unit"]
+    import ctypes
+    need = mp.lib.mpattn_workspace_bytes(ctypes.byref(p.c()), st.capacity_clusters, st.capacity_coarse,
+                                         mp.OP_DECODE)
+    assert 32 << 20 < need <= mp.lib.mpattn_decode_noalloc_max_bytes()
+    _check(mp, w, means, p, st, Kd, Vd, 0, 1638)
+    _check(mp, w, means, p, st, Kd, Vd, 1, 1638)
