@@ -465,9 +465,7 @@ __device__ __forceinline__ void lds_barrier() {
 // s_red, which may alias LDS data that is dead once every wave got here).
 // With one workgroup per unit (R = 1) it writes the normalised output outu
 // [G][d].  Otherwise each of the R workgroups counts itself in on the unit's
-// arrival counter *xcount as it enters (or has done so earlier, counted_in:
-// then *s_flag already holds whether it arrived last); all but the last to
-// arrive post their partial (per head the state m, l and the 128 sums) as words (tag <<
+// arrival counter *xcount as it enters; all but the last to arrive post their partial (per head the state m, l and the 128 sums) as words (tag <<
 // 32 | value) into their slot of xp [R][G][d + 2] and are done.  The last
 // one reads the others' partials -- polling a word that still carries
 // another call's tag for at most wait_ticks of the 100 MHz constant clock (a
@@ -479,7 +477,7 @@ template <int G, int NW>
 __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][kHeadDim + 2], int* s_flag,
                                             float* outu, uint64_t* xp, uint64_t* xcount, uint32_t tag,
                                             uint32_t* epoch, uint32_t* status, int R, int rep,
-                                            uint64_t wait_ticks, bool counted_in = false) {
+                                            uint64_t wait_ticks) {
     constexpr int kThreads = NW * kWave;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int rg = lane >> 4, li = lane & 15;
@@ -488,7 +486,7 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     // round trip runs beside the combine below (the replica that sees R - 1
     // arrivals before its own merges; it finds the others' partials by their
     // tags, polling while a partner still stores them)
-    if (R > 1 && !counted_in && tid == 0) {
+    if (R > 1 && tid == 0) {
         const uint64_t arrivals = __hip_atomic_fetch_add(xcount, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = arrivals + 1 == (uint64_t)R;  // read after the barriers below
     }

@@ -509,17 +509,6 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
                     __hip_atomic_store(xu + (size_t)r2 * a.Cmax + i, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // The replica counts itself in on the unit's arrival counter now, behind
-    // its key words: the round trip runs beside the value stream and the
-    // exact rows instead of at the end of the step.  The replica that sees
-    // R - 1 arrivals before its own merges the partials (finish_step); every
-    // replica it waits for there has started.  Wave 4 counts in: its value
-    // rows go out behind its key stores anyway.
-    if (R > 1 && tid == kCutWaves * kWave) {
-        const uint64_t arrivals =
-            __hip_atomic_fetch_add(a.xcount + unit, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_misc[0] = arrivals + 1 == (uint64_t)R;  // read after the barriers of finish_step
-    }
     if (a.pseudo) {
 #pragma unroll
         for (int g = 0; g < G; ++g) st.m[g] = Mref[g];
@@ -879,10 +868,15 @@ __global__ __launch_bounds__(kUnitThreads) void unit_decode_kernel(UnitArgs a) {
             }
         }
     }
+    // The replicas count in on the unit's arrival counter as they enter the
+    // combine, so the one that merges is the last to finish its rows: the
+    // others' partials are posted (or nearly) when it reads them.  Counting
+    // in right after the score pass instead picked the replica that finished
+    // first about a third of the time, which then waited for its partner's
+    // combine and post (measured 0.3-0.7 us slower per step).
     finish_step<G, kUnitWaves>(st, s_red, s_misc, a.out + ((size_t)b * a.Hq + (size_t)h * G) * kHeadDim,
                                a.xpart + (size_t)unit * R * G * (kHeadDim + 2), a.xcount + unit, tag,
-                               R > 1 ? a.xepoch + unit : nullptr, a.status, R, rep, kPartialWaitTicks,
-                               /*counted_in=*/true);
+                               R > 1 ? a.xepoch + unit : nullptr, a.status, R, rep, kPartialWaitTicks);
 }
 
 // One replica per unit only once the units alone give a workgroup to every CU
