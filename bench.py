@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+HBM_TARGET_FRAC = 0.60           # decode target: this fraction of peak on the bytes read
 DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 
 # HBM bytes per launch of the one-launch decode kernels, from two rocprofv3
@@ -491,6 +492,10 @@ def main():
         "effective_frac_of_hbm_peak": round(eff_gbps / HBM_PEAK_GBPS, 4),
         "hbm_read_probe_GBps": round(probe_gbps, 1),
         "effective_frac_of_read_probe": round(eff_gbps / probe_gbps, 4),
+        # the target: 60% of HBM peak on the bytes the step reads
+        "hbm_target": {"frac": HBM_TARGET_FRAC,
+                       "us_per_step": round(float(byts.mean()) / (HBM_TARGET_FRAC * HBM_PEAK_GBPS * 1e3), 2),
+                       "met": bool(eff_gbps >= HBM_TARGET_FRAC * HBM_PEAK_GBPS)},
         "algorithmic_MB_per_step": round(float(byts.mean()) / 1e6, 2),
         "warm_us_per_step": round(warm_us, 2),
         "cold_back_to_back_rounds_us": [round(x, 2) for x in b2b_rounds],
