@@ -493,34 +493,46 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
     // ---- combine the row groups, 4 per wave, then the waves through LDS (in
     //      wave order).  When the row groups of the wave share each head's
     //      reference exponent (the exact-row steps keep one per wave) their
-    //      sums just add: pairs of rows by v_permlane16_swap, then pairs of
-    //      halves by v_permlane32_swap, the same additions in the same order
-    //      as the general merge below, which shuffles through LDS. ----------
+    //      sums just add, four values at a time: v_permlane16_swap of two
+    //      values adds pairs of rows of both (a in rows 0 and 2, b in rows 1
+    //      and 3), v_permlane32_swap of two such results adds the halves, and
+    //      row group k ends up with the wave's total of the k-th value.  These
+    //      are the additions of the general merge below, in its order, which
+    //      shuffles through LDS and leaves every total in row group 0. -------
     bool uniform = true;
 #pragma unroll
     for (int g = 0; g < G; ++g)
         uniform = uniform && __builtin_amdgcn_ballot_w64(st.m[g] != __int_as_float(__builtin_amdgcn_readlane(
                                                              __float_as_int(st.m[g]), 0))) == 0;
+    auto quad_sum = [](float a, float b, float c, float d) {
+        const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        const float s1 = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+        const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(d), false, false);
+        const float s2 = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+        const auto r3 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1), __float_as_uint(s2), false, false);
+        return __uint_as_float(r3[0]) + __uint_as_float(r3[1]);
+    };
+    constexpr int kLq = G % 4 == 0 ? G / 4 : 0;  // quadruples of heads for the weight sums
+    float qacc[G][2];                             // row group rg: dimension li * 8 + 4 q + rg
+    float ql[kLq > 0 ? kLq : 1];                  // row group rg: head 4 j + rg
     if (uniform) {  // (wave-uniform)
-        auto add16 = [](float& x) {
-            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-            x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        };
-        auto add32 = [](float& x) {
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-            x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-        };
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            add16(st.l[g]);
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add16(st.acc[g][e]);
-        }
+            for (int q = 0; q < 2; ++q)
+                qacc[g][q] = quad_sum(st.acc[g][4 * q], st.acc[g][4 * q + 1], st.acc[g][4 * q + 2], st.acc[g][4 * q + 3]);
+        if constexpr (kLq > 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            add32(st.l[g]);
+            for (int j = 0; j < kLq; ++j)
+                ql[j] = quad_sum(st.l[4 * j], st.l[4 * j + 1], st.l[4 * j + 2], st.l[4 * j + 3]);
+        } else {  // one or two heads: the weight sums of every row group, one at a time
 #pragma unroll
-            for (int e = 0; e < 8; ++e) add32(st.acc[g][e]);
+            for (int g = 0; g < G; ++g) {
+                auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.l[g]), __float_as_uint(st.l[g]), false, false);
+                st.l[g] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                r = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l[g]), __float_as_uint(st.l[g]), false, false);
+                st.l[g] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            }
         }
     } else {
 #pragma unroll
@@ -537,7 +549,28 @@ __device__ __forceinline__ void finish_step(SoftState<G>& st, float (*s_red)[G][
         }
     }
     lds_barrier();  // the big region is free
-    if (rg == 0) {
+    if (uniform) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) s_red[wave][g][li * 8 + 4 * q + rg] = qacc[g][q];
+        if (li == 0) {
+            if constexpr (kLq > 0) {
+                if (rg == 0) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) s_red[wave][g][kHeadDim] = st.m[g];
+                }
+#pragma unroll
+                for (int j = 0; j < kLq; ++j) s_red[wave][4 * j + rg][kHeadDim + 1] = ql[j];
+            } else if (rg == 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    s_red[wave][g][kHeadDim] = st.m[g];
+                    s_red[wave][g][kHeadDim + 1] = st.l[g];
+                }
+            }
+        }
+    } else if (rg == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
 #pragma unroll
