@@ -50,23 +50,23 @@ DEFAULT_WORKLOAD = "qwen3-8b-layer-b16-32k-s95"
 # the listed files, in that order); otherwise reported null.
 UNIT_TRAFFIC = {  # per centroid format
     "stored": {
-        "sources_sha256": "311a6d56c0ff0a113a4032e40c9a504b4e65786fbaa61d93e18f0868dc1ab754",
-        "fetch_bytes": int(122937.9 * 2.0 * 1024),
+        "sources_sha256": "e16e2b42a822fec0a3ac0257b7f51845c7ea3aeefdd3784d3767deb7ae92b4b9",
+        "fetch_bytes": int(122922.2 * 2.0 * 1024),
         "write_bytes": int(3476.0 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
     "fp8": {
-        "sources_sha256": "311a6d56c0ff0a113a4032e40c9a504b4e65786fbaa61d93e18f0868dc1ab754",
-        "fetch_bytes": int(90263.7 * 2.0 * 1024),
+        "sources_sha256": "e16e2b42a822fec0a3ac0257b7f51845c7ea3aeefdd3784d3767deb7ae92b4b9",
+        "fetch_bytes": int(90231.6 * 2.0 * 1024),
         "write_bytes": int(3475.9 * 1.0 * 1024),
         "profile": "profiles/decode_b16_32k_s95_unit_hbm_counters.md",
     },
 }
 HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
-    "sources_sha256": "a5814c3e68a41fdbfac623ceea95cc684d57d7c210504b3dfa9678181765be17",
+    "sources_sha256": "1a9c8bf5cb34aa2b22280bbad6ae7b33bf55d0898185ffbb5b4633987cb13101",
     "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
-    "fetch_bytes": int(18459.9 * 2.0 * 1024),
-    "write_bytes": int(3054.0 * 1.0 * 1024),
+    "fetch_bytes": int(18373.0 * 2.0 * 1024),
+    "write_bytes": int(3054.5 * 1.0 * 1024),
     "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
