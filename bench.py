@@ -63,10 +63,10 @@ UNIT_TRAFFIC = {  # per centroid format
     },
 }
 HIER_TRAFFIC = {  # the one-launch hierarchical decode, 131072 tokens, batch 4
-    "sources_sha256": "1a9c8bf5cb34aa2b22280bbad6ae7b33bf55d0898185ffbb5b4633987cb13101",
+    "sources_sha256": "43b09a4a57c30a4567bb7a0f2e94b1077204e769155c48d927a7bd9e4453cc6c",
     "files": ("hier.hip", "attn.hpp", "device.hpp", "kernels.hpp"),
-    "fetch_bytes": int(18373.0 * 2.0 * 1024),
-    "write_bytes": int(3054.5 * 1.0 * 1024),
+    "fetch_bytes": int(18356.8 * 2.0 * 1024),
+    "write_bytes": int(3054.0 * 1.0 * 1024),
     "profile": "profiles/decode_b4_128k_hier_kernel.md",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16

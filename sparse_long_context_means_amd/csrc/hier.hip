@@ -64,6 +64,32 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int& tot, int* lds) {
     return base + inc - v;
 }
 
+// Exclusive scans of two counters over the workgroup in thread order, with
+// one barrier each way (`lds`: 2 kHWaves ints); the totals in tot.
+__device__ __forceinline__ int2 block_exclusive_sum2(int2 v, int2& tot, int* lds) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int ix = wave_inclusive_sum(v.x), iy = wave_inclusive_sum(v.y);
+    if (lane == kWave - 1) {
+        lds[2 * wave] = ix;
+        lds[2 * wave + 1] = iy;
+    }
+    lds_barrier();
+    int bx = 0, by = 0, tx = 0, ty = 0;
+#pragma unroll
+    for (int w = 0; w < kHWaves; ++w) {
+        const int x = lds[2 * w], y = lds[2 * w + 1];
+        if (w < wave) {
+            bx += x;
+            by += y;
+        }
+        tx += x;
+        ty += y;
+    }
+    lds_barrier();  // lds may be reused right after
+    tot = make_int2(tx, ty);
+    return make_int2(bx + ix - v.x, by + iy - v.y);
+}
+
 // Budget cut over n items by the whole workgroup: the longest prefix of the
 // non-empty items in (key desc, id asc) order whose sizes sum to at most
 // `budget`.  A pass over equal-width value bins usually settles it; else four
@@ -427,10 +453,11 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
         const uint32_t shifted = cbits << ((tid * kCItems) & 31);
         atomicOr(&s_cmask[(tid * kCItems) >> 5], shifted);
     }
-    int ncand_t = __popc(cbits), ncand;
-    const int k0 = block_exclusive_sum(ncand_t, ncand, s_scan);
-    int F;
-    int m0 = block_exclusive_sum(nmem, F, s_scan + 16);
+    int2 tot2;
+    const int2 ex2 = block_exclusive_sum2(make_int2(__popc(cbits), nmem), tot2, s_scan);
+    const int k0 = ex2.x, ncand = tot2.x;
+    int F = tot2.y;
+    int m0 = ex2.y;
     // F <= candidate budget <= kHierMaxF for any state the build wrote: every
     // candidate fine cluster holds at least one of the candidates' tokens
     F = min(F, kHierMaxF);
@@ -511,9 +538,10 @@ __global__ __launch_bounds__(kHThreads) void hier_decode_kernel(HierArgs a) {
 #pragma unroll
     for (int j = 0; j < kFItems; ++j)
         if ((fbits >> j) & 1u) rows_t += s_fsz[tid * kFItems + j];
-    int nsel, E;
-    const int sk0 = block_exclusive_sum(__popc(fbits), nsel, s_scan);
-    int ro = block_exclusive_sum(rows_t, E, s_scan + 16);
+    int2 tot4;
+    const int2 ex4 = block_exclusive_sum2(make_int2(__popc(fbits), rows_t), tot4, s_scan);
+    const int sk0 = ex4.x, nsel = tot4.x, E = tot4.y;
+    int ro = ex4.y;
     {
         int k = sk0;
 #pragma unroll
